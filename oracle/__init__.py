@@ -1,0 +1,29 @@
+"""CPU fp64 oracle for mixed-head attention over a block-paged, per-head circular KV cache.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The library (``kv_cache_sparsity_amd``) never imports it and
+shares no code with it: no kernels, headers, helpers, tables or pre/post-processing. The oracle is
+slow on purpose; every function follows the definition on the pages step by step.
+
+Sources (the four web pages on KV-cache sparsity):
+  * DuoAttention README ("DuoAttention: efficient long-context LLM inference with retrieval and
+    streaming heads"), abstract and quick-start: retrieval heads keep full attention over all
+    tokens; streaming heads keep only the attention sinks and the recent tokens.
+  * vLLM issue "Could you support Attention Sink?": block-paged cache, the circular-buffer slot
+    tables (with and without in-place sinks) and option 3 (sinks in their own block, a ring for the
+    streamed tokens).
+  * transformers PR "[WIP] Dynamic length in static cache", description: a new position only needs
+    attention against the positions up to itself, not the whole static cache.
+  * vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models", review thread: the softmax
+    scale is applied in fp32 to the q.k product.
+
+Parity status of each function is stated in its docstring; every function here is pinned by tests
+in ``tests/test_oracle_*.py`` (worked tables, brute force, a library cross-check, closed forms and
+invariants).
+"""
+from .cache import (slot_of, table_position, append, gather, pool_shapes, to_f64,
+                    new_pools, ring_capacity)
+from .attention import visible_positions, attend_row, attend, attend_paged
+
+__all__ = ["slot_of", "table_position", "append", "gather", "pool_shapes", "to_f64", "new_pools",
+           "ring_capacity", "visible_positions", "attend_row", "attend", "attend_paged"]

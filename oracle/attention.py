@@ -1,0 +1,95 @@
+"""Oracle: mixed-head attention restricted to each head's visible positions, in float64.
+
+Test infrastructure only (see the package docstring).
+
+What a query at position p of sequence b, q head hq sees (h = hq // (q_heads / kv_heads) is its kv
+head; a contiguous group of q heads shares one kv head, the usual grouped-query convention, which the
+pages do not spell out -- parity unpinned by the pages for this mapping, pinned here only by the
+"repeat kv heads" invariant):
+  * every head: only positions j <= p of its own sequence (transformers PR "[WIP] Dynamic length in
+    static cache", description: attend to the positions up to the current one, not the whole cache);
+  * a retrieval head: all of them (DuoAttention README, abstract);
+  * a streaming head: the attention sinks j < sink and the recent window p - j < recent, each
+    position once (DuoAttention README, abstract and quick-start's sink_size / recent_size; vLLM issue
+    "Could you support Attention Sink?", the sink tokens kept beside the streamed ones). The window
+    counts the query's own position.
+Query row i of a call with q_len rows sits at position seq_len - q_len + i: the new tokens are in the
+cache when they are attended (transformers PR, cache update then attention).
+
+Scores are scale * (q . k) with the scale applied to the dot product (vLLM DualChunkAttention PR,
+review thread on applying the softmax scale in fp32 rather than folding it into q). The output is
+softmax-weighted V; an empty visible set (only possible for a row with p < 0) gives 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .cache import to_f64, gather
+
+
+def visible_positions(p: int, *, retrieval: bool, sink: int, recent: int) -> np.ndarray:
+    """Sorted logical positions a query at position p may attend to."""
+    if p < 0:
+        return np.zeros(0, dtype=np.int64)
+    j = np.arange(p + 1, dtype=np.int64)
+    if retrieval:
+        return j
+    return j[(j < sink) | (p - j < recent)]
+
+
+def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of one query over the given rows (all float64). Empty rows -> zeros."""
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1] if V.ndim == 2 else q.shape[0], dtype=np.float64)
+    s = scale * (K @ q)
+    m = s.max()
+    w = np.exp(s - m)
+    return (w @ V) / w.sum()
+
+
+def attend(q, k, v, seq_lens, retrieval_mask, *, sink, recent, scale, dtype, rows=None):
+    """Reference output for every (or the selected) query rows, float64.
+
+    q: [B][q_len][Hq][D] stored elements; k, v: logical caches [B][Hkv][>= max len][D] stored
+    elements (position j of head h of sequence b at k[b, h, j]); seq_lens: [B] valid lengths
+    including the query rows. rows: optional iterable of (b, i, hq); by default every row.
+    Returns out [B][q_len][Hq][D] float64 (unselected rows stay NaN).
+    """
+    B, q_len, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.full((B, q_len, Hq, D), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, i, hq) for b in range(B) for i in range(q_len) for hq in range(Hq)]
+    cache = {}
+    for b, i, hq in rows:
+        h = hq // G
+        p = int(seq_lens[b]) - q_len + i
+        J = visible_positions(p, retrieval=bool(retrieval_mask[h]), sink=sink, recent=recent)
+        key = (b, h)
+        if key not in cache:
+            cache = {key: (to_f64(k[b, h], dtype), to_f64(v[b, h], dtype))}
+        Kf, Vf = cache[key]
+        out[b, i, hq] = attend_row(to_f64(q[b, i, hq], dtype), Kf[J], Vf[J], scale)
+    return out
+
+
+def attend_paged(q, k_pool, v_pool, table, seq_lens, retrieval_mask, *, sink, recent, scale,
+                 dtype, block_size, ring_blocks, rows=None):
+    """Same as ``attend`` but reads K and V out of the paged pools through the oracle's own layout."""
+    B, q_len, Hq, D = q.shape
+    Hkv = table.shape[1]
+    G = Hq // Hkv
+    out = np.full((B, q_len, Hq, D), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, i, hq) for b in range(B) for i in range(q_len) for hq in range(Hq)]
+    for b, i, hq in rows:
+        h = hq // G
+        ret = bool(retrieval_mask[h])
+        p = int(seq_lens[b]) - q_len + i
+        J = visible_positions(p, retrieval=ret, sink=sink, recent=recent)
+        Ks, Vs = gather(k_pool, v_pool, table, b, h, J, retrieval=ret, sink=sink,
+                        block_size=block_size, ring_blocks=ring_blocks)
+        out[b, i, hq] = attend_row(to_f64(q[b, i, hq], dtype), to_f64(Ks, dtype),
+                                   to_f64(Vs, dtype), scale)
+    return out
