@@ -1,0 +1,176 @@
+/*
+ * duo_attn.h -- C ABI of libduoattn, mixed-head attention over a block-paged, per-head circular KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The problem (four web pages on KV-cache sparsity):
+ *   - DuoAttention README, abstract and quick-start: some kv heads ("retrieval heads") attend to every
+ *     cached token; the others ("streaming heads") keep and attend only the first sink_size tokens
+ *     (attention sinks) and the most recent recent_size tokens. The per-head split, sink_size and
+ *     recent_size are exactly the arguments of its enable call.
+ *   - vLLM issue "Could you support Attention Sink?", sh1ng's comment: a block-paged cache in which a
+ *     streaming head's sink tokens sit in block(s) of their own and the other tokens cycle through a
+ *     circular buffer (option 3); its worked tables give the ring index (t - sink) mod ring size.
+ *   - transformers PR "[WIP] Dynamic length in static cache", description: a query only needs the
+ *     positions up to its own, not the whole allocated cache; lengths therefore live in a device
+ *     array read by the kernels, never on the host, and no launch shape depends on them.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous arrays, 16-byte aligned, owned by
+ *     the caller. The library never allocates, frees, synchronizes, or reads device data on the host.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL = the default stream).
+ *     Buffers must stay alive until the queued work has finished.
+ *   - `head_is_retrieval` is a HOST array of num_kv_heads bytes (1 = retrieval head, 0 = streaming
+ *     head). It is read during the call; the caller may free it on return.
+ *   - q head hq uses kv head hq / (num_q_heads / num_kv_heads) (contiguous grouping).
+ *   - On any error the call returns a non-zero status and launches nothing. A failed kernel launch
+ *     returns DUO_ERR_HIP.
+ *   - Element types: DUO_F32 (float), DUO_F16 (IEEE half), DUO_BF16 (bfloat16). Every tensor of one
+ *     call (q, pools, new tokens, out) has the call's dtype. Outputs are rounded to nearest even.
+ *
+ * Cache layout (shared by all three calls):
+ *   k_pool [num_blocks][block_size][head_dim]   (a K page is token-major)
+ *   v_pool [num_blocks][head_dim][block_size]   (a V page is channel-major, so that 8 consecutive
+ *                                                tokens of one channel are one 16-byte load)
+ *   block_table [batch][num_kv_heads][max_blocks_per_head] int32: physical page of each table column.
+ *   Each (sequence b, kv head h) owns the row block_table[b][h]. Slot s of a row is row
+ *   s % block_size of page block_table[b][h][s / block_size]. Logical position t is stored at:
+ *     retrieval head: slot t                       (needs t < max_blocks_per_head * block_size)
+ *     streaming head: slot t                       if t < sink_size (the sink pages)
+ *                     slot SB*block_size + (t - sink_size) mod (ring_blocks*block_size) otherwise,
+ *                     with SB = ceil(sink_size / block_size) sink pages in front of the ring.
+ *   A streaming head uses table columns [0, SB + ring_blocks); a retrieval head uses every column.
+ *   Page ids outside [0, num_blocks) are clamped into range by the kernels (wrong results, no fault).
+ */
+#ifndef DUO_ATTN_H
+#define DUO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUO_ATTN_ABI_VERSION 1
+
+typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
+
+typedef enum {
+  DUO_OK = 0,
+  DUO_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, non-positive size, bad mask value, aliasing */
+  DUO_ERR_UNSUPPORTED = 2,   /* head_dim not in {64,128,256}, block_size not supported, group > 16 */
+  DUO_ERR_CAPACITY = 3,      /* ring or table too small for the requested window / chunk */
+  DUO_ERR_WORKSPACE = 4,     /* decode workspace missing or smaller than the size query says */
+  DUO_ERR_HIP = 5            /* a HIP launch failed */
+} duo_status_t;
+
+/*
+ * kv_append_circular -- write t_new new tokens per sequence into the paged cache.
+ *
+ * Source: vLLM issue "Could you support Attention Sink?" (the circular-buffer tables and option 3)
+ * and transformers PR "[WIP] Dynamic length in static cache" (the cache is updated at the new
+ * positions before they are attended).
+ *
+ *   k_pool, v_pool      device, layout above; written.
+ *   block_table         device int32 [batch][num_kv_heads][max_blocks_per_head].
+ *   k_new, v_new        device [batch][t_new][num_kv_heads][head_dim] of dtype.
+ *   seq_lens_before     device int32 [batch]: tokens already written; token i of sequence b goes to
+ *                       position seq_lens_before[b] + i.
+ *   seq_lens_after      device int32 [batch] or NULL: receives seq_lens_before[b] + t_new. Must not
+ *                       alias seq_lens_before.
+ *   head_is_retrieval   host uint8 [num_kv_heads].
+ *   block_size          power of two in [1, 256].
+ * Semantics: the copy is bit-exact. If several new tokens of one streaming head land on the same
+ * ring slot, the newest one is what the slot holds afterwards (older ones are not written). Tokens
+ * of a retrieval head at positions >= max_blocks_per_head*block_size are not written.
+ * Errors: INVALID_ARG (pointers, sizes, aliasing), UNSUPPORTED (head_dim, dtype, block_size),
+ *         CAPACITY (streaming heads present and SB + ring_blocks > max_blocks_per_head or
+ *         ring_blocks < 1).
+ */
+int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_table,
+                           int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
+                           const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                           int32_t* seq_lens_after, int32_t batch, int32_t t_new,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                           const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                           int32_t ring_blocks, void* stream);
+
+/*
+ * duo_attn_decode_workspace_size -- bytes of device workspace duo_attn_decode needs for these static
+ * sizes (split_tokens as passed to duo_attn_decode; 0 = the library's choice). The caller zero-fills
+ * the workspace once after allocating it; every completed decode call leaves it ready for the next.
+ * Returns 0 for invalid sizes.
+ */
+size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_blocks_per_head,
+                                      int32_t block_size, int32_t split_tokens);
+
+/*
+ * duo_attn_decode -- one new query token per sequence attends over its head's visible positions.
+ *
+ * Source: DuoAttention README (retrieval heads: all positions; streaming heads: sinks + recent
+ * window); transformers PR "[WIP] Dynamic length in static cache" (only positions < seq_len);
+ * vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models", review thread (partial attentions
+ * merge through their log-sum-exp; the softmax scale is applied in fp32 to q.k).
+ *
+ *   q                   device [batch][num_q_heads][head_dim] of dtype.
+ *   seq_lens            device int32 [batch]: valid tokens INCLUDING the one being decoded (append
+ *                       it first). The query sits at position seq_lens[b] - 1.
+ *   softmax_scale       multiplies q.k in fp32 (1/sqrt(head_dim) for standard attention).
+ *   out                 device [batch][num_q_heads][head_dim] of dtype.
+ *   workspace           device, >= duo_attn_decode_workspace_size(...) bytes, zero-filled once.
+ *   split_tokens        keys per split-K work item: 0 = library's choice, else a multiple of 128.
+ * Visible positions of the query at p = seq_lens[b] - 1: retrieval head j in [0, p]; streaming head
+ * j < sink_size or p - j < recent_size (within [0, p]). seq_lens[b] = 0 yields a zero output row.
+ * Retrieval lengths above max_blocks_per_head*block_size are clamped to it.
+ * Calls sharing one workspace must not run concurrently.
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16,
+ *         num_q_heads/num_kv_heads > 16), CAPACITY (streaming heads present and
+ *         ring_blocks*block_size < recent_size or SB + ring_blocks > max_blocks_per_head),
+ *         WORKSPACE.
+ */
+int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                        int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                        int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/*
+ * duo_attn_prefill -- q_len query rows per sequence (a prompt chunk already appended to the cache)
+ * attend causally over their head's visible positions.
+ *
+ * Source: as for duo_attn_decode; chunked prefill is the DualChunkAttention PR's recommended mode and
+ * the DuoAttention README's prefill-chunk-size trade-off (efficiency section).
+ *
+ *   q                   device [batch][q_len][num_q_heads][head_dim] of dtype.
+ *   seq_lens            device int32 [batch]: valid tokens AFTER the chunk was appended; query row
+ *                       i sits at position seq_lens[b] - q_len + i (rows at negative positions
+ *                       produce zeros).
+ *   out                 device [batch][q_len][num_q_heads][head_dim] of dtype.
+ * Visible set of row i at position p: as for decode. Streaming heads need
+ * ring_blocks*block_size >= recent_size + q_len - 1 so that the oldest key of the first row is still
+ * in the ring.
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16),
+ *         CAPACITY.
+ */
+int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                         int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                         int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                         float softmax_scale, void* out, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* duo_status_string(int32_t status);
+
+/* DUO_ATTN_ABI_VERSION of the loaded library. */
+int32_t duo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUO_ATTN_H */

@@ -1,0 +1,288 @@
+// C ABI of libduoattn: argument validation, static work planning and kernel launches.
+// Every check runs before any HIP call, so invalid calls return an error without touching a device.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/duo_attn.h"
+#include "duo_kernels.h"
+
+namespace {
+
+using namespace duo;
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int32_t x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool dtype_ok(int32_t t) { return t == DUO_F32 || t == DUO_F16 || t == DUO_BF16; }
+int elem_bytes(int32_t t) { return t == DUO_F32 ? 4 : 2; }
+int32_t sink_blocks(int32_t sink, int32_t bs) { return (sink + bs - 1) / bs; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Mask -> lists of retrieval / streaming kv heads. Returns false on a value other than 0/1.
+bool split_heads(const uint8_t* mask, int32_t hkv, uint8_t* ret, int32_t* n_ret, uint8_t* str,
+                 int32_t* n_str) {
+  *n_ret = *n_str = 0;
+  for (int32_t h = 0; h < hkv; ++h) {
+    if (mask[h] > 1) return false;
+    if (mask[h]) ret[(*n_ret)++] = (uint8_t)h;
+    else str[(*n_str)++] = (uint8_t)h;
+  }
+  return true;
+}
+
+// Checks common to the two attention calls (everything except q/out/workspace/q_len specifics).
+int32_t check_cache(const void* k_pool, const void* v_pool, const int32_t* table, int32_t num_blocks,
+                    int32_t bs, int32_t mbph, const int32_t* seq_lens, int32_t batch, int32_t hq,
+                    int32_t hkv, int32_t head_dim, int32_t dtype, const uint8_t* mask) {
+  if (!k_pool || !v_pool || !table || !seq_lens || !mask) return DUO_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(table, 4) || !aligned(seq_lens, 4))
+    return DUO_ERR_INVALID_ARG;
+  if (batch < 1 || hq < 1 || hkv < 1 || num_blocks < 1 || mbph < 1) return DUO_ERR_INVALID_ARG;
+  if (batch > 65535) return DUO_ERR_UNSUPPORTED;
+  if (hq % hkv != 0) return DUO_ERR_INVALID_ARG;
+  if (hkv > kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return DUO_ERR_UNSUPPORTED;
+  if (!is_pow2(bs) || bs < 16 || bs > 256) return DUO_ERR_UNSUPPORTED;
+  if ((int64_t)mbph * bs > INT32_MAX) return DUO_ERR_INVALID_ARG;
+  return DUO_OK;
+}
+
+int32_t check_stream_geometry(int32_t n_str, int32_t sink, int32_t recent, int32_t ring_blocks,
+                              int32_t bs, int32_t mbph, int32_t q_len) {
+  if (sink < 0) return DUO_ERR_INVALID_ARG;
+  if (n_str == 0) return DUO_OK;
+  if (recent < 1 || ring_blocks < 1) return DUO_ERR_INVALID_ARG;
+  if ((int64_t)sink_blocks(sink, bs) + ring_blocks > mbph) return DUO_ERR_CAPACITY;
+  if ((int64_t)ring_blocks * bs < (int64_t)recent + q_len - 1) return DUO_ERR_CAPACITY;
+  return DUO_OK;
+}
+
+int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbph,
+                    int32_t bs, int32_t split_req, int32_t* split_tokens, int32_t* n_split,
+                    size_t* ws_bytes) {
+  if (split_req < 0 || (split_req % 128) != 0) return DUO_ERR_INVALID_ARG;
+  const int32_t cap = mbph * bs;
+  const int32_t S = decode_split_tokens(batch, hkv, cap, split_req);
+  const int32_t ns = (cap + S - 1) / S;
+  const int32_t G = hq / hkv;
+  *split_tokens = S;
+  *n_split = ns;
+  *ws_bytes = align256((size_t)batch * hkv * sizeof(int32_t)) +
+              (size_t)batch * hkv * ns * G * (head_dim + 2) * sizeof(float);
+  return DUO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t duo_abi_version(void) { return DUO_ATTN_ABI_VERSION; }
+
+const char* duo_status_string(int32_t s) {
+  switch (s) {
+    case DUO_OK: return "ok";
+    case DUO_ERR_INVALID_ARG: return "invalid argument";
+    case DUO_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DUO_ERR_CAPACITY: return "cache capacity too small for the request";
+    case DUO_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case DUO_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_table,
+                           int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
+                           const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                           int32_t* seq_lens_after, int32_t batch, int32_t t_new,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                           const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                           int32_t ring_blocks, void* stream) {
+  (void)recent_size;  // the append keeps every ring slot; the window is applied when attending
+  if (!k_pool || !v_pool || !block_table || !k_new || !v_new || !seq_lens_before ||
+      !head_is_retrieval)
+    return DUO_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens_before, 4) ||
+      (seq_lens_after && !aligned(seq_lens_after, 4)))
+    return DUO_ERR_INVALID_ARG;
+  if (seq_lens_after == seq_lens_before) return DUO_ERR_INVALID_ARG;
+  if (batch < 1 || t_new < 1 || num_kv_heads < 1 || num_blocks < 1 || max_blocks_per_head < 1)
+    return DUO_ERR_INVALID_ARG;
+  if (batch > 65535 || num_kv_heads > kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return DUO_ERR_UNSUPPORTED;
+  if (!is_pow2(block_size) || block_size > 256) return DUO_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_head * block_size > INT32_MAX) return DUO_ERR_INVALID_ARG;
+  if (t_new > INT32_MAX - 64 * 16) return DUO_ERR_INVALID_ARG;
+  uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
+  int32_t n_ret, n_str;
+  if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str))
+    return DUO_ERR_INVALID_ARG;
+  if (sink_size < 0) return DUO_ERR_INVALID_ARG;
+  if (n_str > 0) {
+    if (ring_blocks < 1) return DUO_ERR_INVALID_ARG;
+    if ((int64_t)sink_blocks(sink_size, block_size) + ring_blocks > max_blocks_per_head)
+      return DUO_ERR_CAPACITY;
+  }
+  AppendParams p{};
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.table = block_table;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.lens_before = seq_lens_before;
+  p.lens_after = seq_lens_after;
+  p.num_blocks = num_blocks;
+  p.log2_bs = log2i(block_size);
+  p.max_blocks_per_head = max_blocks_per_head;
+  p.batch = batch;
+  p.t_new = t_new;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.sink = sink_size;
+  p.sink_blocks = sink_blocks(sink_size, block_size);
+  p.ring_slots = n_str > 0 ? ring_blocks * block_size : 1;
+  p.retrieval_bits = 0;
+  for (int32_t i = 0; i < n_ret; ++i) p.retrieval_bits |= 1ull << ret[i];
+  if (launch_append(p, elem_bytes(dtype), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_blocks_per_head,
+                                      int32_t block_size, int32_t split_tokens) {
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      !head_dim_ok(head_dim) || max_blocks_per_head < 1 || !is_pow2(block_size) ||
+      (int64_t)max_blocks_per_head * block_size > INT32_MAX)
+    return 0;
+  int32_t S, ns;
+  size_t bytes;
+  if (decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
+                  split_tokens, &S, &ns, &bytes) != DUO_OK)
+    return 0;
+  return bytes;
+}
+
+int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                        int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                        int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t split_tokens, void* stream) {
+  int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
+                           seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
+                           head_is_retrieval);
+  if (st != DUO_OK) return st;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
+  if (num_q_heads / num_kv_heads > 16) return DUO_ERR_UNSUPPORTED;
+  uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
+  int32_t n_ret, n_str;
+  if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str))
+    return DUO_ERR_INVALID_ARG;
+  st = check_stream_geometry(n_str, sink_size, recent_size, ring_blocks, block_size,
+                             max_blocks_per_head, 1);
+  if (st != DUO_OK) return st;
+  int32_t S, ns;
+  size_t need;
+  st = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
+                   split_tokens, &S, &ns, &need);
+  if (st != DUO_OK) return st;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return DUO_ERR_WORKSPACE;
+  const int64_t grid = (int64_t)batch * n_ret * ns + (int64_t)batch * n_str;
+  if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
+
+  DecodeParams p{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.table = block_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.counter = static_cast<int32_t*>(workspace);
+  p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256((size_t)batch * num_kv_heads * sizeof(int32_t)));
+  p.num_blocks = num_blocks;
+  p.log2_bs = log2i(block_size);
+  p.max_blocks_per_head = max_blocks_per_head;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.sink = sink_size;
+  p.recent = recent_size;
+  p.sink_blocks = sink_blocks(sink_size, block_size);
+  p.ring_slots = n_str > 0 ? ring_blocks * block_size : block_size;
+  p.split_tokens = S;
+  p.n_split = ns;
+  p.n_ret = n_ret;
+  p.n_str = n_str;
+  p.scale_log2 = softmax_scale * kLog2e;
+  for (int32_t i = 0; i < n_ret; ++i) p.ret_heads[i] = ret[i];
+  for (int32_t i = 0; i < n_str; ++i) p.str_heads[i] = str[i];
+  if (launch_decode(p, dtype, head_dim, (int)grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                         int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                         int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                         float softmax_scale, void* out, void* stream) {
+  int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
+                           seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
+                           head_is_retrieval);
+  if (st != DUO_OK) return st;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
+  if (q_len < 1) return DUO_ERR_INVALID_ARG;
+  if (dtype == DUO_F32 && head_dim > 128) return DUO_ERR_UNSUPPORTED;
+  uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
+  int32_t n_ret, n_str;
+  if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str))
+    return DUO_ERR_INVALID_ARG;
+  st = check_stream_geometry(n_str, sink_size, recent_size, ring_blocks, block_size,
+                             max_blocks_per_head, q_len);
+  if (st != DUO_OK) return st;
+  const int32_t n_qt = (q_len + kPrefillRows - 1) / kPrefillRows;
+  const int64_t grid = (int64_t)batch * num_q_heads * n_qt;
+  if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
+
+  PrefillParams p{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.table = block_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.num_blocks = num_blocks;
+  p.log2_bs = log2i(block_size);
+  p.max_blocks_per_head = max_blocks_per_head;
+  p.batch = batch;
+  p.q_len = q_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.sink = sink_size;
+  p.recent = recent_size;
+  p.sink_blocks = sink_blocks(sink_size, block_size);
+  p.ring_slots = n_str > 0 ? ring_blocks * block_size : block_size;
+  p.n_qtiles = n_qt;
+  p.n_ret = n_ret;
+  p.n_str = n_str;
+  p.scale_log2 = softmax_scale * kLog2e;
+  for (int32_t i = 0; i < n_ret; ++i) p.ret_heads[i] = ret[i];
+  for (int32_t i = 0; i < n_str; ++i) p.str_heads[i] = str[i];
+  if (launch_prefill(p, dtype, head_dim, (int)grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// kv_append_circular kernel: copy new K/V tokens into their head's pages.
+//
+// Slot rule (vLLM issue "Could you support Attention Sink?", sh1ng's comment, option 3 and the
+// circular-buffer tables): a retrieval head stores position t at slot t; a streaming head stores
+// sinks (t < sink) at slot t and every later position in a ring of ring_slots slots after the sink
+// pages, at ring index (t - sink) mod ring_slots.
+//
+// One workgroup copies one 16-position run of one (sequence, kv head). Within one call only the
+// newest ring_slots streamed positions of a head are written; older ones would be overwritten by a
+// newer position of the same call, so the final cache equals writing every token in order.
+// K rows are copied 16 bytes per lane into the token-major K page; V rows go through LDS and are
+// written channel-major (16 consecutive lanes fill one channel's 16 rows).
+#include "duo_common.h"
+#include "duo_kernels.h"
+
+namespace duo {
+
+namespace {
+
+constexpr int kAppendThreads = 256;
+constexpr int kMaxHeadDim = 256;
+
+template <typename E>  // raw element bits: uint16_t or uint32_t
+__global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendParams p) {
+  __shared__ E vstage[16][kMaxHeadDim];
+  const int vg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int D = p.head_dim;
+  const int32_t L0 = min(max(p.lens_before[b], 0), INT32_MAX - p.t_new);  // no position overflow
+  const int32_t L1 = L0 + p.t_new;
+  if (vg == 0 && h == 0 && threadIdx.x == 0 && p.lens_after != nullptr) p.lens_after[b] = L1;
+
+  const bool ret = (p.retrieval_bits >> h) & 1ull;
+  const int32_t bs_mask = (1 << p.log2_bs) - 1;
+  int32_t t_lo, t_hi;
+  if (ret) {
+    const int32_t end = min(L1, p.max_blocks_per_head << p.log2_bs);
+    const int32_t g = L0 / 16 + vg;
+    t_lo = max(g * 16, L0);
+    t_hi = min(g * 16 + 16, end);
+  } else {
+    const int32_t s_end = min(L1, p.sink);
+    const int32_t ns = (L0 < s_end) ? ((s_end - 1) / 16 - L0 / 16 + 1) : 0;
+    if (vg < ns) {
+      const int32_t g = L0 / 16 + vg;
+      t_lo = max(g * 16, L0);
+      t_hi = min(g * 16 + 16, s_end);
+    } else {
+      // ring positions that survive this call: the newest ring_slots of them
+      const int32_t r_start = max(max(p.sink, L0), L1 - p.ring_slots);
+      const int32_t k = (r_start - p.sink) / 16 + (vg - ns);
+      t_lo = max(p.sink + k * 16, r_start);
+      t_hi = min(p.sink + k * 16 + 16, L1);
+    }
+  }
+  if (t_lo >= t_hi) return;
+  const int n_tok = t_hi - t_lo;
+
+  const int32_t* trow = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
+  auto slot_of = [&](int32_t t) -> int32_t {
+    if (ret || t < p.sink) return t;
+    return (p.sink_blocks << p.log2_bs) + (int32_t)((int64_t)(t - p.sink) % p.ring_slots);
+  };
+
+  constexpr int kVec = 16 / sizeof(E);  // elements per 16-byte chunk
+  const int chunks = D / kVec;
+  const E* kn = static_cast<const E*>(p.k_new);
+  const E* vn = static_cast<const E*>(p.v_new);
+  E* kp = static_cast<E*>(p.k_pool);
+  E* vp = static_cast<E*>(p.v_pool);
+  const int64_t tok_stride = (int64_t)p.num_kv_heads * D;            // elements between tokens
+  const int64_t src0 = ((int64_t)b * p.t_new) * tok_stride + (int64_t)h * D;
+
+  for (int idx = threadIdx.x; idx < n_tok * chunks; idx += kAppendThreads) {
+    const int r = idx / chunks, c = idx % chunks;
+    const int32_t t = t_lo + r;
+    const int64_t src = src0 + (int64_t)(t - L0) * tok_stride + c * kVec;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(kn + src);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(vn + src);
+    const int32_t s = slot_of(t);
+    const int64_t page = clamp_page(trow[s >> p.log2_bs], p.num_blocks);
+    const int64_t dst = ((page << p.log2_bs) + (s & bs_mask)) * D + c * kVec;
+    *reinterpret_cast<u32x4*>(kp + dst) = kv;
+    *reinterpret_cast<u32x4*>(&vstage[r][c * kVec]) = vv;
+  }
+  __syncthreads();
+  // V page is [D][block_size]: element (d, row) at page * D * bs + d * bs + row.
+  for (int idx = threadIdx.x; idx < 16 * D; idx += kAppendThreads) {
+    const int r = idx & 15, d = idx >> 4;
+    if (r >= n_tok) continue;
+    const int32_t s = slot_of(t_lo + r);
+    const int64_t page = clamp_page(trow[s >> p.log2_bs], p.num_blocks);
+    vp[(page * D + d) * ((int64_t)1 << p.log2_bs) + (s & bs_mask)] = vstage[r][d];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream) {
+  const int groups = (p.t_new + 15) / 16 + 3;
+  const dim3 grid(groups, p.num_kv_heads, p.batch);
+  (void)hipGetLastError();  // report only this launch's status
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(append_kernel<uint32_t>, grid, dim3(kAppendThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace duo

@@ -1,0 +1,304 @@
+// duo_attn_decode kernel: split-K flash-decode over the paged, per-head circular cache with the
+// split merge fused into the same launch.
+//
+// What is computed (DuoAttention README, abstract; transformers PR "[WIP] Dynamic length in static
+// cache", description): the query of sequence b at position p = L - 1 attends, per kv head h, to
+//   retrieval head: positions [0, L)
+//   streaming head: positions [0, min(sink, L)) and [max(sink, L - recent), L)
+// with scores softmax_scale * (q . k) formed in fp32 (vLLM DualChunkAttention PR, review thread on
+// the fp32 scale). Partial results over disjoint key ranges are merged through their log-sum-exp
+// (same review thread).
+//
+// Work decomposition. One workgroup (4 waves) = one work item:
+//   retrieval head: (b, h, split s) over keys [s*S, (s+1)*S), S = split_tokens;
+//   streaming head: (b, h) over its sink runs and the ring runs that meet the recent window.
+// The grid comes from static capacities only (no host read of the lengths); items past the valid
+// length exit at once. A wave processes steps of two 16-key runs (32 keys); waves take steps
+// round-robin and are merged in LDS at the end.
+//
+// MFMA formulation (16x16x32, one k-step = 8 elements per lane). All q heads of a kv head (the GQA
+// group, G <= 16) ride in the 16 columns, so K and V are read once per kv head:
+//   S^T[key, g] = sum_d K[key, d] Q[g, d]       A = K rows (from the token-major K page),
+//                                               B = Q^T (registers for the whole item)
+//   O^T[d, g]  += sum_key V^T[d, key] P^T[key, g] A = V^T (from the channel-major V page),
+//                                               B = P^T straight from the S^T accumulators.
+// The K rows of each 16-row MFMA are permuted so that the S^T accumulator a lane holds covers the
+// same 8 consecutive keys that the lane loads as its V^T operand: no LDS, no cross-lane moves.
+//
+// Split merge: each retrieval item writes (m, l, O) for its G q heads to the workspace, then takes a
+// ticket on the (b, h) counter; the last item merges the partials, writes the output and resets the
+// counter to zero for the next call.
+#include "duo_common.h"
+#include "duo_kernels.h"
+
+namespace duo {
+
+namespace {
+
+constexpr int kThreads = kDecodeWaves * kWave;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) {
+  constexpr int KC = D / 32;  // k-steps of S^T over the head dim
+  constexpr int DT = D / 16;  // 16-row tiles of O^T
+  __shared__ float sm_o[kDecodeWaves][16][D];
+  __shared__ float sm_m[kDecodeWaves][16];
+  __shared__ float sm_l[kDecodeWaves][16];
+  __shared__ int sm_ticket;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15;   // MFMA column = q head within the group
+  const int quad = lane >> 4;  // k-group of the lane
+  const int G = p.group;
+
+  // ---- which item -------------------------------------------------------------------------
+  const int n_ret_items = p.batch * p.n_ret * p.n_split;
+  int b, h, split;
+  bool ret;
+  if ((int)blockIdx.x < n_ret_items) {
+    split = blockIdx.x % p.n_split;
+    const int bh = blockIdx.x / p.n_split;
+    b = bh / p.n_ret;
+    h = p.ret_heads[bh % p.n_ret];
+    ret = true;
+  } else {
+    const int it = blockIdx.x - n_ret_items;
+    b = it / p.n_str;
+    h = p.str_heads[it % p.n_str];
+    split = 0;
+    ret = false;
+  }
+  int32_t L = max(p.seq_lens[b], 0);
+  if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
+
+  HeadGeom geo;
+  geo.row = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
+  geo.num_blocks = p.num_blocks;
+  geo.log2_bs = p.log2_bs;
+  geo.sink = p.sink;
+  geo.sink_blocks = p.sink_blocks;
+  geo.ring_slots = p.ring_slots;
+
+  // ---- the item's runs ----------------------------------------------------------------------
+  int32_t n_runs, split_t0 = 0, n_sink_runs = 0, k_lo = 0, win_lo = 0;
+  if (ret) {
+    split_t0 = split * p.split_tokens;
+    const int32_t end = min(L, split_t0 + p.split_tokens);
+    n_runs = end > split_t0 ? (end - split_t0 + 15) / 16 : 0;
+  } else {
+    n_sink_runs = (min(p.sink, L) + 15) / 16;
+    win_lo = max(p.sink, L - p.recent);
+    int32_t n_ring = 0;
+    if (L > p.sink) {
+      k_lo = (win_lo - p.sink) / 16;
+      n_ring = (L - 1 - p.sink) / 16 - k_lo + 1;
+    }
+    n_runs = n_sink_runs + n_ring;
+  }
+  auto run_at = [&](int32_t v) -> Run {
+    if (v >= n_runs) return geo.empty_run();
+    if (ret) return geo.retrieval_run(split_t0 / 16 + v, L);
+    if (v < n_sink_runs) return geo.sink_run(v, L);
+    return geo.ring_run(k_lo + (v - n_sink_runs), win_lo, L);
+  };
+
+  const T* kpool = static_cast<const T*>(p.k_pool);
+  const T* vpool = static_cast<const T*>(p.v_pool);
+  const int64_t page_elems = (int64_t)D << p.log2_bs;
+  const int bs = 1 << p.log2_bs;
+
+  if (n_runs > 0) {
+    // ---- Q^T operand (B of S^T): column = q head, k = head-dim chunk ------------------------
+    v8<T> qT[KC];
+    {
+      const T* qrow = static_cast<const T*>(p.q) + ((int64_t)b * p.num_q_heads + h * G + col) * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qT[c] = (col < G) ? load8(qrow + c * 32 + quad * 8) : zero8<T>();
+    }
+    f32x4 oT[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) oT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const int n_steps = (n_runs + 1) / 2;
+
+    for (int step = wave; step < n_steps; step += kDecodeWaves) {
+      const Run ra = run_at(2 * step), rb = run_at(2 * step + 1);
+      // K rows: MFMA row r of tile t holds key 8*(r/4) + 4*t + r%4 of the 32-key step; keys 0..15
+      // are run a, 16..31 run b.
+      v8<T> kA[2][KC];
+      {
+        const int r = col;
+        const Run& rk = (r >> 3) ? rb : ra;
+        const T* base = kpool + rk.page * page_elems + (int64_t)rk.row0 * D + quad * 8;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+#pragma unroll
+          for (int c = 0; c < KC; ++c) kA[t][c] = load8(base + krow * D + c * 32);
+        }
+      }
+      // V^T rows: head-dim channel dt*16 + col, keys 8*quad .. 8*quad+7 of the step.
+      const Run& rv = (quad >> 1) ? rb : ra;
+      const int vrow = (quad & 1) * 8;
+      v8<T> vA[DT];
+      {
+        const T* base = vpool + rv.page * page_elems + rv.row0 + vrow;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vA[dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
+      }
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < KC; ++c) s[t] = mfma16(kA[t][c], qT[c], s[t]);
+
+      // Lane holds keys rv.t0 + vrow + i, i = 4*t + j (same keys as its V^T operand).
+      const int32_t key0 = rv.t0 + vrow;
+      uint32_t keep = 0;
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int32_t t = key0 + i;
+        const bool ok = (t >= rv.lo) && (t < rv.hi);
+        keep |= (uint32_t)ok << i;
+        x[i] = ok ? s[i >> 2][i & 3] * p.scale_log2 : -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = fast_exp2(x[i] - m_use);
+        psum += x[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const v8<T> pB = pack8<T>(x);
+      if (keep != 0xFFu) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vA[dt] = select8<T>(vA[dt], keep);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        oT[dt] *= alpha;
+        oT[dt] = mfma16(vA[dt], pB, oT[dt]);
+      }
+    }
+    // lanes sharing a column hold partial sums over disjoint keys
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if (quad == 0) {
+      sm_m[wave][col] = m_run;
+      sm_l[wave][col] = l_run;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_o[wave][col][dt * 16 + quad * 4 + j] = oT[dt][j];
+    __syncthreads();
+
+    // ---- merge the waves; write the output (single item) or a partial -----------------------
+    const bool direct = !ret || p.n_split == 1;
+    float* part = p.partial + ((((int64_t)b * p.num_kv_heads + h) * p.n_split + split) * G) * (D + 2);
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, d = idx % D;
+      float M = sm_m[0][g];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float c = fast_exp2(sm_m[w][g] - Mu);
+        num += c * sm_o[w][g][d];
+        den += c * sm_l[w][g];
+      }
+      if (direct) {
+        T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G + g) * D;
+        o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+      } else {
+        part[g * (D + 2) + d] = num;
+        if (d == 0) {
+          part[g * (D + 2) + D] = M;
+          part[g * (D + 2) + D + 1] = den;
+        }
+      }
+    }
+    if (direct) return;
+  } else if (!ret || p.n_split == 1) {
+    // nothing visible (L == 0): zero output row(s)
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G) * D;
+      o[idx] = from_f32<T>(0.f);
+    }
+    return;
+  }
+
+  // ---- split merge: the last item of (b, h) to arrive reduces all partials ------------------
+  __threadfence();
+  __syncthreads();
+  int32_t* ctr = p.counter + (int64_t)b * p.num_kv_heads + h;
+  if (tid == 0) sm_ticket = atomicAdd(ctr, 1);
+  __syncthreads();
+  if (sm_ticket != p.n_split - 1) return;
+  __threadfence();
+  const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
+  const float* base = p.partial + (((int64_t)b * p.num_kv_heads + h) * p.n_split) * G * (D + 2);
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx % D;
+    float M = -INFINITY;
+    for (int s = 0; s < n_act; ++s) M = fmaxf(M, __builtin_nontemporal_load(base + (s * G + g) * (D + 2) + D));
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < n_act; ++s) {
+      const float* rec = base + (s * G + g) * (D + 2);
+      const float c = fast_exp2(__builtin_nontemporal_load(rec + D) - Mu);
+      num += c * __builtin_nontemporal_load(rec + d);
+      den += c * __builtin_nontemporal_load(rec + D + 1);
+    }
+    T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G + g) * D;
+    o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+  }
+  if (tid == 0) atomicExch(ctr, 0);
+}
+
+template <typename T>
+hipError_t launch_t(const DecodeParams& p, int head_dim, int grid, hipStream_t stream) {
+  (void)hipGetLastError();  // report only this launch's status
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((decode_kernel<T, 64>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((decode_kernel<T, 128>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((decode_kernel<T, 256>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int grid,
+                         hipStream_t stream) {
+  if (dtype == 0) return launch_t<float>(p, head_dim, grid, stream);
+  if (dtype == 1) return launch_t<_Float16>(p, head_dim, grid, stream);
+  return launch_t<__bf16>(p, head_dim, grid, stream);
+}
+
+int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
+                            int32_t requested) {
+  if (requested > 0) return requested;
+  // Aim for ~1024 work items if every head were a retrieval head; at least 256 keys per item
+  // (two 32-key steps per wave), at most 8192.
+  const int64_t total = (int64_t)batch * num_kv_heads * capacity_tokens;
+  int64_t s = 256;
+  while (s < 8192 && s * 1024 < total) s *= 2;
+  return (int32_t)s;
+}
+
+}  // namespace duo

@@ -1,0 +1,161 @@
+// Device-side building blocks shared by the append, decode and prefill kernels (gfx950 only).
+//
+// Element types: float, _Float16, __bf16. An "8-vector" is the per-lane operand of one MFMA
+// k-step: 8 consecutive elements of the contraction dimension (16 bytes for 16-bit types, 32 bytes
+// for fp32). For fp32 one k-step of 8 is issued as eight k=4 (16x16) or k=2 (32x32) fp32 MFMAs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duo {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+template <typename T> struct V8;
+template <> struct V8<__bf16> { using type = bf16x8; };
+template <> struct V8<_Float16> { using type = f16x8; };
+template <> struct V8<float> { using type = f32x8; };
+template <typename T> using v8 = typename V8<T>::type;
+
+// 16-byte-aligned loads of 8 elements.
+template <typename T>
+__device__ __forceinline__ v8<T> load8(const T* p) {
+  return *reinterpret_cast<const v8<T>*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ v8<T> zero8() {
+  v8<T> z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = T(0.0f);
+  return z;
+}
+
+// fp32 -> element, round to nearest even (hardware conversions on gfx950).
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return T(x); }
+
+template <typename T>
+__device__ __forceinline__ v8<T> pack8(const float* x) {
+  v8<T> r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = from_f32<T>(x[i]);
+  return r;
+}
+
+// Keep element i of `v` where bit i of `keep` is set, else 0. Works on the raw bits so that NaN or
+// Inf garbage is replaced, never multiplied.
+template <typename T>
+__device__ __forceinline__ v8<T> select8(v8<T> v, uint32_t keep) {
+  v8<T> r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = ((keep >> i) & 1u) ? v[i] : T(0.0f);
+  return r;
+}
+
+// ---- MFMA: C[16x16] += A[16 x 8k] * B[8k x 16] over one 8-element k-step per lane ---------------
+// Lane layout (16x16 family): A row = lane % 16, B col = lane % 16, the lane's 8 k-elements belong
+// to k-group lane / 16; C: col = lane % 16, rows 4 * (lane / 16) + [0..3].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+// ---- MFMA: C[32x32] += A[32 x 8k] * B[8k x 32] -------------------------------------------------
+// Lane layout (32x32 family): A row = lane % 32, B col = lane % 32, k-group lane / 32;
+// C: col = lane % 32, rows 8 * i + 4 * (lane / 32) + j for register 4 * i + j.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f32x8 a, f32x8 b, f32x16 c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ int clamp_page(int32_t phys, int32_t num_blocks) {
+  return min(max(phys, 0), num_blocks - 1);
+}
+
+// A 16-token run of one head's logical positions and where it lives: t0 is the first position,
+// `page` the physical page, `row0` the first row inside that page (0 unless block_size > 16).
+// Keys t in [lo, hi) are present and may be attended; `windowed` marks a streaming head's ring
+// run, whose keys are further limited to the recent window of each query.
+struct Run {
+  int32_t t0, page, row0, lo, hi;
+  bool windowed;
+};
+
+// Which 16-position runs a head exposes (pages hold >= 16 positions, so a run never spans pages):
+//   retrieval: runs at t0 = 16 g, g = 0, 1, ...   (slot t0)
+//   streaming: sink runs at t0 = 16 j while 16 j < sink (slot t0);
+//              ring runs at t0 = sink + 16 k       (slot SB*bs + (16 k mod ring_slots))
+struct HeadGeom {
+  const int32_t* row;     // this (sequence, kv head)'s block-table row
+  int32_t num_blocks, log2_bs, sink, sink_blocks, ring_slots;
+  __device__ __forceinline__ void locate(int32_t slot, int32_t& page, int32_t& row0) const {
+    page = clamp_page(row[slot >> log2_bs], num_blocks);
+    row0 = slot & ((1 << log2_bs) - 1);
+  }
+  __device__ __forceinline__ Run retrieval_run(int32_t g, int32_t L) const {
+    Run r;
+    r.t0 = g * 16;
+    locate(r.t0, r.page, r.row0);
+    r.lo = 0;
+    r.hi = L;
+    r.windowed = false;
+    return r;
+  }
+  __device__ __forceinline__ Run sink_run(int32_t j, int32_t L) const {
+    Run r;
+    r.t0 = j * 16;
+    locate(r.t0, r.page, r.row0);
+    r.lo = 0;
+    r.hi = min(sink, L);
+    r.windowed = false;
+    return r;
+  }
+  __device__ __forceinline__ Run ring_run(int32_t k, int32_t lo, int32_t L) const {
+    Run r;
+    r.t0 = sink + k * 16;
+    const int32_t off = (int32_t)(((int64_t)k * 16) % ring_slots);
+    locate((sink_blocks << log2_bs) + off, r.page, r.row0);
+    r.lo = lo;
+    r.hi = L;
+    r.windowed = true;
+    return r;
+  }
+  __device__ __forceinline__ Run empty_run() const {
+    Run r;
+    r.t0 = 0;
+    r.page = 0;
+    r.row0 = 0;
+    r.lo = 0;
+    r.hi = 0;
+    r.windowed = false;
+    return r;
+  }
+};
+
+}  // namespace duo

@@ -1,0 +1,74 @@
+// Internal interface between the C-ABI host layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duo {
+
+constexpr int kMaxKvHeads = 64;
+constexpr float kLog2e = 1.4426950408889634f;  // scores are kept in the log2 domain
+
+struct AppendParams {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* table;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* lens_before;
+  int32_t* lens_after;
+  int32_t num_blocks, log2_bs, max_blocks_per_head;
+  int32_t batch, t_new, num_kv_heads, head_dim;
+  int32_t sink, sink_blocks, ring_slots;
+  uint64_t retrieval_bits;  // bit h set = kv head h is a retrieval head
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  void* out;
+  float* partial;     // [batch][num_kv_heads][n_split][group][head_dim + 2]
+  int32_t* counter;   // [batch][num_kv_heads]
+  int32_t num_blocks, log2_bs, max_blocks_per_head;
+  int32_t batch, num_q_heads, num_kv_heads, group;
+  int32_t sink, recent, sink_blocks, ring_slots;
+  int32_t split_tokens, n_split, n_ret, n_str;
+  float scale_log2;  // softmax_scale * log2(e)
+  uint8_t ret_heads[kMaxKvHeads];
+  uint8_t str_heads[kMaxKvHeads];
+};
+
+struct PrefillParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  void* out;
+  int32_t num_blocks, log2_bs, max_blocks_per_head;
+  int32_t batch, q_len, num_q_heads, num_kv_heads, group;
+  int32_t sink, recent, sink_blocks, ring_slots;
+  int32_t n_qtiles, n_ret, n_str;
+  float scale_log2;
+  uint8_t ret_heads[kMaxKvHeads];
+  uint8_t str_heads[kMaxKvHeads];
+};
+
+// Launchers (return the HIP launch status). dtype: 0 f32, 1 f16, 2 bf16.
+hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int grid,
+                         hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid,
+                          hipStream_t stream);
+
+// Decode planning shared by the workspace-size query and the call.
+int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
+                            int32_t requested);
+constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
+constexpr int kDecodeWaves = 4;     // waves per decode workgroup
+constexpr int kDecodeStep = 32;     // keys per wave step (two 16-key runs)
+
+}  // namespace duo

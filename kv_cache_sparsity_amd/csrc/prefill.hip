@@ -1,0 +1,357 @@
+// duo_attn_prefill kernel: tiled flash attention of a prompt chunk over the paged cache.
+//
+// What is computed (DuoAttention README, abstract and efficiency section; transformers PR
+// "[WIP] Dynamic length in static cache"): query row i of sequence b sits at position
+// p = L - q_len + i and attends causally (keys j <= p); a streaming head further keeps only the sink
+// positions j < sink and its recent window p - j < recent. Scores are softmax_scale * (q . k) in
+// fp32 (vLLM DualChunkAttention PR, review thread).
+//
+// Work decomposition: one workgroup (4 waves, 128 query rows, 32 per wave) per (b, q head, row
+// tile); retrieval heads' tiles come first, latest rows first (they scan the most keys). The
+// workgroup walks only the 16-key runs that can be visible to its rows:
+//   retrieval head: runs 0 .. p_hi / 16;
+//   streaming head: the sink runs, then the ring runs covering [p_lo - recent + 1, p_hi].
+// So a streaming tile costs about (sink + recent + 128) keys whatever the context length. Four
+// runs (64 keys) form one K/V tile, staged into LDS (double-buffered, next tile's global loads in
+// flight during this tile's math). Per wave and tile, each run is classified as fully visible,
+// invisible or partial for the wave's 32 rows: fully invisible tiles are skipped, fully visible
+// tiles skip the element mask.
+//
+// MFMA formulation (32x32x16, k-step of 8 elements per lane), per 32-key block:
+//   S^T[key, row] = sum_d K[key, d] Q[row, d]       A = K rows (LDS), B = Q^T (registers)
+//   O^T[d, row]  += sum_key V^T[d, key] P^T[key, row] A = V^T (LDS, channel-major like the V page),
+//                                                     B = P^T taken from the S^T accumulators.
+// K rows are staged into LDS in a permuted order so that the eight S^T accumulators a lane holds
+// per 16-key chunk are the chunk's keys 8*(lane/32) .. +7, the k-group of its P^T operand.
+#include "duo_common.h"
+#include "duo_kernels.h"
+
+namespace duo {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = kPrefillRows;  // 128 query rows per workgroup
+constexpr int kKeys = 64;            // keys per K/V tile (four 16-key runs)
+
+// Row of the 32-key block that holds key r of the block (an involution: swaps the middle two
+// groups of four in each half).
+__device__ __forceinline__ int perm32(int r) {
+  const int a = (r >> 2) & 3;
+  const int off = (a == 1) ? 8 : (a == 2) ? 4 : (a == 3) ? 12 : 0;
+  return (r & 16) + off + (r & 3);
+}
+
+template <typename T, int D>
+struct Tile {
+  static constexpr int kPad = 8;                   // row padding: one 8-element operand
+  static constexpr int kKStride = D + kPad;        // K tile: [64 keys][D]
+  static constexpr int kVStride = kKeys + kPad;    // V tile: [D][64 keys]
+  static constexpr int kChunk = 16 / sizeof(T);    // elements per 16-byte chunk
+  static constexpr int kKChunks = kKeys * D / kChunk;
+  static constexpr int kVChunks = D * kKeys / kChunk;
+  static constexpr int kKPer = kKChunks / kThreads;
+  static constexpr int kVPer = kVChunks / kThreads;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p) {
+  using TL = Tile<T, D>;
+  constexpr int DC = D / 16;  // k-steps over the head dim (16 channels per 32x32 MFMA step)
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) T k_lds[2][kKeys * TL::kKStride];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][D * TL::kVStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rcol = lane & 31;  // MFMA column = query row within the wave
+  const int half = lane >> 5;  // k-group of the lane
+  const int G = p.group;
+
+  // ---- which item ---------------------------------------------------------------------------
+  const int per_tile_r = p.batch * p.n_ret * G;
+  const int ret_items = per_tile_r * p.n_qtiles;
+  int b, hq, qt;
+  bool ret;
+  if ((int)blockIdx.x < ret_items) {
+    qt = p.n_qtiles - 1 - blockIdx.x / per_tile_r;
+    int r = blockIdx.x % per_tile_r;
+    b = r / (p.n_ret * G);
+    r %= p.n_ret * G;
+    hq = p.ret_heads[r / G] * G + r % G;
+    ret = true;
+  } else {
+    const int per_tile_s = p.batch * p.n_str * G;
+    const int it = blockIdx.x - ret_items;
+    qt = p.n_qtiles - 1 - it / per_tile_s;
+    int r = it % per_tile_s;
+    b = r / (p.n_str * G);
+    r %= p.n_str * G;
+    hq = p.str_heads[r / G] * G + r % G;
+    ret = false;
+  }
+  const int h = hq / G;
+  int32_t L = max(p.seq_lens[b], 0);
+  if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
+  const int row0 = qt * kRows;
+  const int n_rows = min(kRows, p.q_len - row0);
+  const int32_t p_lo = L - p.q_len + row0;       // position of the tile's first row
+  const int32_t p_hi = p_lo + n_rows - 1;
+
+  HeadGeom geo;
+  geo.row = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
+  geo.num_blocks = p.num_blocks;
+  geo.log2_bs = p.log2_bs;
+  geo.sink = p.sink;
+  geo.sink_blocks = p.sink_blocks;
+  geo.ring_slots = p.ring_slots;
+
+  int32_t n_runs = 0, n_sink_runs = 0, k_lo = 0;
+  if (p_hi >= 0) {
+    if (ret) {
+      n_runs = p_hi / 16 + 1;
+    } else {
+      n_sink_runs = (min(p.sink, p_hi + 1) + 15) / 16;
+      int32_t n_ring = 0;
+      if (p_hi >= p.sink) {
+        k_lo = (max(p.sink, p_lo - p.recent + 1) - p.sink) / 16;
+        n_ring = (p_hi - p.sink) / 16 - k_lo + 1;
+      }
+      n_runs = n_sink_runs + n_ring;
+    }
+  }
+  auto run_at = [&](int32_t v) -> Run {
+    if (v >= n_runs) return geo.empty_run();
+    if (ret) return geo.retrieval_run(v, L);
+    if (v < n_sink_runs) return geo.sink_run(v, L);
+    return geo.ring_run(k_lo + (v - n_sink_runs), p.sink, L);
+  };
+
+  const T* kpool = static_cast<const T*>(p.k_pool);
+  const T* vpool = static_cast<const T*>(p.v_pool);
+  const int64_t page_elems = (int64_t)D << p.log2_bs;
+  const int bs = 1 << p.log2_bs;
+
+  // ---- staging of one tile: global -> registers -> LDS --------------------------------------
+  u32x4 k_stage[TL::kKPer], v_stage[TL::kVPer];
+  auto stage_load = [&](int tile) {
+#pragma unroll
+    for (int it = 0; it < TL::kKPer; ++it) {
+      const int idx = it * kThreads + tid;
+      const int kt = idx / (D / TL::kChunk), c = idx % (D / TL::kChunk);
+      const Run r = run_at(tile * 4 + kt / 16);
+      if (r.lo < r.hi) {
+        const T* src = kpool + r.page * page_elems + (int64_t)(r.row0 + (kt & 15)) * D + c * TL::kChunk;
+        k_stage[it] = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        k_stage[it] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < TL::kVPer; ++it) {
+      const int idx = it * kThreads + tid;
+      constexpr int per_d = 16 / TL::kChunk;               // chunks per channel per run
+      const int run = idx / (D * per_d);
+      const int rem = idx % (D * per_d);
+      const int d = rem / per_d, c = rem % per_d;
+      const Run r = run_at(tile * 4 + run);
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      const int32_t t0 = r.t0 + c * TL::kChunk;
+      if (r.lo < r.hi && t0 + TL::kChunk > r.lo && t0 < r.hi) {
+        const T* src = vpool + r.page * page_elems + (int64_t)d * bs + r.row0 + c * TL::kChunk;
+        v = *reinterpret_cast<const u32x4*>(src);
+        if (t0 < r.lo || t0 + TL::kChunk > r.hi) {
+          // zero the channel values of absent keys (their bits may be NaN or Inf)
+          T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+          for (int i = 0; i < TL::kChunk; ++i)
+            if (t0 + i < r.lo || t0 + i >= r.hi) e[i] = T(0.0f);
+        }
+      }
+      v_stage[it] = v;
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < TL::kKPer; ++it) {
+      const int idx = it * kThreads + tid;
+      const int kt = idx / (D / TL::kChunk), c = idx % (D / TL::kChunk);
+      const int lrow = (kt & 32) + perm32(kt & 31);
+      *reinterpret_cast<u32x4*>(&k_lds[buf][lrow * TL::kKStride + c * TL::kChunk]) = k_stage[it];
+    }
+#pragma unroll
+    for (int it = 0; it < TL::kVPer; ++it) {
+      const int idx = it * kThreads + tid;
+      constexpr int per_d = 16 / TL::kChunk;
+      const int run = idx / (D * per_d);
+      const int rem = idx % (D * per_d);
+      const int d = rem / per_d, c = rem % per_d;
+      *reinterpret_cast<u32x4*>(&v_lds[buf][d * TL::kVStride + run * 16 + c * TL::kChunk]) = v_stage[it];
+    }
+  };
+
+  // ---- the wave's query rows: Q^T operand (B of S^T) ----------------------------------------
+  const int wrow0 = wave * 32;                       // first row of this wave inside the tile
+  const int qrow = row0 + wrow0 + rcol;              // chunk row of this lane's column
+  const int32_t pw_lo = p_lo + wrow0;
+  const int32_t pw_hi = min(pw_lo + 31, p_hi);
+  const bool wave_live = wrow0 < n_rows;
+  v8<T> qT[DC];
+  {
+    const bool ok = qrow < p.q_len;
+    const T* src = static_cast<const T*>(p.q) + (((int64_t)b * p.q_len + (ok ? qrow : 0)) * p.num_q_heads + hq) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qT[dc] = ok ? load8(src + dc * 16 + half * 8) : zero8<T>();
+  }
+  f32x16 oT[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oT[i][j] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int32_t my_p = p_lo + wrow0 + rcol;          // this lane's query position
+
+  const int n_tiles = (n_runs + 3) / 4;
+  if (n_tiles > 0) {
+    stage_load(0);
+    stage_store(0);
+  }
+  __syncthreads();
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < n_tiles) stage_load(tile + 1);
+
+    // classify this tile's runs for the wave's rows
+    Run runs[4];
+    bool all_full = true, any_vis = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      runs[i] = run_at(tile * 4 + i);
+      const Run& r = runs[i];
+      const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
+      const bool present = a < e;
+      // Some key visible to some row: the closest (key, row) pair is key t = min(e-1, pw_hi) seen
+      // from row max(pw_lo, t).
+      const bool vis = present && a <= pw_hi &&
+                       (!r.windowed || pw_lo - min(e - 1, pw_hi) < p.recent);
+      const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= pw_lo &&
+                        (!r.windowed || pw_hi - r.t0 < p.recent);
+      all_full = all_full && full;
+      any_vis = any_vis || vis;
+    }
+
+    if (wave_live && any_vis) {
+      const T* kl = k_lds[buf];
+      const T* vl = v_lds[buf];
+      f32x16 s[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[b2][j] = 0.f;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const v8<T> a = load8(kl + (b2 * 32 + rcol) * TL::kKStride + dc * 16 + half * 8);
+          s[b2] = mfma32(a, qT[dc], s[b2]);
+        }
+      }
+      // accumulator 4*i + j of block b2 is key 8*half + 4*(i&1) + j of run 2*b2 + (i>>1)
+      float x[2][16];
+      if (all_full) {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) x[b2][k] = s[b2][k] * p.scale_log2;
+      } else {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const Run& r = runs[2 * b2 + (i >> 1)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int32_t t = r.t0 + 8 * half + 4 * (i & 1) + j;
+              const bool ok = t >= r.lo && t < r.hi && t <= my_p &&
+                              (!r.windowed || my_p - t < p.recent);
+              x[b2][4 * i + j] = ok ? s[b2][4 * i + j] * p.scale_log2 : -INFINITY;
+            }
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) mx = fmaxf(mx, x[b2][k]);
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          x[b2][k] = fast_exp2(x[b2][k] - m_use);
+          psum += x[b2][k];
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oT[db] *= alpha;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const v8<T> pB = pack8<T>(&x[b2][8 * kc]);
+          const int chunk = 2 * b2 + kc;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const v8<T> a = load8(vl + (db * 32 + rcol) * TL::kVStride + chunk * 16 + half * 8);
+            oT[db] = mfma32(a, pB, oT[db]);
+          }
+        }
+    }
+    if (tile + 1 < n_tiles) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store -----------------------------------------------------------------
+  l_run += shfl_xor(l_run, 32);
+  if (qrow < p.q_len && wave_live) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    T* dst = static_cast<T*>(p.out) + (((int64_t)b * p.q_len + qrow) * p.num_q_heads + hq) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[db * 32 + 8 * i + 4 * half + j] = from_f32<T>(oT[db][4 * i + j] * inv);
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const PrefillParams& p, int head_dim, int grid, hipStream_t stream) {
+  (void)hipGetLastError();  // report only this launch's status
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 256:
+      if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((prefill_kernel<T, 256>), dim3(grid), dim3(kThreads), 0, stream, p);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid,
+                          hipStream_t stream) {
+  if (dtype == 0) return launch_t<float>(p, head_dim, grid, stream);
+  if (dtype == 1) return launch_t<_Float16>(p, head_dim, grid, stream);
+  return launch_t<__bf16>(p, head_dim, grid, stream);
+}
+
+}  // namespace duo

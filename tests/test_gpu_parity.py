@@ -1,0 +1,414 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded bits.
+
+Bars: KV slot placement bit-exact (whole pools compared); attention outputs within max abs error
+1e-4 (fp32) or 2e-2 (bf16/fp16) of the fp64 oracle. Pools start filled with NaN, so every slot the
+kernels must not read is poisoned.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_sparsity_amd as duo
+import oracle
+import synth
+from tests.gpu_harness import (Cache, check_close, logical_kv, q_decode, q_prefill, say, to_dev,
+                               to_host_bits, to_host_f64, fill_bits, oracle_decode, TOL)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(duo.LIB_PATH):
+        pytest.fail("libduoattn.so is not built; the GPU tests need the HIP library")
+
+
+def _mask(hkv, ret):
+    m = np.zeros(hkv, np.uint8)
+    m[list(ret)] = 1
+    return m
+
+
+def _append_per_sequence(cache, K, V, lens):
+    """Fill each sequence b with positions [0, lens[b]) (batch-1 calls on row slices)."""
+    w = cache.w
+    final = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+    for b in range(w.batch):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        kn = np.ascontiguousarray(K[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(V[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        before = torch.zeros(1, dtype=torch.int32, device="cuda")
+        after = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, cache.table[b:b + 1],
+                               to_dev(kn, w.dtype), to_dev(vn, w.dtype), before, after,
+                               cache.mask, w.sink, w.recent, w.ring_blocks)
+        final[b] = after[0]
+    cache.lens = final
+
+
+# ------------------------------------------------------------------------------------------------
+# kv_append_circular: bit-exact pools
+# ------------------------------------------------------------------------------------------------
+APPEND_CASES = [
+    dict(name="bf16-d128-bs16-sink4-ring2", dtype=synth.BF16, head_dim=128, block_size=16, sink=4,
+         recent=24, ring_blocks=2, kv=3, ret=(0,), calls=[5, 40, 1, 1, 70]),
+    dict(name="f32-d64-bs32-sink0-ring1", dtype=synth.F32, head_dim=64, block_size=32, sink=0,
+         recent=20, ring_blocks=1, kv=2, ret=(1,), calls=[33, 2, 64, 7]),
+    dict(name="f16-d256-bs16-sink20-ring3", dtype=synth.F16, head_dim=256, block_size=16, sink=20,
+         recent=40, ring_blocks=3, kv=2, ret=(), calls=[1, 19, 3, 100, 16]),
+    dict(name="bf16-d64-bs4-sink2-ring3", dtype=synth.BF16, head_dim=64, block_size=4, sink=2,
+         recent=10, ring_blocks=3, kv=2, ret=(0,), calls=[17, 3, 30]),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c["name"] for c in APPEND_CASES])
+def test_append_bit_exact(case):
+    say(f"append {case['name']}")
+    total = sum(case["calls"])
+    w = synth.small(case["name"], batch=2, q_heads=case["kv"], kv_heads=case["kv"],
+                    head_dim=case["head_dim"], dtype=case["dtype"], block_size=case["block_size"],
+                    sink=case["sink"], recent=case["recent"], retrieval=case["ret"],
+                    context=total, ring_blocks=case["ring_blocks"], seed=21)
+    cache = Cache(w, fill="sentinel")
+    K = logical_kv(w, total, synth.S_K)
+    V = logical_kv(w, total, synth.S_V)
+    kp = to_host_bits(cache.k_pool, w.dtype).copy()
+    vp = to_host_bits(cache.v_pool, w.dtype).copy()
+    pos = 0
+    for n in case["calls"]:
+        kn = np.ascontiguousarray(K[:, :, pos:pos + n].transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(V[:, :, pos:pos + n].transpose(0, 2, 1, 3))
+        before = cache.lens.cpu().numpy()
+        cache.append(kn, vn)
+        oracle.append(kp, vp, cache.table_h, kn, vn, before, cache.mask, sink=w.sink,
+                      block_size=w.block_size, ring_blocks=w.ring_blocks,
+                      max_blocks_per_head=w.max_blocks_per_head)
+        pos += n
+        assert cache.lens.cpu().tolist() == [pos] * w.batch
+        gk = to_host_bits(cache.k_pool, w.dtype)
+        gv = to_host_bits(cache.v_pool, w.dtype)
+        assert gk.tobytes() == kp.tobytes(), f"K pool differs after {pos} tokens"
+        assert gv.tobytes() == vp.tobytes(), f"V pool differs after {pos} tokens"
+
+
+def test_append_reproduces_the_pages_circular_buffer_table():
+    """vLLM issue 'Could you support Attention Sink?': the no-sink table (4 blocks of 4 slots)."""
+    import tests.test_oracle_pins as pins
+    table = pins._load_tables()["no_sink"]["states"]
+    w = synth.small("page-table", batch=1, q_heads=1, kv_heads=1, head_dim=64, dtype=synth.F32,
+                    block_size=4, sink=0, recent=16, retrieval=(), context=18, ring_blocks=4,
+                    seed=1)
+    cache = Cache(w, fill="sentinel", identity=True)
+    for t in range(18):
+        tok = np.full((1, 1, 1, 64), float(t), dtype=np.float32)
+        cache.append(tok, tok)
+        if t in table:
+            k = to_host_bits(cache.k_pool, w.dtype)[:, :, 0]     # [4 pages][4 rows]
+            got = [[None if x == cache.fill_value else int(x) for x in page] for page in k]
+            assert got == table[t], (t, got)
+
+
+# ------------------------------------------------------------------------------------------------
+# decode
+# ------------------------------------------------------------------------------------------------
+DECODE_CASES = [
+    dict(name="bf16-d128-g4-mixed", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(0,),
+         block_size=16, sink=4, recent=24, ring_blocks=2, lens=[1, 37, 300]),
+    dict(name="f16-d256-g8-mqa", dtype=synth.F16, head_dim=256, group=8, kv=1, ret=(0,),
+         block_size=16, sink=0, recent=1, ring_blocks=1, lens=[100, 1000, 4097]),
+    dict(name="f32-d64-g1-mha", dtype=synth.F32, head_dim=64, group=1, kv=4, ret=(0, 2),
+         block_size=16, sink=4, recent=64, ring_blocks=4, lens=[0, 3, 513]),
+    dict(name="bf16-d64-g16-bs32-ringwrap", dtype=synth.BF16, head_dim=64, group=16, kv=2,
+         ret=(1,), block_size=32, sink=0, recent=7, ring_blocks=1, lens=[50, 2000]),
+    dict(name="bf16-d128-g2-bs64-sink70", dtype=synth.BF16, head_dim=128, group=2, kv=2, ret=(1,),
+         block_size=64, sink=70, recent=100, ring_blocks=2, lens=[69, 70, 71, 170, 171, 5000]),
+    dict(name="f16-d128-g4-all-streaming", dtype=synth.F16, head_dim=128, group=4, kv=3, ret=(),
+         block_size=16, sink=16, recent=32, ring_blocks=2, lens=[16, 48, 49, 777]),
+]
+
+
+def _decode_case(case, split_tokens=0):
+    lens = case["lens"]
+    Lmax = max(lens)
+    w = synth.small(case["name"], batch=len(lens), q_heads=case["kv"] * case["group"],
+                    kv_heads=case["kv"], head_dim=case["head_dim"], dtype=case["dtype"],
+                    block_size=case["block_size"], sink=case["sink"], recent=case["recent"],
+                    retrieval=case["ret"], context=Lmax, ring_blocks=case["ring_blocks"], seed=31)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, Lmax, synth.S_K)
+    V = logical_kv(w, Lmax, synth.S_V)
+    _append_per_sequence(cache, K, V, lens)
+    q = q_decode(w, 0)
+    return w, cache, K, V, q
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c["name"] for c in DECODE_CASES])
+def test_decode_parity(case):
+    say(f"decode {case['name']}")
+    w, cache, K, V, q = _decode_case(case)
+    got = to_host_f64(cache.decode(q), w.dtype)
+    want = oracle_decode(w, q, K, V, np.asarray(case["lens"]), cache.mask)
+    check_close(got, want, w.dtype, case["name"])
+    zero_rows = [b for b, L in enumerate(case["lens"]) if L == 0]
+    for b in zero_rows:
+        assert (got[b] == 0).all()
+
+
+@pytest.mark.parametrize("split", [128, 256, 1024, 0])
+def test_decode_split_count_invariance(split):
+    case = DECODE_CASES[1]
+    say(f"decode split {split}")
+    w, cache, K, V, q = _decode_case(case)
+    got = to_host_f64(cache.decode(q, split_tokens=split), w.dtype)
+    want = oracle_decode(w, q, K, V, np.asarray(case["lens"]), cache.mask)
+    check_close(got, want, w.dtype, f"split={split}")
+
+
+def test_decode_is_deterministic_and_workspace_reusable():
+    case = DECODE_CASES[0]
+    w, cache, K, V, q = _decode_case(case)
+    qd = to_dev(q, w.dtype)
+    ws = duo.decode_workspace(qd, cache.table, w.block_size, 128)
+    a = to_host_bits(cache.decode(q, split_tokens=128, workspace=ws), w.dtype)
+    b = to_host_bits(cache.decode(q, split_tokens=128, workspace=ws), w.dtype)
+    assert a.tobytes() == b.tobytes()
+    # the counters were left at zero by the last item of each (sequence, head)
+    nctr = w.batch * w.num_kv_heads * 4
+    assert int(ws[:nctr].view(torch.int32).abs().sum().item()) == 0
+
+
+# ------------------------------------------------------------------------------------------------
+# prefill
+# ------------------------------------------------------------------------------------------------
+PREFILL_CASES = [
+    dict(name="bf16-d128-mha-ragged300", dtype=synth.BF16, head_dim=128, group=1, kv=4,
+         ret=(0, 3), block_size=16, sink=8, recent=40, chunks=[300]),
+    dict(name="bf16-d128-chunked3x200", dtype=synth.BF16, head_dim=128, group=1, kv=2, ret=(1,),
+         block_size=16, sink=8, recent=40, chunks=[200, 200, 200]),
+    dict(name="f16-d64-gqa4-q129", dtype=synth.F16, head_dim=64, group=4, kv=2, ret=(0,),
+         block_size=16, sink=3, recent=20, chunks=[129]),
+    dict(name="f32-d64-q512", dtype=synth.F32, head_dim=64, group=1, kv=4, ret=(0, 1),
+         block_size=16, sink=4, recent=64, chunks=[512]),
+    dict(name="f16-d256-q64x2", dtype=synth.F16, head_dim=256, group=2, kv=1, ret=(), block_size=16,
+         sink=16, recent=16, chunks=[64, 64]),
+    dict(name="bf16-d128-bs32-sink5", dtype=synth.BF16, head_dim=128, group=1, kv=2, ret=(0,),
+         block_size=32, sink=5, recent=77, chunks=[150, 260]),
+    dict(name="f32-d128-g2-chunks", dtype=synth.F32, head_dim=128, group=2, kv=2, ret=(1,),
+         block_size=16, sink=1, recent=1, chunks=[33, 1, 128]),
+]
+
+
+def _rows_all(B, q_len, Hq):
+    return [(b, i, hq) for b in range(B) for hq in range(Hq) for i in range(q_len)]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c["name"] for c in PREFILL_CASES])
+def test_prefill_parity(case):
+    say(f"prefill {case['name']}")
+    chunks = case["chunks"]
+    total = sum(chunks)
+    w = synth.small(case["name"], batch=2, q_heads=case["kv"] * case["group"], kv_heads=case["kv"],
+                    head_dim=case["head_dim"], dtype=case["dtype"], block_size=case["block_size"],
+                    sink=case["sink"], recent=case["recent"], retrieval=case["ret"], context=total,
+                    q_len=max(chunks), seed=41)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, total, synth.S_K)
+    V = logical_kv(w, total, synth.S_V)
+    pos = 0
+    for ci, n in enumerate(chunks):
+        cache.append_logical(K, V, pos, pos + n)
+        pos += n
+        q = q_prefill(w, ci, n)
+        got = to_host_f64(cache.prefill(q), w.dtype)
+        want = oracle.attend(q, K, V, np.full(w.batch, pos), cache.mask, sink=w.sink,
+                             recent=w.recent, scale=w.scale, dtype=w.dtype,
+                             rows=_rows_all(w.batch, n, w.num_q_heads))
+        check_close(got, want, w.dtype, f"{case['name']} chunk {ci}")
+
+
+def test_prefill_rows_before_the_sequence_start_are_zero():
+    """seq_len < q_len: rows at negative positions see nothing (zero output)."""
+    w = synth.small("neg-rows", batch=1, q_heads=2, kv_heads=2, head_dim=64, dtype=synth.BF16,
+                    block_size=16, sink=2, recent=8, retrieval=(0,), context=20, q_len=25, seed=43)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, 20, synth.S_K)
+    V = logical_kv(w, 20, synth.S_V)
+    cache.append_logical(K, V, 0, 20)
+    q = q_prefill(w, 0, 25)
+    got = to_host_f64(cache.prefill(q), w.dtype)
+    want = oracle.attend(q, K, V, np.array([20]), cache.mask, sink=w.sink, recent=w.recent,
+                         scale=w.scale, dtype=w.dtype)
+    assert (got[0, :5] == 0).all()
+    check_close(got, want, w.dtype, "negative rows")
+
+
+def test_prefill_is_deterministic():
+    case = PREFILL_CASES[0]
+    w = synth.small("det", batch=1, q_heads=4, kv_heads=4, head_dim=128, dtype=synth.BF16,
+                    block_size=16, sink=8, recent=40, retrieval=(0, 3), context=300, q_len=300,
+                    seed=44)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, 300, synth.S_K)
+    V = logical_kv(w, 300, synth.S_V)
+    cache.append_logical(K, V, 0, 300)
+    q = q_prefill(w, 0, 300)
+    a = to_host_bits(cache.prefill(q), w.dtype)
+    b = to_host_bits(cache.prefill(q), w.dtype)
+    assert a.tobytes() == b.tobytes()
+
+
+# ------------------------------------------------------------------------------------------------
+# The five workloads at their real shapes
+# ------------------------------------------------------------------------------------------------
+def test_tiny_f32_prefill_then_16_decode_steps():
+    w = synth.tiny()
+    say(f"workload {w.name}")
+    total = w.context + w.steps
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, total, synth.S_K)
+    V = logical_kv(w, total, synth.S_V)
+    cache.append_logical(K, V, 0, w.context)
+    q = q_prefill(w, 0, w.q_len)
+    got = to_host_f64(cache.prefill(q), w.dtype)
+    want = oracle.attend(q, K, V, np.array([w.context]), cache.mask, sink=w.sink, recent=w.recent,
+                         scale=w.scale, dtype=w.dtype)
+    check_close(got, want, w.dtype, "tiny prefill 512")
+    for step in range(1, w.steps + 1):
+        L = w.context + step
+        cache.append_logical(K, V, L - 1, L)
+        q1 = q_decode(w, step)
+        got = to_host_f64(cache.decode(q1), w.dtype)
+        want = oracle_decode(w, q1, K, V, np.array([L]), cache.mask)
+        check_close(got, want, w.dtype, f"tiny decode step {step}")
+
+
+def test_llama3_8b_gqa_decode_batch8_ctx32768():
+    w = synth.llama3_8b_decode()
+    say(f"workload {w.name}")
+    L = w.context
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, L, synth.S_K)
+    V = logical_kv(w, L, synth.S_V)
+    cache.append_logical(K, V, 0, L - 1, chunk=8192)
+    cache.append_logical(K, V, L - 1, L)          # the decoded token
+    q = q_decode(w, 0)
+    got = to_host_f64(cache.decode(q), w.dtype)
+    want = oracle_decode(w, q, K, V, np.full(w.batch, L), cache.mask)
+    check_close(got, want, w.dtype, w.name)
+    # spot-check slot placement on the big pools: pages of sequence 0 against the oracle's gather
+    kp = to_host_bits(cache.k_pool, w.dtype)
+    vp = to_host_bits(cache.v_pool, w.dtype)
+    for h in range(w.num_kv_heads):
+        ret = bool(cache.mask[h])
+        pos = np.arange(L) if ret else np.r_[np.arange(w.sink), np.arange(L - 256, L)]
+        kg, vg = oracle.gather(kp, vp, cache.table_h, 0, h, pos, retrieval=ret, sink=w.sink,
+                               block_size=w.block_size, ring_blocks=w.ring_blocks)
+        assert kg.tobytes() == K[0, h, pos].tobytes()
+        assert vg.tobytes() == V[0, h, pos].tobytes()
+
+
+def test_llama2_7b_mha_chunked_prefill_sampled_rows():
+    w = synth.llama2_7b_chunked_prefill()
+    say(f"workload {w.name}")
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, w.context, synth.S_K)
+    V = logical_kv(w, w.context, synth.S_V)
+    rng = np.random.default_rng(99)
+    for c in range(w.steps):
+        lo = c * w.q_len
+        cache.append_logical(K, V, lo, lo + w.q_len, chunk=w.q_len)
+        q = q_prefill(w, c, w.q_len)
+        got = to_host_f64(cache.prefill(q), w.dtype)
+        rows_i = sorted(set([0, 1, 127, 128, 2047, w.q_len - 1] +
+                            rng.integers(0, w.q_len, 6).tolist()))
+        rows = [(0, i, hq) for hq in range(w.num_q_heads) for i in rows_i]
+        want = oracle.attend(q, K, V, np.array([lo + w.q_len]), cache.mask, sink=w.sink,
+                             recent=w.recent, scale=w.scale, dtype=w.dtype, rows=rows)
+        sel = np.zeros(got.shape[:3], bool)
+        for b, i, hq in rows:
+            sel[b, i, hq] = True
+        check_close(got[sel], want[sel], w.dtype, f"chunk {c} ({len(rows)} rows)")
+        assert np.isfinite(got).all()
+
+
+def test_gemma_2b_mqa_static_decode_with_garbage_past_lengths():
+    w = synth.gemma_2b_static_decode()
+    say(f"workload {w.name}")
+    cap = w.context
+    lens = synth.valid_lengths(w, 1024, cap)
+    K = logical_kv(w, cap, synth.S_K)
+    V = logical_kv(w, cap, synth.S_V)
+    for b in range(w.batch):    # slots past each length hold arbitrary bits (NaN/Inf included)
+        n = cap - int(lens[b])
+        K[b, 0, lens[b]:] = synth.garbage_bits(w.seed, 0, b, shape=(n, w.head_dim), dtype=w.dtype)
+        V[b, 0, lens[b]:] = synth.garbage_bits(w.seed, 1, b, shape=(n, w.head_dim), dtype=w.dtype)
+    cache = Cache(w, fill="nan", identity=True)
+    cache.append_logical(K, V, 0, cap, chunk=4096)
+    cache.set_lens(lens)
+    q = q_decode(w, 0)
+    got = to_host_f64(cache.decode(q), w.dtype)
+    want = oracle_decode(w, q, K, V, lens, cache.mask)
+    check_close(got, want, w.dtype, w.name)
+
+
+@pytest.mark.timeout(600)
+def test_long_context_decode_1m_tokens_64_steps():
+    w = synth.long_context_decode()
+    say(f"workload {w.name}")
+    L0 = w.context
+    cache = Cache(w, fill="nan")
+    mask = cache.mask
+    # fill 1,048,576 tokens head by head in 64K-token pieces (setup, not checked here)
+    piece = 65536
+    for s in range(0, L0, piece):
+        kn = np.empty((1, piece, w.num_kv_heads, w.head_dim), np.uint16)
+        vn = np.empty_like(kn)
+        for h in range(w.num_kv_heads):
+            kn[0, :, h] = synth.f32_to_storage(synth.kv_tokens(w, synth.S_K, 0, h, s, s + piece), w.dtype)
+            vn[0, :, h] = synth.f32_to_storage(synth.kv_tokens(w, synth.S_V, 0, h, s, s + piece), w.dtype)
+        cache.append(kn, vn)
+    say("  filled")
+    check_steps = {1, 32, 64}
+    Lf = L0 + w.steps
+    full = {}
+    for h in range(w.num_kv_heads):
+        if mask[h]:
+            full[h] = (oracle.to_f64(synth.f32_to_storage(synth.kv_tokens(w, synth.S_K, 0, h, 0, Lf), w.dtype), w.dtype),
+                       oracle.to_f64(synth.f32_to_storage(synth.kv_tokens(w, synth.S_V, 0, h, 0, Lf), w.dtype), w.dtype))
+    for step in range(1, w.steps + 1):
+        L = L0 + step
+        kn = np.empty((1, 1, w.num_kv_heads, w.head_dim), np.uint16)
+        vn = np.empty_like(kn)
+        for h in range(w.num_kv_heads):
+            kn[0, 0, h] = synth.f32_to_storage(synth.kv_tokens(w, synth.S_K, 0, h, L - 1, L), w.dtype)[0]
+            vn[0, 0, h] = synth.f32_to_storage(synth.kv_tokens(w, synth.S_V, 0, h, L - 1, L), w.dtype)[0]
+        cache.append(kn, vn)
+        q = q_decode(w, step)
+        out = cache.decode(q)
+        if step not in check_steps:
+            continue
+        got = to_host_f64(out, w.dtype)
+        want = np.empty_like(got)
+        for hq in range(w.num_q_heads):
+            h = hq // w.group
+            J = oracle.visible_positions(L - 1, retrieval=bool(mask[h]), sink=w.sink,
+                                         recent=w.recent)
+            if mask[h]:
+                Kf, Vf = full[h]
+                Kj, Vj = Kf[J], Vf[J]
+            else:
+                # sinks then the recent window (disjoint at this length)
+                assert J.tolist() == list(range(w.sink)) + list(range(L - w.recent, L))
+                parts = [(0, w.sink), (L - w.recent, L)]
+                Kj = oracle.to_f64(np.concatenate([synth.f32_to_storage(
+                    synth.kv_tokens(w, synth.S_K, 0, h, a, e), w.dtype) for a, e in parts]), w.dtype)
+                Vj = oracle.to_f64(np.concatenate([synth.f32_to_storage(
+                    synth.kv_tokens(w, synth.S_V, 0, h, a, e), w.dtype) for a, e in parts]), w.dtype)
+            want[0, hq] = oracle.attend_row(oracle.to_f64(q[0, hq], w.dtype), Kj, Vj, w.scale)
+        check_close(got, want, w.dtype, f"1M decode step {step}")
