@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-head KV-cache attention path on one MI355X.
+
+Decode leg (the headline number): Llama-3-8B-shaped decode, batch 8, 32768 valid tokens, 32 q / 8 kv
+heads, 4 retrieval kv heads, sink 64 / recent 256, bf16, pages of 16. One step = append one token
+per sequence (kv_append_circular) + duo_attn_decode. Four layers' caches are rotated so that every
+step reads cache lines last touched >1.5 GB earlier (the 256 MB Infinity Cache cannot serve them).
+value = algorithmic decode bytes per step / wall time per step.
+
+Prefill leg: Llama-2-7B-shaped MHA chunked prefill, eight 4096-token chunks building a 32768-token
+context, 8 of 32 heads retrieval, sink 128 / recent 1024. One pass = 8 x (append chunk + prefill).
+Reported as algorithmic TFLOP/s (4 * head_dim per visible (query, key) pair).
+
+Inputs are seeded synthetic tensors (synth/), already resident in HBM when timing starts.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode attn HBM GB/s + prefill TFLOP/s (% of MI355X roofline), mixed heads"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "duo_common.h", "duo_kernels.h"],
+    "prefill": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "kv_cache_sparsity_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the source."""
+    try:
+        with open(COUNTERS) as fh:
+            c = json.load(fh).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not c or c.get("source_sha") != source_sha(kernel):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+# ---- algorithmic units ---------------------------------------------------------------------------
+def visible_count(p: np.ndarray, retrieval: bool, sink: int, recent: int) -> np.ndarray:
+    """Number of keys a query at position p sees (union of sinks and the recent window)."""
+    p = np.asarray(p, dtype=np.int64)
+    n = np.maximum(p + 1, 0)
+    if retrieval:
+        return n
+    a = np.minimum(sink, n)                               # [0, min(sink, p+1))
+    b_lo = np.maximum(p - recent + 1, 0)
+    b = np.maximum(p + 1 - b_lo, 0)                       # [b_lo, p+1)
+    overlap = np.maximum(np.minimum(sink, p + 1) - b_lo, 0)
+    return a + b - overlap
+
+
+def decode_bytes(w: synth.Workload, lens: np.ndarray) -> int:
+    """K+V rows each head must read + q + out + block-table entries."""
+    row = 2 * w.head_dim * w.elem_bytes
+    total = 0
+    for b in range(w.batch):
+        L = int(lens[b])
+        for h in range(w.num_kv_heads):
+            ret = h in w.retrieval
+            n = int(visible_count(np.array([L - 1]), ret, w.sink, w.recent)[0])
+            total += n * row
+            if ret:
+                pages = -(-L // w.block_size)
+            else:
+                sink_pages = -(-min(w.sink, L) // w.block_size)
+                lo = max(w.sink, L - w.recent)
+                ring_pages = 0
+                if L > w.sink:
+                    ring_pages = (L - 1 - w.sink) // w.block_size - (lo - w.sink) // w.block_size + 1
+                pages = sink_pages + ring_pages
+            total += pages * 4
+    total += 2 * w.batch * w.num_q_heads * w.head_dim * w.elem_bytes
+    return total
+
+
+def prefill_flops(w: synth.Workload, L: int, q_len: int) -> int:
+    p = np.arange(L - q_len, L)
+    total = 0
+    for hq in range(w.num_q_heads):
+        ret = (hq // w.group) in w.retrieval
+        total += int(visible_count(p, ret, w.sink, w.recent).sum())
+    return 4 * w.head_dim * total * w.batch
+
+
+# ---- device helpers --------------------------------------------------------------------------
+def to_dev(torch, arr, dtype, device):
+    if dtype == synth.F32:
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+    return t.view(torch.bfloat16 if dtype == synth.BF16 else torch.float16)
+
+
+def logical_bits(w, L, which):
+    out = np.empty((w.batch, w.num_kv_heads, L, w.head_dim), dtype=synth.storage_np_dtype(w.dtype))
+    for b in range(w.batch):
+        for h in range(w.num_kv_heads):
+            out[b, h] = synth.f32_to_storage(synth.kv_tokens(w, which, b, h, 0, L), w.dtype)
+    return out
+
+
+def torch_dtype(torch, dtype):
+    return {synth.F32: torch.float32, synth.F16: torch.float16, synth.BF16: torch.bfloat16}[dtype]
+
+
+# ---- decode leg ------------------------------------------------------------------------------
+def decode_leg(args, torch, duo):
+    w = synth.llama3_8b_decode()
+    dev = torch.device("cuda:0")
+    L = w.context
+    log(f"[decode] generating {w.name}")
+    K = logical_bits(w, L, synth.S_K)
+    V = logical_bits(w, L, synth.S_V)
+    table_h, nblocks = synth.block_table(w)
+    table = torch.from_numpy(table_h).to(dev)
+    mask = w.retrieval_mask
+    tdt = torch_dtype(torch, w.dtype)
+    ks = (nblocks, w.block_size, w.head_dim)
+    vs = (nblocks, w.head_dim, w.block_size)
+    layers = []
+    zero = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    after = torch.empty_like(zero)
+    for li in range(args.layers):
+        kp = torch.empty(ks, dtype=tdt, device=dev)
+        vp = torch.empty(vs, dtype=tdt, device=dev)
+        if li == 0:
+            for s in range(0, L - 1, 8192):
+                e = min(L - 1, s + 8192)
+                kn = to_dev(torch, K[:, :, s:e].transpose(0, 2, 1, 3), w.dtype, dev)
+                vn = to_dev(torch, V[:, :, s:e].transpose(0, 2, 1, 3), w.dtype, dev)
+                lb = torch.full((w.batch,), s, dtype=torch.int32, device=dev)
+                duo.kv_append_circular(kp, vp, table, kn, vn, lb, after, mask, w.sink, w.recent,
+                                       w.ring_blocks)
+        else:
+            kp.copy_(layers[0][0])
+            vp.copy_(layers[0][1])
+        layers.append((kp, vp))
+    # the token decoded at every step (position L-1) and its query
+    k_tok = to_dev(torch, K[:, :, L - 1:L].transpose(0, 2, 1, 3), w.dtype, dev)
+    v_tok = to_dev(torch, V[:, :, L - 1:L].transpose(0, 2, 1, 3), w.dtype, dev)
+    q_bits = synth.f32_to_storage(synth.queries(w, 0, q_len=1)[:, 0], w.dtype)
+    q = to_dev(torch, q_bits, w.dtype, dev)
+    out = torch.empty_like(q)
+    ws = duo.decode_workspace(q, table, w.block_size)
+    lens_before = torch.full((w.batch,), L - 1, dtype=torch.int32, device=dev)
+    lens = torch.empty_like(lens_before)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kp, vp = layers[i % len(layers)]
+        duo.kv_append_circular(kp, vp, table, k_tok, v_tok, lens_before, lens, mask, w.sink,
+                               w.recent, w.ring_blocks)
+        if ev is not None:
+            ev[0].record()
+        duo.duo_attn_decode(q, kp, vp, table, lens, mask, w.sink, w.recent, w.ring_blocks,
+                            w.scale, out, ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    nbytes = decode_bytes(w, np.full(w.batch, L))
+    traffic = measured_traffic("decode")
+    res = {
+        "w": w, "K": K, "V": V, "q_bits": q_bits, "out": out,
+        "value": nbytes / step_s / 1e9, "ms_per_step": step_s * 1e3, "bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / kern_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "duo::decode_kernel<bf16,128>",
+                     "kernel_us": round(kern_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    log(f"[decode] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
+        f"{res['value']:.0f} GB/s per step, {nbytes / kern_s / 1e9:.0f} GB/s kernel")
+    return res
+
+
+# ---- prefill leg -----------------------------------------------------------------------------
+def prefill_leg(args, torch, duo):
+    w = synth.llama2_7b_chunked_prefill()
+    dev = torch.device("cuda:0")
+    log(f"[prefill] generating {w.name}")
+    L = w.context
+    K = logical_bits(w, L, synth.S_K)
+    V = logical_bits(w, L, synth.S_V)
+    table_h, nblocks = synth.block_table(w)
+    table = torch.from_numpy(table_h).to(dev)
+    mask = w.retrieval_mask
+    tdt = torch_dtype(torch, w.dtype)
+    kp = torch.empty((nblocks, w.block_size, w.head_dim), dtype=tdt, device=dev)
+    vp = torch.empty((nblocks, w.head_dim, w.block_size), dtype=tdt, device=dev)
+    chunks = []
+    for c in range(w.steps):
+        s, e = c * w.q_len, (c + 1) * w.q_len
+        kn = to_dev(torch, K[:, :, s:e].transpose(0, 2, 1, 3), w.dtype, dev)
+        vn = to_dev(torch, V[:, :, s:e].transpose(0, 2, 1, 3), w.dtype, dev)
+        q = to_dev(torch, synth.f32_to_storage(synth.queries(w, c), w.dtype), w.dtype, dev)
+        lb = torch.full((w.batch,), s, dtype=torch.int32, device=dev)
+        la = torch.full((w.batch,), e, dtype=torch.int32, device=dev)
+        chunks.append((kn, vn, q, lb, la, torch.empty_like(q)))
+    del K, V
+    torch.cuda.synchronize()
+
+    def one_pass(evs=None):
+        for c, (kn, vn, q, lb, la, out) in enumerate(chunks):
+            duo.kv_append_circular(kp, vp, table, kn, vn, lb, la, mask, w.sink, w.recent,
+                                   w.ring_blocks)
+            if evs is not None:
+                evs[c][0].record()
+            duo.duo_attn_prefill(q, kp, vp, table, la, mask, w.sink, w.recent, w.ring_blocks,
+                                 w.scale, out)
+            if evs is not None:
+                evs[c][1].record()
+
+    for _ in range(args.prefill_warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    all_evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in chunks] for _ in range(args.prefill_passes)]
+    t0 = time.perf_counter()
+    for p in range(args.prefill_passes):
+        one_pass(all_evs[p])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pass_s = (t1 - t0) / args.prefill_passes
+    per_chunk_flops = [prefill_flops(w, (c + 1) * w.q_len, w.q_len) for c in range(w.steps)]
+    flops = sum(per_chunk_flops)
+    kern = np.array([[a.elapsed_time(b) * 1e-3 for a, b in pe] for pe in all_evs]).mean(axis=0)
+    kern_total = float(kern.sum())
+    traffic = measured_traffic("prefill")
+    res = {
+        "workload": w.name, "value": round(flops / pass_s / 1e12, 2), "unit": "TFLOP/s",
+        "ms_per_pass": round(pass_s * 1e3, 3), "flops_per_pass": flops,
+        "chunk7_tflops": round(per_chunk_flops[-1] / kern[-1] / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(flops / kern_total / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / kern_total / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "duo::prefill_kernel<bf16,128>",
+                     "kernel_us_per_chunk": [round(x * 1e6, 1) for x in kern]},
+    }
+    log(f"[prefill] pass {pass_s * 1e3:.3f} ms, kernels {kern_total * 1e3:.3f} ms, "
+        f"{res['value']} TFLOP/s per pass, {res['roofline']['achieved']} TFLOP/s kernels")
+    return res
+
+
+# ---- CPU baseline: the oracle on a bounded sample ----------------------------------------------
+def cpu_baseline(dec, budget_s: float):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w, K, V, q_bits = dec["w"], dec["K"], dec["V"], dec["q_bits"]
+    L = w.context
+    done, spent, nbytes = 0, 0.0, 0
+    per_seq = decode_bytes(synth.replace(w, batch=1), np.array([L]))
+    while done < w.batch and (spent < budget_s or done == 0):
+        b = done
+        t0 = time.perf_counter()
+        oracle.attend(q_bits[b:b + 1, None], K[b:b + 1], V[b:b + 1], np.array([L]), w.retrieval_mask,
+                      sink=w.sink, recent=w.recent, scale=w.scale, dtype=w.dtype)
+        spent += time.perf_counter() - t0
+        nbytes += per_seq
+        done += 1
+    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences of the decode workload (all 32 q heads), "
+                      f"{spent:.1f} s of fp64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=4, help="decode caches rotated across steps")
+    ap.add_argument("--prefill-passes", type=int, default=5)
+    ap.add_argument("--prefill-warmup", type=int, default=1)
+    ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its "
+              "own share of heads; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_sparsity_amd as duo
+    duo.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    legs = set(args.legs.split(","))
+    dec = decode_leg(args, torch, duo) if "decode" in legs else None
+    pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
+    cpu = None
+    if dec is not None and not args.no_cpu_baseline:
+        log("[cpu] timing the oracle")
+        cpu = cpu_baseline(dec, args.cpu_budget)
+    w = synth.llama3_8b_decode()
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 1) if dec else None,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4) if dec else None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V/Q, random page placement)",
+        "config": {"workload": w.name, "batch": w.batch, "context": w.context,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "retrieval_kv_heads": list(w.retrieval), "sink": w.sink, "recent": w.recent,
+                   "block_size": w.block_size, "layers_rotated": args.layers,
+                   "step": "kv_append_circular(1 token/seq) + duo_attn_decode",
+                   "algorithmic_bytes_per_step": dec["bytes"] if dec else None},
+        "roofline": dec["roofline"] if dec else None,
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
