@@ -180,6 +180,7 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                            head_is_retrieval);
   if (st != DUO_OK) return st;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
   if (num_q_heads / num_kv_heads > 16) return DUO_ERR_UNSUPPORTED;
   uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
   int32_t n_ret, n_str;
@@ -243,6 +244,7 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
   if (st != DUO_OK) return st;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
   if (q_len < 1) return DUO_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
   if (dtype == DUO_F32 && head_dim > 128) return DUO_ERR_UNSUPPORTED;
   uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
   int32_t n_ret, n_str;

@@ -45,6 +45,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ int sm_ticket;
+  __shared__ int32_t sm_page[kRunSeg];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -81,27 +82,26 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
   geo.ring_slots = p.ring_slots;
 
   // ---- the item's runs ----------------------------------------------------------------------
-  int32_t n_runs, split_t0 = 0, n_sink_runs = 0, k_lo = 0, win_lo = 0;
+  RunList rl;
+  rl.ret = ret;
+  rl.L = L;
+  rl.first = rl.n_sink = rl.k_lo = rl.ring_lo = 0;
   if (ret) {
-    split_t0 = split * p.split_tokens;
-    const int32_t end = min(L, split_t0 + p.split_tokens);
-    n_runs = end > split_t0 ? (end - split_t0 + 15) / 16 : 0;
+    const int32_t t0 = split * p.split_tokens;
+    const int32_t end = min(L, t0 + p.split_tokens);
+    rl.first = t0 / 16;
+    rl.n = end > t0 ? (end - t0 + 15) / 16 : 0;
   } else {
-    n_sink_runs = (min(p.sink, L) + 15) / 16;
-    win_lo = max(p.sink, L - p.recent);
+    rl.n_sink = (min(p.sink, L) + 15) / 16;
+    rl.ring_lo = max(p.sink, L - p.recent);
     int32_t n_ring = 0;
     if (L > p.sink) {
-      k_lo = (win_lo - p.sink) / 16;
-      n_ring = (L - 1 - p.sink) / 16 - k_lo + 1;
+      rl.k_lo = (rl.ring_lo - p.sink) / 16;
+      n_ring = (L - 1 - p.sink) / 16 - rl.k_lo + 1;
     }
-    n_runs = n_sink_runs + n_ring;
+    rl.n = rl.n_sink + n_ring;
   }
-  auto run_at = [&](int32_t v) -> Run {
-    if (v >= n_runs) return geo.empty_run();
-    if (ret) return geo.retrieval_run(split_t0 / 16 + v, L);
-    if (v < n_sink_runs) return geo.sink_run(v, L);
-    return geo.ring_run(k_lo + (v - n_sink_runs), win_lo, L);
-  };
+  const int32_t n_runs = rl.n;
 
   const T* kpool = static_cast<const T*>(p.k_pool);
   const T* vpool = static_cast<const T*>(p.v_pool);
@@ -120,75 +120,94 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
 #pragma unroll
     for (int i = 0; i < DT; ++i) oT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    const int n_steps = (n_runs + 1) / 2;
 
-    for (int step = wave; step < n_steps; step += kDecodeWaves) {
-      const Run ra = run_at(2 * step), rb = run_at(2 * step + 1);
-      // K rows: MFMA row r of tile t holds key 8*(r/4) + 4*t + r%4 of the 32-key step; keys 0..15
-      // are run a, 16..31 run b.
-      v8<T> kA[2][KC];
-      {
-        const int r = col;
-        const Run& rk = (r >> 3) ? rb : ra;
-        const T* base = kpool + rk.page * page_elems + (int64_t)rk.row0 * D + quad * 8;
+    // K rows of step j: MFMA row r of tile t holds key 8*(r/4) + 4*t + r%4 of the 32-key step
+    // (keys 0..15 are the step's first run, 16..31 its second). V^T: channel dt*16 + col, keys
+    // 8*quad .. 8*quad+7 of the step.
+    v8<T> kA[2][KC], vA[DT];
+    auto load_k = [&](int32_t seg0, int step) {
+      const int r = col;
+      const int v = 2 * step + (r >> 3);
+      const Run run = rl.at(geo, seg0 + v);
+      const int32_t page = sm_page[min(v, kRunSeg - 1)];
+      const T* base = kpool + page * page_elems + (int64_t)geo.row0(run.slot) * D + quad * 8;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+      for (int t = 0; t < 2; ++t) {
+        const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
 #pragma unroll
-          for (int c = 0; c < KC; ++c) kA[t][c] = load8(base + krow * D + c * 32);
+        for (int c = 0; c < KC; ++c) kA[t][c] = load8(base + krow * D + c * 32);
+      }
+    };
+    auto load_v = [&](int32_t seg0, int step) {
+      const int v = 2 * step + (quad >> 1);
+      const Run run = rl.at(geo, seg0 + v);
+      const int32_t page = sm_page[min(v, kRunSeg - 1)];
+      const T* base = vpool + page * page_elems + geo.row0(run.slot) + (quad & 1) * 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vA[dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
+    };
+
+    for (int32_t seg0 = 0; seg0 < n_runs; seg0 += kRunSeg) {
+      const int32_t nseg = min(kRunSeg, n_runs - seg0);
+      if (seg0 > 0) __syncthreads();   // everyone is done with the previous segment's pages
+      load_pages<kThreads>(sm_page, geo, rl, seg0, nseg);
+      for (int i = nseg + (int)threadIdx.x; i < kRunSeg && i < nseg + 2; i += kThreads) sm_page[i] = 0;
+      __syncthreads();
+      const int n_steps = (nseg + 1) / 2;
+      int step = wave;
+      if (step < n_steps) {
+        load_k(seg0, step);
+        load_v(seg0, step);
+      }
+      for (; step < n_steps; step += kDecodeWaves) {
+        const int nxt = step + kDecodeWaves;
+        const bool has_next = nxt < n_steps;
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int c = 0; c < KC; ++c) s[t] = mfma16(kA[t][c], qT[c], s[t]);
+        if (has_next) load_k(seg0, nxt);   // next step's K streams in during this step's math
+
+        // Lane holds keys t0 + vrow + i, i = 4*t + j (the same keys as its V^T operand).
+        const Run rv = rl.at(geo, seg0 + 2 * step + (quad >> 1));
+        const int32_t key0 = rv.t0 + (quad & 1) * 8;
+        uint32_t keep = 0;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int32_t t = key0 + i;
+          const bool ok = (t >= rv.lo) && (t < rv.hi);
+          keep |= (uint32_t)ok << i;
+          x[i] = ok ? s[i >> 2][i & 3] * p.scale_log2 : -INFINITY;
         }
-      }
-      // V^T rows: head-dim channel dt*16 + col, keys 8*quad .. 8*quad+7 of the step.
-      const Run& rv = (quad >> 1) ? rb : ra;
-      const int vrow = (quad & 1) * 8;
-      v8<T> vA[DT];
-      {
-        const T* base = vpool + rv.page * page_elems + rv.row0 + vrow;
+        float mx = x[0];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vA[dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
-      }
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float psum = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < 8; ++i) {
+          x[i] = fast_exp2(x[i] - m_use);
+          psum += x[i];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        const v8<T> pB = pack8<T>(x);
+        if (keep != 0xFFu) {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) s[t] = mfma16(kA[t][c], qT[c], s[t]);
-
-      // Lane holds keys rv.t0 + vrow + i, i = 4*t + j (same keys as its V^T operand).
-      const int32_t key0 = rv.t0 + vrow;
-      uint32_t keep = 0;
-      float x[8];
+          for (int dt = 0; dt < DT; ++dt) vA[dt] = select8<T>(vA[dt], keep);
+        }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int32_t t = key0 + i;
-        const bool ok = (t >= rv.lo) && (t < rv.hi);
-        keep |= (uint32_t)ok << i;
-        x[i] = ok ? s[i >> 2][i & 3] * p.scale_log2 : -INFINITY;
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = fast_exp2(x[i] - m_use);
-        psum += x[i];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      const v8<T> pB = pack8<T>(x);
-      if (keep != 0xFFu) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vA[dt] = select8<T>(vA[dt], keep);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        oT[dt] *= alpha;
-        oT[dt] = mfma16(vA[dt], pB, oT[dt]);
+        for (int dt = 0; dt < DT; ++dt) {
+          oT[dt] *= alpha;
+          oT[dt] = mfma16(vA[dt], pB, oT[dt]);
+        }
+        if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
       }
     }
     // lanes sharing a column hold partial sums over disjoint keys
@@ -224,10 +243,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
         T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G + g) * D;
         o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
       } else {
-        part[g * (D + 2) + d] = num;
+        store_coherent(part + g * (D + 2) + d, num);
         if (d == 0) {
-          part[g * (D + 2) + D] = M;
-          part[g * (D + 2) + D + 1] = den;
+          store_coherent(part + g * (D + 2) + D, M);
+          store_coherent(part + g * (D + 2) + D + 1, den);
         }
       }
     }
@@ -242,31 +261,34 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
   }
 
   // ---- split merge: the last item of (b, h) to arrive reduces all partials ------------------
-  __threadfence();
+  // Partials were written with device-coherent (write-through) stores; waiting for them to
+  // complete before the ticket makes them visible to whichever workgroup, on any XCD, draws the
+  // last ticket, which reads them back with device-coherent loads. No cache-wide write-back or
+  // invalidate is needed, so other workgroups' cached K/V lines are left alone.
+  wait_stores_complete();
   __syncthreads();
   int32_t* ctr = p.counter + (int64_t)b * p.num_kv_heads + h;
-  if (tid == 0) sm_ticket = atomicAdd(ctr, 1);
+  if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sm_ticket != p.n_split - 1) return;
-  __threadfence();
   const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
   const float* base = p.partial + (((int64_t)b * p.num_kv_heads + h) * p.n_split) * G * (D + 2);
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
     float M = -INFINITY;
-    for (int s = 0; s < n_act; ++s) M = fmaxf(M, __builtin_nontemporal_load(base + (s * G + g) * (D + 2) + D));
+    for (int s = 0; s < n_act; ++s) M = fmaxf(M, load_coherent(base + (s * G + g) * (D + 2) + D));
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float num = 0.f, den = 0.f;
     for (int s = 0; s < n_act; ++s) {
       const float* rec = base + (s * G + g) * (D + 2);
-      const float c = fast_exp2(__builtin_nontemporal_load(rec + D) - Mu);
-      num += c * __builtin_nontemporal_load(rec + d);
-      den += c * __builtin_nontemporal_load(rec + D + 1);
+      const float c = fast_exp2(load_coherent(rec + D) - Mu);
+      num += c * load_coherent(rec + d);
+      den += c * load_coherent(rec + D + 1);
     }
     T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G + g) * D;
     o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
   }
-  if (tid == 0) atomicExch(ctr, 0);
+  if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T>

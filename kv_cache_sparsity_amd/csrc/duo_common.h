@@ -94,68 +94,79 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Device-scope coherent store / load (write-through / read-through the XCD-local L2): used for
+// the few bytes that one workgroup hands to another within a launch.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding memory operations have completed.
+__device__ __forceinline__ void wait_stores_complete() {
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ int clamp_page(int32_t phys, int32_t num_blocks) {
   return min(max(phys, 0), num_blocks - 1);
 }
 
-// A 16-token run of one head's logical positions and where it lives: t0 is the first position,
-// `page` the physical page, `row0` the first row inside that page (0 unless block_size > 16).
-// Keys t in [lo, hi) are present and may be attended; `windowed` marks a streaming head's ring
-// run, whose keys are further limited to the recent window of each query.
+// A 16-position run of one head's logical positions: t0 is the first position and `slot` the
+// slot holding it (pages hold >= 16 slots and runs start at multiples of 16 slots, so a run never
+// spans pages). Keys t in [lo, hi) are present and may be attended; `windowed` marks a streaming
+// head's ring run, whose keys are further limited to the recent window of each query.
 struct Run {
-  int32_t t0, page, row0, lo, hi;
+  int32_t t0, slot, lo, hi;
   bool windowed;
 };
 
-// Which 16-position runs a head exposes (pages hold >= 16 positions, so a run never spans pages):
+// Which 16-position runs a head exposes:
 //   retrieval: runs at t0 = 16 g, g = 0, 1, ...   (slot t0)
 //   streaming: sink runs at t0 = 16 j while 16 j < sink (slot t0);
 //              ring runs at t0 = sink + 16 k       (slot SB*bs + (16 k mod ring_slots))
+// Run positions are pure arithmetic; the page of a slot is one block-table read (page_of).
 struct HeadGeom {
   const int32_t* row;     // this (sequence, kv head)'s block-table row
   int32_t num_blocks, log2_bs, sink, sink_blocks, ring_slots;
-  __device__ __forceinline__ void locate(int32_t slot, int32_t& page, int32_t& row0) const {
-    page = clamp_page(row[slot >> log2_bs], num_blocks);
-    row0 = slot & ((1 << log2_bs) - 1);
+  __device__ __forceinline__ int32_t page_of(int32_t slot) const {
+    return clamp_page(row[slot >> log2_bs], num_blocks);
+  }
+  __device__ __forceinline__ int32_t row0(int32_t slot) const {
+    return slot & ((1 << log2_bs) - 1);
   }
   __device__ __forceinline__ Run retrieval_run(int32_t g, int32_t L) const {
-    Run r;
-    r.t0 = g * 16;
-    locate(r.t0, r.page, r.row0);
-    r.lo = 0;
-    r.hi = L;
-    r.windowed = false;
-    return r;
+    return Run{g * 16, g * 16, 0, L, false};
   }
   __device__ __forceinline__ Run sink_run(int32_t j, int32_t L) const {
-    Run r;
-    r.t0 = j * 16;
-    locate(r.t0, r.page, r.row0);
-    r.lo = 0;
-    r.hi = min(sink, L);
-    r.windowed = false;
-    return r;
+    return Run{j * 16, j * 16, 0, min(sink, L), false};
   }
   __device__ __forceinline__ Run ring_run(int32_t k, int32_t lo, int32_t L) const {
-    Run r;
-    r.t0 = sink + k * 16;
     const int32_t off = (int32_t)(((int64_t)k * 16) % ring_slots);
-    locate((sink_blocks << log2_bs) + off, r.page, r.row0);
-    r.lo = lo;
-    r.hi = L;
-    r.windowed = true;
-    return r;
+    return Run{sink + k * 16, (sink_blocks << log2_bs) + off, lo, L, true};
   }
-  __device__ __forceinline__ Run empty_run() const {
-    Run r;
-    r.t0 = 0;
-    r.page = 0;
-    r.row0 = 0;
-    r.lo = 0;
-    r.hi = 0;
-    r.windowed = false;
-    return r;
+  __device__ __forceinline__ Run empty_run() const { return Run{0, 0, 0, 0, false}; }
+};
+
+// Runs of one work item, enumerated 0 .. n-1: a retrieval key range, or a streaming head's sink
+// runs followed by the ring runs meeting a window.
+struct RunList {
+  bool ret;
+  int32_t n, first, n_sink, k_lo, ring_lo, L;
+  __device__ __forceinline__ Run at(const HeadGeom& g, int32_t v) const {
+    if (v >= n) return g.empty_run();
+    if (ret) return g.retrieval_run(first + v, L);
+    if (v < n_sink) return g.sink_run(v, L);
+    return g.ring_run(k_lo + (v - n_sink), ring_lo, L);
   }
 };
+
+// Page ids of a segment of runs, staged in LDS so that no K/V load waits on a table read.
+constexpr int kRunSeg = 512;
+
+template <int kThreads>
+__device__ __forceinline__ void load_pages(int32_t* sm_page, const HeadGeom& g, const RunList& rl,
+                                           int32_t seg0, int32_t nseg) {
+  for (int i = threadIdx.x; i < nseg; i += kThreads) sm_page[i] = g.page_of(rl.at(g, seg0 + i).slot);
+}
 
 }  // namespace duo

@@ -55,12 +55,13 @@ struct Tile {
 };
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParams p) {
   using TL = Tile<T, D>;
   constexpr int DC = D / 16;  // k-steps over the head dim (16 channels per 32x32 MFMA step)
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   __shared__ __attribute__((aligned(16))) T k_lds[2][kKeys * TL::kKStride];
   __shared__ __attribute__((aligned(16))) T v_lds[2][D * TL::kVStride];
+  __shared__ int32_t sm_page[kRunSeg];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rcol = lane & 31;  // MFMA column = query row within the wave
@@ -105,31 +106,31 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
   geo.sink_blocks = p.sink_blocks;
   geo.ring_slots = p.ring_slots;
 
-  int32_t n_runs = 0, n_sink_runs = 0, k_lo = 0;
+  RunList rl;
+  rl.ret = ret;
+  rl.L = L;
+  rl.n = rl.first = rl.n_sink = rl.k_lo = 0;
+  rl.ring_lo = p.sink;   // ring keys are present from the sink on; the window is per row
   if (p_hi >= 0) {
     if (ret) {
-      n_runs = p_hi / 16 + 1;
+      rl.n = p_hi / 16 + 1;
     } else {
-      n_sink_runs = (min(p.sink, p_hi + 1) + 15) / 16;
+      rl.n_sink = (min(p.sink, p_hi + 1) + 15) / 16;
       int32_t n_ring = 0;
       if (p_hi >= p.sink) {
-        k_lo = (max(p.sink, p_lo - p.recent + 1) - p.sink) / 16;
-        n_ring = (p_hi - p.sink) / 16 - k_lo + 1;
+        rl.k_lo = (max(p.sink, p_lo - p.recent + 1) - p.sink) / 16;
+        n_ring = (p_hi - p.sink) / 16 - rl.k_lo + 1;
       }
-      n_runs = n_sink_runs + n_ring;
+      rl.n = rl.n_sink + n_ring;
     }
   }
-  auto run_at = [&](int32_t v) -> Run {
-    if (v >= n_runs) return geo.empty_run();
-    if (ret) return geo.retrieval_run(v, L);
-    if (v < n_sink_runs) return geo.sink_run(v, L);
-    return geo.ring_run(k_lo + (v - n_sink_runs), p.sink, L);
-  };
+  const int32_t n_runs = rl.n;
 
   const T* kpool = static_cast<const T*>(p.k_pool);
   const T* vpool = static_cast<const T*>(p.v_pool);
   const int64_t page_elems = (int64_t)D << p.log2_bs;
   const int bs = 1 << p.log2_bs;
+  int32_t seg0 = 0;   // first run whose page id sits in sm_page[0]
 
   // ---- staging of one tile: global -> registers -> LDS --------------------------------------
   u32x4 k_stage[TL::kKPer], v_stage[TL::kVPer];
@@ -138,9 +139,11 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
     for (int it = 0; it < TL::kKPer; ++it) {
       const int idx = it * kThreads + tid;
       const int kt = idx / (D / TL::kChunk), c = idx % (D / TL::kChunk);
-      const Run r = run_at(tile * 4 + kt / 16);
+      const int v = tile * 4 + kt / 16;
+      const Run r = rl.at(geo, v);
       if (r.lo < r.hi) {
-        const T* src = kpool + r.page * page_elems + (int64_t)(r.row0 + (kt & 15)) * D + c * TL::kChunk;
+        const int32_t page = sm_page[v - seg0];
+        const T* src = kpool + page * page_elems + (int64_t)(geo.row0(r.slot) + (kt & 15)) * D + c * TL::kChunk;
         k_stage[it] = *reinterpret_cast<const u32x4*>(src);
       } else {
         k_stage[it] = u32x4{0u, 0u, 0u, 0u};
@@ -153,21 +156,23 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
       const int run = idx / (D * per_d);
       const int rem = idx % (D * per_d);
       const int d = rem / per_d, c = rem % per_d;
-      const Run r = run_at(tile * 4 + run);
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      const int v = tile * 4 + run;
+      const Run r = rl.at(geo, v);
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
       const int32_t t0 = r.t0 + c * TL::kChunk;
       if (r.lo < r.hi && t0 + TL::kChunk > r.lo && t0 < r.hi) {
-        const T* src = vpool + r.page * page_elems + (int64_t)d * bs + r.row0 + c * TL::kChunk;
-        v = *reinterpret_cast<const u32x4*>(src);
+        const int32_t page = sm_page[v - seg0];
+        const T* src = vpool + page * page_elems + (int64_t)d * bs + geo.row0(r.slot) + c * TL::kChunk;
+        val = *reinterpret_cast<const u32x4*>(src);
         if (t0 < r.lo || t0 + TL::kChunk > r.hi) {
           // zero the channel values of absent keys (their bits may be NaN or Inf)
-          T* e = reinterpret_cast<T*>(&v);
+          T* e = reinterpret_cast<T*>(&val);
 #pragma unroll
           for (int i = 0; i < TL::kChunk; ++i)
             if (t0 + i < r.lo || t0 + i >= r.hi) e[i] = T(0.0f);
         }
       }
-      v_stage[it] = v;
+      v_stage[it] = val;
     }
   };
   auto stage_store = [&](int buf) {
@@ -212,6 +217,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
 
   const int n_tiles = (n_runs + 3) / 4;
   if (n_tiles > 0) {
+    load_pages<kThreads>(sm_page, geo, rl, 0, min(kRunSeg, n_runs));
+    __syncthreads();
     stage_load(0);
     stage_store(0);
   }
@@ -219,14 +226,21 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
-    if (tile + 1 < n_tiles) stage_load(tile + 1);
+    if (tile + 1 < n_tiles) {
+      if ((((tile + 1) * 4) % kRunSeg) == 0) {   // next tile starts a new segment of page ids
+        seg0 = (tile + 1) * 4;
+        load_pages<kThreads>(sm_page, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
+        __syncthreads();
+      }
+      stage_load(tile + 1);
+    }
 
     // classify this tile's runs for the wave's rows
     Run runs[4];
     bool all_full = true, any_vis = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      runs[i] = run_at(tile * 4 + i);
+      runs[i] = rl.at(geo, tile * 4 + i);
       const Run& r = runs[i];
       const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
       const bool present = a < e;
@@ -255,13 +269,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
         }
       }
       // accumulator 4*i + j of block b2 is key 8*half + 4*(i&1) + j of run 2*b2 + (i>>1)
-      float x[2][16];
-      if (all_full) {
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int k = 0; k < 16; ++k) x[b2][k] = s[b2][k] * p.scale_log2;
-      } else {
+      if (!all_full) {
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
@@ -272,31 +280,39 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
               const int32_t t = r.t0 + 8 * half + 4 * (i & 1) + j;
               const bool ok = t >= r.lo && t < r.hi && t <= my_p &&
                               (!r.windowed || my_p - t < p.recent);
-              x[b2][4 * i + j] = ok ? s[b2][4 * i + j] * p.scale_log2 : -INFINITY;
+              s[b2][4 * i + j] = ok ? s[b2][4 * i + j] : -INFINITY;
             }
           }
       }
+      // Row max of the raw scores (softmax_scale > 0, so scaling after the max is exact).
       float mx = -INFINITY;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int k = 0; k < 16; ++k) mx = fmaxf(mx, x[b2][k]);
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+        for (int k = 0; k < 16; ++k) mx = fmaxf(mx, s[b2][k]);
+      mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
+      // Lazy reference max: it moves only when some row of the wave exceeds it by more than 8
+      // (log2 units), so p <= 256 and O / l are rescaled on few tiles. The final O / l is exact
+      // whatever reference was used.
+      if (__any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oT[db] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float x[2][16];
       float psum = 0.f;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          x[b2][k] = fast_exp2(x[b2][k] - m_use);
+          x[b2][k] = fast_exp2(fmaf(s[b2][k], p.scale_log2, -m_use));
           psum += x[b2][k];
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oT[db] *= alpha;
+      l_run += psum;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
