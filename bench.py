@@ -308,6 +308,73 @@ def cpu_baseline(dec, budget_s: float):
                       f"{spent:.1f} s of fp64 NumPy"}
 
 
+# ---- rocprofv3 counter bookkeeping -------------------------------------------------------------
+COPY_KERNEL_HINT = "copy"   # the device-to-device copy (a runtime blit kernel) has "copy" in its name
+CALIBRATION_REPS = 3
+
+
+def calibrate_copy(torch, mib: int, reps: int = CALIBRATION_REPS):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[calibrate] copied {mib} MiB x {reps}")
+
+
+def _read_counter_csv(path):
+    import csv
+    rows = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            rows.append(r)
+    return rows
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: str, command: str):
+    """Per-launch HBM bytes of the decode and prefill kernels from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), scaled by what the same counters read for a
+    copy of copy_mib MiB. Writes profiles/counters.json keyed by kernel, with the source hash."""
+    def per_kernel(path, counter):
+        acc, copies = {}, []
+        for r in _read_counter_csv(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            val = float(r["Counter_Value"]) * 1024.0          # counters are KiB per dispatch
+            if "decode_kernel" in name:
+                acc.setdefault("decode", []).append(val)
+            elif "prefill_kernel" in name:
+                acc.setdefault("prefill", []).append(val)
+            elif COPY_KERNEL_HINT in name.lower():
+                copies.append((int(r["Dispatch_Id"]), val))
+        # the calibration copies are the last CALIBRATION_REPS copy dispatches of the run
+        copies.sort()
+        if copies:
+            acc["copy"] = [v for _, v in copies[-CALIBRATION_REPS:]]
+        return {k: float(np.mean(v)) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    known = float(copy_mib << 20)
+    f_scale = known / fetch["copy"] if fetch.get("copy") else 1.0
+    w_scale = known / write["copy"] if write.get("copy") else 1.0
+    out = {"calibration": {"copy_bytes": known, "fetch_raw": fetch.get("copy"),
+                           "write_raw": write.get("copy"), "fetch_scale": f_scale,
+                           "write_scale": w_scale, "command": command}}
+    for k in ("decode", "prefill"):
+        if k in fetch and k in write:
+            out[k] = {"source_sha": source_sha(k),
+                      "fetch_bytes_per_launch": fetch[k] * f_scale,
+                      "write_bytes_per_launch": write[k] * w_scale,
+                      "hbm_bytes_per_launch": fetch[k] * f_scale + write[k] * w_scale,
+                      "dispatches": [nf.get(k), nw.get(k)]}
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,7 +386,16 @@ def main():
     ap.add_argument("--legs", default="decode,prefill")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs into profiles/counters.json")
+    ap.add_argument("--counters-command", default="", help="command recorded with the summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1],
+                           args.calibrate_copy, COUNTERS, args.counters_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its "
               "own share of heads; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -334,6 +410,8 @@ def main():
     legs = set(args.legs.split(","))
     dec = decode_leg(args, torch, duo) if "decode" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
     cpu = None
     if dec is not None and not args.no_cpu_baseline:
         log("[cpu] timing the oracle")

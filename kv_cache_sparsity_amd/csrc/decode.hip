@@ -38,14 +38,14 @@ namespace {
 constexpr int kThreads = kDecodeWaves * kWave;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(const DecodeParams p) {
   constexpr int KC = D / 32;  // k-steps of S^T over the head dim
   constexpr int DT = D / 16;  // 16-row tiles of O^T
   __shared__ float sm_o[kDecodeWaves][16][D];
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ int sm_ticket;
-  __shared__ int32_t sm_page[kRunSeg];
+  __shared__ int32_t sm_page[kRunSeg + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -121,39 +121,49 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
     for (int i = 0; i < DT; ++i) oT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // K rows of step j: MFMA row r of tile t holds key 8*(r/4) + 4*t + r%4 of the 32-key step
-    // (keys 0..15 are the step's first run, 16..31 its second). V^T: channel dt*16 + col, keys
-    // 8*quad .. 8*quad+7 of the step.
-    v8<T> kA[2][KC], vA[DT];
+    // A wave step covers kChunks 32-key chunks (4 runs of 16 keys). In chunk c, K tile t' (two
+    // per chunk) puts key 8*(r/4) + 4*t' + r%4 of the chunk in MFMA row r, so the S^T accumulator
+    // a lane holds for chunk c is keys 8*quad .. 8*quad+7 of the chunk: exactly the keys of its
+    // V^T operand (channel dt*16 + col) and of its P^T operand.
+    constexpr int kChunks = 1;
+    constexpr int kRunsPerStep = 2 * kChunks;
+    v8<T> kA[kChunks][2][KC], vA[kChunks][DT];
     auto load_k = [&](int32_t seg0, int step) {
       const int r = col;
-      const int v = 2 * step + (r >> 3);
-      const Run run = rl.at(geo, seg0 + v);
-      const int32_t page = sm_page[min(v, kRunSeg - 1)];
-      const T* base = kpool + page * page_elems + (int64_t)geo.row0(run.slot) * D + quad * 8;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+      for (int c = 0; c < kChunks; ++c) {
+        const int v = kRunsPerStep * step + 2 * c + (r >> 3);
+        const Run run = rl.at(geo, seg0 + v);
+        const int32_t page = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const T* base = kpool + page * page_elems + (int64_t)geo.row0(run.slot) * D + quad * 8;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) kA[t][c] = load8(base + krow * D + c * 32);
+        for (int t = 0; t < 2; ++t) {
+          const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) kA[c][t][kc] = load8(base + krow * D + kc * 32);
+        }
       }
     };
     auto load_v = [&](int32_t seg0, int step) {
-      const int v = 2 * step + (quad >> 1);
-      const Run run = rl.at(geo, seg0 + v);
-      const int32_t page = sm_page[min(v, kRunSeg - 1)];
-      const T* base = vpool + page * page_elems + geo.row0(run.slot) + (quad & 1) * 8;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vA[dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
+      for (int c = 0; c < kChunks; ++c) {
+        const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
+        const Run run = rl.at(geo, seg0 + v);
+        const int32_t page = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const T* base = vpool + page * page_elems + geo.row0(run.slot) + (quad & 1) * 8;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vA[c][dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
+      }
     };
 
     for (int32_t seg0 = 0; seg0 < n_runs; seg0 += kRunSeg) {
       const int32_t nseg = min(kRunSeg, n_runs - seg0);
       if (seg0 > 0) __syncthreads();   // everyone is done with the previous segment's pages
       load_pages<kThreads>(sm_page, geo, rl, seg0, nseg);
-      for (int i = nseg + (int)threadIdx.x; i < kRunSeg && i < nseg + 2; i += kThreads) sm_page[i] = 0;
+      // runs past the end of the list read page 0 (valid memory, fully masked)
+      for (int i = nseg + (int)threadIdx.x; i < nseg + kRunsPerStep; i += kThreads) sm_page[i] = 0;
       __syncthreads();
-      const int n_steps = (nseg + 1) / 2;
+      const int n_steps = (nseg + kRunsPerStep - 1) / kRunsPerStep;
       int step = wave;
       if (step < n_steps) {
         load_k(seg0, step);
@@ -162,50 +172,69 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
       for (; step < n_steps; step += kDecodeWaves) {
         const int nxt = step + kDecodeWaves;
         const bool has_next = nxt < n_steps;
-        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        f32x4 s[kChunks][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-          for (int c = 0; c < KC; ++c) s[t] = mfma16(kA[t][c], qT[c], s[t]);
+          for (int t = 0; t < 2; ++t) {
+            s[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) s[c][t] = mfma16(kA[c][t][kc], qT[kc], s[c][t]);
+          }
         if (has_next) load_k(seg0, nxt);   // next step's K streams in during this step's math
 
-        // Lane holds keys t0 + vrow + i, i = 4*t + j (the same keys as its V^T operand).
-        const Run rv = rl.at(geo, seg0 + 2 * step + (quad >> 1));
-        const int32_t key0 = rv.t0 + (quad & 1) * 8;
-        uint32_t keep = 0;
-        float x[8];
+        // Lane holds keys t0 + 8*(quad&1) + i of run 2c + quad/2, i = 4*t + j.
+        uint32_t keep[kChunks];
+        bool full = true;
+        float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int32_t t = key0 + i;
-          const bool ok = (t >= rv.lo) && (t < rv.hi);
-          keep |= (uint32_t)ok << i;
-          x[i] = ok ? s[i >> 2][i & 3] * p.scale_log2 : -INFINITY;
+        for (int c = 0; c < kChunks; ++c) {
+          const Run rv = rl.at(geo, seg0 + kRunsPerStep * step + 2 * c + (quad >> 1));
+          const int32_t key0 = rv.t0 + (quad & 1) * 8;
+          keep[c] = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int32_t t = key0 + i;
+            keep[c] |= (uint32_t)((t >= rv.lo) && (t < rv.hi)) << i;
+          }
+          full = full && keep[c] == 0xFFu;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float e = ((keep[c] >> i) & 1u) ? s[c][i >> 2][i & 3] : -INFINITY;
+            s[c][i >> 2][i & 3] = e;
+            mloc = fmaxf(mloc, e);
+          }
         }
-        float mx = x[0];
+        mloc *= p.scale_log2;   // softmax_scale > 0: max commutes with the scale
+        // Lazy reference max, shared by the four lanes of a column: it moves only when a score
+        // exceeds it by more than 8 (log2 units), so the cross-lane max and the O rescale run on
+        // few steps; p = 2^(x - m_run) <= 256 in between.
+        if (__any(mloc > m_run + 8.f)) {
+          float mx = fmaxf(mloc, shfl_xor(mloc, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          x[i] = fast_exp2(x[i] - m_use);
-          psum += x[i];
+          for (int dt = 0; dt < DT; ++dt) oT[dt] *= alpha;
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        const v8<T> pB = pack8<T>(x);
-        if (keep != 0xFFu) {
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) vA[dt] = select8<T>(vA[dt], keep);
-        }
+        for (int c = 0; c < kChunks; ++c) {
+          float x[8];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          oT[dt] *= alpha;
-          oT[dt] = mfma16(vA[dt], pB, oT[dt]);
+          for (int i = 0; i < 8; ++i) {
+            x[i] = fast_exp2(fmaf(s[c][i >> 2][i & 3], p.scale_log2, -m_use));
+            l_run += x[i];
+          }
+          const v8<T> pB = pack8<T>(x);
+          if (!full) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vA[c][dt] = select8<T>(vA[c][dt], keep[c]);
+          }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
         }
         if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
       }
@@ -271,19 +300,34 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeParams p) 
   if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sm_ticket != p.n_split - 1) return;
+  // One pass over the partials, online: a chunk of kMergeChunk splits is loaded at once (one
+  // round trip per chunk), then folded into the running (M, num, den) of each (q head, channel).
+  constexpr int kMergeChunk = 16;
   const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
   const float* base = p.partial + (((int64_t)b * p.num_kv_heads + h) * p.n_split) * G * (D + 2);
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int s = 0; s < n_act; ++s) M = fmaxf(M, load_coherent(base + (s * G + g) * (D + 2) + D));
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < n_act; ++s) {
-      const float* rec = base + (s * G + g) * (D + 2);
-      const float c = fast_exp2(load_coherent(rec + D) - Mu);
-      num += c * load_coherent(rec + d);
-      den += c * load_coherent(rec + D + 1);
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = 0; s0 < n_act; s0 += kMergeChunk) {
+      float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
+#pragma unroll
+      for (int i = 0; i < kMergeChunk; ++i) {
+        const float* rec = base + (int64_t)(min(s0 + i, n_act - 1) * G + g) * (D + 2);
+        mv[i] = load_coherent(rec + D);
+        lv[i] = load_coherent(rec + D + 1);
+        ov[i] = load_coherent(rec + d);
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeChunk; ++i) {
+        if (s0 + i < n_act) {
+          const float mn = fmaxf(M, mv[i]);
+          const float keep = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
+          const float c = fast_exp2(mv[i] - mn);
+          num = num * keep + c * ov[i];
+          den = den * keep + c * lv[i];
+          M = mn;
+        }
+      }
     }
     T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G + g) * D;
     o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
@@ -315,11 +359,12 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int gri
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
                             int32_t requested) {
   if (requested > 0) return requested;
-  // Aim for ~1024 work items if every head were a retrieval head; at least 256 keys per item
-  // (two 32-key steps per wave), at most 8192.
+  // About 512 work items if every kv head were a retrieval head (so ~one workgroup per CU at the
+  // usual mixes): fewer, longer items amortise each item's start-up round trips and its share of
+  // the split merge. Between 256 and 65536 keys per item.
   const int64_t total = (int64_t)batch * num_kv_heads * capacity_tokens;
   int64_t s = 256;
-  while (s < 8192 && s * 1024 < total) s *= 2;
+  while (s < 65536 && s * 512 < total) s *= 2;
   return (int32_t)s;
 }
 
