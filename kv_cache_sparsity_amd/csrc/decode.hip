@@ -38,7 +38,7 @@ namespace {
 constexpr int kThreads = kDecodeWaves * kWave;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(const DecodeParams p) {
   constexpr int KC = D / 32;  // k-steps of S^T over the head dim
   constexpr int DT = D / 16;  // 16-row tiles of O^T
   __shared__ float sm_o[kDecodeWaves][16][D];
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(const DecodeParams 
     // per chunk) puts key 8*(r/4) + 4*t' + r%4 of the chunk in MFMA row r, so the S^T accumulator
     // a lane holds for chunk c is keys 8*quad .. 8*quad+7 of the chunk: exactly the keys of its
     // V^T operand (channel dt*16 + col) and of its P^T operand.
-    constexpr int kChunks = 1;
+    constexpr int kChunks = 1;   // one 32-key chunk per step (measured best: two waves per SIMD)
     constexpr int kRunsPerStep = 2 * kChunks;
     v8<T> kA[kChunks][2][KC], vA[kChunks][DT];
     auto load_k = [&](int32_t seg0, int step) {
