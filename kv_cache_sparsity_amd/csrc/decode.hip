@@ -48,7 +48,8 @@ __global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(co
   __shared__ int32_t sm_page[kRunSeg + 4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int col = lane & 15;   // MFMA column = q head within the group
   const int quad = lane >> 4;  // k-group of the lane
   const int G = p.group;
@@ -133,9 +134,8 @@ __global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(co
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (r >> 3);
-        const Run run = rl.at(geo, seg0 + v);
-        const int32_t page = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
-        const T* base = kpool + page * page_elems + (int64_t)geo.row0(run.slot) * D + quad * 8;
+        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const T* base = kpool + packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D + quad * 8;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
@@ -148,9 +148,8 @@ __global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(co
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
-        const Run run = rl.at(geo, seg0 + v);
-        const int32_t page = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
-        const T* base = vpool + page * page_elems + geo.row0(run.slot) + (quad & 1) * 8;
+        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const T* base = vpool + packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vA[c][dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
       }

@@ -60,6 +60,26 @@ __device__ __forceinline__ v8<T> select8(v8<T> v, uint32_t keep) {
   return r;
 }
 
+// Zero the elements of a 16-byte chunk whose keys t0 + i fall outside [lo, hi), on the raw
+// 32-bit words (so NaN or Inf garbage is replaced, never multiplied). Element i of a chunk of
+// 16-bit values is half (i & 1) of word i / 2; a chunk of fp32 values holds one element per word.
+template <int kElemBytes>
+__device__ __forceinline__ u32x4 zero_absent(u32x4 v, int32_t t0, int32_t lo, int32_t hi) {
+  constexpr int kPerWord = 4 / kElemBytes;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < kPerWord; ++e) {
+      const int32_t t = t0 + w * kPerWord + e;
+      const uint32_t lane_bits = kPerWord == 2 ? (0xFFFFu << (16 * e)) : 0xFFFFFFFFu;
+      m |= (t >= lo && t < hi) ? lane_bits : 0u;
+    }
+    v[w] &= m;
+  }
+  return v;
+}
+
 // ---- MFMA: C[16x16] += A[16 x 8k] * B[8k x 16] over one 8-element k-step per lane ---------------
 // Lane layout (16x16 family): A row = lane % 16, B col = lane % 16, the lane's 8 k-elements belong
 // to k-group lane / 16; C: col = lane % 16, rows 4 * (lane / 16) + [0..3].
@@ -152,6 +172,13 @@ struct HeadGeom {
 struct RunList {
   bool ret;
   int32_t n, first, n_sink, k_lo, ring_lo, L;
+  // Positions only (no slot): what masks and visibility need, no division.
+  __device__ __forceinline__ Run pos(const HeadGeom& g, int32_t v) const {
+    if (v >= n) return Run{0, 0, 0, 0, false};
+    if (ret) return Run{(first + v) * 16, 0, 0, L, false};
+    if (v < n_sink) return Run{v * 16, 0, 0, min(g.sink, L), false};
+    return Run{g.sink + (k_lo + v - n_sink) * 16, 0, ring_lo, L, true};
+  }
   __device__ __forceinline__ Run at(const HeadGeom& g, int32_t v) const {
     if (v >= n) return g.empty_run();
     if (ret) return g.retrieval_run(first + v, L);
@@ -160,13 +187,21 @@ struct RunList {
   }
 };
 
-// Page ids of a segment of runs, staged in LDS so that no K/V load waits on a table read.
+// Where a segment of runs lives, staged in LDS so that no K/V load waits on a block-table read:
+// packed = page * 16 + row0 / 16 (row0 is a multiple of 16 below block_size <= 256).
 constexpr int kRunSeg = 512;
 
+__device__ __forceinline__ int32_t pack_run(int32_t page, int32_t row0) { return page * 16 + (row0 >> 4); }
+__device__ __forceinline__ int32_t packed_page(int32_t packed) { return packed >> 4; }
+__device__ __forceinline__ int32_t packed_row0(int32_t packed) { return (packed & 15) << 4; }
+
 template <int kThreads>
-__device__ __forceinline__ void load_pages(int32_t* sm_page, const HeadGeom& g, const RunList& rl,
+__device__ __forceinline__ void load_pages(int32_t* sm_run, const HeadGeom& g, const RunList& rl,
                                            int32_t seg0, int32_t nseg) {
-  for (int i = threadIdx.x; i < nseg; i += kThreads) sm_page[i] = g.page_of(rl.at(g, seg0 + i).slot);
+  for (int i = threadIdx.x; i < nseg; i += kThreads) {
+    const int32_t slot = rl.at(g, seg0 + i).slot;
+    sm_run[i] = pack_run(g.page_of(slot), g.row0(slot));
+  }
 }
 
 }  // namespace duo

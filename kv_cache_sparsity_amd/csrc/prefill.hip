@@ -13,9 +13,10 @@
 //   streaming head: the sink runs, then the ring runs covering [p_lo - recent + 1, p_hi].
 // So a streaming tile costs about (sink + recent + 128) keys whatever the context length. Four
 // runs (64 keys) form one K/V tile, staged into LDS (double-buffered, next tile's global loads in
-// flight during this tile's math). Per wave and tile, each run is classified as fully visible,
-// invisible or partial for the wave's 32 rows: fully invisible tiles are skipped, fully visible
-// tiles skip the element mask.
+// flight during this tile's math). Where each run lives (page, row) is resolved once per segment
+// of 512 runs into LDS; inside the tile loop a run is a base pointer plus per-thread constant
+// offsets. Per wave and tile, each run is classified as fully visible, invisible or partial for
+// the wave's 32 rows: fully invisible tiles are skipped, fully visible tiles skip the element mask.
 //
 // MFMA formulation (32x32x16, k-step of 8 elements per lane), per 32-key block:
 //   S^T[key, row] = sum_d K[key, d] Q[row, d]       A = K rows (LDS), B = Q^T (registers)
@@ -48,11 +49,23 @@ struct Tile {
   static constexpr int kKStride = D + kPad;        // K tile: [64 keys][D]
   static constexpr int kVStride = kKeys + kPad;    // V tile: [D][64 keys]
   static constexpr int kChunk = 16 / sizeof(T);    // elements per 16-byte chunk
-  static constexpr int kKChunks = kKeys * D / kChunk;
-  static constexpr int kVChunks = D * kKeys / kChunk;
-  static constexpr int kKPer = kKChunks / kThreads;
-  static constexpr int kVPer = kVChunks / kThreads;
+  static constexpr int kRowChunks = D / kChunk;    // 16-byte chunks per K row
+  static constexpr int kRunChunks = 16 / kChunk;   // 16-byte chunks per V channel per run
+  static constexpr int kKPer = kKeys * kRowChunks / kThreads;
+  static constexpr int kVPer = D * 4 * kRunChunks / kThreads;
 };
+
+// Element offsets and key ranges of the four runs of a tile (uniform values).
+struct TileRuns {
+  int64_t kofs[4];   // K rows of run i: k_pool + kofs[i] + row * D
+  int64_t vofs[4];   // V channels of run i: v_pool + vofs[i] + d * block_size
+  int32_t t0[4], lo[4], hi[4];
+};
+
+template <typename V>
+__device__ __forceinline__ V sel4(const V (&a)[4], int i) {
+  return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
+}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParams p) {
@@ -61,9 +74,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   __shared__ __attribute__((aligned(16))) T k_lds[2][kKeys * TL::kKStride];
   __shared__ __attribute__((aligned(16))) T v_lds[2][D * TL::kVStride];
-  __shared__ int32_t sm_page[kRunSeg];
+  __shared__ int32_t sm_run[kRunSeg];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int rcol = lane & 31;  // MFMA column = query row within the wave
   const int half = lane >> 5;  // k-group of the lane
   const int G = p.group;
@@ -130,48 +144,48 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   const T* vpool = static_cast<const T*>(p.v_pool);
   const int64_t page_elems = (int64_t)D << p.log2_bs;
   const int bs = 1 << p.log2_bs;
-  int32_t seg0 = 0;   // first run whose page id sits in sm_page[0]
+  int32_t seg0 = 0;   // first run whose location sits in sm_run[0]
+
+  auto tile_runs = [&](int tile, TileRuns& tr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tile * 4 + i;
+      const Run r = rl.pos(geo, v);
+      const int32_t pr = sm_run[min(max(v - seg0, 0), kRunSeg - 1)];
+      const int32_t page = v < n_runs ? packed_page(pr) : 0;      // absent runs read page 0
+      const int32_t r0 = v < n_runs ? packed_row0(pr) : 0;        // (their keys are masked)
+      const int64_t pe = (int64_t)page * page_elems;
+      tr.kofs[i] = pe + (int64_t)r0 * D;
+      tr.vofs[i] = pe + r0;
+      tr.t0[i] = r.t0;
+      tr.lo[i] = r.lo;
+      tr.hi[i] = r.hi;
+    }
+  };
 
   // ---- staging of one tile: global -> registers -> LDS --------------------------------------
   u32x4 k_stage[TL::kKPer], v_stage[TL::kVPer];
-  auto stage_load = [&](int tile) {
+  auto stage_load = [&](const TileRuns& tr) {
 #pragma unroll
     for (int it = 0; it < TL::kKPer; ++it) {
       const int idx = it * kThreads + tid;
-      const int kt = idx / (D / TL::kChunk), c = idx % (D / TL::kChunk);
-      const int v = tile * 4 + kt / 16;
-      const Run r = rl.at(geo, v);
-      if (r.lo < r.hi) {
-        const int32_t page = sm_page[v - seg0];
-        const T* src = kpool + page * page_elems + (int64_t)(geo.row0(r.slot) + (kt & 15)) * D + c * TL::kChunk;
-        k_stage[it] = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        k_stage[it] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int kt = idx / TL::kRowChunks, c = idx % TL::kRowChunks;
+      // rows of absent keys may hold anything: their scores are masked by position
+      k_stage[it] = *reinterpret_cast<const u32x4*>(kpool + sel4(tr.kofs, kt >> 4) + (kt & 15) * D +
+                                                    c * TL::kChunk);
     }
 #pragma unroll
     for (int it = 0; it < TL::kVPer; ++it) {
       const int idx = it * kThreads + tid;
-      constexpr int per_d = 16 / TL::kChunk;               // chunks per channel per run
-      const int run = idx / (D * per_d);
-      const int rem = idx % (D * per_d);
-      const int d = rem / per_d, c = rem % per_d;
-      const int v = tile * 4 + run;
-      const Run r = rl.at(geo, v);
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      const int32_t t0 = r.t0 + c * TL::kChunk;
-      if (r.lo < r.hi && t0 + TL::kChunk > r.lo && t0 < r.hi) {
-        const int32_t page = sm_page[v - seg0];
-        const T* src = vpool + page * page_elems + (int64_t)d * bs + geo.row0(r.slot) + c * TL::kChunk;
-        val = *reinterpret_cast<const u32x4*>(src);
-        if (t0 < r.lo || t0 + TL::kChunk > r.hi) {
-          // zero the channel values of absent keys (their bits may be NaN or Inf)
-          T* e = reinterpret_cast<T*>(&val);
-#pragma unroll
-          for (int i = 0; i < TL::kChunk; ++i)
-            if (t0 + i < r.lo || t0 + i >= r.hi) e[i] = T(0.0f);
-        }
-      }
+      const int run = idx / (D * TL::kRunChunks);
+      const int rem = idx % (D * TL::kRunChunks);
+      const int d = rem / TL::kRunChunks, c = rem % TL::kRunChunks;
+      u32x4 val = *reinterpret_cast<const u32x4*>(vpool + sel4(tr.vofs, run) + (int64_t)d * bs +
+                                                  c * TL::kChunk);
+      const int32_t t0 = sel4(tr.t0, run) + c * TL::kChunk;
+      const int32_t lo = sel4(tr.lo, run), hi = sel4(tr.hi, run);
+      // the channel values of absent keys may be NaN or Inf: zero them
+      if (t0 < lo || t0 + TL::kChunk > hi) val = zero_absent<sizeof(T)>(val, t0, lo, hi);
       v_stage[it] = val;
     }
   };
@@ -179,17 +193,16 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
 #pragma unroll
     for (int it = 0; it < TL::kKPer; ++it) {
       const int idx = it * kThreads + tid;
-      const int kt = idx / (D / TL::kChunk), c = idx % (D / TL::kChunk);
+      const int kt = idx / TL::kRowChunks, c = idx % TL::kRowChunks;
       const int lrow = (kt & 32) + perm32(kt & 31);
       *reinterpret_cast<u32x4*>(&k_lds[buf][lrow * TL::kKStride + c * TL::kChunk]) = k_stage[it];
     }
 #pragma unroll
     for (int it = 0; it < TL::kVPer; ++it) {
       const int idx = it * kThreads + tid;
-      constexpr int per_d = 16 / TL::kChunk;
-      const int run = idx / (D * per_d);
-      const int rem = idx % (D * per_d);
-      const int d = rem / per_d, c = rem % per_d;
+      const int run = idx / (D * TL::kRunChunks);
+      const int rem = idx % (D * TL::kRunChunks);
+      const int d = rem / TL::kRunChunks, c = rem % TL::kRunChunks;
       *reinterpret_cast<u32x4*>(&v_lds[buf][d * TL::kVStride + run * 16 + c * TL::kChunk]) = v_stage[it];
     }
   };
@@ -216,10 +229,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   const int32_t my_p = p_lo + wrow0 + rcol;          // this lane's query position
 
   const int n_tiles = (n_runs + 3) / 4;
+  TileRuns tr_next;
   if (n_tiles > 0) {
-    load_pages<kThreads>(sm_page, geo, rl, 0, min(kRunSeg, n_runs));
+    load_pages<kThreads>(sm_run, geo, rl, 0, min(kRunSeg, n_runs));
     __syncthreads();
-    stage_load(0);
+    tile_runs(0, tr_next);
+    stage_load(tr_next);
     stage_store(0);
   }
   __syncthreads();
@@ -227,12 +242,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
     if (tile + 1 < n_tiles) {
-      if ((((tile + 1) * 4) % kRunSeg) == 0) {   // next tile starts a new segment of page ids
+      if ((((tile + 1) * 4) % kRunSeg) == 0) {   // next tile starts a new segment of runs
         seg0 = (tile + 1) * 4;
-        load_pages<kThreads>(sm_page, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
+        load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
         __syncthreads();
       }
-      stage_load(tile + 1);
+      tile_runs(tile + 1, tr_next);
+      stage_load(tr_next);
     }
 
     // classify this tile's runs for the wave's rows
@@ -240,7 +256,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
     bool all_full = true, any_vis = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      runs[i] = rl.at(geo, tile * 4 + i);
+      runs[i] = rl.pos(geo, tile * 4 + i);
       const Run& r = runs[i];
       const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
       const bool present = a < e;
