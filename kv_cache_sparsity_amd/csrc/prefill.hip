@@ -11,27 +11,36 @@
 // workgroup walks only the 16-key runs that can be visible to its rows:
 //   retrieval head: runs 0 .. p_hi / 16;
 //   streaming head: the sink runs, then the ring runs covering [p_lo - recent + 1, p_hi].
-// So a streaming tile costs about (sink + recent + 128) keys whatever the context length. Four
-// runs (64 keys) form one K/V tile, staged into LDS (double-buffered, next tile's global loads in
-// flight during this tile's math). Where each run lives (page, row) is resolved once per segment
-// of 512 runs into LDS; inside the tile loop a run is a base pointer plus per-thread constant
-// offsets. Per wave and tile, each run is classified as fully visible, invisible or partial for
-// the wave's 32 rows: fully invisible tiles are skipped, fully visible tiles skip the element mask.
+// So a streaming tile costs about (sink + recent + 128) keys whatever the context length.
+//
+// Data movement: four runs (64 keys) form one K/V tile. Tiles are copied straight from the pages
+// into a two-stage LDS ring by 16-byte global->LDS loads (no staging registers): while the waves
+// compute on one stage, the next tile streams into the other. Rows are XOR-swizzled in 16-byte
+// units instead of padded, so both the copies and the MFMA operand reads are free of LDS bank
+// conflicts. V channels of absent keys (past the valid length, unwritten sink slots) are read
+// from a zero chunk, or zeroed in LDS when a chunk is only partly absent; absent K rows are
+// masked by position. Where each run lives (page, row) is resolved once per segment of 512 runs.
+// One barrier per tile: each wave waits for its own copies of tile t, the barrier makes all of
+// them visible and frees the other stage, then the copies of tile t+1 are issued.
 //
 // MFMA formulation (32x32x16, k-step of 8 elements per lane), per 32-key block:
 //   S^T[key, row] = sum_d K[key, d] Q[row, d]       A = K rows (LDS), B = Q^T (registers)
 //   O^T[d, row]  += sum_key V^T[d, key] P^T[key, row] A = V^T (LDS, channel-major like the V page),
 //                                                     B = P^T taken from the S^T accumulators.
-// K rows are staged into LDS in a permuted order so that the eight S^T accumulators a lane holds
-// per 16-key chunk are the chunk's keys 8*(lane/32) .. +7, the k-group of its P^T operand.
+// K rows sit in LDS in a permuted order so that the eight S^T accumulators a lane holds per
+// 16-key chunk are the chunk's keys 8*(lane/32) .. +7, the k-group of its P^T operand.
 #include "duo_common.h"
 #include "duo_kernels.h"
 
 namespace duo {
 
+// Sixteen zero bytes: the source of V chunks whose keys are all absent.
+__device__ __attribute__((aligned(64))) uint32_t g_prefill_zero_chunk[16];
+
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int kRows = kPrefillRows;  // 128 query rows per workgroup
 constexpr int kKeys = 64;            // keys per K/V tile (four 16-key runs)
 
@@ -44,15 +53,18 @@ __device__ __forceinline__ int perm32(int r) {
 }
 
 template <typename T, int D>
-struct Tile {
-  static constexpr int kPad = 8;                   // row padding: one 8-element operand
-  static constexpr int kKStride = D + kPad;        // K tile: [64 keys][D]
-  static constexpr int kVStride = kKeys + kPad;    // V tile: [D][64 keys]
-  static constexpr int kChunk = 16 / sizeof(T);    // elements per 16-byte chunk
-  static constexpr int kRowChunks = D / kChunk;    // 16-byte chunks per K row
-  static constexpr int kRunChunks = 16 / kChunk;   // 16-byte chunks per V channel per run
-  static constexpr int kKPer = kKeys * kRowChunks / kThreads;
-  static constexpr int kVPer = D * 4 * kRunChunks / kThreads;
+struct TileGeo {
+  static constexpr int kChunk = 16 / sizeof(T);              // elements per 16-byte chunk
+  static constexpr int kKRowBytes = D * sizeof(T);
+  static constexpr int kKRowChunks = D / kChunk;             // chunks per K row
+  static constexpr int kKSwz = kKRowChunks < 16 ? kKRowChunks : 16;
+  static constexpr int kVRowBytes = kKeys * sizeof(T);
+  static constexpr int kVRowChunks = kKeys / kChunk;         // chunks per V channel row
+  static constexpr int kVSwz = kVRowChunks < 16 ? kVRowChunks : 16;
+  static constexpr int kKBytes = kKeys * kKRowBytes;
+  static constexpr int kVBytes = D * kVRowBytes;
+  static constexpr int kKLoadsPerWave = kKBytes / 1024 / kWaves;  // 1 KiB per wave copy
+  static constexpr int kVLoadsPerWave = kVBytes / 1024 / kWaves;
 };
 
 // Element offsets and key ranges of the four runs of a tile (uniform values).
@@ -67,13 +79,31 @@ __device__ __forceinline__ V sel4(const V (&a)[4], int i) {
   return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
 }
 
+// 8-element MFMA operand from a swizzled LDS row: logical chunk `chunk` sits at chunk ^ swz.
+template <typename T>
+__device__ __forceinline__ v8<T> lds_operand(const char* row, int chunk, int swz) {
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const v8<T>*>(row + ((chunk ^ swz) << 4));
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + ((chunk ^ swz) << 4));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + (((chunk + 1) ^ swz) << 4));
+    return v8<T>{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
+__device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParams p) {
-  using TL = Tile<T, D>;
+  using TG = TileGeo<T, D>;
   constexpr int DC = D / 16;  // k-steps over the head dim (16 channels per 32x32 MFMA step)
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) T k_lds[2][kKeys * TL::kKStride];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][D * TL::kVStride];
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TG::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TG::kVBytes];
   __shared__ int32_t sm_run[kRunSeg];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -146,67 +176,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   const int bs = 1 << p.log2_bs;
   int32_t seg0 = 0;   // first run whose location sits in sm_run[0]
 
-  auto tile_runs = [&](int tile, TileRuns& tr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tile * 4 + i;
-      const Run r = rl.pos(geo, v);
-      const int32_t pr = sm_run[min(max(v - seg0, 0), kRunSeg - 1)];
-      const int32_t page = v < n_runs ? packed_page(pr) : 0;      // absent runs read page 0
-      const int32_t r0 = v < n_runs ? packed_row0(pr) : 0;        // (their keys are masked)
-      const int64_t pe = (int64_t)page * page_elems;
-      tr.kofs[i] = pe + (int64_t)r0 * D;
-      tr.vofs[i] = pe + r0;
-      tr.t0[i] = r.t0;
-      tr.lo[i] = r.lo;
-      tr.hi[i] = r.hi;
-    }
-  };
-
-  // ---- staging of one tile: global -> registers -> LDS --------------------------------------
-  u32x4 k_stage[TL::kKPer], v_stage[TL::kVPer];
-  auto stage_load = [&](const TileRuns& tr) {
-#pragma unroll
-    for (int it = 0; it < TL::kKPer; ++it) {
-      const int idx = it * kThreads + tid;
-      const int kt = idx / TL::kRowChunks, c = idx % TL::kRowChunks;
-      // rows of absent keys may hold anything: their scores are masked by position
-      k_stage[it] = *reinterpret_cast<const u32x4*>(kpool + sel4(tr.kofs, kt >> 4) + (kt & 15) * D +
-                                                    c * TL::kChunk);
-    }
-#pragma unroll
-    for (int it = 0; it < TL::kVPer; ++it) {
-      const int idx = it * kThreads + tid;
-      const int run = idx / (D * TL::kRunChunks);
-      const int rem = idx % (D * TL::kRunChunks);
-      const int d = rem / TL::kRunChunks, c = rem % TL::kRunChunks;
-      u32x4 val = *reinterpret_cast<const u32x4*>(vpool + sel4(tr.vofs, run) + (int64_t)d * bs +
-                                                  c * TL::kChunk);
-      const int32_t t0 = sel4(tr.t0, run) + c * TL::kChunk;
-      const int32_t lo = sel4(tr.lo, run), hi = sel4(tr.hi, run);
-      // the channel values of absent keys may be NaN or Inf: zero them
-      if (t0 < lo || t0 + TL::kChunk > hi) val = zero_absent<sizeof(T)>(val, t0, lo, hi);
-      v_stage[it] = val;
-    }
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < TL::kKPer; ++it) {
-      const int idx = it * kThreads + tid;
-      const int kt = idx / TL::kRowChunks, c = idx % TL::kRowChunks;
-      const int lrow = (kt & 32) + perm32(kt & 31);
-      *reinterpret_cast<u32x4*>(&k_lds[buf][lrow * TL::kKStride + c * TL::kChunk]) = k_stage[it];
-    }
-#pragma unroll
-    for (int it = 0; it < TL::kVPer; ++it) {
-      const int idx = it * kThreads + tid;
-      const int run = idx / (D * TL::kRunChunks);
-      const int rem = idx % (D * TL::kRunChunks);
-      const int d = rem / TL::kRunChunks, c = rem % TL::kRunChunks;
-      *reinterpret_cast<u32x4*>(&v_lds[buf][d * TL::kVStride + run * 16 + c * TL::kChunk]) = v_stage[it];
-    }
-  };
-
   // ---- the wave's query rows: Q^T operand (B of S^T) ----------------------------------------
   const int wrow0 = wave * 32;                       // first row of this wave inside the tile
   const int qrow = row0 + wrow0 + rcol;              // chunk row of this lane's column
@@ -228,59 +197,113 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   float m_run = -INFINITY, l_run = 0.f;
   const int32_t my_p = p_lo + wrow0 + rcol;          // this lane's query position
 
-  const int n_tiles = (n_runs + 3) / 4;
-  TileRuns tr_next;
-  if (n_tiles > 0) {
-    load_pages<kThreads>(sm_run, geo, rl, 0, min(kRunSeg, n_runs));
-    __syncthreads();
-    tile_runs(0, tr_next);
-    stage_load(tr_next);
-    stage_store(0);
-  }
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) {
-      if ((((tile + 1) * 4) % kRunSeg) == 0) {   // next tile starts a new segment of runs
-        seg0 = (tile + 1) * 4;
-        load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
-        __syncthreads();
+  // The tile loop, specialised for retrieval / streaming heads.
+  auto body = [&](auto RET_C) {
+    constexpr bool RET = decltype(RET_C)::value;
+    auto run_pos = [&](int32_t v) -> Run {
+      if constexpr (RET) {
+        return Run{v * 16, 0, 0, v < n_runs ? L : 0, false};
+      } else {
+        return rl.pos(geo, v);
       }
-      tile_runs(tile + 1, tr_next);
-      stage_load(tr_next);
-    }
-
-    // classify this tile's runs for the wave's rows
-    Run runs[4];
-    bool all_full = true, any_vis = false;
+    };
+    auto tile_runs = [&](int tile, TileRuns& tr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      runs[i] = rl.pos(geo, tile * 4 + i);
-      const Run& r = runs[i];
-      const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
-      const bool present = a < e;
-      // Some key visible to some row: the closest (key, row) pair is key t = min(e-1, pw_hi) seen
-      // from row max(pw_lo, t).
-      const bool vis = present && a <= pw_hi &&
-                       (!r.windowed || pw_lo - min(e - 1, pw_hi) < p.recent);
-      const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= pw_lo &&
-                        (!r.windowed || pw_hi - r.t0 < p.recent);
-      all_full = all_full && full;
-      any_vis = any_vis || vis;
-    }
-
-    if (wave_live && any_vis) {
-      const T* kl = k_lds[buf];
-      const T* vl = v_lds[buf];
+      for (int i = 0; i < 4; ++i) {
+        const int v = tile * 4 + i;
+        const Run r = run_pos(v);
+        const int32_t pr = sm_run[min(max(v - seg0, 0), kRunSeg - 1)];
+        const int32_t page = v < n_runs ? packed_page(pr) : 0;   // absent runs: page 0, masked
+        const int32_t r0 = v < n_runs ? packed_row0(pr) : 0;
+        const int64_t pe = (int64_t)page * page_elems;
+        tr.kofs[i] = pe + (int64_t)r0 * D;
+        tr.vofs[i] = pe + r0;
+        tr.t0[i] = r.t0;
+        tr.lo[i] = r.lo;
+        tr.hi[i] = r.hi;
+      }
+    };
+    // Does any 16-byte V chunk of the tile mix present and absent keys?
+    auto partial_chunks = [&](const TileRuns& tr) -> bool {
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t a = max(tr.t0[i], tr.lo[i]) - tr.t0[i];
+        const int32_t e = min(tr.t0[i] + 16, tr.hi[i]) - tr.t0[i];
+        if (a < e) any = any || (a % TG::kChunk) != 0 || (e % TG::kChunk) != 0;
+      }
+      return any;
+    };
+    auto issue = [&](const TileRuns& tr, char* k_st, char* v_st) {
+#pragma unroll
+      for (int i = 0; i < TG::kKLoadsPerWave; ++i) {
+        const int inst = wave * TG::kKLoadsPerWave + i;
+        const int idx = inst * 64 + lane;
+        const int R = idx / TG::kKRowChunks, pos = idx % TG::kKRowChunks;
+        const int key = (R & 32) + perm32(R & 31);
+        const int j = pos ^ (R & (TG::kKSwz - 1));
+        // rows of absent keys may hold anything: their scores are masked by position
+        copy16_to_lds(kpool + sel4(tr.kofs, key >> 4) + (key & 15) * D + j * TG::kChunk,
+                      k_st + inst * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < TG::kVLoadsPerWave; ++i) {
+        const int inst = wave * TG::kVLoadsPerWave + i;
+        const int idx = inst * 64 + lane;
+        const int d = idx / TG::kVRowChunks, pos = idx % TG::kVRowChunks;
+        const int c = pos ^ (d & (TG::kVSwz - 1));
+        const int key0 = c * TG::kChunk;
+        const int run = key0 >> 4, koff = key0 & 15;
+        const int32_t t = sel4(tr.t0, run) + koff;
+        const bool absent = t + TG::kChunk <= sel4(tr.lo, run) || t >= sel4(tr.hi, run);
+        const void* src = absent ? static_cast<const void*>(g_prefill_zero_chunk)
+                                 : static_cast<const void*>(vpool + sel4(tr.vofs, run) + (int64_t)d * bs + koff);
+        copy16_to_lds(src, v_st + inst * 1024);
+      }
+    };
+    // Zero, in LDS, the V channels of absent keys inside partly present chunks (rare tiles).
+    auto fixup = [&](const TileRuns& tr, char* v_st) {
+      for (int idx = tid; idx < kKeys * D; idx += kThreads) {
+        const int k = idx & (kKeys - 1), d = idx / kKeys;
+        const int run = k >> 4;
+        const int32_t t = sel4(tr.t0, run) + (k & 15);
+        if (t < sel4(tr.lo, run) || t >= sel4(tr.hi, run)) {
+          const int c = k / TG::kChunk;
+          const int pos = c ^ (d & (TG::kVSwz - 1));
+          *reinterpret_cast<T*>(v_st + d * TG::kVRowBytes + pos * 16 + (k % TG::kChunk) * (int)sizeof(T)) = T(0.0f);
+        }
+      }
+    };
+    auto compute = [&](int tile, const char* k_st, const char* v_st) {
+      // classify this tile's runs for the wave's rows
+      Run runs[4];
+      bool all_full = true, any_vis = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        runs[i] = run_pos(tile * 4 + i);
+        const Run& r = runs[i];
+        const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
+        // some key visible to some row: the closest pair is key min(e-1, pw_hi) seen from row
+        // max(pw_lo, that key)
+        const bool vis = a < e && a <= pw_hi &&
+                         (!r.windowed || pw_lo - min(e - 1, pw_hi) < p.recent);
+        const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= pw_lo &&
+                          (!r.windowed || pw_hi - r.t0 < p.recent);
+        all_full = all_full && full;
+        any_vis = any_vis || vis;
+      }
+      if (!wave_live || !any_vis) return;
       f32x16 s[2];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
+        const int R = b2 * 32 + rcol;
+        const char* row = k_st + R * TG::kKRowBytes;
+        const int swz = R & (TG::kKSwz - 1);
 #pragma unroll
         for (int j = 0; j < 16; ++j) s[b2][j] = 0.f;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          const v8<T> a = load8(kl + (b2 * 32 + rcol) * TL::kKStride + dc * 16 + half * 8);
+          const v8<T> a = lds_operand<T>(row, (dc * 16 + half * 8) / TG::kChunk, swz);
           s[b2] = mfma32(a, qT[dc], s[b2]);
         }
       }
@@ -337,14 +360,50 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
           const int chunk = 2 * b2 + kc;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const v8<T> a = load8(vl + (db * 32 + rcol) * TL::kVStride + chunk * 16 + half * 8);
+            const int d = db * 32 + rcol;
+            const v8<T> a = lds_operand<T>(v_st + d * TG::kVRowBytes,
+                                           (chunk * 16 + half * 8) / TG::kChunk,
+                                           d & (TG::kVSwz - 1));
             oT[db] = mfma32(a, pB, oT[db]);
           }
         }
-    }
-    if (tile + 1 < n_tiles) stage_store(buf ^ 1);
+    };
+
+    const int n_tiles = (n_runs + 3) / 4;
+    if (n_tiles == 0) return;
+    TileRuns tr_cur, tr_next;
+    load_pages<kThreads>(sm_run, geo, rl, 0, min(kRunSeg, n_runs));
     __syncthreads();
-  }
+    tile_runs(0, tr_cur);
+    issue(tr_cur, k_lds0, v_lds0);
+    // One step per tile on a fixed stage (the loop is unrolled by two so that each stage is a
+    // distinct LDS object and copies into one never wait on reads of the other).
+    auto step = [&](int tile, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
+      wait_stores_complete();   // this wave's copies of `tile` have landed
+      __syncthreads();          // everyone's have; everyone is done with the other stage
+      if (tile + 1 < n_tiles) {
+        if ((((tile + 1) * 4) % kRunSeg) == 0) {   // next tile starts a new segment of runs
+          seg0 = (tile + 1) * 4;
+          load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
+          __syncthreads();
+        }
+        tile_runs(tile + 1, tr_next);
+        issue(tr_next, k_nxt, v_nxt);
+      }
+      if (partial_chunks(tr_cur)) {
+        fixup(tr_cur, v_cur);
+        __syncthreads();
+      }
+      compute(tile, k_cur, v_cur);
+      tr_cur = tr_next;
+    };
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      step(tile, k_lds0, v_lds0, k_lds1, v_lds1);
+      if (tile + 1 < n_tiles) step(tile + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    }
+  };
+  if (ret) body(std::integral_constant<bool, true>{});
+  else body(std::integral_constant<bool, false>{});
 
   // ---- normalise and store -----------------------------------------------------------------
   l_run += shfl_xor(l_run, 32);
