@@ -19,7 +19,9 @@ Sources (the four web pages on KV-cache sparsity):
 
 Parity status of each function is stated in its docstring; every function here is pinned by tests
 in ``tests/test_oracle_*.py`` (worked tables, brute force, a library cross-check, closed forms and
-invariants).
+invariants). Two conventions inside ``attend`` are parity unpinned by the pages, which fix neither:
+the grouping of q heads onto kv heads (contiguous, hq // (Hq / Hkv); pinned only internally by
+"repeating each kv head turns GQA into MHA") and the value of the softmax scale (an argument).
 """
 from .cache import (slot_of, table_position, append, gather, pool_shapes, to_f64,
                     new_pools, ring_capacity)
