@@ -6,22 +6,28 @@
 // positions j < sink and its recent window p - j < recent. Scores are softmax_scale * (q . k) in
 // fp32 (vLLM DualChunkAttention PR, review thread).
 //
-// Work decomposition: one workgroup (4 waves, 128 query rows, 32 per wave) per (b, q head, row
-// tile); retrieval heads' tiles come first, latest rows first (they scan the most keys). The
-// workgroup walks only the 16-key runs that can be visible to its rows:
+// Work decomposition: one workgroup per (b, q head, 128-row tile); retrieval heads' tiles come
+// first, latest rows first (they scan the most keys). The workgroup walks only the 16-key runs that
+// can be visible to its rows:
 //   retrieval head: runs 0 .. p_hi / 16;
 //   streaming head: the sink runs, then the ring runs covering [p_lo - recent + 1, p_hi].
 // So a streaming tile costs about (sink + recent + 128) keys whatever the context length.
 //
+// Inside the workgroup, four waves cover the 128 rows (32 each). Where LDS allows, there are two such
+// groups of four waves (eight waves, two per SIMD): group g takes the key tiles g, g+2, g+4, ... for
+// the same rows, and the two partial softmax states (m, l, O) are merged through LDS at the end. Two
+// waves per SIMD on the same long retrieval item let one wave's softmax and LDS reads overlap the
+// other's MFMAs.
+//
 // Data movement: four runs (64 keys) form one K/V tile. Tiles are copied straight from the pages
-// into a two-stage LDS ring by 16-byte global->LDS loads (no staging registers): while the waves
-// compute on one stage, the next tile streams into the other. Rows are XOR-swizzled in 16-byte
-// units instead of padded, so both the copies and the MFMA operand reads are free of LDS bank
-// conflicts. V channels of absent keys (past the valid length, unwritten sink slots) are read
-// from a zero chunk, or zeroed in LDS when a chunk is only partly absent; absent K rows are
-// masked by position. Where each run lives (page, row) is resolved once per segment of 512 runs.
-// One barrier per tile: each wave waits for its own copies of tile t, the barrier makes all of
-// them visible and frees the other stage, then the copies of tile t+1 are issued.
+// into LDS by 16-byte global->LDS loads (no staging registers), into a ring of two stages of one
+// tile per group: while the waves compute on one stage, the next tiles stream into the other. Rows
+// are XOR-swizzled in 16-byte units instead of padded, so both the copies and the MFMA operand
+// reads are free of LDS bank conflicts. V channels of absent keys (past the valid length, unwritten
+// sink slots) are read from a zero chunk, or zeroed in LDS when a chunk is only partly absent;
+// absent K rows are masked by position. Where each run lives (page, row) is resolved once per
+// segment of 512 runs. One barrier per step: each wave waits for its own copies, the barrier makes
+// all of them visible and frees the other stage, then the copies of the next step are issued.
 //
 // MFMA formulation (32x32x16, k-step of 8 elements per lane), per 32-key block:
 //   S^T[key, row] = sum_d K[key, d] Q[row, d]       A = K rows (LDS), B = Q^T (registers)
@@ -39,8 +45,7 @@ __device__ __attribute__((aligned(64))) uint32_t g_prefill_zero_chunk[16];
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kGroupWaves = 4;       // waves covering the workgroup's rows (32 rows each)
 constexpr int kRows = kPrefillRows;  // 128 query rows per workgroup
 constexpr int kKeys = 64;            // keys per K/V tile (four 16-key runs)
 
@@ -55,23 +60,27 @@ __device__ __forceinline__ int perm32(int r) {
 template <typename T, int D>
 struct TileGeo {
   static constexpr int kChunk = 16 / sizeof(T);              // elements per 16-byte chunk
+  // K tile: [64 keys][D], rows permuted (perm32) and 16-byte chunks XOR-swizzled by row
   static constexpr int kKRowBytes = D * sizeof(T);
   static constexpr int kKRowChunks = D / kChunk;             // chunks per K row
   static constexpr int kKSwz = kKRowChunks < 16 ? kKRowChunks : 16;
-  static constexpr int kVRowBytes = kKeys * sizeof(T);
-  static constexpr int kVRowChunks = kKeys / kChunk;         // chunks per V channel row
-  static constexpr int kVSwz = kVRowChunks < 16 ? kVRowChunks : 16;
-  static constexpr int kKBytes = kKeys * kKRowBytes;
-  static constexpr int kVBytes = D * kVRowBytes;
-  static constexpr int kKLoadsPerWave = kKBytes / 1024 / kWaves;  // 1 KiB per wave copy
-  static constexpr int kVLoadsPerWave = kVBytes / 1024 / kWaves;
-};
-
-// Element offsets and key ranges of the four runs of a tile (uniform values).
-struct TileRuns {
-  int64_t kofs[4];   // K rows of run i: k_pool + kofs[i] + row * D
-  int64_t vofs[4];   // V channels of run i: v_pool + vofs[i] + d * block_size
-  int32_t t0[4], lo[4], hi[4];
+  static constexpr int kKRunBytes = 16 * kKRowBytes;         // one 16-key run
+  static constexpr int kKBytes = 4 * kKRunBytes;
+  // V tile: [4 runs][D channels][16 keys], as in the page; the 16-byte chunks of a channel row are
+  // XOR-swizzled by (d / rows per 256 bytes) so that 32 lanes reading one chunk each of 32
+  // consecutive channels hit distinct banks
+  static constexpr int kVRowBytes = 16 * sizeof(T);          // one channel of one run
+  static constexpr int kVRowChunks = kVRowBytes / 16;
+  static constexpr int kVRowsPer256 = 256 / kVRowBytes;
+  static constexpr int kVRunBytes = D * kVRowBytes;
+  static constexpr int kVBytes = 4 * kVRunBytes;
+  // wave w of a group copies run w of its tile: 1 KiB per instruction
+  static constexpr int kKLoadsPerWave = kKRunBytes / 1024;
+  static constexpr int kVLoadsPerWave = kVRunBytes / 1024;
+  // Two groups when two stages of two tiles fit in 128 KiB of LDS, else one.
+  static constexpr int kGroups = (4 * (kKBytes + kVBytes) <= 128 * 1024) ? 2 : 1;
+  static constexpr int kThreads = kGroups * kGroupWaves * 64;
+  __device__ static __forceinline__ int vswz(int d) { return (d / kVRowsPer256) & (kVRowChunks - 1); }
 };
 
 template <typename V>
@@ -96,18 +105,23 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(const PrefillParams p) {
   using TG = TileGeo<T, D>;
+  constexpr int kThreads = TG::kThreads;
+  constexpr int kG = TG::kGroups;
   constexpr int DC = D / 16;  // k-steps over the head dim (16 channels per 32x32 MFMA step)
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TG::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TG::kVBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TG::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TG::kVBytes];
+  // stage s holds one K and one V tile per group: group g's tile at offset g * tile bytes
+  __shared__ __attribute__((aligned(1024))) char k_lds0[kG * TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[kG * TG::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[kG * TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[kG * TG::kVBytes];
   __shared__ int32_t sm_run[kRunSeg];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int grp = wave_id / kGroupWaves;   // key-tile group
+  const int wave = wave_id % kGroupWaves;  // row block of the wave
   const int rcol = lane & 31;  // MFMA column = query row within the wave
   const int half = lane >> 5;  // k-group of the lane
   const int G = p.group;
@@ -197,6 +211,24 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   float m_run = -INFINITY, l_run = 0.f;
   const int32_t my_p = p_lo + wrow0 + rcol;          // this lane's query position
 
+  // Loop-invariant per-lane copy offsets (elements) for the run a wave copies.
+  int32_t k_lane[TG::kKLoadsPerWave], v_lane[TG::kVLoadsPerWave], v_key[TG::kVLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < TG::kKLoadsPerWave; ++i) {
+    const int idx = i * 64 + lane;
+    const int rl_ = idx / TG::kKRowChunks, pos = idx % TG::kKRowChunks;   // LDS row in the run
+    const int j = pos ^ (rl_ & (TG::kKSwz - 1));                           // logical chunk
+    k_lane[i] = perm32(rl_) * D + j * TG::kChunk;                          // key perm32(row)
+  }
+#pragma unroll
+  for (int i = 0; i < TG::kVLoadsPerWave; ++i) {
+    const int idx = i * 64 + lane;
+    const int d = idx / TG::kVRowChunks, pos = idx % TG::kVRowChunks;
+    const int c = pos ^ TG::vswz(d);
+    v_key[i] = c * TG::kChunk;
+    v_lane[i] = d * bs + c * TG::kChunk;
+  }
+
   // The tile loop, specialised for retrieval / streaming heads.
   auto body = [&](auto RET_C) {
     constexpr bool RET = decltype(RET_C)::value;
@@ -207,70 +239,60 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
         return rl.pos(geo, v);
       }
     };
-    auto tile_runs = [&](int tile, TileRuns& tr) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = tile * 4 + i;
-        const Run r = run_pos(v);
-        const int32_t pr = sm_run[min(max(v - seg0, 0), kRunSeg - 1)];
-        const int32_t page = v < n_runs ? packed_page(pr) : 0;   // absent runs: page 0, masked
-        const int32_t r0 = v < n_runs ? packed_row0(pr) : 0;
-        const int64_t pe = (int64_t)page * page_elems;
-        tr.kofs[i] = pe + (int64_t)r0 * D;
-        tr.vofs[i] = pe + r0;
-        tr.t0[i] = r.t0;
-        tr.lo[i] = r.lo;
-        tr.hi[i] = r.hi;
-      }
-    };
-    // Does any 16-byte V chunk of the tile mix present and absent keys?
-    auto partial_chunks = [&](const TileRuns& tr) -> bool {
+    // Does any 16-byte V chunk of `tile` mix present and absent keys? (position arithmetic only)
+    auto partial_chunks = [&](int tile) -> bool {
       bool any = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int32_t a = max(tr.t0[i], tr.lo[i]) - tr.t0[i];
-        const int32_t e = min(tr.t0[i] + 16, tr.hi[i]) - tr.t0[i];
+        const Run r = run_pos(tile * 4 + i);
+        const int32_t a = max(r.t0, r.lo) - r.t0;
+        const int32_t e = min(r.t0 + 16, r.hi) - r.t0;
         if (a < e) any = any || (a % TG::kChunk) != 0 || (e % TG::kChunk) != 0;
       }
       return any;
     };
-    auto issue = [&](const TileRuns& tr, char* k_st, char* v_st) {
+    // Copy run `wave` of `tile` (16 keys of K and V) into the stage: a scalar page base plus the
+    // lane's loop-invariant offsets.
+    auto issue = [&](int tile, char* k_st, char* v_st) {
+      const int v = tile * 4 + wave;
+      const Run r = run_pos(v);
+      const int32_t pr = sm_run[min(max(v - seg0, 0), kRunSeg - 1)];
+      const int32_t page = v < n_runs ? packed_page(pr) : 0;   // absent runs: page 0, masked
+      const int32_t r0 = v < n_runs ? packed_row0(pr) : 0;
+      const int64_t pe = (int64_t)page * page_elems;
+      const T* kbase = kpool + pe + (int64_t)r0 * D;
+      const T* vbase = vpool + pe + r0;
 #pragma unroll
-      for (int i = 0; i < TG::kKLoadsPerWave; ++i) {
-        const int inst = wave * TG::kKLoadsPerWave + i;
-        const int idx = inst * 64 + lane;
-        const int R = idx / TG::kKRowChunks, pos = idx % TG::kKRowChunks;
-        const int key = (R & 32) + perm32(R & 31);
-        const int j = pos ^ (R & (TG::kKSwz - 1));
-        // rows of absent keys may hold anything: their scores are masked by position
-        copy16_to_lds(kpool + sel4(tr.kofs, key >> 4) + (key & 15) * D + j * TG::kChunk,
-                      k_st + inst * 1024);
-      }
+      for (int i = 0; i < TG::kKLoadsPerWave; ++i)   // absent keys' rows are masked by position
+        copy16_to_lds(kbase + k_lane[i], k_st + wave * TG::kKRunBytes + i * 1024);
 #pragma unroll
       for (int i = 0; i < TG::kVLoadsPerWave; ++i) {
-        const int inst = wave * TG::kVLoadsPerWave + i;
-        const int idx = inst * 64 + lane;
-        const int d = idx / TG::kVRowChunks, pos = idx % TG::kVRowChunks;
-        const int c = pos ^ (d & (TG::kVSwz - 1));
-        const int key0 = c * TG::kChunk;
-        const int run = key0 >> 4, koff = key0 & 15;
-        const int32_t t = sel4(tr.t0, run) + koff;
-        const bool absent = t + TG::kChunk <= sel4(tr.lo, run) || t >= sel4(tr.hi, run);
+        const int32_t t = r.t0 + v_key[i];
+        const bool absent = t + TG::kChunk <= r.lo || t >= r.hi;
         const void* src = absent ? static_cast<const void*>(g_prefill_zero_chunk)
-                                 : static_cast<const void*>(vpool + sel4(tr.vofs, run) + (int64_t)d * bs + koff);
-        copy16_to_lds(src, v_st + inst * 1024);
+                                 : static_cast<const void*>(vbase + v_lane[i]);
+        copy16_to_lds(src, v_st + wave * TG::kVRunBytes + i * 1024);
       }
     };
-    // Zero, in LDS, the V channels of absent keys inside partly present chunks (rare tiles).
-    auto fixup = [&](const TileRuns& tr, char* v_st) {
+    // Zero, in LDS, the V channels of absent keys inside partly present chunks of `tile` (rare).
+    auto fixup = [&](int tile, char* v_st) {
+      int32_t t0[4], lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const Run r = run_pos(tile * 4 + i);
+        t0[i] = r.t0;
+        lo[i] = r.lo;
+        hi[i] = r.hi;
+      }
       for (int idx = tid; idx < kKeys * D; idx += kThreads) {
         const int k = idx & (kKeys - 1), d = idx / kKeys;
         const int run = k >> 4;
-        const int32_t t = sel4(tr.t0, run) + (k & 15);
-        if (t < sel4(tr.lo, run) || t >= sel4(tr.hi, run)) {
-          const int c = k / TG::kChunk;
-          const int pos = c ^ (d & (TG::kVSwz - 1));
-          *reinterpret_cast<T*>(v_st + d * TG::kVRowBytes + pos * 16 + (k % TG::kChunk) * (int)sizeof(T)) = T(0.0f);
+        const int32_t t = sel4(t0, run) + (k & 15);
+        if (t < sel4(lo, run) || t >= sel4(hi, run)) {
+          const int c = (k & 15) / TG::kChunk;
+          const int pos = c ^ TG::vswz(d);
+          *reinterpret_cast<T*>(v_st + run * TG::kVRunBytes + d * TG::kVRowBytes + pos * 16 +
+                                (k % TG::kChunk) * (int)sizeof(T)) = T(0.0f);
         }
       }
     };
@@ -361,9 +383,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const int d = db * 32 + rcol;
-            const v8<T> a = lds_operand<T>(v_st + d * TG::kVRowBytes,
-                                           (chunk * 16 + half * 8) / TG::kChunk,
-                                           d & (TG::kVSwz - 1));
+            const v8<T> a = lds_operand<T>(v_st + chunk * TG::kVRunBytes + d * TG::kVRowBytes,
+                                           (half * 8) / TG::kChunk, TG::vswz(d));
             oT[db] = mfma32(a, pB, oT[db]);
           }
         }
@@ -371,39 +392,75 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
 
     const int n_tiles = (n_runs + 3) / 4;
     if (n_tiles == 0) return;
-    TileRuns tr_cur, tr_next;
     load_pages<kThreads>(sm_run, geo, rl, 0, min(kRunSeg, n_runs));
     __syncthreads();
-    tile_runs(0, tr_cur);
-    issue(tr_cur, k_lds0, v_lds0);
-    // One step per tile on a fixed stage (the loop is unrolled by two so that each stage is a
-    // distinct LDS object and copies into one never wait on reads of the other).
-    auto step = [&](int tile, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
-      wait_stores_complete();   // this wave's copies of `tile` have landed
+    if (grp < n_tiles) issue(grp, k_lds0 + grp * TG::kKBytes, v_lds0 + grp * TG::kVBytes);
+    // Step s: group g computes tile s * kG + g from stage s % 2 while the copies of step s + 1 fill
+    // the other stage. The loop is unrolled by two so that each stage is a distinct LDS object and
+    // copies into one never wait on reads of the other.
+    const int n_steps = (n_tiles + kG - 1) / kG;
+    auto step = [&](int s, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
+      wait_stores_complete();   // this wave's copies for step s have landed
       __syncthreads();          // everyone's have; everyone is done with the other stage
-      if (tile + 1 < n_tiles) {
-        if ((((tile + 1) * 4) % kRunSeg) == 0) {   // next tile starts a new segment of runs
-          seg0 = (tile + 1) * 4;
+      const int first_next = (s + 1) * kG;
+      if (first_next < n_tiles) {
+        if (((first_next * 4) % kRunSeg) == 0) {   // the next step starts a new segment of runs
+          seg0 = first_next * 4;
           load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
           __syncthreads();
         }
-        tile_runs(tile + 1, tr_next);
-        issue(tr_next, k_nxt, v_nxt);
+        if (first_next + grp < n_tiles)
+          issue(first_next + grp, k_nxt + grp * TG::kKBytes, v_nxt + grp * TG::kVBytes);
       }
-      if (partial_chunks(tr_cur)) {
-        fixup(tr_cur, v_cur);
+      bool fix = false;
+#pragma unroll
+      for (int g = 0; g < kG; ++g) fix = fix || (s * kG + g < n_tiles && partial_chunks(s * kG + g));
+      if (fix) {
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+          if (s * kG + g < n_tiles && partial_chunks(s * kG + g)) fixup(s * kG + g, v_cur + g * TG::kVBytes);
         __syncthreads();
       }
-      compute(tile, k_cur, v_cur);
-      tr_cur = tr_next;
+      if (s * kG + grp < n_tiles) compute(s * kG + grp, k_cur + grp * TG::kKBytes, v_cur + grp * TG::kVBytes);
     };
-    for (int tile = 0; tile < n_tiles; tile += 2) {
-      step(tile, k_lds0, v_lds0, k_lds1, v_lds1);
-      if (tile + 1 < n_tiles) step(tile + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    for (int s = 0; s < n_steps; s += 2) {
+      step(s, k_lds0, v_lds0, k_lds1, v_lds1);
+      if (s + 1 < n_steps) step(s + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
   };
   if (ret) body(std::integral_constant<bool, true>{});
   else body(std::integral_constant<bool, false>{});
+
+  // ---- merge the groups' partial states (same rows, disjoint key tiles) -----------------------
+  if constexpr (kG == 2) {
+    wait_stores_complete();
+    __syncthreads();   // the tile loop is over everywhere: the stages are free
+    // group 1 parks m, l and O^T per lane (lane-contiguous, so conflict-free); the k_lds0 / v_lds0
+    // stages hold 4 waves x DB x 16 x 64 floats, m and l go to k_lds1
+    float* park_o = reinterpret_cast<float*>(wave < 2 ? k_lds0 : v_lds0) + (wave & 1) * (DB * 16 * 64);
+    float* park_ml = reinterpret_cast<float*>(k_lds1) + wave * 128;
+    static_assert(2 * DB * 16 * 64 * 4 <= kG * TG::kKBytes && 2 * DB * 16 * 64 * 4 <= kG * TG::kVBytes,
+                  "parked O^T must fit the stage");
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) park_o[(db * 16 + j) * 64 + lane] = oT[db][j];
+      park_ml[lane] = m_run;
+      park_ml[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m_o = park_ml[lane], l_o = park_ml[64 + lane];
+    const float m_new = fmaxf(m_run, m_o);
+    const float f_me = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+    const float f_o = (m_o == -INFINITY) ? 0.f : fast_exp2(m_o - m_new);
+    l_run = l_run * f_me + l_o * f_o;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oT[db][j] = oT[db][j] * f_me + park_o[(db * 16 + j) * 64 + lane] * f_o;
+  }
 
   // ---- normalise and store -----------------------------------------------------------------
   l_run += shfl_xor(l_run, 32);
@@ -419,15 +476,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(const PrefillParam
   }
 }
 
+template <typename T, int D>
+void launch_d(const PrefillParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<T, D>), dim3(grid), dim3(TileGeo<T, D>::kThreads), 0, stream, p);
+}
+
 template <typename T>
 hipError_t launch_t(const PrefillParams& p, int head_dim, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's status
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3(grid), dim3(kThreads), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 64: launch_d<T, 64>(p, grid, stream); break;
+    case 128: launch_d<T, 128>(p, grid, stream); break;
     case 256:
       if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((prefill_kernel<T, 256>), dim3(grid), dim3(kThreads), 0, stream, p);
+        launch_d<T, 256>(p, grid, stream);
         break;
       }
       return hipErrorInvalidValue;
