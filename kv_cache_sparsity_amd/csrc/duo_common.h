@@ -50,6 +50,28 @@ __device__ __forceinline__ v8<T> pack8(const float* x) {
   return r;
 }
 
+// acc + the sum of the 8 elements of `p` (paired dot products with ones for 16-bit types, so that
+// a softmax normaliser sums exactly the rounded weights the MFMA multiplies).
+__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {__bf16(1.0f), __bf16(1.0f)};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+}
+__device__ __forceinline__ float sum8(f16x8 p, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {_Float16(1.0f), _Float16(1.0f)};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+}
+__device__ __forceinline__ float sum8(f32x8 p, float acc) {
+  return acc + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+}
+
 // Keep element i of `v` where bit i of `keep` is set, else 0. Works on the raw bits so that NaN or
 // Inf garbage is replaced, never multiplied.
 template <typename T>

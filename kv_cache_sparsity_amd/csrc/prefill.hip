@@ -48,6 +48,7 @@ namespace {
 constexpr int kGroupWaves = 4;       // waves covering the workgroup's rows (32 rows each)
 constexpr int kRows = kPrefillRows;  // 128 query rows per workgroup
 constexpr int kKeys = 64;            // keys per K/V tile (four 16-key runs)
+constexpr int kLdsAhead = 4;         // LDS operand reads kept in flight ahead of the MFMAs
 
 // Row of the 32-key block that holds key r of the block (an involution: swaps the middle two
 // groups of four in each half).
@@ -102,6 +103,23 @@ __device__ __forceinline__ v8<T> lds_operand(const char* row, int chunk, int swz
 
 __device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+// Scheduling hint for a run of `n` MFMAs whose A operands are `n` LDS reads issued in the same
+// region: keep `ahead` reads in flight (reads first, then one MFMA per further read), so that each
+// MFMA waits for a read issued `ahead` operands earlier instead of the one just before it.
+template <int n, int ahead>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+#pragma unroll
+  for (int i = 0; i < ahead; ++i) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+#pragma unroll
+  for (int i = 0; i < n - ahead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < ahead; ++i) __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
 }
 
 template <typename T, int D>
@@ -296,41 +314,32 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
         }
       }
     };
-    auto compute = [&](int tile, const char* k_st, const char* v_st) {
-      // classify this tile's runs for the wave's rows
-      Run runs[4];
-      bool all_full = true, any_vis = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        runs[i] = run_pos(tile * 4 + i);
-        const Run& r = runs[i];
-        const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
-        // some key visible to some row: the closest pair is key min(e-1, pw_hi) seen from row
-        // max(pw_lo, that key)
-        const bool vis = a < e && a <= pw_hi &&
-                         (!r.windowed || pw_lo - min(e - 1, pw_hi) < p.recent);
-        const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= pw_lo &&
-                          (!r.windowed || pw_hi - r.t0 < p.recent);
-        all_full = all_full && full;
-        any_vis = any_vis || vis;
-      }
-      if (!wave_live || !any_vis) return;
-      f32x16 s[2];
+    // The weights of one tile: S^T, the element mask when `mask`, online softmax; the tile's P^T
+    // operands (one per 16-key chunk) go to `P`. (One body for both cases: two inlined copies
+    // would each hoist their own LDS addresses out of the loop and run out of registers.)
+    auto scores = [&](bool mask, const Run* runs, const char* k_st, v8<T> (&P)[4]) {
+      // All K operands of the tile are read first, then the MFMAs run back to back: the LDS
+      // latency is paid once per tile instead of once per MFMA.
+      v8<T> ka[2][DC];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
         const int R = b2 * 32 + rcol;
         const char* row = k_st + R * TG::kKRowBytes;
         const int swz = R & (TG::kKSwz - 1);
 #pragma unroll
+        for (int dc = 0; dc < DC; ++dc) ka[b2][dc] = lds_operand<T>(row, (dc * 16 + half * 8) / TG::kChunk, swz);
+      }
+      f32x16 s[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
         for (int j = 0; j < 16; ++j) s[b2][j] = 0.f;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const v8<T> a = lds_operand<T>(row, (dc * 16 + half * 8) / TG::kChunk, swz);
-          s[b2] = mfma32(a, qT[dc], s[b2]);
-        }
+        for (int dc = 0; dc < DC; ++dc) s[b2] = mfma32(ka[b2][dc], qT[dc], s[b2]);
       }
+      if constexpr (sizeof(T) == 2) pipeline_lds_mfma<2 * DC, kLdsAhead>();
       // accumulator 4*i + j of block b2 is key 8*half + 4*(i&1) + j of run 2*b2 + (i>>1)
-      if (!all_full) {
+      if (mask) {
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
@@ -348,13 +357,11 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       // Row max of the raw scores (softmax_scale > 0, so scaling after the max is exact).
       float mx = -INFINITY;
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) mx = fmaxf(mx, s[b2][k]);
+      for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s[0][k], s[1][k]));
       mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
       // Lazy reference max: it moves only when some row of the wave exceeds it by more than 8
       // (log2 units), so p <= 256 and O / l are rescaled on few tiles. The final O / l is exact
-      // whatever reference was used.
+      // whatever reference was used. O holds every earlier tile's PV at this point.
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
@@ -364,30 +371,54 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
         for (int db = 0; db < DB; ++db) oT[db] *= alpha;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float x[2][16];
-      float psum = 0.f;
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
+      for (int c = 0; c < 4; ++c) {
+        float x[8];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          x[b2][k] = fast_exp2(fmaf(s[b2][k], p.scale_log2, -m_use));
-          psum += x[b2][k];
+        for (int k = 0; k < 8; ++k) x[k] = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + k], p.scale_log2, -m_use));
+        P[c] = pack8<T>(x);
+        l_run = sum8(P[c], l_run);
+      }
+    };
+    // O^T += V^T P^T over the tile's four 16-key chunks.
+    auto pv = [&](const v8<T> (&P)[4], const char* v_st) {
+      v8<T> va[4][DB];   // operands first, as for S
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + rcol;
+          va[c][db] = lds_operand<T>(v_st + c * TG::kVRunBytes + d * TG::kVRowBytes,
+                                     (half * 8) / TG::kChunk, TG::vswz(d));
         }
-      l_run += psum;
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const v8<T> pB = pack8<T>(&x[b2][8 * kc]);
-          const int chunk = 2 * b2 + kc;
+        for (int db = 0; db < DB; ++db) oT[db] = mfma32(va[c][db], P[c], oT[db]);
+      if constexpr (sizeof(T) == 2) pipeline_lds_mfma<4 * DB, kLdsAhead>();
+    };
+    // lean: the tile is known to be fully visible to every row (retrieval tiles below the
+    // workgroup's first row), so the classification is skipped.
+    auto compute = [&](int tile, bool lean, const char* k_st, v8<T> (&P)[4]) -> bool {
+      Run runs[4];
+      bool all_full = true, any_vis = lean;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + rcol;
-            const v8<T> a = lds_operand<T>(v_st + chunk * TG::kVRunBytes + d * TG::kVRowBytes,
-                                           (half * 8) / TG::kChunk, TG::vswz(d));
-            oT[db] = mfma32(a, pB, oT[db]);
-          }
-        }
+      for (int i = 0; i < 4 && !lean; ++i) {
+        runs[i] = run_pos(tile * 4 + i);
+        const Run& r = runs[i];
+        const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
+        // some key visible to some row: the closest pair is key min(e-1, pw_hi) seen from row
+        // max(pw_lo, that key)
+        const bool vis = a < e && a <= pw_hi &&
+                         (!r.windowed || pw_lo - min(e - 1, pw_hi) < p.recent);
+        const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= pw_lo &&
+                          (!r.windowed || pw_hi - r.t0 < p.recent);
+        all_full = all_full && full;
+        any_vis = any_vis || vis;
+      }
+      if (!wave_live || !any_vis) return false;
+      scores(!all_full, runs, k_st, P);
+      return true;
     };
 
     const int n_tiles = (n_runs + 3) / 4;
@@ -399,9 +430,21 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     // the other stage. The loop is unrolled by two so that each stage is a distinct LDS object and
     // copies into one never wait on reads of the other.
     const int n_steps = (n_tiles + kG - 1) / kG;
+    const int n_full_steps = RET ? max(0, (p_lo + 1) / kKeys) / kG : 0;
+    // The two groups run half a tile apart so that on each SIMD one wave's softmax overlaps the
+    // other's MFMAs: group 0 does S, softmax and PV of its tile; group 1 first does the PV of its
+    // previous tile (P kept in registers, V still in its slot of the other stage, which only its
+    // own copies overwrite, issued right after), then S and softmax of the current tile.
+    v8<T> P[4];
+    bool pend = false;        // group 1: P holds a tile whose PV is still to be done
+    const char* pend_v = nullptr;
     auto step = [&](int s, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
       wait_stores_complete();   // this wave's copies for step s have landed
       __syncthreads();          // everyone's have; everyone is done with the other stage
+      if (pend) {
+        pv(P, pend_v);
+        pend = false;
+      }
       const int first_next = (s + 1) * kG;
       if (first_next < n_tiles) {
         if (((first_next * 4) % kRunSeg) == 0) {   // the next step starts a new segment of runs
@@ -412,21 +455,32 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
         if (first_next + grp < n_tiles)
           issue(first_next + grp, k_nxt + grp * TG::kKBytes, v_nxt + grp * TG::kVBytes);
       }
+      // Retrieval steps whose tiles lie below the workgroup's first row are fully visible to every
+      // row: no classification, no mask, no partly absent chunk.
+      const bool lean = s < n_full_steps;
       bool fix = false;
 #pragma unroll
-      for (int g = 0; g < kG; ++g) fix = fix || (s * kG + g < n_tiles && partial_chunks(s * kG + g));
+      for (int g = 0; g < kG; ++g) fix = fix || (!lean && s * kG + g < n_tiles && partial_chunks(s * kG + g));
       if (fix) {
 #pragma unroll
         for (int g = 0; g < kG; ++g)
           if (s * kG + g < n_tiles && partial_chunks(s * kG + g)) fixup(s * kG + g, v_cur + g * TG::kVBytes);
         __syncthreads();
       }
-      if (s * kG + grp < n_tiles) compute(s * kG + grp, k_cur + grp * TG::kKBytes, v_cur + grp * TG::kVBytes);
+      if (s * kG + grp < n_tiles && compute(s * kG + grp, lean, k_cur + grp * TG::kKBytes, P)) {
+        pend = true;
+        pend_v = v_cur + grp * TG::kVBytes;
+        if (grp == 0) {
+          pv(P, pend_v);
+          pend = false;
+        }
+      }
     };
     for (int s = 0; s < n_steps; s += 2) {
       step(s, k_lds0, v_lds0, k_lds1, v_lds1);
       if (s + 1 < n_steps) step(s + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
+    if (pend) pv(P, pend_v);   // group 1's last tile (no copies follow)
   };
   if (ret) body(std::integral_constant<bool, true>{});
   else body(std::integral_constant<bool, false>{});
