@@ -294,8 +294,9 @@ def cpu_baseline(dec, budget_s: float):
     L = w.context
     done, spent, nbytes = 0, 0.0, 0
     per_seq = decode_bytes(synth.replace(w, batch=1), np.array([L]))
-    while done < w.batch and (spent < budget_s or done == 0):
-        b = done
+    # whole sequences of the workload, cycling through the batch until the time budget is spent
+    while spent < budget_s or done == 0:
+        b = done % w.batch
         t0 = time.perf_counter()
         oracle.attend(q_bits[b:b + 1, None], K[b:b + 1], V[b:b + 1], np.array([L]), w.retrieval_mask,
                       sink=w.sink, recent=w.recent, scale=w.scale, dtype=w.dtype)
@@ -304,8 +305,8 @@ def cpu_baseline(dec, budget_s: float):
         done += 1
     return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {w.batch} sequences of the decode workload (all 32 q heads), "
-                      f"{spent:.1f} s of fp64 NumPy"}
+            "sample": f"{done} sequence-steps of the decode workload (batch {w.batch} cycled, all "
+                      f"{w.num_q_heads} q heads, context {L}), {spent:.1f} s of fp64 NumPy"}
 
 
 # ---- rocprofv3 counter bookkeeping -------------------------------------------------------------
