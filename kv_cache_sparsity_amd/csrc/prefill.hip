@@ -135,6 +135,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   __shared__ __attribute__((aligned(1024))) char k_lds1[kG * TG::kKBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds1[kG * TG::kVBytes];
   __shared__ int32_t sm_run[kRunSeg];
+  __shared__ int32_t sm_flags[kRunSeg / 4];   // per tile of the segment: see tile_flags
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -397,26 +398,48 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
         for (int db = 0; db < DB; ++db) oT[db] = mfma32(va[c][db], P[c], oT[db]);
       if constexpr (sizeof(T) == 2) pipeline_lds_mfma<4 * DB, kLdsAhead>();
     };
-    // lean: the tile is known to be fully visible to every row (retrieval tiles below the
-    // workgroup's first row), so the classification is skipped.
-    auto compute = [&](int tile, bool lean, const char* k_st, v8<T> (&P)[4]) -> bool {
+    // Classification of a tile for the four row blocks, computed once per segment of runs:
+    // bit w: some key of the tile is visible to some row of wave w; bit 4 + w: every key is present
+    // and visible to every row of wave w (no mask); bit 8: some 16-byte V chunk mixes present and
+    // absent keys (zeroed in LDS before use).
+    auto tile_flags = [&](int tile) -> int32_t {
       Run runs[4];
-      bool all_full = true, any_vis = lean;
 #pragma unroll
-      for (int i = 0; i < 4 && !lean; ++i) {
-        runs[i] = run_pos(tile * 4 + i);
-        const Run& r = runs[i];
-        const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
-        // some key visible to some row: the closest pair is key min(e-1, pw_hi) seen from row
-        // max(pw_lo, that key)
-        const bool vis = a < e && a <= pw_hi &&
-                         (!r.windowed || pw_lo - min(e - 1, pw_hi) < p.recent);
-        const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= pw_lo &&
-                          (!r.windowed || pw_hi - r.t0 < p.recent);
-        all_full = all_full && full;
-        any_vis = any_vis || vis;
+      for (int i = 0; i < 4; ++i) runs[i] = run_pos(tile * 4 + i);
+      int32_t f = 0;
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) {
+        if (w * 32 >= n_rows) continue;   // the wave has no rows
+        const int32_t lo = p_lo + w * 32, hi = min(lo + 31, p_hi);
+        bool all_full = true, any_vis = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const Run& r = runs[i];
+          const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
+          // some key visible to some row: the closest pair is key min(e-1, hi) seen from row
+          // max(lo, that key)
+          const bool vis = a < e && a <= hi && (!r.windowed || lo - min(e - 1, hi) < p.recent);
+          const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= lo &&
+                            (!r.windowed || hi - r.t0 < p.recent);
+          all_full = all_full && full;
+          any_vis = any_vis || vis;
+        }
+        f |= (any_vis ? 1 : 0) << w;
+        f |= (all_full ? 1 : 0) << (4 + w);
       }
-      if (!wave_live || !any_vis) return false;
+      return f | (partial_chunks(tile) ? 1 << 8 : 0);
+    };
+    auto load_flags = [&](int32_t tile0, int32_t ntiles) {
+      for (int i = tid; i < ntiles; i += kThreads) sm_flags[i] = tile_flags(tile0 + i);
+    };
+    auto compute = [&](int tile, int32_t flags, const char* k_st, v8<T> (&P)[4]) -> bool {
+      if (!((flags >> wave) & 1)) return false;
+      const bool all_full = (flags >> (4 + wave)) & 1;
+      Run runs[4];
+      if (!all_full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) runs[i] = run_pos(tile * 4 + i);
+      }
       scores(!all_full, runs, k_st, P);
       return true;
     };
@@ -424,13 +447,16 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     const int n_tiles = (n_runs + 3) / 4;
     if (n_tiles == 0) return;
     load_pages<kThreads>(sm_run, geo, rl, 0, min(kRunSeg, n_runs));
+    load_flags(0, min(kRunSeg / 4, n_tiles));
     __syncthreads();
+    const int n_full_steps = RET ? max(0, (p_lo + 1) / kKeys) / kG : 0;
+    const int32_t live = (1 << min(kGroupWaves, (n_rows + 31) / 32)) - 1;
+    const int32_t lean_flags = live | (live << 4);
     if (grp < n_tiles) issue(grp, k_lds0 + grp * TG::kKBytes, v_lds0 + grp * TG::kVBytes);
     // Step s: group g computes tile s * kG + g from stage s % 2 while the copies of step s + 1 fill
     // the other stage. The loop is unrolled by two so that each stage is a distinct LDS object and
     // copies into one never wait on reads of the other.
     const int n_steps = (n_tiles + kG - 1) / kG;
-    const int n_full_steps = RET ? max(0, (p_lo + 1) / kKeys) / kG : 0;
     // The two groups run half a tile apart so that on each SIMD one wave's softmax overlaps the
     // other's MFMAs: group 0 does S, softmax and PV of its tile; group 1 first does the PV of its
     // previous tile (P kept in registers, V still in its slot of the other stage, which only its
@@ -445,29 +471,35 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
         pv(P, pend_v);
         pend = false;
       }
+      // this step's tiles' classification, read before the segment may be refilled below
+      // (retrieval tiles below the workgroup's first row are fully visible to every live wave)
+      const bool lean = s < n_full_steps;
+      int32_t fl[kG];
+#pragma unroll
+      for (int g = 0; g < kG; ++g)
+        fl[g] = lean ? lean_flags : s * kG + g < n_tiles ? sm_flags[s * kG + g - seg0 / 4] : 0;
       const int first_next = (s + 1) * kG;
       if (first_next < n_tiles) {
         if (((first_next * 4) % kRunSeg) == 0) {   // the next step starts a new segment of runs
+          __syncthreads();                         // everyone has read this segment's flags
           seg0 = first_next * 4;
           load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
+          load_flags(first_next, min(kRunSeg / 4, n_tiles - first_next));
           __syncthreads();
         }
         if (first_next + grp < n_tiles)
           issue(first_next + grp, k_nxt + grp * TG::kKBytes, v_nxt + grp * TG::kVBytes);
       }
-      // Retrieval steps whose tiles lie below the workgroup's first row are fully visible to every
-      // row: no classification, no mask, no partly absent chunk.
-      const bool lean = s < n_full_steps;
       bool fix = false;
 #pragma unroll
-      for (int g = 0; g < kG; ++g) fix = fix || (!lean && s * kG + g < n_tiles && partial_chunks(s * kG + g));
+      for (int g = 0; g < kG; ++g) fix = fix || ((fl[g] >> 8) & 1);
       if (fix) {
 #pragma unroll
         for (int g = 0; g < kG; ++g)
-          if (s * kG + g < n_tiles && partial_chunks(s * kG + g)) fixup(s * kG + g, v_cur + g * TG::kVBytes);
+          if ((fl[g] >> 8) & 1) fixup(s * kG + g, v_cur + g * TG::kVBytes);
         __syncthreads();
       }
-      if (s * kG + grp < n_tiles && compute(s * kG + grp, lean, k_cur + grp * TG::kKBytes, P)) {
+      if (s * kG + grp < n_tiles && compute(s * kG + grp, (kG == 2 && grp == 1) ? fl[kG - 1] : fl[0], k_cur + grp * TG::kKBytes, P)) {
         pend = true;
         pend_v = v_cur + grp * TG::kVBytes;
         if (grp == 0) {
