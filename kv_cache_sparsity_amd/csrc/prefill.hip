@@ -355,10 +355,17 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
             }
           }
       }
-      // Row max of the raw scores (softmax_scale > 0, so scaling after the max is exact).
-      float mx = -INFINITY;
+      // Row max of the raw scores (softmax_scale > 0, so scaling after the max is exact). The
+      // scores are finite or -inf here (absent keys were masked), so the NaN-propagating maximum
+      // equals fmaxf and needs no input canonicalisation; a balanced tree keeps it short.
+      float t16[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s[0][k], s[1][k]));
+      for (int k = 0; k < 16; ++k) t16[k] = __builtin_elementwise_maximum(s[0][k], s[1][k]);
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int k = 0; k < w; ++k) t16[k] = __builtin_elementwise_maximum(t16[k], t16[k + w]);
+      float mx = t16[0];
       mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
       // Lazy reference max: it moves only when some row of the wave exceeds it by more than 8
       // (log2 units), so p <= 256 and O / l are rescaled on few tiles. The final O / l is exact
