@@ -25,6 +25,8 @@
 // The K rows of each 16-row MFMA are permuted so that the S^T accumulator a lane holds covers the
 // same 8 consecutive keys that the lane loads as its V^T operand: no LDS, no cross-lane moves.
 //
+// K and V are streamed with non-temporal loads: each byte is read once per launch.
+//
 // Split merge: each retrieval item writes (m, l, O) for its G q heads to the workspace, then takes a
 // ticket on the (b, h) counter; the last item merges the partials, writes the output and resets the
 // counter to zero for the next call.
@@ -140,7 +142,7 @@ __global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(co
         for (int t = 0; t < 2; ++t) {
           const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) kA[c][t][kc] = load8(base + krow * D + kc * 32);
+          for (int kc = 0; kc < KC; ++kc) kA[c][t][kc] = load8_stream(base + krow * D + kc * 32);
         }
       }
     };
@@ -151,7 +153,7 @@ __global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(co
         const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
         const T* base = vpool + packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vA[c][dt] = load8(base + (int64_t)(dt * 16 + col) * bs);
+        for (int dt = 0; dt < DT; ++dt) vA[c][dt] = load8_stream(base + (int64_t)(dt * 16 + col) * bs);
       }
     };
 
@@ -358,12 +360,13 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int gri
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
                             int32_t requested) {
   if (requested > 0) return requested;
-  // About 512 work items if every kv head were a retrieval head (so ~one workgroup per CU at the
-  // usual mixes): fewer, longer items amortise each item's start-up round trips and its share of
-  // the split merge. Between 256 and 65536 keys per item.
+  // About 1024 work items if every kv head were a retrieval head (two or more workgroups per CU at
+  // the usual mixes, so one item's start-up round trips overlap another's stream), but at most 64
+  // splits per (sequence, kv head), which keeps the fused merge at the tail short. Between 256 and
+  // 65536 keys per item.
   const int64_t total = (int64_t)batch * num_kv_heads * capacity_tokens;
   int64_t s = 256;
-  while (s < 65536 && s * 512 < total) s *= 2;
+  while (s < 65536 && (s * 1024 < total || capacity_tokens > 64 * s)) s *= 2;
   return (int32_t)s;
 }
 

@@ -31,6 +31,19 @@ __device__ __forceinline__ v8<T> load8(const T* p) {
   return *reinterpret_cast<const v8<T>*>(p);
 }
 
+// The same load marked non-temporal: data read once (streamed K/V) should not displace reused
+// lines in the caches.
+template <typename T>
+__device__ __forceinline__ v8<T> load8_stream(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(v8<T>, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  } else {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    return v8<T>{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ v8<T> zero8() {
   v8<T> z;
