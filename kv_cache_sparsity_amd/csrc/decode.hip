@@ -37,10 +37,14 @@ namespace duo {
 
 namespace {
 
-constexpr int kThreads = kDecodeWaves * kWave;
+// Waves per workgroup: eight up to D = 128 (more loads in flight per CU); four at D = 256, where
+// eight waves' merge buffers would not fit in LDS next to a second workgroup.
+template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) decode_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(const DecodeParams p) {
+  constexpr int kDecodeWaves = decode_waves<D>();
+  constexpr int kThreads = kDecodeWaves * kWave;
   constexpr int KC = D / 32;  // k-steps of S^T over the head dim
   constexpr int DT = D / 16;  // 16-row tiles of O^T
   __shared__ float sm_o[kDecodeWaves][16][D];
@@ -340,9 +344,9 @@ template <typename T>
 hipError_t launch_t(const DecodeParams& p, int head_dim, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's status
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((decode_kernel<T, 64>), dim3(grid), dim3(kThreads), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<T, 128>), dim3(grid), dim3(kThreads), 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((decode_kernel<T, 256>), dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((decode_kernel<T, 64>), dim3(grid), dim3(decode_waves<64>() * kWave), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((decode_kernel<T, 128>), dim3(grid), dim3(decode_waves<128>() * kWave), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((decode_kernel<T, 256>), dim3(grid), dim3(decode_waves<256>() * kWave), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -360,13 +364,13 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int gri
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
                             int32_t requested) {
   if (requested > 0) return requested;
-  // About 1024 work items if every kv head were a retrieval head (two or more workgroups per CU at
-  // the usual mixes, so one item's start-up round trips overlap another's stream), but at most 64
+  // About 512 work items if every kv head were a retrieval head (so about one workgroup per CU at
+  // the usual mixes: fewer, longer items amortise each item's start-up round trips), but at most 64
   // splits per (sequence, kv head), which keeps the fused merge at the tail short. Between 256 and
   // 65536 keys per item.
   const int64_t total = (int64_t)batch * num_kv_heads * capacity_tokens;
   int64_t s = 256;
-  while (s < 65536 && (s * 1024 < total || capacity_tokens > 64 * s)) s *= 2;
+  while (s < 65536 && (s * 512 < total || capacity_tokens > 64 * s)) s *= 2;
   return (int32_t)s;
 }
 

@@ -68,7 +68,6 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
                             int32_t requested);
 constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
-constexpr int kDecodeWaves = 4;     // waves per decode workgroup
 constexpr int kDecodeStep = 32;     // keys per wave step (two 16-key runs)
 
 }  // namespace duo
