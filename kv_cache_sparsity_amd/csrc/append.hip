@@ -84,6 +84,28 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendPara
   }
   __syncthreads();
   // V page is [D][block_size]: element (d, row) at page * D * bs + d * bs + row.
+  const int32_t s0 = slot_of(t_lo);
+  if (n_tok == 16 && (s0 & 15) == 0 && p.log2_bs >= 4) {
+    // A whole run of 16 consecutive slots in one page (pages of >= 16 slots; ring size a
+    // multiple of the page size): each thread writes 8 (16-bit) or 4 (32-bit) consecutive slots of
+    // one channel as one 16-byte store.
+    const int64_t page = clamp_page(trow[s0 >> p.log2_bs], p.num_blocks);
+    E* vrow = vp + page * D * ((int64_t)1 << p.log2_bs) + (s0 & bs_mask);
+    constexpr int kPer = 16 / sizeof(E);                 // slots per 16-byte store
+    for (int idx = threadIdx.x; idx < D * (16 / kPer); idx += kAppendThreads) {
+      const int d = idx / (16 / kPer), r0 = (idx % (16 / kPer)) * kPer;
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(E) == 2)
+          w[j] = (uint32_t)vstage[r0 + 2 * j][d] | ((uint32_t)vstage[r0 + 2 * j + 1][d] << 16);
+        else
+          w[j] = vstage[r0 + j][d];
+      }
+      *reinterpret_cast<u32x4*>(vrow + (int64_t)d * ((int64_t)1 << p.log2_bs) + r0) = w;
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < 16 * D; idx += kAppendThreads) {
     const int r = idx & 15, d = idx >> 4;
     if (r >= n_tok) continue;
@@ -96,7 +118,9 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendPara
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream) {
-  const int groups = (p.t_new + 15) / 16 + 3;
+  // Runs of 16 positions a (sequence, kv head) can touch: a single new token is one run; longer
+  // appends may start mid-run and split at the sink / ring boundary.
+  const int groups = p.t_new == 1 ? 1 : (p.t_new + 15) / 16 + 3;
   const dim3 grid(groups, p.num_kv_heads, p.batch);
   (void)hipGetLastError();  // report only this launch's status
   if (elem_bytes == 2)
