@@ -130,6 +130,8 @@ DECODE_CASES = [
          block_size=64, sink=70, recent=100, ring_blocks=2, lens=[69, 70, 71, 170, 171, 5000]),
     dict(name="f16-d128-g4-all-streaming", dtype=synth.F16, head_dim=128, group=4, kv=3, ret=(),
          block_size=16, sink=16, recent=32, ring_blocks=2, lens=[16, 48, 49, 777]),
+    dict(name="bf16-d128-g4-bs256", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(0,),
+         block_size=256, sink=3, recent=300, ring_blocks=2, lens=[255, 256, 257, 3000]),
 ]
 
 
@@ -201,6 +203,10 @@ PREFILL_CASES = [
          block_size=32, sink=5, recent=77, chunks=[150, 260]),
     dict(name="f32-d128-g2-chunks", dtype=synth.F32, head_dim=128, group=2, kv=2, ret=(1,),
          block_size=16, sink=1, recent=1, chunks=[33, 1, 128]),
+    dict(name="bf16-d128-bs64-q333x2", dtype=synth.BF16, head_dim=128, group=1, kv=2, ret=(0,),
+         block_size=64, sink=20, recent=200, chunks=[333, 333]),
+    dict(name="bf16-d64-g2-bs256-q700", dtype=synth.BF16, head_dim=64, group=2, kv=2, ret=(1,),
+         block_size=256, sink=0, recent=128, chunks=[700]),
 ]
 
 
