@@ -242,6 +242,7 @@ def prefill_leg(args, torch, duo):
         la = torch.full((w.batch,), e, dtype=torch.int32, device=dev)
         chunks.append((kn, vn, q, lb, la, torch.empty_like(q)))
     del K, V
+    ws = duo.prefill_workspace(chunks[0][2], table, mask)
     torch.cuda.synchronize()
 
     def one_pass(evs=None):
@@ -251,7 +252,7 @@ def prefill_leg(args, torch, duo):
             if evs is not None:
                 evs[c][0].record()
             duo.duo_attn_prefill(q, kp, vp, table, la, mask, w.sink, w.recent, w.ring_blocks,
-                                 w.scale, out)
+                                 w.scale, out, ws)
             if evs is not None:
                 evs[c][1].record()
 

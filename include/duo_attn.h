@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 1
+#define DUO_ATTN_ABI_VERSION 2
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -60,7 +60,7 @@ typedef enum {
   DUO_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, non-positive size, bad mask value, aliasing */
   DUO_ERR_UNSUPPORTED = 2,   /* head_dim not in {64,128,256}, block_size not supported, group > 16 */
   DUO_ERR_CAPACITY = 3,      /* ring or table too small for the requested window / chunk */
-  DUO_ERR_WORKSPACE = 4,     /* decode workspace missing or smaller than the size query says */
+  DUO_ERR_WORKSPACE = 4,     /* workspace missing or smaller than the size query says */
   DUO_ERR_HIP = 5            /* a HIP launch failed */
 } duo_status_t;
 
@@ -138,6 +138,17 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                         size_t workspace_bytes, int32_t split_tokens, void* stream);
 
 /*
+ * duo_attn_prefill_workspace_size -- bytes of device workspace duo_attn_prefill needs for these
+ * sizes and this retrieval/streaming split of the kv heads (head_is_retrieval: host, num_kv_heads
+ * bytes). A retrieval head's row tiles split their keys over several workgroups whose partial
+ * softmax states meet in the workspace. The caller zero-fills the workspace once after allocating
+ * it; every completed prefill call leaves it ready for the next. Returns 0 for invalid sizes.
+ */
+size_t duo_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                       const uint8_t* head_is_retrieval);
+
+/*
  * duo_attn_prefill -- q_len query rows per sequence (a prompt chunk already appended to the cache)
  * attend causally over their head's visible positions.
  *
@@ -149,11 +160,14 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
  *                       i sits at position seq_lens[b] - q_len + i (rows at negative positions
  *                       produce zeros).
  *   out                 device [batch][q_len][num_q_heads][head_dim] of dtype.
+ *   workspace           device, >= duo_attn_prefill_workspace_size(...) bytes, zero-filled once
+ *                       (may be NULL when no kv head is a retrieval head).
  * Visible set of row i at position p: as for decode. Streaming heads need
  * ring_blocks*block_size >= recent_size + q_len - 1 so that the oldest key of the first row is still
  * in the ring.
+ * Calls sharing one workspace must not run concurrently.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16),
- *         CAPACITY.
+ *         CAPACITY, WORKSPACE.
  */
 int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* block_table, int32_t num_blocks, int32_t block_size,
@@ -161,7 +175,8 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                          int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
                          int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
-                         float softmax_scale, void* out, void* stream);
+                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* duo_status_string(int32_t status);

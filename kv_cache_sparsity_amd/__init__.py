@@ -24,7 +24,8 @@ DUO_F32, DUO_F16, DUO_BF16 = 0, 1, 2
 STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "DUO_ERR_CAPACITY",
           4: "DUO_ERR_WORKSPACE", 5: "DUO_ERR_HIP"}
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
-           "duo_attn_prefill", "duo_status_string", "duo_abi_version")
+           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_status_string",
+           "duo_abi_version")
 
 
 class DuoAttnError(RuntimeError):
@@ -54,9 +55,12 @@ def lib() -> ctypes.CDLL:
         L.duo_attn_decode.restype = _I32
         L.duo_attn_decode.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                       _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ, _I32, _P]
+        L.duo_attn_prefill_workspace_size.restype = _SZ
+        L.duo_attn_prefill_workspace_size.argtypes = [_I32] * 6 + [_P]
         L.duo_attn_prefill.restype = _I32
         L.duo_attn_prefill.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32, _I32,
-                                       _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P]
+                                       _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
+                                       _P]
         L.duo_status_string.restype = ctypes.c_char_p
         L.duo_status_string.argtypes = [_I32]
         L.duo_abi_version.restype = _I32
@@ -162,8 +166,26 @@ def duo_attn_decode(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval,
     _check("duo_attn_decode", st)
 
 
+def duo_attn_prefill_workspace_size(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, dtype: int, head_is_retrieval) -> int:
+    mask = _HostMask(head_is_retrieval)
+    return lib().duo_attn_prefill_workspace_size(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                                 dtype, mask.ptr)
+
+
+def prefill_workspace(q, block_table, head_is_retrieval, head_dim: int | None = None):
+    """Allocate a zero-filled workspace for duo_attn_prefill with these shapes."""
+    import torch
+    batch, q_len, num_q_heads, d = q.shape
+    n = duo_attn_prefill_workspace_size(batch, q_len, num_q_heads, block_table.shape[1],
+                                        head_dim or d, _dtype_tag(q), head_is_retrieval)
+    if n == 0:
+        raise ValueError("invalid sizes for the prefill workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
 def duo_attn_prefill(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval, sink_size: int,
-                     recent_size: int, ring_blocks: int, softmax_scale: float, out,
+                     recent_size: int, ring_blocks: int, softmax_scale: float, out, workspace,
                      stream=None) -> None:
     num_blocks, block_size, head_dim = k_pool.shape
     batch, q_len, num_q_heads, _ = q.shape
@@ -172,10 +194,12 @@ def duo_attn_prefill(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
         block_table.shape[2], _ptr(seq_lens), batch, q_len, num_q_heads, block_table.shape[1],
         head_dim, _dtype_tag(q), mask.ptr, sink_size, recent_size, ring_blocks, softmax_scale,
-        _ptr(out), _stream(stream))
+        _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
     _check("duo_attn_prefill", st)
 
 
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
-           "duo_attn_decode_workspace_size", "decode_workspace", "status_string", "abi_version",
+           "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",
+           "prefill_workspace", "status_string", "abi_version",
            "DuoAttnError", "lib", "LIB_PATH", "SYMBOLS", "DUO_F32", "DUO_F16", "DUO_BF16"]

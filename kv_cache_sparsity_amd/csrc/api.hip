@@ -77,6 +77,20 @@ int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, in
   return DUO_OK;
 }
 
+// Prefill work layout: row tiles of prefill_rows() rows; retrieval items split their keys in
+// kPrefillSplits workgroups that merge through the workspace (tickets, then partials).
+void prefill_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t n_ret_kv, int32_t hkv,
+                  int32_t head_dim, int32_t dtype, int32_t* n_qtiles, int64_t* ret_items,
+                  size_t* ws_bytes) {
+  const int eb = elem_bytes(dtype);
+  const int rows = prefill_rows(eb, head_dim);
+  *n_qtiles = (q_len + rows - 1) / rows;
+  *ret_items = (int64_t)batch * n_ret_kv * (hq / hkv) * *n_qtiles;
+  *ws_bytes = *ret_items == 0 ? 0
+              : align256((size_t)*ret_items * sizeof(int32_t)) +
+                (size_t)*ret_items * kPrefillSplits * prefill_partial_floats(eb, head_dim) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,13 +245,32 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
   return DUO_OK;
 }
 
+size_t duo_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                       const uint8_t* head_is_retrieval) {
+  if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_kv_heads > kMaxKvHeads || num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) ||
+      !dtype_ok(dtype) || !head_is_retrieval)
+    return 0;
+  uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
+  int32_t n_ret, n_str;
+  if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str)) return 0;
+  int32_t n_qt;
+  int64_t ret_items;
+  size_t bytes;
+  prefill_plan(batch, q_len, num_q_heads, n_ret, num_kv_heads, head_dim, dtype, &n_qt, &ret_items,
+               &bytes);
+  return bytes > 0 ? bytes : 256;   // 0 means invalid arguments
+}
+
 int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* block_table, int32_t num_blocks, int32_t block_size,
                          int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
                          int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
                          int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
-                         float softmax_scale, void* out, void* stream) {
+                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);
@@ -253,8 +286,15 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
   st = check_stream_geometry(n_str, sink_size, recent_size, ring_blocks, block_size,
                              max_blocks_per_head, q_len);
   if (st != DUO_OK) return st;
-  const int32_t n_qt = (q_len + kPrefillRows - 1) / kPrefillRows;
-  const int64_t grid = (int64_t)batch * num_q_heads * n_qt;
+  int32_t n_qt;
+  int64_t ret_items;
+  size_t need;
+  prefill_plan(batch, q_len, num_q_heads, n_ret, num_kv_heads, head_dim, dtype, &n_qt, &ret_items,
+               &need);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return DUO_ERR_WORKSPACE;
+  const int64_t grid = ret_items * kPrefillSplits +
+                       (int64_t)batch * n_str * (num_q_heads / num_kv_heads) * n_qt;
   if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
 
   PrefillParams p{};
@@ -264,6 +304,10 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
   p.table = block_table;
   p.seq_lens = seq_lens;
   p.out = out;
+  p.counter = need > 0 ? static_cast<int32_t*>(workspace) : nullptr;
+  p.partial = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                  align256((size_t)ret_items * sizeof(int32_t)))
+                       : nullptr;
   p.num_blocks = num_blocks;
   p.log2_bs = log2i(block_size);
   p.max_blocks_per_head = max_blocks_per_head;
@@ -279,6 +323,7 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
   p.n_qtiles = n_qt;
   p.n_ret = n_ret;
   p.n_str = n_str;
+  p.n_split = kPrefillSplits;
   p.scale_log2 = softmax_scale * kLog2e;
   for (int32_t i = 0; i < n_ret; ++i) p.ret_heads[i] = ret[i];
   for (int32_t i = 0; i < n_str; ++i) p.str_heads[i] = str[i];

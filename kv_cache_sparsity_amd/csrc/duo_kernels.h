@@ -48,10 +48,12 @@ struct PrefillParams {
   const int32_t* table;
   const int32_t* seq_lens;
   void* out;
+  int32_t* counter;   // [retrieval items] arrival tickets (zero between calls)
+  float* partial;     // [retrieval items][n_split] partial (m, l, O^T) of every row
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group;
   int32_t sink, recent, sink_blocks, ring_slots;
-  int32_t n_qtiles, n_ret, n_str;
+  int32_t n_qtiles, n_ret, n_str, n_split;
   float scale_log2;
   uint8_t ret_heads[kMaxKvHeads];
   uint8_t str_heads[kMaxKvHeads];
@@ -67,7 +69,17 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
 // Decode planning shared by the workspace-size query and the call.
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
                             int32_t requested);
-constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
+// Prefill workgroup shape: eight waves (two per SIMD, 32 query rows each) while one 64-key K+V tile
+// takes at most 32 KiB, so that four tile stages fit in LDS; four waves otherwise.
+constexpr int prefill_waves(int elem_bytes, int head_dim) {
+  return 64 * head_dim * elem_bytes * 2 <= 32768 ? 8 : 4;
+}
+constexpr int prefill_rows(int elem_bytes, int head_dim) { return 32 * prefill_waves(elem_bytes, head_dim); }
+constexpr int kPrefillSplits = 2;   // key-range splits of a retrieval item (merged in the launch)
+// Workspace floats of one split's partial: per wave and lane, m, l and the D / 2 O^T accumulators.
+constexpr int64_t prefill_partial_floats(int elem_bytes, int head_dim) {
+  return (int64_t)prefill_waves(elem_bytes, head_dim) * 64 * (2 + head_dim / 2);
+}
 constexpr int kDecodeStep = 32;     // keys per wave step (two 16-key runs)
 
 }  // namespace duo

@@ -6,28 +6,33 @@
 // positions j < sink and its recent window p - j < recent. Scores are softmax_scale * (q . k) in
 // fp32 (vLLM DualChunkAttention PR, review thread).
 //
-// Work decomposition: one workgroup per (b, q head, 128-row tile); retrieval heads' tiles come
-// first, latest rows first (they scan the most keys). The workgroup walks only the 16-key runs that
-// can be visible to its rows:
+// Work decomposition. A work item is (b, q head, tile of R query rows); R = 32 x waves (256 with
+// eight waves, 128 with four). The item walks only the 16-key runs that can be visible to its rows:
 //   retrieval head: runs 0 .. p_hi / 16;
 //   streaming head: the sink runs, then the ring runs covering [p_lo - recent + 1, p_hi].
-// So a streaming tile costs about (sink + recent + 128) keys whatever the context length.
+// So a streaming item costs about (sink + recent + R) keys whatever the context length. A retrieval
+// item's key tiles are split in n_split contiguous ranges, one workgroup each; the workgroups write
+// partial softmax states (m, l, O) to the workspace and the last to arrive merges them through
+// their log-sum-exp (vLLM DualChunkAttention PR, review thread) and writes the output. Retrieval
+// items come first in the grid, latest rows first (they scan the most keys).
 //
-// Inside the workgroup, four waves cover the 128 rows (32 each). Where LDS allows, there are two such
-// groups of four waves (eight waves, two per SIMD): group g takes the key tiles g, g+2, g+4, ... for
-// the same rows, and the two partial softmax states (m, l, O) are merged through LDS at the end. Two
-// waves per SIMD on the same long retrieval item let one wave's softmax and LDS reads overlap the
-// other's MFMAs.
+// Inside a workgroup every wave owns 32 rows and all waves work on the same 64-key tile, so each
+// K/V byte brought into LDS serves all R rows: copy traffic per MFMA is what the L2 -> LDS path
+// (and the chip's power) pays for, and it halves from 128 to 256 rows.
 //
-// Data movement: four runs (64 keys) form one K/V tile. Tiles are copied straight from the pages
-// into LDS by 16-byte global->LDS loads (no staging registers), into a ring of two stages of one
-// tile per group: while the waves compute on one stage, the next tiles stream into the other. Rows
-// are XOR-swizzled in 16-byte units instead of padded, so both the copies and the MFMA operand
+// Data movement: four runs (64 keys) form one K/V tile, copied straight from the pages into LDS by
+// 16-byte global->LDS loads (no staging registers); run r of a tile is copied by the waves w with
+// w mod 4 = r. Tiles rotate through a ring of stages: with four stages the copies run two tiles
+// ahead of the math, and the second half of the waves works half a tile behind the first (the PV
+// of its previous tile, whose V is still in its stage, comes first), so that on each SIMD one wave's
+// softmax overlaps the other's MFMAs; with two stages (64 KiB tiles) the copies run one tile ahead.
+// Rows are XOR-swizzled in 16-byte units instead of padded, so both the copies and the MFMA operand
 // reads are free of LDS bank conflicts. V channels of absent keys (past the valid length, unwritten
 // sink slots) are read from a zero chunk, or zeroed in LDS when a chunk is only partly absent;
-// absent K rows are masked by position. Where each run lives (page, row) is resolved once per
-// segment of 512 runs. One barrier per step: each wave waits for its own copies, the barrier makes
-// all of them visible and frees the other stage, then the copies of the next step are issued.
+// absent K rows are masked by position. Where each run lives (page, row) and how each tile is
+// classified for each wave are resolved once per segment of 512 runs; a tile's classification is
+// taken when its copies are issued. One barrier per tile: each wave waits for its own copies of the
+// tile (later tiles' copies stay in flight), then the barrier makes all of them visible.
 //
 // MFMA formulation (32x32x16, k-step of 8 elements per lane), per 32-key block:
 //   S^T[key, row] = sum_d K[key, d] Q[row, d]       A = K rows (LDS), B = Q^T (registers)
@@ -45,10 +50,8 @@ __device__ __attribute__((aligned(64))) uint32_t g_prefill_zero_chunk[16];
 
 namespace {
 
-constexpr int kGroupWaves = 4;       // waves covering the workgroup's rows (32 rows each)
-constexpr int kRows = kPrefillRows;  // 128 query rows per workgroup
-constexpr int kKeys = 64;            // keys per K/V tile (four 16-key runs)
-constexpr int kLdsAhead = 4;         // LDS operand reads kept in flight ahead of the MFMAs
+constexpr int kKeys = 64;      // keys per K/V tile (four 16-key runs)
+constexpr int kLdsAhead = 4;   // LDS operand reads kept in flight ahead of the MFMAs
 
 // Row of the 32-key block that holds key r of the block (an involution: swaps the middle two
 // groups of four in each half).
@@ -75,12 +78,18 @@ struct TileGeo {
   static constexpr int kVRowsPer256 = 256 / kVRowBytes;
   static constexpr int kVRunBytes = D * kVRowBytes;
   static constexpr int kVBytes = 4 * kVRunBytes;
-  // wave w of a group copies run w of its tile: 1 KiB per instruction
-  static constexpr int kKLoadsPerWave = kKRunBytes / 1024;
-  static constexpr int kVLoadsPerWave = kVRunBytes / 1024;
-  // Two groups when two stages of two tiles fit in 128 KiB of LDS, else one.
-  static constexpr int kGroups = (4 * (kKBytes + kVBytes) <= 128 * 1024) ? 2 : 1;
-  static constexpr int kThreads = kGroups * kGroupWaves * 64;
+  // workgroup shape
+  static constexpr int kWaves = prefill_waves(sizeof(T), D);
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRows = 32 * kWaves;
+  static constexpr int kStages = 4 * (kKBytes + kVBytes) <= 128 * 1024 ? 4 : 2;
+  static constexpr int kAhead = kStages == 4 ? 2 : 1;        // tiles in flight ahead of the math
+  static constexpr bool kLag = kStages == 4 && kWaves == 8;  // second half of the waves lags
+  // run r of a tile is copied by the waves w = r (mod 4), 1 KiB per instruction
+  static constexpr int kCopyWaves = kWaves / 4;
+  static constexpr int kKLoadsPerWave = kKRunBytes / 1024 / kCopyWaves;
+  static constexpr int kVLoadsPerWave = kVRunBytes / 1024 / kCopyWaves;
+  static constexpr int kCopiesPerTile = kKLoadsPerWave + kVLoadsPerWave;
   __device__ static __forceinline__ int vswz(int d) { return (d / kVRowsPer256) & (kVRowChunks - 1); }
 };
 
@@ -105,6 +114,19 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
+// Wait until at most `n` of this wave's vector memory operations are outstanding (they complete in
+// order, so every older one has landed) and its LDS operations have completed, then meet the other
+// waves at the barrier. Unlike __syncthreads() this leaves younger copies in flight.
+template <int n>
+__device__ __forceinline__ void wait_older_then_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  constexpr int kImm = (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14);   // vmcnt(n) expcnt(7) lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kImm);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Scheduling hint for a run of `n` MFMAs whose A operands are `n` LDS reads issued in the same
 // region: keep `ahead` reads in flight (reads first, then one MFMA per further read), so that each
 // MFMA waits for a read issued `ahead` operands earlier instead of the one just before it.
@@ -122,44 +144,74 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
   for (int i = 0; i < ahead; ++i) __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
 }
 
+template <int bytes, bool used>
+struct StageBytes { static constexpr int value = used ? bytes : 16; };
+
 template <typename T, int D>
 __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(const PrefillParams p) {
   using TG = TileGeo<T, D>;
   constexpr int kThreads = TG::kThreads;
-  constexpr int kG = TG::kGroups;
+  constexpr int kWaves = TG::kWaves;
+  constexpr int kRows = TG::kRows;
+  constexpr int kStages = TG::kStages;
+  constexpr int kAhead = TG::kAhead;
+  constexpr bool kLag = TG::kLag;
   constexpr int DC = D / 16;  // k-steps over the head dim (16 channels per 32x32 MFMA step)
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  // stage s holds one K and one V tile per group: group g's tile at offset g * tile bytes
-  __shared__ __attribute__((aligned(1024))) char k_lds0[kG * TG::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[kG * TG::kVBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[kG * TG::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[kG * TG::kVBytes];
+  // the stage ring (stages 2 and 3 only with four stages)
+  constexpr int kK23 = StageBytes<TG::kKBytes, kStages == 4>::value;
+  constexpr int kV23 = StageBytes<TG::kVBytes, kStages == 4>::value;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TG::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TG::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[kK23];
+  __shared__ __attribute__((aligned(1024))) char v_lds2[kV23];
+  __shared__ __attribute__((aligned(1024))) char k_lds3[kK23];
+  __shared__ __attribute__((aligned(1024))) char v_lds3[kV23];
   __shared__ int32_t sm_run[kRunSeg];
   __shared__ int32_t sm_flags[kRunSeg / 4];   // per tile of the segment: see tile_flags
+  __shared__ int sm_ticket;
+  auto kst = [&](auto C) -> char* {
+    constexpr int c = decltype(C)::value;
+    if constexpr (c == 0) return k_lds0;
+    else if constexpr (c == 1) return k_lds1;
+    else if constexpr (c == 2) return k_lds2;
+    else return k_lds3;
+  };
+  auto vst = [&](auto C) -> char* {
+    constexpr int c = decltype(C)::value;
+    if constexpr (c == 0) return v_lds0;
+    else if constexpr (c == 1) return v_lds1;
+    else if constexpr (c == 2) return v_lds2;
+    else return v_lds3;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
-  const int grp = wave_id / kGroupWaves;   // key-tile group
-  const int wave = wave_id % kGroupWaves;  // row block of the wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int rcol = lane & 31;  // MFMA column = query row within the wave
   const int half = lane >> 5;  // k-group of the lane
   const int G = p.group;
 
-  // ---- which item ---------------------------------------------------------------------------
+  // ---- which item -------------------------------------------------------------------------------
+  const int n_split = p.n_split;
   const int per_tile_r = p.batch * p.n_ret * G;
   const int ret_items = per_tile_r * p.n_qtiles;
-  int b, hq, qt;
+  int b, hq, qt, split = 0, item = 0;
   bool ret;
-  if ((int)blockIdx.x < ret_items) {
-    qt = p.n_qtiles - 1 - blockIdx.x / per_tile_r;
-    int r = blockIdx.x % per_tile_r;
+  if ((int)blockIdx.x < ret_items * n_split) {
+    // split-major, so that the workgroups of one head and split (same keys) share an XCD's L2
+    split = blockIdx.x / ret_items;
+    item = blockIdx.x % ret_items;
+    qt = p.n_qtiles - 1 - item / per_tile_r;
+    int r = item % per_tile_r;
     b = r / (p.n_ret * G);
     r %= p.n_ret * G;
     hq = p.ret_heads[r / G] * G + r % G;
     ret = true;
   } else {
     const int per_tile_s = p.batch * p.n_str * G;
-    const int it = blockIdx.x - ret_items;
+    const int it = blockIdx.x - ret_items * n_split;
     qt = p.n_qtiles - 1 - it / per_tile_s;
     int r = it % per_tile_s;
     b = r / (p.n_str * G);
@@ -212,8 +264,6 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   // ---- the wave's query rows: Q^T operand (B of S^T) ----------------------------------------
   const int wrow0 = wave * 32;                       // first row of this wave inside the tile
   const int qrow = row0 + wrow0 + rcol;              // chunk row of this lane's column
-  const int32_t pw_lo = p_lo + wrow0;
-  const int32_t pw_hi = min(pw_lo + 31, p_hi);
   const bool wave_live = wrow0 < n_rows;
   v8<T> qT[DC];
   {
@@ -230,18 +280,20 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   float m_run = -INFINITY, l_run = 0.f;
   const int32_t my_p = p_lo + wrow0 + rcol;          // this lane's query position
 
-  // Loop-invariant per-lane copy offsets (elements) for the run a wave copies.
+  // Loop-invariant per-lane copy offsets (elements): this wave copies part (wave / 4) of run
+  // (wave mod 4) of every tile.
+  const int crun = wave & 3, cpart = wave >> 2;
   int32_t k_lane[TG::kKLoadsPerWave], v_lane[TG::kVLoadsPerWave], v_key[TG::kVLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < TG::kKLoadsPerWave; ++i) {
-    const int idx = i * 64 + lane;
+    const int idx = (cpart * TG::kKLoadsPerWave + i) * 64 + lane;
     const int rl_ = idx / TG::kKRowChunks, pos = idx % TG::kKRowChunks;   // LDS row in the run
     const int j = pos ^ (rl_ & (TG::kKSwz - 1));                           // logical chunk
     k_lane[i] = perm32(rl_) * D + j * TG::kChunk;                          // key perm32(row)
   }
 #pragma unroll
   for (int i = 0; i < TG::kVLoadsPerWave; ++i) {
-    const int idx = i * 64 + lane;
+    const int idx = (cpart * TG::kVLoadsPerWave + i) * 64 + lane;
     const int d = idx / TG::kVRowChunks, pos = idx % TG::kVRowChunks;
     const int c = pos ^ TG::vswz(d);
     v_key[i] = c * TG::kChunk;
@@ -270,10 +322,10 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       }
       return any;
     };
-    // Copy run `wave` of `tile` (16 keys of K and V) into the stage: a scalar page base plus the
-    // lane's loop-invariant offsets.
+    // Copy this wave's part of run (wave mod 4) of `tile` into the stage: a scalar page base plus
+    // the lane's loop-invariant offsets.
     auto issue = [&](int tile, char* k_st, char* v_st) {
-      const int v = tile * 4 + wave;
+      const int v = tile * 4 + crun;
       const Run r = run_pos(v);
       const int32_t pr = sm_run[min(max(v - seg0, 0), kRunSeg - 1)];
       const int32_t page = v < n_runs ? packed_page(pr) : 0;   // absent runs: page 0, masked
@@ -281,16 +333,18 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       const int64_t pe = (int64_t)page * page_elems;
       const T* kbase = kpool + pe + (int64_t)r0 * D;
       const T* vbase = vpool + pe + r0;
+      char* kdst = k_st + crun * TG::kKRunBytes + cpart * TG::kKLoadsPerWave * 1024;
+      char* vdst = v_st + crun * TG::kVRunBytes + cpart * TG::kVLoadsPerWave * 1024;
 #pragma unroll
       for (int i = 0; i < TG::kKLoadsPerWave; ++i)   // absent keys' rows are masked by position
-        copy16_to_lds(kbase + k_lane[i], k_st + wave * TG::kKRunBytes + i * 1024);
+        copy16_to_lds(kbase + k_lane[i], kdst + i * 1024);
 #pragma unroll
       for (int i = 0; i < TG::kVLoadsPerWave; ++i) {
         const int32_t t = r.t0 + v_key[i];
         const bool absent = t + TG::kChunk <= r.lo || t >= r.hi;
         const void* src = absent ? static_cast<const void*>(g_prefill_zero_chunk)
                                  : static_cast<const void*>(vbase + v_lane[i]);
-        copy16_to_lds(src, v_st + wave * TG::kVRunBytes + i * 1024);
+        copy16_to_lds(src, vdst + i * 1024);
       }
     };
     // Zero, in LDS, the V channels of absent keys inside partly present chunks of `tile` (rare).
@@ -405,17 +459,17 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
         for (int db = 0; db < DB; ++db) oT[db] = mfma32(va[c][db], P[c], oT[db]);
       if constexpr (sizeof(T) == 2) pipeline_lds_mfma<4 * DB, kLdsAhead>();
     };
-    // Classification of a tile for the four row blocks, computed once per segment of runs:
-    // bit w: some key of the tile is visible to some row of wave w; bit 4 + w: every key is present
-    // and visible to every row of wave w (no mask); bit 8: some 16-byte V chunk mixes present and
-    // absent keys (zeroed in LDS before use).
+    // Classification of a tile for the row blocks, computed once per segment of runs: bit w: some
+    // key of the tile is visible to some row of wave w; bit 8 + w: every key is present and visible
+    // to every row of wave w (no mask); bit 16: some 16-byte V chunk mixes present and absent keys
+    // (zeroed in LDS before use).
     auto tile_flags = [&](int tile) -> int32_t {
       Run runs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) runs[i] = run_pos(tile * 4 + i);
       int32_t f = 0;
 #pragma unroll
-      for (int w = 0; w < kGroupWaves; ++w) {
+      for (int w = 0; w < kWaves; ++w) {
         if (w * 32 >= n_rows) continue;   // the wave has no rows
         const int32_t lo = p_lo + w * 32, hi = min(lo + 31, p_hi);
         bool all_full = true, any_vis = false;
@@ -432,16 +486,16 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
           any_vis = any_vis || vis;
         }
         f |= (any_vis ? 1 : 0) << w;
-        f |= (all_full ? 1 : 0) << (4 + w);
+        f |= (all_full ? 1 : 0) << (8 + w);
       }
-      return f | (partial_chunks(tile) ? 1 << 8 : 0);
+      return f | (partial_chunks(tile) ? 1 << 16 : 0);
     };
     auto load_flags = [&](int32_t tile0, int32_t ntiles) {
       for (int i = tid; i < ntiles; i += kThreads) sm_flags[i] = tile_flags(tile0 + i);
     };
     auto compute = [&](int tile, int32_t flags, const char* k_st, v8<T> (&P)[4]) -> bool {
       if (!((flags >> wave) & 1)) return false;
-      const bool all_full = (flags >> (4 + wave)) & 1;
+      const bool all_full = (flags >> (8 + wave)) & 1;
       Run runs[4];
       if (!all_full) {
 #pragma unroll
@@ -451,108 +505,130 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       return true;
     };
 
-    const int n_tiles = (n_runs + 3) / 4;
-    if (n_tiles == 0) return;
-    load_pages<kThreads>(sm_run, geo, rl, 0, min(kRunSeg, n_runs));
-    load_flags(0, min(kRunSeg / 4, n_tiles));
+    // This workgroup's tiles: all of a streaming item, a contiguous share of a retrieval item's.
+    const int n_all = (n_runs + 3) / 4;
+    const int per = RET ? (n_all + n_split - 1) / n_split : n_all;
+    const int t_begin = min(n_all, split * per);
+    const int n_tiles = min(n_all, t_begin + per) - t_begin;
+    if (n_tiles <= 0) return;
+    seg0 = ((t_begin * 4) / kRunSeg) * kRunSeg;
+    load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
+    load_flags(seg0 / 4, min(kRunSeg / 4, n_all - seg0 / 4));
     __syncthreads();
-    const int n_full_steps = RET ? max(0, (p_lo + 1) / kKeys) / kG : 0;
-    const int32_t live = (1 << min(kGroupWaves, (n_rows + 31) / 32)) - 1;
-    const int32_t lean_flags = live | (live << 4);
-    if (grp < n_tiles) issue(grp, k_lds0 + grp * TG::kKBytes, v_lds0 + grp * TG::kVBytes);
-    // Step s: group g computes tile s * kG + g from stage s % 2 while the copies of step s + 1 fill
-    // the other stage. The loop is unrolled by two so that each stage is a distinct LDS object and
-    // copies into one never wait on reads of the other.
-    const int n_steps = (n_tiles + kG - 1) / kG;
-    // The two groups run half a tile apart so that on each SIMD one wave's softmax overlaps the
-    // other's MFMAs: group 0 does S, softmax and PV of its tile; group 1 first does the PV of its
-    // previous tile (P kept in registers, V still in its slot of the other stage, which only its
-    // own copies overwrite, issued right after), then S and softmax of the current tile.
+    // retrieval tiles below the workgroup's first row are fully visible to every live wave
+    const int n_full = RET ? max(0, (p_lo + 1) / kKeys) : 0;
+    const int32_t live = (1 << min(kWaves, (n_rows + 31) / 32)) - 1;
+    const int32_t lean_flags = live | (live << 8);
+    auto flags_of = [&](int t) -> int32_t {
+      return t < n_full ? lean_flags : sm_flags[t - seg0 / 4];
+    };
+    // Tile tn is about to be copied: when it starts a new segment of runs (it always lies past
+    // the current one's start), stage that segment once nobody reads the current one any more.
+    auto enter = [&](int tn) {
+      if (((tn * 4) % kRunSeg) != 0 || tn * 4 == seg0) return;
+      __syncthreads();
+      seg0 = tn * 4;
+      load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
+      load_flags(tn, min(kRunSeg / 4, n_all - tn));
+      __syncthreads();
+    };
+    // a tile's classification, taken when its copies are issued (a later segment refill cannot
+    // overwrite it), indexed by stage
+    int32_t fq[kStages];
+#pragma unroll
+    for (int c = 0; c < kStages; ++c) fq[c] = 0;
+    // prologue: the first kAhead tiles (the first lies in the staged segment)
+    issue(t_begin, kst(std::integral_constant<int, 0>{}), vst(std::integral_constant<int, 0>{}));
+    fq[0] = flags_of(t_begin);
+    if constexpr (kAhead == 2) {
+      if (n_tiles > 1) {
+        enter(t_begin + 1);
+        issue(t_begin + 1, kst(std::integral_constant<int, 1>{}), vst(std::integral_constant<int, 1>{}));
+        fq[1] = flags_of(t_begin + 1);
+      }
+    }
     v8<T> P[4];
-    bool pend = false;        // group 1: P holds a tile whose PV is still to be done
+    bool pend = false;        // lagging waves: P holds a tile whose PV is still to be done
     const char* pend_v = nullptr;
-    auto step = [&](int s, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
-      wait_stores_complete();   // this wave's copies for step s have landed
-      __syncthreads();          // everyone's have; everyone is done with the other stage
-      if (pend) {
+    // Step s (tile t_begin + s) on stage c = s mod kStages: copies of tile s + kAhead go to stage
+    // (c + kAhead) mod kStages, which holds no tile still in use (with four stages: tile s - 1 is in
+    // stage c - 1 for the lagging waves' PV, tiles s and s + 1 in c and c + 1).
+    auto step = [&](auto C, int s) {
+      constexpr int c = decltype(C)::value;
+      constexpr int cn = (c + kAhead) % kStages;
+      const int t = t_begin + s;
+      if (kAhead == 2 && s + 1 < n_tiles) wait_older_then_barrier<TG::kCopiesPerTile>();
+      else wait_older_then_barrier<0>();
+      if (kLag && pend) {   // the lagging waves finish the previous tile first
         pv(P, pend_v);
         pend = false;
       }
-      // this step's tiles' classification, read before the segment may be refilled below
-      // (retrieval tiles below the workgroup's first row are fully visible to every live wave)
-      const bool lean = s < n_full_steps;
-      int32_t fl[kG];
-#pragma unroll
-      for (int g = 0; g < kG; ++g)
-        fl[g] = lean ? lean_flags : s * kG + g < n_tiles ? sm_flags[s * kG + g - seg0 / 4] : 0;
-      const int first_next = (s + 1) * kG;
-      if (first_next < n_tiles) {
-        if (((first_next * 4) % kRunSeg) == 0) {   // the next step starts a new segment of runs
-          __syncthreads();                         // everyone has read this segment's flags
-          seg0 = first_next * 4;
-          load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
-          load_flags(first_next, min(kRunSeg / 4, n_tiles - first_next));
-          __syncthreads();
-        }
-        if (first_next + grp < n_tiles)
-          issue(first_next + grp, k_nxt + grp * TG::kKBytes, v_nxt + grp * TG::kVBytes);
+      const int32_t flags = fq[c];
+      if (s + kAhead < n_tiles) {
+        const int tn = t + kAhead;
+        enter(tn);
+        issue(tn, kst(std::integral_constant<int, cn>{}), vst(std::integral_constant<int, cn>{}));
+        fq[cn] = flags_of(tn);
       }
-      bool fix = false;
-#pragma unroll
-      for (int g = 0; g < kG; ++g) fix = fix || ((fl[g] >> 8) & 1);
-      if (fix) {
-#pragma unroll
-        for (int g = 0; g < kG; ++g)
-          if ((fl[g] >> 8) & 1) fixup(s * kG + g, v_cur + g * TG::kVBytes);
+      if ((flags >> 16) & 1) {   // uniform: the same word for every wave
+        fixup(t, vst(C));
         __syncthreads();
       }
-      if (s * kG + grp < n_tiles && compute(s * kG + grp, (kG == 2 && grp == 1) ? fl[kG - 1] : fl[0], k_cur + grp * TG::kKBytes, P)) {
-        pend = true;
-        pend_v = v_cur + grp * TG::kVBytes;
-        if (grp == 0) {
-          pv(P, pend_v);
-          pend = false;
-        }
+      if (compute(t, flags, kst(C), P)) {
+        pend_v = vst(C);
+        if (kLag && wave >= kWaves / 2) pend = true;
+        else pv(P, pend_v);
       }
     };
-    for (int s = 0; s < n_steps; s += 2) {
-      step(s, k_lds0, v_lds0, k_lds1, v_lds1);
-      if (s + 1 < n_steps) step(s + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    for (int s = 0; s < n_tiles; s += kStages) {
+      step(std::integral_constant<int, 0>{}, s);
+      if (s + 1 < n_tiles) step(std::integral_constant<int, 1>{}, s + 1);
+      if constexpr (kStages == 4) {
+        if (s + 2 < n_tiles) step(std::integral_constant<int, 2 % kStages>{}, s + 2);
+        if (s + 3 < n_tiles) step(std::integral_constant<int, 3 % kStages>{}, s + 3);
+      }
     }
-    if (pend) pv(P, pend_v);   // group 1's last tile (no copies follow)
+    if (pend) pv(P, pend_v);   // the lagging waves' last tile (no copies follow)
   };
   if (ret) body(std::integral_constant<bool, true>{});
   else body(std::integral_constant<bool, false>{});
 
-  // ---- merge the groups' partial states (same rows, disjoint key tiles) -----------------------
-  if constexpr (kG == 2) {
-    wait_stores_complete();
-    __syncthreads();   // the tile loop is over everywhere: the stages are free
-    // group 1 parks m, l and O^T per lane (lane-contiguous, so conflict-free); the k_lds0 / v_lds0
-    // stages hold 4 waves x DB x 16 x 64 floats, m and l go to k_lds1
-    float* park_o = reinterpret_cast<float*>(wave < 2 ? k_lds0 : v_lds0) + (wave & 1) * (DB * 16 * 64);
-    float* park_ml = reinterpret_cast<float*>(k_lds1) + wave * 128;
-    static_assert(2 * DB * 16 * 64 * 4 <= kG * TG::kKBytes && 2 * DB * 16 * 64 * 4 <= kG * TG::kVBytes,
-                  "parked O^T must fit the stage");
-    if (grp == 1) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) park_o[(db * 16 + j) * 64 + lane] = oT[db][j];
-      park_ml[lane] = m_run;
-      park_ml[64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (grp == 1) return;
-    const float m_o = park_ml[lane], l_o = park_ml[64 + lane];
-    const float m_new = fmaxf(m_run, m_o);
-    const float f_me = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-    const float f_o = (m_o == -INFINITY) ? 0.f : fast_exp2(m_o - m_new);
-    l_run = l_run * f_me + l_o * f_o;
+  // ---- split merge: the last workgroup of a retrieval item to arrive reduces the partials ---
+  // Partials go out with device-coherent (write-through) stores; waiting for them to complete
+  // before the ticket makes them visible to whichever workgroup, on any XCD, draws the last
+  // ticket, which reads them back with device-coherent loads.
+  if (ret && n_split > 1) {
+    constexpr int64_t kPart = prefill_partial_floats(sizeof(T), D);
+    constexpr int kWavePart = 64 * (2 + DB * 16);
+    float* mine = p.partial + ((int64_t)item * n_split + split) * kPart + wave * kWavePart;
+    store_coherent(mine + lane, m_run);
+    store_coherent(mine + 64 + lane, l_run);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) oT[db][j] = oT[db][j] * f_me + park_o[(db * 16 + j) * 64 + lane] * f_o;
+      for (int j = 0; j < 16; ++j) store_coherent(mine + 128 + (db * 16 + j) * 64 + lane, oT[db][j]);
+    wait_stores_complete();
+    __syncthreads();
+    int32_t* ctr = p.counter + item;
+    if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sm_ticket != n_split - 1) return;
+    for (int sp = 0; sp < n_split; ++sp) {
+      if (sp == split) continue;
+      const float* other = p.partial + ((int64_t)item * n_split + sp) * kPart + wave * kWavePart;
+      const float m_o = load_coherent(other + lane), l_o = load_coherent(other + 64 + lane);
+      const float m_new = fmaxf(m_run, m_o);
+      const float f_me = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      const float f_o = (m_o == -INFINITY) ? 0.f : fast_exp2(m_o - m_new);
+      m_run = m_new;
+      l_run = l_run * f_me + l_o * f_o;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          oT[db][j] = oT[db][j] * f_me + load_coherent(other + 128 + (db * 16 + j) * 64 + lane) * f_o;
+    }
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- normalise and store -----------------------------------------------------------------

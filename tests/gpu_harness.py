@@ -105,12 +105,13 @@ class Cache:
                             w.recent, w.ring_blocks, w.scale, out, ws, split_tokens)
         return out
 
-    def prefill(self, q_bits: np.ndarray):
+    def prefill(self, q_bits: np.ndarray, workspace=None):
         w = self.w
         q = to_dev(q_bits, w.dtype)
         out = torch.empty_like(q)
+        ws = workspace if workspace is not None else duo.prefill_workspace(q, self.table, self.mask)
         duo.duo_attn_prefill(q, self.k_pool, self.v_pool, self.table, self.lens, self.mask, w.sink,
-                             w.recent, w.ring_blocks, w.scale, out)
+                             w.recent, w.ring_blocks, w.scale, out, ws)
         return out
 
 

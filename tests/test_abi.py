@@ -23,6 +23,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(duo.LIB_PATH),
 FAKE = 0x100000  # a 4 KiB-aligned, never dereferenced address
 MASK_RS = (ctypes.c_uint8 * 2)(1, 0)
 MASK_R = (ctypes.c_uint8 * 2)(1, 1)
+MASK_S = (ctypes.c_uint8 * 2)(0, 0)
 MASK_BAD = (ctypes.c_uint8 * 2)(1, 2)
 
 
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 1
+    assert duo.abi_version() == 2
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -125,12 +126,13 @@ def prefill(**kw):
     a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, table=FAKE, num_blocks=64, bs=16, mbph=20,
              lens=FAKE, batch=1, q_len=32, hq=4, hkv=2, d=128, dtype=2,
              mask=ctypes.cast(MASK_RS, ctypes.c_void_p), sink=4, recent=16, rb=4, scale=0.1,
-             out=FAKE)
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     return duo.lib().duo_attn_prefill(a["q"], a["k_pool"], a["v_pool"], a["table"],
                                       a["num_blocks"], a["bs"], a["mbph"], a["lens"], a["batch"],
                                       a["q_len"], a["hq"], a["hkv"], a["d"], a["dtype"], a["mask"],
-                                      a["sink"], a["recent"], a["rb"], a["scale"], a["out"], None)
+                                      a["sink"], a["recent"], a["rb"], a["scale"], a["out"],
+                                      a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -141,6 +143,28 @@ def prefill(**kw):
 ])
 def test_prefill_rejects(kw, status):
     assert prefill(**kw) == status
+
+
+def test_prefill_workspace_size_query():
+    L = duo.lib()
+    rs = ctypes.cast(MASK_RS, ctypes.c_void_p)
+    n = L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 128, 2, rs)
+    assert n > 0 and n % 4 == 0
+    # more rows or more retrieval heads need more room; no retrieval head needs almost none
+    assert L.duo_attn_prefill_workspace_size(1, 4096, 4, 2, 128, 2, rs) > n
+    r_only = ctypes.cast(MASK_R, ctypes.c_void_p)
+    assert L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 128, 2, r_only) > n
+    s_only = ctypes.cast(MASK_S, ctypes.c_void_p)
+    assert L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 128, 2, s_only) == 256
+    # invalid sizes
+    assert L.duo_attn_prefill_workspace_size(1, 0, 4, 2, 128, 2, rs) == 0
+    assert L.duo_attn_prefill_workspace_size(1, 32, 4, 3, 128, 2, rs) == 0
+    assert L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 96, 2, rs) == 0
+    assert L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 128, 7, rs) == 0
+    assert L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 128, 2, None) == 0
+    # a call with a missing or short workspace is rejected before anything is launched
+    assert prefill(ws=None) == WORKSPACE
+    assert prefill(ws_bytes=n - 1) == WORKSPACE
 
 
 def test_all_retrieval_prefill_ignores_ring_geometry_but_checks_the_rest():

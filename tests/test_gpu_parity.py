@@ -269,6 +269,28 @@ def test_prefill_is_deterministic():
     assert a.tobytes() == b.tobytes()
 
 
+@pytest.mark.parametrize("context", [16250, 16384, 20000])
+def test_prefill_long_retrieval_rows(context):
+    """A short chunk at the end of a long context: a retrieval item's keys are split between
+    workgroups, and the split point and the edges of the kernel's staged page lists (512 runs)
+    fall one tile apart (16250), together (16384) or apart (20000)."""
+    q_len = 40
+    w = synth.small(f"long-ret-{context}", batch=1, q_heads=4, kv_heads=2, head_dim=64,
+                    dtype=synth.BF16, block_size=16, sink=4, recent=64, retrieval=(0,),
+                    context=context, q_len=q_len, seed=45)
+    say(f"prefill long retrieval rows, context {context}")
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, context, synth.S_K)
+    V = logical_kv(w, context, synth.S_V)
+    cache.append_logical(K, V, 0, context)
+    q = q_prefill(w, 0, q_len)
+    got = to_host_f64(cache.prefill(q), w.dtype)
+    want = oracle.attend(q, K, V, np.full(w.batch, context), cache.mask, sink=w.sink,
+                         recent=w.recent, scale=w.scale, dtype=w.dtype,
+                         rows=_rows_all(w.batch, q_len, w.num_q_heads))
+    check_close(got, want, w.dtype, f"context {context}")
+
+
 # ------------------------------------------------------------------------------------------------
 # The five workloads at their real shapes
 # ------------------------------------------------------------------------------------------------
