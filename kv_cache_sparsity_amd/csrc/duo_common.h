@@ -149,6 +149,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// A value combined with the same value of lane (lane ^ 32) by one v_permlane32_swap, which trades
+// the upper 32 lanes of its first operand for the lower 32 of its second: given v twice, every lane
+// gets back its own v and its partner's, one in each result. (A shuffle would go through LDS.)
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Device-scope coherent store / load (write-through / read-through the XCD-local L2): used for
 // the few bytes that one workgroup hands to another within a launch.
 __device__ __forceinline__ void store_coherent(float* p, float v) {

@@ -420,7 +420,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
 #pragma unroll
         for (int k = 0; k < w; ++k) t16[k] = __builtin_elementwise_maximum(t16[k], t16[k + w]);
       float mx = t16[0];
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
+      mx = max_xor32(mx) * p.scale_log2;
       // Lazy reference max: it moves only when some row of the wave exceeds it by more than 8
       // (log2 units), so p <= 256 and O / l are rescaled on few tiles. The final O / l is exact
       // whatever reference was used. O holds every earlier tile's PV at this point.
@@ -506,8 +506,11 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     };
 
     // This workgroup's tiles: all of a streaming item, a contiguous share of a retrieval item's.
+    // The shares are cut at the same key tiles for every row tile of the sequence (those of its
+    // last rows, which see all L keys), so that the workgroups of one head and share, which run
+    // side by side on one XCD, walk the same keys together through its L2.
     const int n_all = (n_runs + 3) / 4;
-    const int per = RET ? (n_all + n_split - 1) / n_split : n_all;
+    const int per = RET ? ((L + kKeys - 1) / kKeys + n_split - 1) / n_split : n_all;
     const int t_begin = min(n_all, split * per);
     const int n_tiles = min(n_all, t_begin + per) - t_begin;
     if (n_tiles <= 0) return;
@@ -632,7 +635,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   }
 
   // ---- normalise and store -----------------------------------------------------------------
-  l_run += shfl_xor(l_run, 32);
+  l_run = add_xor32(l_run);
   if (qrow < p.q_len && wave_live) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     T* dst = static_cast<T*>(p.out) + (((int64_t)b * p.q_len + qrow) * p.num_q_heads + hq) * D;
