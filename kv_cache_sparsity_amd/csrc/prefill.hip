@@ -110,13 +110,30 @@ __device__ __forceinline__ v8<T> lds_operand(const char* row, int chunk, int swz
   }
 }
 
-__device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// Byte address of a location in LDS (what M0 and ds instructions take).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// 16 bytes per lane from global memory straight into LDS: global_load_lds_dwordx4 writes lane i's
+// bytes at M0 + 16 i (M0 = lds_base, wave-uniform; one wait state after M0 is written). It is
+// issued as inline assembly so that the compiler does not track it: it cannot tell which stage an
+// LDS read touches, so it would make every operand read wait for all copies in flight, the
+// look-ahead ones included. The kernel orders copies and reads itself, by vmcnt and barrier
+// (wait_older_then_barrier).
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
 }
 
 // Wait until at most `n` of this wave's vector memory operations are outstanding (they complete in
 // order, so every older one has landed) and its LDS operations have completed, then meet the other
 // waves at the barrier. Unlike __syncthreads() this leaves younger copies in flight.
+// s_waitcnt immediate: vmcnt(0), other counters not waited on.
+constexpr int kWaitVmcnt0 = (0 & 15) | (7 << 4) | (15 << 8) | ((0 >> 4) << 14);
+
 template <int n>
 __device__ __forceinline__ void wait_older_then_barrier() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
@@ -271,6 +288,10 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     const T* src = static_cast<const T*>(p.q) + (((int64_t)b * p.q_len + (ok ? qrow : 0)) * p.num_q_heads + hq) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qT[dc] = ok ? load8(src + dc * 16 + half * 8) : zero8<T>();
+    // Retire the Q loads here. Left pending, the compiler would wait for them at their first use
+    // inside the tile loop, by a full vmcnt wait that every step would then pay for the copies
+    // in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   f32x16 oT[DB];
 #pragma unroll
@@ -333,8 +354,8 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       const int64_t pe = (int64_t)page * page_elems;
       const T* kbase = kpool + pe + (int64_t)r0 * D;
       const T* vbase = vpool + pe + r0;
-      char* kdst = k_st + crun * TG::kKRunBytes + cpart * TG::kKLoadsPerWave * 1024;
-      char* vdst = v_st + crun * TG::kVRunBytes + cpart * TG::kVLoadsPerWave * 1024;
+      const uint32_t kdst = lds_addr(k_st) + crun * TG::kKRunBytes + cpart * TG::kKLoadsPerWave * 1024;
+      const uint32_t vdst = lds_addr(v_st) + crun * TG::kVRunBytes + cpart * TG::kVLoadsPerWave * 1024;
 #pragma unroll
       for (int i = 0; i < TG::kKLoadsPerWave; ++i)   // absent keys' rows are masked by position
         copy16_to_lds(kbase + k_lane[i], kdst + i * 1024);
