@@ -416,19 +416,25 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       if constexpr (sizeof(T) == 2) pipeline_lds_mfma<2 * DC, kLdsAhead>();
       // accumulator 4*i + j of block b2 is key 8*half + 4*(i&1) + j of run 2*b2 + (i>>1)
       if (mask) {
+        // The keys of run k that this lane's row may see form one interval [lo, hi): present
+        // keys [r.lo, r.hi), causal t <= my_p and, in a ring run, the window t > my_p - recent.
+        // Key t is kept iff t - lo, taken unsigned, is below hi - lo: one compare per score.
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
+        for (int k = 0; k < 4; ++k) {
+          const Run& r = runs[k];
+          const int32_t lo = r.windowed ? max(r.lo, my_p - p.recent + 1) : r.lo;
+          const int32_t hi = min(r.hi, my_p + 1);
+          const uint32_t width = (uint32_t)max(hi - lo, 0);
+          const int32_t d0 = r.t0 + 8 * half - lo;   // the lane's first key of the run, from lo
+          const int b2 = k >> 1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const Run& r = runs[2 * b2 + (i >> 1)];
+          for (int i = 2 * (k & 1); i < 2 * (k & 1) + 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int32_t t = r.t0 + 8 * half + 4 * (i & 1) + j;
-              const bool ok = t >= r.lo && t < r.hi && t <= my_p &&
-                              (!r.windowed || my_p - t < p.recent);
+              const bool ok = (uint32_t)(d0 + 4 * (i & 1) + j) < width;
               s[b2][4 * i + j] = ok ? s[b2][4 * i + j] : -INFINITY;
             }
-          }
+        }
       }
       // Row max of the raw scores (softmax_scale > 0, so scaling after the max is exact). The
       // scores are finite or -inf here (absent keys were masked), so the NaN-propagating maximum
