@@ -288,10 +288,6 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     const T* src = static_cast<const T*>(p.q) + (((int64_t)b * p.q_len + (ok ? qrow : 0)) * p.num_q_heads + hq) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qT[dc] = ok ? load8(src + dc * 16 + half * 8) : zero8<T>();
-    // Retire the Q loads here. Left pending, the compiler would wait for them at their first use
-    // inside the tile loop, by a full vmcnt wait that every step would then pay for the copies
-    // in flight.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   f32x16 oT[DB];
 #pragma unroll
@@ -545,6 +541,10 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     load_pages<kThreads>(sm_run, geo, rl, seg0, min(kRunSeg, n_runs - seg0));
     load_flags(seg0 / 4, min(kRunSeg / 4, n_all - seg0 / 4));
     __syncthreads();
+    // Retire the Q loads (issued before the page staging, whose latency they share) before the
+    // first copy. Left pending, the compiler would wait for them at their first use inside the
+    // tile loop, by a full vmcnt wait that every step would then pay for the copies in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     // retrieval tiles below the workgroup's first row are fully visible to every live wave
     const int n_full = RET ? max(0, (p_lo + 1) / kKeys) : 0;
     const int32_t live = (1 << min(kWaves, (n_rows + 31) / 32)) - 1;
