@@ -26,6 +26,8 @@ the grouping of q heads onto kv heads (contiguous, hq // (Hq / Hkv); pinned only
 from .cache import (slot_of, table_position, append, gather, pool_shapes, to_f64,
                     new_pools, ring_capacity)
 from .attention import visible_positions, attend_row, attend, attend_paged
+from .quant import quantize_rows, dequantize, scale_pool_shape, append_int8, attend_int8
 
 __all__ = ["slot_of", "table_position", "append", "gather", "pool_shapes", "to_f64", "new_pools",
-           "ring_capacity", "visible_positions", "attend_row", "attend", "attend_paged"]
+           "ring_capacity", "visible_positions", "attend_row", "attend", "attend_paged",
+           "quantize_rows", "dequantize", "scale_pool_shape", "append_int8", "attend_int8"]
