@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 2
+#define DUO_ATTN_ABI_VERSION 3
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -177,6 +177,58 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                          int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * The int8 cache -- the same paged, per-head circular layout with 8-bit codes and one fp32 scale per
+ * slot for K and one for V.
+ *
+ * Source: DuoAttention README, installation and usage (the QServe install step and the demo): the
+ * retrieval/streaming split is paired with a quantized KV cache, which is how one GPU holds
+ * multi-million-token contexts. The pages fix no quantization scheme; this library's is:
+ *   amax  = max |x| over one stored row (the head_dim values of one token of one kv head, K and V
+ *           separately), exact in fp32;
+ *   scale = amax / 127 and inv = 127 / amax, correctly rounded fp32 divisions;
+ *   code  = x * inv (correctly rounded fp32 product), rounded half to even, clamped to [-127, 127];
+ *   an all-zero row stores codes 0 and scale 0. The row's value is code * scale.
+ * Layout:
+ *   k_pool  int8 [num_blocks][block_size][head_dim]     (token-major, as the K pages above)
+ *   v_pool  int8 [num_blocks][head_dim][block_size]     (channel-major, as the V pages above)
+ *   k_scale, v_scale  float [num_blocks][block_size]: the scale of slot row r of page P at [P][r].
+ * Block table, slots, lengths and every other convention are those of the calls above. New rows
+ * (k_new, v_new) and q / out are DUO_F32, DUO_F16 or DUO_BF16 (the call's dtype). The new rows must
+ * be finite.
+ */
+
+/*
+ * kv_append_circular_int8 -- as kv_append_circular, quantizing each new K and V row: its codes go
+ * to the row's slot in the pages and its scale to [page][row] of k_scale / v_scale. Codes and scales
+ * are bit-exact functions of the row (the scheme above). Errors: as kv_append_circular, and
+ * INVALID_ARG for a missing, misaligned or shared scale pool.
+ */
+int32_t kv_append_circular_int8(int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                                const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                                int32_t batch, int32_t t_new, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                void* stream);
+
+/*
+ * duo_attn_decode_int8 -- as duo_attn_decode over the int8 cache: a score is softmax_scale times q
+ * dotted with the key's codes times the key's K scale, and a value row is its codes times its V
+ * scale. The workspace is the one duo_attn_decode_workspace_size gives for the same sizes. Errors:
+ * as duo_attn_decode, and INVALID_ARG for a missing or misaligned scale pool.
+ */
+int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* v_pool,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                             int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, const uint8_t* head_is_retrieval, int32_t sink_size,
+                             int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             int32_t split_tokens, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* duo_status_string(int32_t status);

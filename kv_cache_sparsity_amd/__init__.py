@@ -24,8 +24,8 @@ DUO_F32, DUO_F16, DUO_BF16 = 0, 1, 2
 STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "DUO_ERR_CAPACITY",
           4: "DUO_ERR_WORKSPACE", 5: "DUO_ERR_HIP"}
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
-           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_status_string",
-           "duo_abi_version")
+           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "kv_append_circular_int8",
+           "duo_attn_decode_int8", "duo_status_string", "duo_abi_version")
 
 
 class DuoAttnError(RuntimeError):
@@ -61,6 +61,14 @@ def lib() -> ctypes.CDLL:
         L.duo_attn_prefill.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                        _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
                                        _P]
+        L.kv_append_circular_int8.restype = _I32
+        L.kv_append_circular_int8.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                                              _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
+                                              _P]
+        L.duo_attn_decode_int8.restype = _I32
+        L.duo_attn_decode_int8.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32,
+                                           _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
+                                           _I32, _P]
         L.duo_status_string.restype = ctypes.c_char_p
         L.duo_status_string.argtypes = [_I32]
         L.duo_abi_version.restype = _I32
@@ -199,7 +207,51 @@ def duo_attn_prefill(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval
     _check("duo_attn_prefill", st)
 
 
+def _int8_pools(k_pool, v_pool, k_scale, v_scale):
+    import torch
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
+        raise TypeError("int8 cache pools must be torch.int8")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise TypeError("int8 cache scales must be torch.float32")
+
+
+def kv_append_circular_int8(k_pool, v_pool, k_scale, v_scale, block_table, k_new, v_new,
+                            seq_lens_before, seq_lens_after, head_is_retrieval, sink_size: int,
+                            recent_size: int, ring_blocks: int, stream=None) -> None:
+    """Quantize and append new rows into the int8 cache: k_pool int8 [NB][bs][D], v_pool int8
+    [NB][D][bs], k_scale / v_scale float32 [NB][bs]; k_new / v_new [B][t_new][Hkv][D]."""
+    _int8_pools(k_pool, v_pool, k_scale, v_scale)
+    num_blocks, block_size, head_dim = k_pool.shape
+    batch, t_new, num_kv_heads, _ = k_new.shape
+    mask = _HostMask(head_is_retrieval)
+    st = lib().kv_append_circular_int8(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), num_blocks,
+        block_size, block_table.shape[2], _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
+        _ptr(seq_lens_after), batch, t_new, num_kv_heads, head_dim, _dtype_tag(k_new), mask.ptr,
+        sink_size, recent_size, ring_blocks, _stream(stream))
+    _check("kv_append_circular_int8", st)
+
+
+def duo_attn_decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                         head_is_retrieval, sink_size: int, recent_size: int, ring_blocks: int,
+                         softmax_scale: float, out, workspace, split_tokens: int = 0,
+                         stream=None) -> None:
+    """duo_attn_decode over the int8 cache (pools and scales as for kv_append_circular_int8)."""
+    _int8_pools(k_pool, v_pool, k_scale, v_scale)
+    num_blocks, block_size, head_dim = k_pool.shape
+    batch, num_q_heads, _ = q.shape
+    mask = _HostMask(head_is_retrieval)
+    st = lib().duo_attn_decode_int8(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch, num_q_heads,
+        block_table.shape[1], head_dim, _dtype_tag(q), mask.ptr, sink_size, recent_size,
+        ring_blocks, softmax_scale, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), split_tokens, _stream(stream))
+    _check("duo_attn_decode_int8", st)
+
+
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
+           "kv_append_circular_int8", "duo_attn_decode_int8",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",
            "prefill_workspace", "status_string", "abi_version",
            "DuoAttnError", "lib", "LIB_PATH", "SYMBOLS", "DUO_F32", "DUO_F16", "DUO_BF16"]

@@ -109,16 +109,20 @@ const char* duo_status_string(int32_t s) {
   }
 }
 
-int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_table,
-                           int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
-                           const void* k_new, const void* v_new, const int32_t* seq_lens_before,
-                           int32_t* seq_lens_after, int32_t batch, int32_t t_new,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+// The append behind both caches: int8 = quantize each new row into codes + one scale per slot.
+static int32_t append_impl(bool int8, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                           const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                           int32_t max_blocks_per_head, const void* k_new, const void* v_new,
+                           const int32_t* seq_lens_before, int32_t* seq_lens_after, int32_t batch,
+                           int32_t t_new, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                            const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                            int32_t ring_blocks, void* stream) {
   (void)recent_size;  // the append keeps every ring slot; the window is applied when attending
   if (!k_pool || !v_pool || !block_table || !k_new || !v_new || !seq_lens_before ||
       !head_is_retrieval)
+    return DUO_ERR_INVALID_ARG;
+  if (int8 && (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16) ||
+               k_scale == v_scale))
     return DUO_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens_before, 4) ||
@@ -162,9 +166,39 @@ int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_tabl
   p.ring_slots = n_str > 0 ? ring_blocks * block_size : 1;
   p.retrieval_bits = 0;
   for (int32_t i = 0; i < n_ret; ++i) p.retrieval_bits |= 1ull << ret[i];
-  if (launch_append(p, elem_bytes(dtype), static_cast<hipStream_t>(stream)) != hipSuccess)
-    return DUO_ERR_HIP;
-  return DUO_OK;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.dtype = dtype;
+  const hipError_t e = int8 ? launch_append_int8(p, static_cast<hipStream_t>(stream))
+                            : launch_append(p, elem_bytes(dtype), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DUO_OK : DUO_ERR_HIP;
+}
+
+int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_table,
+                           int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
+                           const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                           int32_t* seq_lens_after, int32_t batch, int32_t t_new,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                           const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                           int32_t ring_blocks, void* stream) {
+  return append_impl(false, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks, block_size,
+                     max_blocks_per_head, k_new, v_new, seq_lens_before, seq_lens_after, batch,
+                     t_new, num_kv_heads, head_dim, dtype, head_is_retrieval, sink_size,
+                     recent_size, ring_blocks, stream);
+}
+
+int32_t kv_append_circular_int8(int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                                const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                                int32_t batch, int32_t t_new, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                void* stream) {
+  return append_impl(true, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks, block_size,
+                     max_blocks_per_head, k_new, v_new, seq_lens_before, seq_lens_after, batch,
+                     t_new, num_kv_heads, head_dim, dtype, head_is_retrieval, sink_size,
+                     recent_size, ring_blocks, stream);
 }
 
 size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -182,17 +216,21 @@ size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_
   return bytes;
 }
 
-int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
-                        const int32_t* block_table, int32_t num_blocks, int32_t block_size,
-                        int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
-                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                        const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
-                        int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
-                        size_t workspace_bytes, int32_t split_tokens, void* stream) {
+// The decode behind both caches: int8 = codes in the pools plus one scale per slot for K and V.
+static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const void* v_pool,
+                           const float* k_scale, const float* v_scale, const int32_t* block_table,
+                           int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
+                           const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                           const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                           int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
+                           size_t workspace_bytes, int32_t split_tokens, void* stream) {
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);
   if (st != DUO_OK) return st;
+  if (int8 && (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16)))
+    return DUO_ERR_INVALID_ARG;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
   if (num_q_heads / num_kv_heads > 16) return DUO_ERR_UNSUPPORTED;
@@ -240,9 +278,40 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
   p.scale_log2 = softmax_scale * kLog2e;
   for (int32_t i = 0; i < n_ret; ++i) p.ret_heads[i] = ret[i];
   for (int32_t i = 0; i < n_str; ++i) p.str_heads[i] = str[i];
-  if (launch_decode(p, dtype, head_dim, (int)grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  if (launch_decode(p, dtype, head_dim, int8, (int)grid, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return DUO_ERR_HIP;
   return DUO_OK;
+}
+
+int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                        int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
+                        int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t split_tokens, void* stream) {
+  return decode_impl(false, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
+                     block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                     softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* v_pool,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                             int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, const uint8_t* head_is_retrieval, int32_t sink_size,
+                             int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             int32_t split_tokens, void* stream) {
+  return decode_impl(true, q, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks,
+                     block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                     softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
 }
 
 size_t duo_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads,

@@ -20,17 +20,27 @@ namespace {
 constexpr int kAppendThreads = 256;
 constexpr int kMaxHeadDim = 256;
 
-template <typename E>  // raw element bits: uint16_t or uint32_t
-__global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendParams p) {
-  __shared__ E vstage[16][kMaxHeadDim];
-  const int vg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int D = p.head_dim;
+// The positions [t_lo, t_hi) of this workgroup's 16-position run (blockIdx.x) of sequence b, kv
+// head h, and where they go. Also writes the sequence's new length (once per sequence).
+struct AppendRun {
+  int32_t L0, t_lo, t_hi;
+  bool ret;
+  const int32_t* trow;
+  __device__ __forceinline__ int32_t slot_of(const AppendParams& p, int32_t t) const {
+    if (ret || t < p.sink) return t;
+    return (p.sink_blocks << p.log2_bs) + (int32_t)((int64_t)(t - p.sink) % p.ring_slots);
+  }
+  __device__ __forceinline__ int64_t page_of(const AppendParams& p, int32_t s) const {
+    return clamp_page(trow[s >> p.log2_bs], p.num_blocks);
+  }
+};
+
+__device__ __forceinline__ AppendRun append_run(const AppendParams& p, int vg, int h, int b) {
+  AppendRun a;
   const int32_t L0 = min(max(p.lens_before[b], 0), INT32_MAX - p.t_new);  // no position overflow
   const int32_t L1 = L0 + p.t_new;
   if (vg == 0 && h == 0 && threadIdx.x == 0 && p.lens_after != nullptr) p.lens_after[b] = L1;
-
   const bool ret = (p.retrieval_bits >> h) & 1ull;
-  const int32_t bs_mask = (1 << p.log2_bs) - 1;
   int32_t t_lo, t_hi;
   if (ret) {
     const int32_t end = min(L1, p.max_blocks_per_head << p.log2_bs);
@@ -52,14 +62,26 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendPara
       t_hi = min(p.sink + k * 16 + 16, L1);
     }
   }
+  a.L0 = L0;
+  a.t_lo = t_lo;
+  a.t_hi = t_hi;
+  a.ret = ret;
+  a.trow = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
+  return a;
+}
+
+template <typename E>  // raw element bits: uint16_t or uint32_t
+__global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendParams p) {
+  __shared__ E vstage[16][kMaxHeadDim];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int D = p.head_dim;
+  const AppendRun run = append_run(p, blockIdx.x, h, b);
+  const int32_t L0 = run.L0, t_lo = run.t_lo, t_hi = run.t_hi;
   if (t_lo >= t_hi) return;
   const int n_tok = t_hi - t_lo;
-
-  const int32_t* trow = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
-  auto slot_of = [&](int32_t t) -> int32_t {
-    if (ret || t < p.sink) return t;
-    return (p.sink_blocks << p.log2_bs) + (int32_t)((int64_t)(t - p.sink) % p.ring_slots);
-  };
+  const int32_t bs_mask = (1 << p.log2_bs) - 1;
+  const int32_t* trow = run.trow;
+  auto slot_of = [&](int32_t t) -> int32_t { return run.slot_of(p, t); };
 
   constexpr int kVec = 16 / sizeof(E);  // elements per 16-byte chunk
   const int chunks = D / kVec;
@@ -115,7 +137,138 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(const AppendPara
   }
 }
 
+// Element bits of the new rows as fp32 (exact): bf16, fp16 or fp32.
+template <typename E>
+__device__ __forceinline__ float elem_to_f32(uint32_t bits, int dtype) {
+  if constexpr (sizeof(E) == 4) {
+    return __uint_as_float(bits);
+  } else {
+    if (dtype == 2) return __uint_as_float(bits << 16);                       // bf16
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);                // fp16
+  }
+}
+
+// Symmetric int8 code of x for a row whose largest magnitude is amax > 0: x * (127 / amax), both
+// operations correctly rounded fp32, rounded half to even and clamped to [-127, 127].
+__device__ __forceinline__ int32_t quant_code(float x, float inv) {
+  const float c = rintf(__fmul_rn(x, inv));
+  return (int32_t)fminf(fmaxf(c, -127.f), 127.f);
+}
+
+// int8 cache: every new K and V row is quantized with one fp32 scale, amax / 127 (0 for an all-zero
+// row, whose codes are 0), and its codes and scale go to the row's slot: codes into the pages (K
+// token-major, V channel-major, one byte per element) and the scale into k_scale / v_scale at
+// [page][row]. The lanes of one row (D / elements-per-16-bytes of them, a divisor of the wave)
+// reduce its amax with xor shuffles.
+template <typename E>  // raw element bits of the new rows: uint16_t or uint32_t
+__global__ void __launch_bounds__(kAppendThreads) append_int8_kernel(const AppendParams p) {
+  __shared__ uint8_t vstage[16][kMaxHeadDim];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int D = p.head_dim;
+  const AppendRun run = append_run(p, blockIdx.x, h, b);
+  const int32_t L0 = run.L0, t_lo = run.t_lo, t_hi = run.t_hi;
+  if (t_lo >= t_hi) return;
+  const int n_tok = t_hi - t_lo;
+  const int32_t bs_mask = (1 << p.log2_bs) - 1;
+
+  constexpr int kVec = 16 / sizeof(E);  // elements per 16-byte chunk
+  const int chunks = D / kVec;          // lanes per row: 8, 16, 32 or 64
+  const E* kn = static_cast<const E*>(p.k_new);
+  const E* vn = static_cast<const E*>(p.v_new);
+  int8_t* kq = static_cast<int8_t*>(p.k_pool);
+  int8_t* vq = static_cast<int8_t*>(p.v_pool);
+  const int64_t tok_stride = (int64_t)p.num_kv_heads * D;            // elements between tokens
+  const int64_t src0 = ((int64_t)b * p.t_new) * tok_stride + (int64_t)h * D;
+
+  // Whole rows per pass (256 threads hold 256 / chunks rows), so a row's lanes are all active.
+  for (int idx = threadIdx.x; idx < n_tok * chunks; idx += kAppendThreads) {
+    const int r = idx / chunks, c = idx % chunks;
+    const int32_t t = t_lo + r;
+    const int64_t src = src0 + (int64_t)(t - L0) * tok_stride + c * kVec;
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(kn + src);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(vn + src);
+    float xk[kVec], xv[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const int word = i / (kVec / 4), sh = 32 / (kVec / 4) * (i % (kVec / 4));
+      const uint32_t mask = sizeof(E) == 4 ? 0xffffffffu : 0xffffu;
+      xk[i] = elem_to_f32<E>((kw[word] >> sh) & mask, p.dtype);
+      xv[i] = elem_to_f32<E>((vw[word] >> sh) & mask, p.dtype);
+    }
+    float ak = 0.f, av = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      ak = fmaxf(ak, fabsf(xk[i]));
+      av = fmaxf(av, fabsf(xv[i]));
+    }
+    for (int m = 1; m < chunks; m <<= 1) {   // the row's lanes are aligned in the wave
+      ak = fmaxf(ak, __shfl_xor(ak, m, kWave));
+      av = fmaxf(av, __shfl_xor(av, m, kWave));
+    }
+    const float inv_k = ak > 0.f ? __fdiv_rn(127.f, ak) : 0.f;
+    const float inv_v = av > 0.f ? __fdiv_rn(127.f, av) : 0.f;
+    const int32_t s = run.slot_of(p, t);
+    const int64_t page = run.page_of(p, s);
+    const int64_t row = (page << p.log2_bs) + (s & bs_mask);
+    // K codes: kVec consecutive bytes of the token-major row, one store
+    uint32_t kb[kVec / 4];
+#pragma unroll
+    for (int w = 0; w < kVec / 4; ++w) {
+      kb[w] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kb[w] |= ((uint32_t)quant_code(xk[4 * w + i], inv_k) & 0xffu) << (8 * i);
+    }
+    int8_t* kdst = kq + row * D + c * kVec;
+    if constexpr (kVec == 8)
+      *reinterpret_cast<u32x2*>(kdst) = u32x2{kb[0], kb[1]};
+    else
+      *reinterpret_cast<uint32_t*>(kdst) = kb[0];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) vstage[r][c * kVec + i] = (uint8_t)quant_code(xv[i], inv_v);
+    if (c == 0) {
+      p.k_scale[row] = ak > 0.f ? __fdiv_rn(ak, 127.f) : 0.f;
+      p.v_scale[row] = av > 0.f ? __fdiv_rn(av, 127.f) : 0.f;
+    }
+  }
+  __syncthreads();
+  // V codes, channel-major: element (d, row) at page * D * bs + d * bs + row.
+  const int32_t s0 = run.slot_of(p, t_lo);
+  if (n_tok == 16 && (s0 & 15) == 0 && p.log2_bs >= 4) {
+    // a whole run of 16 consecutive slots in one page: one 16-byte store per channel
+    const int64_t page = run.page_of(p, s0);
+    int8_t* vrow = vq + page * D * ((int64_t)1 << p.log2_bs) + (s0 & bs_mask);
+    for (int d = threadIdx.x; d < D; d += kAppendThreads) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)vstage[4 * j][d] | ((uint32_t)vstage[4 * j + 1][d] << 8) |
+               ((uint32_t)vstage[4 * j + 2][d] << 16) | ((uint32_t)vstage[4 * j + 3][d] << 24);
+      *reinterpret_cast<u32x4*>(vrow + (int64_t)d * ((int64_t)1 << p.log2_bs)) = w;
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < 16 * D; idx += kAppendThreads) {
+    const int r = idx & 15, d = idx >> 4;
+    if (r >= n_tok) continue;
+    const int32_t s = run.slot_of(p, t_lo + r);
+    const int64_t page = run.page_of(p, s);
+    vq[(page * D + d) * ((int64_t)1 << p.log2_bs) + (s & bs_mask)] = (int8_t)vstage[r][d];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_int8(const AppendParams& p, hipStream_t stream) {
+  const int groups = p.t_new == 1 ? 1 : (p.t_new + 15) / 16 + 3;
+  const dim3 grid(groups, p.num_kv_heads, p.batch);
+  (void)hipGetLastError();  // report only this launch's status
+  if (p.dtype == 0)
+    hipLaunchKernelGGL(append_int8_kernel<uint32_t>, grid, dim3(kAppendThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(append_int8_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream) {
   // Runs of 16 positions a (sequence, kv head) can touch: a single new token is one run; longer

@@ -41,8 +41,11 @@ namespace {
 // eight waves' merge buffers would not fit in LDS next to a second workgroup.
 template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
 
-template <typename T, int D>
-__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(const DecodeParams p) {
+// The decode body. Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
+// (k_scale, v_scale [num_blocks][block_size]); a score is (codes . q) * k_scale of its key, and a
+// key's weight enters PV as p * v_scale of the key (the row sum l takes p itself).
+template <typename T, int D, bool Q8>
+__device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int kDecodeWaves = decode_waves<D>();
   constexpr int kThreads = kDecodeWaves * kWave;
   constexpr int KC = D / 32;  // k-steps of S^T over the head dim
@@ -112,6 +115,8 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(
 
   const T* kpool = static_cast<const T*>(p.k_pool);
   const T* vpool = static_cast<const T*>(p.v_pool);
+  const int8_t* kq = static_cast<const int8_t*>(p.k_pool);   // the int8 cache's codes (Q8)
+  const int8_t* vq = static_cast<const int8_t*>(p.v_pool);
   const int64_t page_elems = (int64_t)D << p.log2_bs;
   const int bs = 1 << p.log2_bs;
 
@@ -135,30 +140,56 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(
     constexpr int kChunks = 1;   // one 32-key chunk per step (measured best: two waves per SIMD)
     constexpr int kRunsPerStep = 2 * kChunks;
     v8<T> kA[kChunks][2][KC], vA[kChunks][DT];
+    f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
+    // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
+    // S^T accumulators and of its P^T operand.
+    auto load_scales = [&](const float* pool, int step, f32x4 (&dst)[kChunks][2]) {
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
+        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const f32x4* sp = reinterpret_cast<const f32x4*>(
+            pool + ((int64_t)packed_page(pr) << p.log2_bs) + packed_row0(pr) + (quad & 1) * 8);
+        dst[c][0] = __builtin_nontemporal_load(sp);
+        dst[c][1] = __builtin_nontemporal_load(sp + 1);
+      }
+    };
     auto load_k = [&](int32_t seg0, int step) {
       const int r = col;
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (r >> 3);
         const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
-        const T* base = kpool + packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D + quad * 8;
+        const int64_t base = packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D + quad * 8;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) kA[c][t][kc] = load8_stream(base + krow * D + kc * 32);
+          for (int kc = 0; kc < KC; ++kc) {
+            if constexpr (Q8)
+              kA[c][t][kc] = codes_to_v8<T>(load_codes8_stream(kq + base + krow * D + kc * 32));
+            else
+              kA[c][t][kc] = load8_stream(kpool + base + krow * D + kc * 32);
+          }
         }
       }
+      if constexpr (Q8) load_scales(p.k_scale, step, kS);
     };
     auto load_v = [&](int32_t seg0, int step) {
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
         const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
-        const T* base = vpool + packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
+        const int64_t base = packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vA[c][dt] = load8_stream(base + (int64_t)(dt * 16 + col) * bs);
+        for (int dt = 0; dt < DT; ++dt) {
+          if constexpr (Q8)
+            vA[c][dt] = codes_to_v8<T>(load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs));
+          else
+            vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
+        }
       }
+      if constexpr (Q8) load_scales(p.v_scale, step, vS);
     };
 
     for (int32_t seg0 = 0; seg0 < n_runs; seg0 += kRunSeg) {
@@ -186,7 +217,21 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) s[c][t] = mfma16(kA[c][t][kc], qT[kc], s[c][t]);
           }
+        f32x4 kS_cur[kChunks][2];   // this step's K scales (the next step's load replaces kS)
+        if constexpr (Q8) {
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c) {
+            kS_cur[c][0] = kS[c][0];
+            kS_cur[c][1] = kS[c][1];
+          }
+        }
         if (has_next) load_k(seg0, nxt);   // next step's K streams in during this step's math
+        if constexpr (Q8) {   // scores of the int8 cache: (codes . q) * the key's K scale
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) s[c][t] *= kS_cur[c][t];
+        }
 
         // Lane holds keys t0 + 8*(quad&1) + i of run 2c + quad/2, i = 4*t + j.
         uint32_t keep[kChunks];
@@ -233,10 +278,19 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(
             x[i] = fast_exp2(fmaf(s[c][i >> 2][i & 3], p.scale_log2, -m_use));
             l_run += x[i];
           }
-          const v8<T> pB = pack8<T>(x);
-          if (!full) {
+          v8<T> pB;
+          if constexpr (Q8) {
+            // weights times the keys' V scales; absent keys (whose scale may be anything) give 0
+            float xv[8];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vA[c][dt] = select8<T>(vA[c][dt], keep[c]);
+            for (int i = 0; i < 8; ++i) xv[i] = ((keep[c] >> i) & 1u) ? x[i] * vS[c][i >> 2][i & 3] : 0.f;
+            pB = pack8<T>(xv);
+          } else {
+            pB = pack8<T>(x);
+            if (!full) {
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) vA[c][dt] = select8<T>(vA[c][dt], keep[c]);
+            }
           }
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
@@ -340,13 +394,32 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(
   if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <typename T, int D>
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_kernel(const DecodeParams p) {
+  decode_body<T, D, false>(p);
+}
+
+// Decode over the int8 cache (one fp32 scale per slot for K and for V).
+template <typename T, int D>
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_kernel(const DecodeParams p) {
+  decode_body<T, D, true>(p);
+}
+
+template <typename T, int D>
+void launch_d(const DecodeParams& p, bool int8_cache, int grid, hipStream_t stream) {
+  if (int8_cache)
+    hipLaunchKernelGGL((decode_int8_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0, stream, p);
+}
+
 template <typename T>
-hipError_t launch_t(const DecodeParams& p, int head_dim, int grid, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, int head_dim, bool int8_cache, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's status
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((decode_kernel<T, 64>), dim3(grid), dim3(decode_waves<64>() * kWave), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<T, 128>), dim3(grid), dim3(decode_waves<128>() * kWave), 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((decode_kernel<T, 256>), dim3(grid), dim3(decode_waves<256>() * kWave), 0, stream, p); break;
+    case 64: launch_d<T, 64>(p, int8_cache, grid, stream); break;
+    case 128: launch_d<T, 128>(p, int8_cache, grid, stream); break;
+    case 256: launch_d<T, 256>(p, int8_cache, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -354,11 +427,11 @@ hipError_t launch_t(const DecodeParams& p, int head_dim, int grid, hipStream_t s
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int grid,
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8_cache, int grid,
                          hipStream_t stream) {
-  if (dtype == 0) return launch_t<float>(p, head_dim, grid, stream);
-  if (dtype == 1) return launch_t<_Float16>(p, head_dim, grid, stream);
-  return launch_t<__bf16>(p, head_dim, grid, stream);
+  if (dtype == 0) return launch_t<float>(p, head_dim, int8_cache, grid, stream);
+  if (dtype == 1) return launch_t<_Float16>(p, head_dim, int8_cache, grid, stream);
+  return launch_t<__bf16>(p, head_dim, int8_cache, grid, stream);
 }
 
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,

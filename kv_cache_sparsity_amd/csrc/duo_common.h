@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -54,6 +55,24 @@ __device__ __forceinline__ v8<T> zero8() {
 
 // fp32 -> element, round to nearest even (hardware conversions on gfx950).
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return T(x); }
+
+// Eight int8 codes (8 consecutive bytes, 8-byte aligned) streamed past the caches, as two words.
+__device__ __forceinline__ u32x2 load_codes8_stream(const int8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// Eight int8 codes (byte i of the two words is code i) as an MFMA operand: every code in
+// [-127, 127] is exact in bf16, fp16 and fp32.
+template <typename T>
+__device__ __forceinline__ v8<T> codes_to_v8(u32x2 w) {
+  v8<T> r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int32_t c = (int32_t)(w[i >> 2] << (24 - 8 * (i & 3))) >> 24;   // sign-extended byte
+    r[i] = from_f32<T>((float)c);
+  }
+  return r;
+}
 
 template <typename T>
 __device__ __forceinline__ v8<T> pack8(const float* x) {

@@ -21,6 +21,11 @@ struct AppendParams {
   int32_t batch, t_new, num_kv_heads, head_dim;
   int32_t sink, sink_blocks, ring_slots;
   uint64_t retrieval_bits;  // bit h set = kv head h is a retrieval head
+  // int8 cache only: one fp32 scale per slot ([num_blocks][block_size]) for K and for V, and the
+  // dtype of k_new / v_new
+  float* k_scale;
+  float* v_scale;
+  int32_t dtype;
 };
 
 struct DecodeParams {
@@ -30,6 +35,8 @@ struct DecodeParams {
   const int32_t* table;
   const int32_t* seq_lens;
   void* out;
+  const float* k_scale;   // int8 cache only: [num_blocks][block_size] per-slot scales of K
+  const float* v_scale;   // and of V
   float* partial;     // [batch][num_kv_heads][n_split][group][head_dim + 2]
   int32_t* counter;   // [batch][num_kv_heads]
   int32_t num_blocks, log2_bs, max_blocks_per_head;
@@ -61,7 +68,8 @@ struct PrefillParams {
 
 // Launchers (return the HIP launch status). dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int grid,
+hipError_t launch_append_int8(const AppendParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8_cache, int grid,
                          hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid,
                           hipStream_t stream);

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 2
+    assert duo.abi_version() == 3
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -106,6 +106,49 @@ def decode(**kw):
 ])
 def test_decode_rejects(kw, status):
     assert decode(**kw) == status
+
+
+# ---- int8 cache ------------------------------------------------------------------------------
+def append_int8(**kw):
+    a = dict(k_pool=FAKE, v_pool=FAKE, ks=FAKE + 4096, vs=FAKE + 8192, table=FAKE, num_blocks=64,
+             bs=16, mbph=8, k_new=FAKE, v_new=FAKE, lb=FAKE, la=FAKE + 256, batch=2, t_new=5, hkv=2,
+             d=128, dtype=2, mask=ctypes.cast(MASK_RS, ctypes.c_void_p), sink=4, recent=16, rb=2)
+    a.update(kw)
+    return duo.lib().kv_append_circular_int8(
+        a["k_pool"], a["v_pool"], a["ks"], a["vs"], a["table"], a["num_blocks"], a["bs"], a["mbph"],
+        a["k_new"], a["v_new"], a["lb"], a["la"], a["batch"], a["t_new"], a["hkv"], a["d"],
+        a["dtype"], a["mask"], a["sink"], a["recent"], a["rb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), INVALID), (dict(vs=None), INVALID), (dict(ks=FAKE + 4), INVALID),
+    (dict(vs=FAKE + 4096), INVALID), (dict(k_pool=None), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED), (dict(rb=8), CAPACITY),
+])
+def test_append_int8_rejects(kw, status):
+    assert append_int8(**kw) == status
+
+
+def decode_int8(**kw):
+    a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, ks=FAKE + 4096, vs=FAKE + 8192, table=FAKE,
+             num_blocks=64, bs=16, mbph=20, lens=FAKE, batch=2, hq=8, hkv=2, d=128, dtype=2,
+             mask=ctypes.cast(MASK_RS, ctypes.c_void_p), sink=4, recent=16, rb=2, scale=0.1,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30, split=0)
+    a.update(kw)
+    return duo.lib().duo_attn_decode_int8(
+        a["q"], a["k_pool"], a["v_pool"], a["ks"], a["vs"], a["table"], a["num_blocks"], a["bs"],
+        a["mbph"], a["lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["dtype"], a["mask"],
+        a["sink"], a["recent"], a["rb"], a["scale"], a["out"], a["ws"], a["ws_bytes"], a["split"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), INVALID), (dict(vs=FAKE + 8), INVALID), (dict(q=None), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(bs=8), UNSUPPORTED), (dict(recent=33), CAPACITY),
+    (dict(ws=None), WORKSPACE), (dict(hq=40, hkv=2), UNSUPPORTED),
+])
+def test_decode_int8_rejects(kw, status):
+    assert decode_int8(**kw) == status
 
 
 def test_decode_workspace_size_query():

@@ -1,0 +1,204 @@
+"""GPU parity for the int8 cache, through the C ABI, against the CPU oracle on the same seeded bits.
+
+* kv_append_circular_int8: whole pools bit-exact against oracle.append_int8 (codes, and scales
+  compared as fp32 bit patterns); the pools start with sentinel codes and NaN scales, so any slot
+  written that should not be, or missed, shows.
+* duo_attn_decode_int8: max abs error within 2e-2 (bf16/fp16) or 1e-4 (fp32) of oracle.attend_int8
+  over the codes and scales the oracle's quantizer gives for the same rows. Unwritten slots keep NaN
+  scales, which the decode must never let through.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_sparsity_amd as duo
+import oracle
+import synth
+from tests.gpu_harness import check_close, logical_kv, q_decode, say, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_CODE = 0x55
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(duo.LIB_PATH):
+        pytest.fail("libduoattn.so is not built; the GPU tests need the HIP library")
+
+
+class Int8Cache:
+    """Device int8 pools + scales + block table for one workload, filled by kv_append_circular_int8."""
+
+    def __init__(self, w: synth.Workload, mask=None):
+        self.w = w
+        self.mask = np.asarray(mask if mask is not None else w.retrieval_mask, dtype=np.uint8)
+        self.table_h, self.num_blocks = synth.block_table(w)
+        self.table = torch.from_numpy(self.table_h).cuda()
+        ks, vs = oracle.pool_shapes(self.num_blocks, w.block_size, w.head_dim)
+        self.k_pool = torch.full(ks, SENTINEL_CODE, dtype=torch.int8, device="cuda")
+        self.v_pool = torch.full(vs, SENTINEL_CODE, dtype=torch.int8, device="cuda")
+        ss = oracle.scale_pool_shape(self.num_blocks, w.block_size)
+        self.k_scale = torch.full(ss, float("nan"), dtype=torch.float32, device="cuda")
+        self.v_scale = torch.full(ss, float("nan"), dtype=torch.float32, device="cuda")
+        self.lens = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+
+    def append(self, kn_bits, vn_bits, table=None, before=None):
+        w = self.w
+        before = self.lens if before is None else before
+        after = torch.empty_like(before)
+        duo.kv_append_circular_int8(self.k_pool, self.v_pool, self.k_scale, self.v_scale,
+                                    self.table if table is None else table,
+                                    to_dev(kn_bits, w.dtype), to_dev(vn_bits, w.dtype), before,
+                                    after, self.mask, w.sink, w.recent, w.ring_blocks)
+        return after
+
+    def fill_per_sequence(self, K, V, lens, chunk=8192):
+        """Positions [0, lens[b]) of logical storage K, V [B][Hkv][L][D], one sequence at a time."""
+        final = torch.zeros(self.w.batch, dtype=torch.int32, device="cuda")
+        for b in range(self.w.batch):
+            L = int(lens[b])
+            before = torch.zeros(1, dtype=torch.int32, device="cuda")
+            for s in range(0, L, chunk):
+                e = min(L, s + chunk)
+                kn = np.ascontiguousarray(K[b:b + 1, :, s:e].transpose(0, 2, 1, 3))
+                vn = np.ascontiguousarray(V[b:b + 1, :, s:e].transpose(0, 2, 1, 3))
+                before = self.append(kn, vn, table=self.table[b:b + 1], before=before)
+            final[b] = before[0] if L > 0 else 0
+        self.lens = final
+
+    def decode(self, q_bits, split_tokens=0):
+        w = self.w
+        q = to_dev(q_bits, w.dtype)
+        out = torch.empty_like(q)
+        ws = duo.decode_workspace(q, self.table, w.block_size, split_tokens)
+        duo.duo_attn_decode_int8(q, self.k_pool, self.v_pool, self.k_scale, self.v_scale,
+                                 self.table, self.lens, self.mask, w.sink, w.recent, w.ring_blocks,
+                                 w.scale, out, ws, split_tokens)
+        return out
+
+
+def _logical_codes(K, V, dtype):
+    """The oracle's codes and scales of logical storage K, V [B][Hkv][L][D], one head at a time."""
+    B, H, L, D = K.shape
+    kc, vc = np.empty(K.shape, np.int8), np.empty(V.shape, np.int8)
+    ks, vs = np.empty((B, H, L), np.float32), np.empty((B, H, L), np.float32)
+    for b in range(B):
+        for h in range(H):
+            kc[b, h], ks[b, h] = oracle.quantize_rows(K[b, h], dtype)
+            vc[b, h], vs[b, h] = oracle.quantize_rows(V[b, h], dtype)
+    return kc, ks, vc, vs
+
+
+# ------------------------------------------------------------------------------------------------
+# kv_append_circular_int8: bit-exact pools
+# ------------------------------------------------------------------------------------------------
+APPEND_CASES = [
+    dict(name="bf16-d128-bs16-sink4-ring2", dtype=synth.BF16, head_dim=128, block_size=16, sink=4,
+         recent=24, ring_blocks=2, kv=3, ret=(0,), calls=[5, 40, 1, 1, 70]),
+    dict(name="f32-d64-bs32-sink0-ring1", dtype=synth.F32, head_dim=64, block_size=32, sink=0,
+         recent=20, ring_blocks=1, kv=2, ret=(1,), calls=[33, 2, 64, 7]),
+    dict(name="f16-d256-bs16-sink20-ring3", dtype=synth.F16, head_dim=256, block_size=16, sink=20,
+         recent=40, ring_blocks=3, kv=2, ret=(), calls=[1, 19, 3, 100, 16]),
+    dict(name="bf16-d64-bs4-sink2-ring3", dtype=synth.BF16, head_dim=64, block_size=4, sink=2,
+         recent=10, ring_blocks=3, kv=2, ret=(0,), calls=[17, 3, 30]),
+    dict(name="f32-d256-bs16-all-retrieval", dtype=synth.F32, head_dim=256, block_size=16, sink=0,
+         recent=16, ring_blocks=1, kv=1, ret=(0,), calls=[48, 1, 15]),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c["name"] for c in APPEND_CASES])
+def test_append_int8_bit_exact(case):
+    say(f"append int8 {case['name']}")
+    total = sum(case["calls"])
+    w = synth.small(case["name"], batch=2, q_heads=case["kv"], kv_heads=case["kv"],
+                    head_dim=case["head_dim"], dtype=case["dtype"], block_size=case["block_size"],
+                    sink=case["sink"], recent=case["recent"], retrieval=case["ret"], context=total,
+                    q_len=1, seed=51, ring_blocks=case["ring_blocks"])
+    cache = Int8Cache(w)
+    ks, vs = oracle.pool_shapes(cache.num_blocks, w.block_size, w.head_dim)
+    kp = np.full(ks, SENTINEL_CODE, np.int8)
+    vp = np.full(vs, SENTINEL_CODE, np.int8)
+    ksc = np.full(oracle.scale_pool_shape(cache.num_blocks, w.block_size), np.nan, np.float32)
+    vsc = ksc.copy()
+    lens = np.zeros(w.batch, np.int64)
+    pos = 0
+    for ci, n in enumerate(case["calls"]):
+        kn = synth.f32_to_storage(synth.kv_new(w, synth.S_K, pos, pos + n), w.dtype)
+        vn = synth.f32_to_storage(synth.kv_new(w, synth.S_V, pos, pos + n), w.dtype)
+        if ci == 1:   # all-zero rows take the scale-0 path
+            kn[:, 0] = 0
+            vn[0, -1] = 0
+        cache.lens = cache.append(kn, vn)
+        lens = oracle.append_int8(kp, vp, ksc, vsc, cache.table_h, kn, vn, lens, cache.mask,
+                                  w.dtype, sink=w.sink, block_size=w.block_size,
+                                  ring_blocks=w.ring_blocks,
+                                  max_blocks_per_head=w.max_blocks_per_head)
+        pos += n
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.lens.cpu().numpy(), lens)
+    assert cache.k_pool.cpu().numpy().tobytes() == kp.tobytes()
+    assert cache.v_pool.cpu().numpy().tobytes() == vp.tobytes()
+    assert cache.k_scale.cpu().numpy().view(np.uint32).tobytes() == ksc.view(np.uint32).tobytes()
+    assert cache.v_scale.cpu().numpy().view(np.uint32).tobytes() == vsc.view(np.uint32).tobytes()
+
+
+# ------------------------------------------------------------------------------------------------
+# duo_attn_decode_int8 against oracle.attend_int8
+# ------------------------------------------------------------------------------------------------
+DECODE_CASES = [
+    dict(name="bf16-d128-gqa4", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(1,),
+         block_size=16, sink=4, recent=64, lens=[700, 333]),
+    dict(name="f16-d64-gqa2-bs64", dtype=synth.F16, head_dim=64, group=2, kv=3, ret=(0, 2),
+         block_size=64, sink=9, recent=100, lens=[1, 1500]),
+    dict(name="f32-d64-mha", dtype=synth.F32, head_dim=64, group=1, kv=4, ret=(0, 3),
+         block_size=16, sink=0, recent=40, lens=[257, 96]),
+    dict(name="bf16-d256-gqa8-all-retrieval", dtype=synth.BF16, head_dim=256, group=8, kv=1,
+         ret=(0,), block_size=16, sink=0, recent=16, lens=[1024, 77]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c["name"] for c in DECODE_CASES])
+def test_decode_int8_parity(case):
+    say(f"decode int8 {case['name']}")
+    Lmax = max(case["lens"])
+    w = synth.small(case["name"], batch=2, q_heads=case["kv"] * case["group"], kv_heads=case["kv"],
+                    head_dim=case["head_dim"], dtype=case["dtype"], block_size=case["block_size"],
+                    sink=case["sink"], recent=case["recent"], retrieval=case["ret"], context=Lmax,
+                    q_len=1, seed=52)
+    cache = Int8Cache(w)
+    K = logical_kv(w, Lmax, synth.S_K)
+    V = logical_kv(w, Lmax, synth.S_V)
+    lens = np.asarray(case["lens"])
+    cache.fill_per_sequence(K, V, lens)
+    kc, ks, vc, vs = _logical_codes(K, V, w.dtype)
+    q = q_decode(w, 0)
+    want = oracle.attend_int8(q[:, None], kc, ks, vc, vs, lens, cache.mask, sink=w.sink,
+                              recent=w.recent, scale=w.scale, dtype=w.dtype)[:, 0]
+    for split in (0, 128):
+        got = to_host_f64(cache.decode(q, split_tokens=split), w.dtype)
+        check_close(got, want, w.dtype, f"{case['name']} split {split}")
+
+
+def test_llama3_8b_gqa_decode_int8_batch8_ctx32768():
+    w = synth.llama3_8b_decode()
+    say(f"workload {w.name}, int8 cache")
+    L = w.context
+    cache = Int8Cache(w)
+    K = logical_kv(w, L, synth.S_K)
+    V = logical_kv(w, L, synth.S_V)
+    cache.fill_per_sequence(K, V, np.full(w.batch, L))
+    kc, ks, vc, vs = _logical_codes(K, V, w.dtype)
+    q = q_decode(w, 0)
+    got = to_host_f64(cache.decode(q), w.dtype)
+    want = oracle.attend_int8(q[:, None], kc, ks, vc, vs, np.full(w.batch, L), cache.mask,
+                              sink=w.sink, recent=w.recent, scale=w.scale, dtype=w.dtype)[:, 0]
+    check_close(got, want, w.dtype, w.name + " int8")
+    # the int8 cache also stays close to the unquantized result (a sanity bound, not parity)
+    full = oracle.attend(q[:, None], K, V, np.full(w.batch, L), cache.mask, sink=w.sink,
+                         recent=w.recent, scale=w.scale, dtype=w.dtype)[:, 0]
+    assert float(np.max(np.abs(got - full))) < 0.05
