@@ -7,6 +7,10 @@ per sequence (kv_append_circular) + duo_attn_decode. Four layers' caches are rot
 step reads cache lines last touched >1.5 GB earlier (the 256 MB Infinity Cache cannot serve them).
 value = algorithmic decode bytes per step / wall time per step.
 
+Int8 decode leg: the same decode workload over the int8 cache (kv_append_circular_int8 +
+duo_attn_decode_int8; 8-bit codes plus one fp32 scale per slot for K and V), reported in the same
+algorithmic GB/s (codes + scales + block table + q/out) and as its step-time speedup over bf16.
+
 Prefill leg: Llama-2-7B-shaped MHA chunked prefill, eight 4096-token chunks building a 32768-token
 context, 8 of 32 heads retrieval, sink 128 / recent 1024. One pass = 8 x (append chunk + prefill).
 Reported as algorithmic TFLOP/s (4 * head_dim per visible (query, key) pair).
@@ -37,6 +41,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 EVENT_EVERY = 8                  # decode launches timed with HIP events: one step in eight
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "duo_common.h", "duo_kernels.h"],
+    "decode_int8": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "prefill": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
 }
 
@@ -79,9 +84,10 @@ def visible_count(p: np.ndarray, retrieval: bool, sink: int, recent: int) -> np.
     return a + b - overlap
 
 
-def decode_bytes(w: synth.Workload, lens: np.ndarray) -> int:
-    """K+V rows each head must read + q + out + block-table entries."""
-    row = 2 * w.head_dim * w.elem_bytes
+def decode_bytes(w: synth.Workload, lens: np.ndarray, int8_cache: bool = False) -> int:
+    """K+V rows each head must read + q + out + block-table entries. With the int8 cache a key's
+    K+V row is 2 * head_dim one-byte codes plus its two fp32 scales."""
+    row = 2 * w.head_dim + 2 * 4 if int8_cache else 2 * w.head_dim * w.elem_bytes
     total = 0
     for b in range(w.batch):
         L = int(lens[b])
@@ -218,6 +224,93 @@ def decode_leg(args, torch, duo):
     return res
 
 
+def decode_int8_leg(args, torch, duo, dec):
+    """The decode workload over the int8 cache, on the bf16 leg's K/V bits (quantized by the
+    library's own append)."""
+    w = dec["w"]
+    K, V = dec["K"], dec["V"]
+    dev = torch.device("cuda:0")
+    L = w.context
+    log("[decode-int8] filling the int8 cache")
+    table_h, nblocks = synth.block_table(w)
+    table = torch.from_numpy(table_h).to(dev)
+    mask = w.retrieval_mask
+    ks = (nblocks, w.block_size, w.head_dim)
+    vs = (nblocks, w.head_dim, w.block_size)
+    ss = (nblocks, w.block_size)
+    after = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    layers = []
+    for li in range(args.layers):
+        pools = (torch.empty(ks, dtype=torch.int8, device=dev),
+                 torch.empty(vs, dtype=torch.int8, device=dev),
+                 torch.empty(ss, dtype=torch.float32, device=dev),
+                 torch.empty(ss, dtype=torch.float32, device=dev))
+        if li == 0:
+            for s0 in range(0, L - 1, 8192):
+                e = min(L - 1, s0 + 8192)
+                kn = to_dev(torch, K[:, :, s0:e].transpose(0, 2, 1, 3), w.dtype, dev)
+                vn = to_dev(torch, V[:, :, s0:e].transpose(0, 2, 1, 3), w.dtype, dev)
+                lb = torch.full((w.batch,), s0, dtype=torch.int32, device=dev)
+                duo.kv_append_circular_int8(*pools, table, kn, vn, lb, after, mask, w.sink,
+                                            w.recent, w.ring_blocks)
+        else:
+            for dst, src in zip(pools, layers[0]):
+                dst.copy_(src)
+        layers.append(pools)
+    k_tok = to_dev(torch, K[:, :, L - 1:L].transpose(0, 2, 1, 3), w.dtype, dev)
+    v_tok = to_dev(torch, V[:, :, L - 1:L].transpose(0, 2, 1, 3), w.dtype, dev)
+    q = to_dev(torch, dec["q_bits"], w.dtype, dev)
+    out = torch.empty_like(q)
+    ws = duo.decode_workspace(q, table, w.block_size)
+    lens_before = torch.full((w.batch,), L - 1, dtype=torch.int32, device=dev)
+    lens = torch.empty_like(lens_before)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        pools = layers[i % len(layers)]
+        duo.kv_append_circular_int8(*pools, table, k_tok, v_tok, lens_before, lens, mask, w.sink,
+                                    w.recent, w.ring_blocks)
+        if ev is not None:
+            ev[0].record()
+        duo.duo_attn_decode_int8(q, *pools, table, lens, mask, w.sink, w.recent, w.ring_blocks,
+                                 w.scale, out, ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in sampled}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs.get(i))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs.values()])) * 1e-3
+    nbytes = decode_bytes(w, np.full(w.batch, L), int8_cache=True)
+    res = {
+        "workload": w.name + "-int8-kv", "value": round(nbytes / step_s / 1e9, 1), "unit": "GB/s",
+        "ms_per_step": round(step_s * 1e3, 4),
+        "step": "kv_append_circular_int8(1 token/seq) + duo_attn_decode_int8",
+        "algorithmic_bytes_per_step": nbytes,
+        "step_speedup_vs_bf16": round(dec["ms_per_step"] / (step_s * 1e3), 3),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / kern_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_int8"),
+                     "kernel": "duo::decode_int8_kernel<bf16,128>",
+                     "kernel_us": round(kern_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    log(f"[decode-int8] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
+        f"{res['value']:.0f} GB/s per step, {nbytes / kern_s / 1e9:.0f} GB/s kernel, "
+        f"{res['step_speedup_vs_bf16']}x the bf16 step")
+    return res
+
+
 # ---- prefill leg -----------------------------------------------------------------------------
 def prefill_leg(args, torch, duo):
     w = synth.llama2_7b_chunked_prefill()
@@ -350,7 +443,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
                 continue
             name = r.get("Kernel_Name", "")
             val = float(r["Counter_Value"]) * 1024.0          # counters are KiB per dispatch
-            if "decode_kernel" in name:
+            if "decode_int8_kernel" in name:
+                acc.setdefault("decode_int8", []).append(val)
+            elif "decode_kernel" in name:
                 acc.setdefault("decode", []).append(val)
             elif "prefill_kernel" in name:
                 acc.setdefault("prefill", []).append(val)
@@ -369,7 +464,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
     out = {"calibration": {"copy_bytes": known, "fetch_raw": fetch.get("copy"),
                            "write_raw": write.get("copy"), "fetch_scale": f_scale,
                            "write_scale": w_scale, "command": command}}
-    for k in ("decode", "prefill"):
+    for k in ("decode", "decode_int8", "prefill"):
         if k in fetch and k in write:
             out[k] = {"source_sha": source_sha(k),
                       "fetch_bytes_per_launch": fetch[k] * f_scale,
@@ -389,7 +484,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="decode caches rotated across steps")
     ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=1)
-    ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--legs", default="decode,decode_int8,prefill")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -414,7 +509,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     legs = set(args.legs.split(","))
-    dec = decode_leg(args, torch, duo) if "decode" in legs else None
+    dec = decode_leg(args, torch, duo) if legs & {"decode", "decode_int8"} else None
+    dq = decode_int8_leg(args, torch, duo, dec) if "decode_int8" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
@@ -440,6 +536,7 @@ def main():
         "roofline": dec["roofline"] if dec else None,
         "cpu_baseline": cpu,
         "prefill": pre,
+        "decode_int8": dq,
     }
     print(json.dumps(line), flush=True)
 

@@ -140,6 +140,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     constexpr int kChunks = 1;   // one 32-key chunk per step (measured best: two waves per SIMD)
     constexpr int kRunsPerStep = 2 * kChunks;
     v8<T> kA[kChunks][2][KC], vA[kChunks][DT];
+    // Q8: the raw code words, converted only where the MFMAs take them, so that the look-ahead
+    // loads are waited for at their use and not at their issue
+    u32x2 kR[kChunks][2][KC], vR[kChunks][DT];
     f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
     // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
     // S^T accumulators and of its P^T operand.
@@ -167,7 +170,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) {
             if constexpr (Q8)
-              kA[c][t][kc] = codes_to_v8<T>(load_codes8_stream(kq + base + krow * D + kc * 32));
+              kR[c][t][kc] = load_codes8_stream(kq + base + krow * D + kc * 32);
             else
               kA[c][t][kc] = load8_stream(kpool + base + krow * D + kc * 32);
           }
@@ -184,7 +187,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           if constexpr (Q8)
-            vA[c][dt] = codes_to_v8<T>(load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs));
+            vR[c][dt] = load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs);
           else
             vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
         }
@@ -215,7 +218,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
           for (int t = 0; t < 2; ++t) {
             s[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) s[c][t] = mfma16(kA[c][t][kc], qT[kc], s[c][t]);
+            for (int kc = 0; kc < KC; ++kc) {
+              if constexpr (Q8) s[c][t] = mfma16(codes_to_v8<T>(kR[c][t][kc]), qT[kc], s[c][t]);
+              else s[c][t] = mfma16(kA[c][t][kc], qT[kc], s[c][t]);
+            }
           }
         f32x4 kS_cur[kChunks][2];   // this step's K scales (the next step's load replaces kS)
         if constexpr (Q8) {
@@ -293,7 +299,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
             }
           }
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            if constexpr (Q8) oT[dt] = mfma16(codes_to_v8<T>(vR[c][dt]), pB, oT[dt]);
+            else oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
+          }
         }
         if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
       }
