@@ -126,7 +126,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     {
       const T* qrow = static_cast<const T*>(p.q) + ((int64_t)b * p.num_q_heads + h * G + col) * D;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) qT[c] = (col < G) ? load8(qrow + c * 32 + quad * 8) : zero8<T>();
+      for (int c = 0; c < KC; ++c) {
+        // Q8 takes each lane's K codes 16 at a time, so its k-step c pairs lane quad with head
+        // dims (c / 2) * 64 + 16 * quad + 8 * (c % 2) .. +7; q must follow the same order
+        const int d0 = Q8 ? (c >> 1) * 64 + quad * 16 + (c & 1) * 8 : c * 32 + quad * 8;
+        qT[c] = (col < G) ? load8(qrow + d0) : zero8<T>();
+      }
     }
     f32x4 oT[DT];
 #pragma unroll
@@ -163,16 +168,24 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (r >> 3);
         const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
-        const int64_t base = packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D + quad * 8;
+        const int64_t base = packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+          if constexpr (Q8) {
+            // 16 codes per load: head dims 64 i + 16 quad .. +15, the lane's slots of k-steps
+            // 2i and 2i + 1
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            if constexpr (Q8)
-              kR[c][t][kc] = load_codes8_stream(kq + base + krow * D + kc * 32);
-            else
-              kA[c][t][kc] = load8_stream(kpool + base + krow * D + kc * 32);
+            for (int i = 0; i < KC / 2; ++i) {
+              const u32x4 w = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4*>(kq + base + krow * D + i * 64 + quad * 16));
+              kR[c][t][2 * i] = u32x2{w[0], w[1]};
+              kR[c][t][2 * i + 1] = u32x2{w[2], w[3]};
+            }
+          } else {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+              kA[c][t][kc] = load8_stream(kpool + base + krow * D + kc * 32 + quad * 8);
           }
         }
       }
