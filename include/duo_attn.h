@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 3
+#define DUO_ATTN_ABI_VERSION 4
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -177,6 +177,38 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                          int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * duo_attn_prefill_varlen -- duo_attn_prefill for a packed batch in which every sequence brings its
+ * own number of query rows (prompt chunks and single decode tokens side by side, as a continuous-
+ * batching step does).
+ *
+ * Source: as for duo_attn_prefill; the DualChunkAttention PR's description adds the per-sequence
+ * prefill lengths to the attention metadata of a batched step, which is what q_start carries here.
+ *
+ *   q, out              device [total_q][num_q_heads][head_dim] of dtype: the rows of all sequences,
+ *                       packed.
+ *   q_start             device int32 [batch + 1]: sequence b owns rows [q_start[b], q_start[b+1]),
+ *                       with q_start[0] = 0, non-decreasing, at most max_q_len rows per sequence and
+ *                       q_start[batch] <= total_q. The kernels clamp every range into [0, total_q)
+ *                       and to max_q_len rows, so malformed offsets give wrong rows, never a fault.
+ *   seq_lens            device int32 [batch]: valid tokens AFTER the rows were appended; row i of
+ *                       sequence b sits at position seq_lens[b] - n_b + i (n_b its number of rows).
+ *   max_q_len           host bound on any sequence's rows: it sizes the launch (no host read of the
+ *                       offsets), the workspace (duo_attn_prefill_workspace_size with
+ *                       q_len = max_q_len) and the ring check.
+ * Everything else is as for duo_attn_prefill. Errors: as duo_attn_prefill, and INVALID_ARG for a
+ * missing or misaligned q_start or total_q, max_q_len < 1.
+ */
+int32_t duo_attn_prefill_varlen(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const int32_t* seq_lens,
+                                const int32_t* q_start, int32_t batch, int32_t total_q,
+                                int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                float softmax_scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * The int8 cache -- the same paged, per-head circular layout with 8-bit codes and one fp32 scale per

@@ -24,7 +24,8 @@ DUO_F32, DUO_F16, DUO_BF16 = 0, 1, 2
 STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "DUO_ERR_CAPACITY",
           4: "DUO_ERR_WORKSPACE", 5: "DUO_ERR_HIP"}
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
-           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "kv_append_circular_int8",
+           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
+           "kv_append_circular_int8",
            "duo_attn_decode_int8", "duo_status_string", "duo_abi_version")
 
 
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.duo_attn_prefill.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                        _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
                                        _P]
+        L.duo_attn_prefill_varlen.restype = _I32
+        L.duo_attn_prefill_varlen.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _I32,
+                                              _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
+                                              _F, _P, _P, _SZ, _P]
         L.kv_append_circular_int8.restype = _I32
         L.kv_append_circular_int8.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
                                               _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
@@ -207,6 +212,36 @@ def duo_attn_prefill(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval
     _check("duo_attn_prefill", st)
 
 
+def duo_attn_prefill_varlen(q, k_pool, v_pool, block_table, seq_lens, q_start, max_q_len: int,
+                            head_is_retrieval, sink_size: int, recent_size: int, ring_blocks: int,
+                            softmax_scale: float, out, workspace, stream=None) -> None:
+    """Prefill of a packed batch: q, out [total_q][Hq][D]; q_start int32 [batch + 1] (device) gives
+    each sequence's rows; max_q_len bounds any sequence's rows (the workspace is
+    prefill_workspace for q_len = max_q_len)."""
+    num_blocks, block_size, head_dim = k_pool.shape
+    total_q, num_q_heads, _ = q.shape
+    batch = q_start.shape[0] - 1
+    mask = _HostMask(head_is_retrieval)
+    st = lib().duo_attn_prefill_varlen(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
+        block_table.shape[2], _ptr(seq_lens), _ptr(q_start), batch, total_q, max_q_len,
+        num_q_heads, block_table.shape[1], head_dim, _dtype_tag(q), mask.ptr, sink_size,
+        recent_size, ring_blocks, softmax_scale, _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("duo_attn_prefill_varlen", st)
+
+
+def prefill_varlen_workspace(q, block_table, head_is_retrieval, max_q_len: int, batch: int):
+    """Zero-filled workspace for duo_attn_prefill_varlen (q: [total_q][Hq][D])."""
+    import torch
+    _, num_q_heads, d = q.shape
+    n = duo_attn_prefill_workspace_size(batch, max_q_len, num_q_heads, block_table.shape[1], d,
+                                        _dtype_tag(q), head_is_retrieval)
+    if n == 0:
+        raise ValueError("invalid sizes for the prefill workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
 def _int8_pools(k_pool, v_pool, k_scale, v_scale):
     import torch
     if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
@@ -251,7 +286,8 @@ def duo_attn_decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_l
 
 
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
-           "kv_append_circular_int8", "duo_attn_decode_int8",
+           "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
+           "prefill_varlen_workspace",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",
            "prefill_workspace", "status_string", "abi_version",
            "DuoAttnError", "lib", "LIB_PATH", "SYMBOLS", "DUO_F32", "DUO_F16", "DUO_BF16"]

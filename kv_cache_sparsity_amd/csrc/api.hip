@@ -332,14 +332,16 @@ size_t duo_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num
   return bytes > 0 ? bytes : 256;   // 0 means invalid arguments
 }
 
-int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
-                         const int32_t* block_table, int32_t num_blocks, int32_t block_size,
-                         int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
-                         int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
-                         int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
-                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+// The prefill behind both layouts of the queries: q_start == nullptr: [batch][q_len] rows;
+// otherwise packed rows, sequence b's at [q_start[b], q_start[b+1]) of total_q, at most q_len each.
+static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                            int32_t max_blocks_per_head, const int32_t* seq_lens,
+                            const int32_t* q_start, int32_t total_q, int32_t batch, int32_t q_len,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t dtype, const uint8_t* head_is_retrieval, int32_t sink_size,
+                            int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);
@@ -373,6 +375,8 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
   p.table = block_table;
   p.seq_lens = seq_lens;
   p.out = out;
+  p.q_start = q_start;
+  p.total_q = total_q;
   p.counter = need > 0 ? static_cast<int32_t*>(workspace) : nullptr;
   p.partial = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                   align256((size_t)ret_items * sizeof(int32_t)))
@@ -399,6 +403,38 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
   if (launch_prefill(p, dtype, head_dim, (int)grid, static_cast<hipStream_t>(stream)) != hipSuccess)
     return DUO_ERR_HIP;
   return DUO_OK;
+}
+
+int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                         int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                         int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (q_len < 1 || (int64_t)batch * q_len > INT32_MAX) return DUO_ERR_INVALID_ARG;
+  return prefill_impl(q, k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
+                      seq_lens, nullptr, batch * q_len, batch, q_len, num_q_heads, num_kv_heads,
+                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                      softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int32_t duo_attn_prefill_varlen(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const int32_t* seq_lens,
+                                const int32_t* q_start, int32_t batch, int32_t total_q,
+                                int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                float softmax_scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!q_start || !aligned(q_start, 4) || total_q < 1 || max_q_len < 1)
+    return DUO_ERR_INVALID_ARG;
+  return prefill_impl(q, k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
+                      seq_lens, q_start, total_q, batch, max_q_len, num_q_heads, num_kv_heads,
+                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                      softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

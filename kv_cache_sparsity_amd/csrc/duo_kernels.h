@@ -57,6 +57,10 @@ struct PrefillParams {
   void* out;
   int32_t* counter;   // [retrieval items] arrival tickets (zero between calls)
   float* partial;     // [retrieval items][n_split] partial (m, l, O^T) of every row
+  // packed (varlen) batches: rows [q_start[b], q_start[b+1]) of q / out belong to sequence b
+  // (at most q_len of them, clamped into [0, total_q)); null: b * q_len .. + q_len
+  const int32_t* q_start;
+  int32_t total_q;
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group;
   int32_t sink, recent, sink_blocks, ring_slots;

@@ -239,9 +239,24 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   const int h = hq / G;
   int32_t L = max(p.seq_lens[b], 0);
   if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
+  // The sequence's query rows: rows [q0, q0 + qn) of q and out.
+  int64_t q0;
+  int32_t qn;
+  if (p.q_start != nullptr) {   // packed batch: bounds from the device, clamped into [0, total_q)
+    const int32_t s0 = min(max(p.q_start[b], 0), p.total_q);
+    const int32_t s1 = min(max(p.q_start[b + 1], s0), p.total_q);
+    q0 = s0;
+    qn = min(s1 - s0, p.q_len);
+  } else {
+    q0 = (int64_t)b * p.q_len;
+    qn = p.q_len;
+  }
   const int row0 = qt * kRows;
-  const int n_rows = min(kRows, p.q_len - row0);
-  const int32_t p_lo = L - p.q_len + row0;       // position of the tile's first row
+  const int n_rows = min(kRows, qn - row0);
+  // A row tile past the sequence's rows has nothing to do; every split of its item sees the same,
+  // so none of them takes a ticket.
+  if (n_rows <= 0) return;
+  const int32_t p_lo = L - qn + row0;            // position of the tile's first row
   const int32_t p_hi = p_lo + n_rows - 1;
 
   HeadGeom geo;
@@ -284,8 +299,8 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   const bool wave_live = wrow0 < n_rows;
   v8<T> qT[DC];
   {
-    const bool ok = qrow < p.q_len;
-    const T* src = static_cast<const T*>(p.q) + (((int64_t)b * p.q_len + (ok ? qrow : 0)) * p.num_q_heads + hq) * D;
+    const bool ok = qrow < qn;
+    const T* src = static_cast<const T*>(p.q) + ((q0 + (ok ? qrow : 0)) * p.num_q_heads + hq) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qT[dc] = ok ? load8(src + dc * 16 + half * 8) : zero8<T>();
   }
@@ -663,9 +678,9 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
 
   // ---- normalise and store -----------------------------------------------------------------
   l_run = add_xor32(l_run);
-  if (qrow < p.q_len && wave_live) {
+  if (qrow < qn && wave_live) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    T* dst = static_cast<T*>(p.out) + (((int64_t)b * p.q_len + qrow) * p.num_q_heads + hq) * D;
+    T* dst = static_cast<T*>(p.out) + ((q0 + qrow) * p.num_q_heads + hq) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 3
+    assert duo.abi_version() == 4
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -106,6 +106,28 @@ def decode(**kw):
 ])
 def test_decode_rejects(kw, status):
     assert decode(**kw) == status
+
+
+# ---- varlen prefill ---------------------------------------------------------------------------
+def prefill_varlen(**kw):
+    a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, table=FAKE, num_blocks=64, bs=16, mbph=40, lens=FAKE,
+             qs=FAKE + 512, batch=2, total=300, maxq=200, hq=8, hkv=2, d=128, dtype=2,
+             mask=ctypes.cast(MASK_RS, ctypes.c_void_p), sink=4, recent=16, rb=16, scale=0.1,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return duo.lib().duo_attn_prefill_varlen(
+        a["q"], a["k_pool"], a["v_pool"], a["table"], a["num_blocks"], a["bs"], a["mbph"], a["lens"],
+        a["qs"], a["batch"], a["total"], a["maxq"], a["hq"], a["hkv"], a["d"], a["dtype"], a["mask"],
+        a["sink"], a["recent"], a["rb"], a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), INVALID), (dict(qs=FAKE + 2), INVALID), (dict(total=0), INVALID),
+    (dict(maxq=0), INVALID), (dict(q=None), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(maxq=300), CAPACITY), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_prefill_varlen_rejects(kw, status):
+    assert prefill_varlen(**kw) == status
 
 
 # ---- int8 cache ------------------------------------------------------------------------------

@@ -238,6 +238,48 @@ def test_prefill_parity(case):
         check_close(got, want, w.dtype, f"{case['name']} chunk {ci}")
 
 
+VARLEN_CASES = [
+    dict(name="bf16-d128-gqa2", dtype=synth.BF16, head_dim=128, group=2, kv=2, ret=(0,),
+         block_size=16, sink=4, recent=64, rows=[300, 1, 0, 37], lens=[700, 512, 100, 37]),
+    dict(name="f16-d64-mha-bs64", dtype=synth.F16, head_dim=64, group=1, kv=3, ret=(1, 2),
+         block_size=64, sink=0, recent=40, rows=[5, 129, 64], lens=[5, 900, 64]),
+    dict(name="f32-d64-all-streaming", dtype=synth.F32, head_dim=64, group=2, kv=1, ret=(),
+         block_size=16, sink=7, recent=30, rows=[33, 2], lens=[400, 40]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[c["name"] for c in VARLEN_CASES])
+def test_prefill_varlen_parity(case):
+    """A packed batch: each sequence brings its own rows (a chunk, a single decode row, none)."""
+    say(f"prefill varlen {case['name']}")
+    rows, lens = case["rows"], np.asarray(case["lens"])
+    B, max_q = len(rows), max(rows)
+    w = synth.small(case["name"], batch=B, q_heads=case["kv"] * case["group"], kv_heads=case["kv"],
+                    head_dim=case["head_dim"], dtype=case["dtype"], block_size=case["block_size"],
+                    sink=case["sink"], recent=case["recent"], retrieval=case["ret"],
+                    context=int(lens.max()), q_len=max_q, seed=46)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, int(lens.max()), synth.S_K)
+    V = logical_kv(w, int(lens.max()), synth.S_V)
+    _append_per_sequence(cache, K, V, lens)
+    qs = [q_prefill(w, b, n)[b:b + 1] for b, n in enumerate(rows)]   # [1][n][Hq][D] per sequence
+    packed = np.concatenate([q[0] for q in qs], axis=0)
+    q_start = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    qd = to_dev(packed, w.dtype)
+    out = torch.full_like(qd, float("nan"))
+    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, max_q, B)
+    duo.duo_attn_prefill_varlen(qd, cache.k_pool, cache.v_pool, cache.table, cache.lens,
+                                torch.from_numpy(q_start).cuda(), max_q, cache.mask, w.sink,
+                                w.recent, w.ring_blocks, w.scale, out, ws)
+    got = to_host_f64(out, w.dtype)
+    for b, n in enumerate(rows):
+        if n == 0:
+            continue
+        want = oracle.attend(qs[b], K[b:b + 1], V[b:b + 1], lens[b:b + 1], cache.mask,
+                             sink=w.sink, recent=w.recent, scale=w.scale, dtype=w.dtype)[0]
+        check_close(got[q_start[b]:q_start[b + 1]], want, w.dtype, f"{case['name']} sequence {b}")
+
+
 def test_prefill_rows_before_the_sequence_start_are_zero():
     """seq_len < q_len: rows at negative positions see nothing (zero output)."""
     w = synth.small("neg-rows", batch=1, q_heads=2, kv_heads=2, head_dim=64, dtype=synth.BF16,
