@@ -15,7 +15,8 @@ Sources (the four web pages on KV-cache sparsity):
   * transformers PR "[WIP] Dynamic length in static cache", description: a new position only needs
     attention against the positions up to itself, not the whole static cache.
   * vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models", review thread: the softmax
-    scale is applied in fp32 to the q.k product.
+    scale is applied in fp32 to the q.k product; Dual Chunk Attention itself (``dca``): three query
+    vectors chosen by the chunk relation of query and key, a float32 mscale per query position.
 
 Parity status of each function is stated in its docstring; every function here is pinned by tests
 in ``tests/test_oracle_*.py`` (worked tables, brute force, a library cross-check, closed forms and
@@ -27,7 +28,9 @@ from .cache import (slot_of, table_position, append, gather, pool_shapes, to_f64
                     new_pools, ring_capacity)
 from .attention import visible_positions, attend_row, attend, attend_paged
 from .quant import quantize_rows, dequantize, scale_pool_shape, append_int8, attend_int8
+from .dca import query_kind, attend_dca_row, attend_dca
 
 __all__ = ["slot_of", "table_position", "append", "gather", "pool_shapes", "to_f64", "new_pools",
            "ring_capacity", "visible_positions", "attend_row", "attend", "attend_paged",
-           "quantize_rows", "dequantize", "scale_pool_shape", "append_int8", "attend_int8"]
+           "quantize_rows", "dequantize", "scale_pool_shape", "append_int8", "attend_int8",
+           "query_kind", "attend_dca_row", "attend_dca"]

@@ -1,0 +1,88 @@
+"""Oracle: Dual Chunk Attention over a full causal cache, in float64.
+
+Test infrastructure only (see the package docstring).
+
+Source: vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models".
+  * Description ("Overview", "Changes"): the sequence is cut into chunks, and the rotary layer hands
+    the attention three query vectors per token, for keys in the same chunk (intra), in the chunk just
+    before (succ) and in any earlier chunk (inter).
+  * Review thread, on the brute-force varlen prefill: the only change from ordinary causal attention
+    is which query meets a key; the query's own for a key of its chunk, q_succ for a key of the
+    preceding chunk, q_inter for a key of any chunk before that.
+  * Review thread, on the intra-chunk length: chunks have the fixed length chunk_len except the last
+    (the query's own), which may be shorter. Chunks are therefore counted from position 0:
+    chunk(t) = t // chunk_len.
+  * Review thread, on the numerical issue: the weight is (query . key) * softmax_scale * mscale, with
+    mscale a float32 value per query position, applied in float32 rather than folded into q.
+  * Review thread, on the softmax LSE typo: the three partial attentions are merged by their
+    log-sum-exp, which is the same as one softmax over the union of the three key sets; that union is
+    every position j <= p, so this oracle takes the single softmax directly.
+
+Readings taken where the page is silent (each listed with the other readings of the pages):
+  * mscale is one float32 per query row, the same for its three query vectors;
+  * every head is a full causal head (the page does not combine DCA with streaming heads), bounded by
+    the sequence's valid length; query row i sits at position seq_len - q_len + i, as in ``attend``;
+  * local_size and the YaRN settings shape the rotary positions baked into q, q_succ and q_inter, so
+    they are not arguments here (positions and RoPE are outside the attention call).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .cache import to_f64
+
+
+def query_kind(p: int, j: int, chunk_len: int) -> int:
+    """0: intra (same chunk), 1: succ (the key's chunk directly precedes the query's), 2: inter."""
+    cq, ck = p // chunk_len, j // chunk_len
+    if ck == cq:
+        return 0
+    if ck == cq - 1:
+        return 1
+    return 2
+
+
+def attend_dca_row(qs, K: np.ndarray, V: np.ndarray, p: int, chunk_len: int, scale: float,
+                   mscale: float) -> np.ndarray:
+    """One query row at position p over keys 0..p (K, V hold at least p + 1 rows, float64).
+
+    qs = (q, q_succ, q_inter), each float64 [D]. Returns float64 [D]; zeros if p < 0.
+    """
+    D = V.shape[1]
+    if p < 0:
+        return np.zeros(D, dtype=np.float64)
+    s = np.empty(p + 1, dtype=np.float64)
+    for j in range(p + 1):
+        s[j] = float(qs[query_kind(p, j, chunk_len)] @ K[j])
+    s *= scale * mscale
+    m = s.max()
+    w = np.exp(s - m)
+    return (w @ V[:p + 1]) / w.sum()
+
+
+def attend_dca(q, q_succ, q_inter, k, v, seq_lens, mscale, *, chunk_len, scale, dtype, rows=None):
+    """Reference output of Dual Chunk Attention, float64.
+
+    q, q_succ, q_inter: [B][q_len][Hq][D] stored elements; k, v: logical caches [B][Hkv][>= len][D];
+    seq_lens: [B] valid lengths including the query rows; mscale: float32 [B][q_len] (upcast exactly).
+    rows: optional iterable of (b, i, hq). Returns [B][q_len][Hq][D] float64 (unselected rows NaN).
+    A q head hq reads kv head hq // (Hq / Hkv), as in ``attend``.
+    """
+    B, q_len, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.full((B, q_len, Hq, D), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, i, hq) for b in range(B) for i in range(q_len) for hq in range(Hq)]
+    cache = {}
+    for b, i, hq in rows:
+        h = hq // G
+        p = int(seq_lens[b]) - q_len + i
+        key = (b, h)
+        if key not in cache:
+            cache = {key: (to_f64(k[b, h], dtype), to_f64(v[b, h], dtype))}
+        Kf, Vf = cache[key]
+        qs = tuple(to_f64(x[b, i, hq], dtype) for x in (q, q_succ, q_inter))
+        out[b, i, hq] = attend_dca_row(qs, Kf, Vf, p, chunk_len, scale,
+                                       float(np.float32(mscale[b, i])))
+    return out
