@@ -32,14 +32,11 @@ import numpy as np
 from .cache import to_f64
 
 
-def query_kind(p: int, j: int, chunk_len: int) -> int:
-    """0: intra (same chunk), 1: succ (the key's chunk directly precedes the query's), 2: inter."""
-    cq, ck = p // chunk_len, j // chunk_len
-    if ck == cq:
-        return 0
-    if ck == cq - 1:
-        return 1
-    return 2
+def query_kind(p: int, j, chunk_len: int):
+    """Which query vector a query at position p uses against key position(s) j (int or int array):
+    0 intra (same chunk), 1 succ (the key's chunk directly precedes the query's), 2 inter."""
+    cq, ck = p // chunk_len, np.asarray(j) // chunk_len
+    return np.where(ck == cq, 0, np.where(ck == cq - 1, 1, 2))
 
 
 def attend_dca_row(qs, K: np.ndarray, V: np.ndarray, p: int, chunk_len: int, scale: float,
@@ -51,10 +48,10 @@ def attend_dca_row(qs, K: np.ndarray, V: np.ndarray, p: int, chunk_len: int, sca
     D = V.shape[1]
     if p < 0:
         return np.zeros(D, dtype=np.float64)
-    s = np.empty(p + 1, dtype=np.float64)
-    for j in range(p + 1):
-        s[j] = float(qs[query_kind(p, j, chunk_len)] @ K[j])
-    s *= scale * mscale
+    kind = query_kind(p, np.arange(p + 1), chunk_len)
+    Kp = K[:p + 1]
+    s = np.where(kind == 0, Kp @ qs[0], np.where(kind == 1, Kp @ qs[1], Kp @ qs[2]))
+    s = s * (scale * mscale)
     m = s.max()
     w = np.exp(s - m)
     return (w @ V[:p + 1]) / w.sum()

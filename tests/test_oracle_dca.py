@@ -146,18 +146,18 @@ def _planted(monkeypatch, kind_fn=None, drop_mscale=False):
 
 
 def _kind_succ_two_back(p, j, C):
-    cq, ck = p // C, j // C
-    return 0 if ck == cq else 1 if ck == cq - 2 else 2
+    cq, ck = p // C, np.asarray(j) // C
+    return np.where(ck == cq, 0, np.where(ck == cq - 2, 1, 2))
 
 
 def _kind_swapped(p, j, C):
-    cq, ck = p // C, j // C
-    return 0 if ck == cq else 2 if ck == cq - 1 else 1
+    cq, ck = p // C, np.asarray(j) // C
+    return np.where(ck == cq, 0, np.where(ck == cq - 1, 2, 1))
 
 
 def _kind_from_query(p, j, C):
-    d = (p - j) // C
-    return 0 if d == 0 else 1 if d == 1 else 2
+    d = (p - np.asarray(j)) // C
+    return np.where(d == 0, 0, np.where(d == 1, 1, 2))
 
 
 @pytest.mark.parametrize("mistake", ["succ_two_back", "swapped", "from_query", "no_mscale"])
