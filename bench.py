@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "decode_int8": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "prefill": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
+    "dca": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
 }
 
 
@@ -380,6 +381,67 @@ def prefill_leg(args, torch, duo):
     return res
 
 
+def dca_flops(w: synth.Workload, L: int, q_len: int) -> int:
+    """4 D FLOP per (query, key) pair; every head sees keys 0..p (Dual Chunk Attention changes which
+    query vector meets a key, not how many keys)."""
+    p = np.arange(L - q_len, L, dtype=np.int64)
+    return int(4 * w.head_dim * w.num_q_heads * w.batch * (p + 1).sum())
+
+
+def dca_leg(args, torch, duo):
+    """Dual Chunk Attention prefill: the last 32768-row chunk of a 131072-token Qwen2-72B context
+    (one GPU's share at tensor parallelism 4), timed with HIP events per launch."""
+    w = synth.qwen2_72b_dca_prefill()
+    dev = torch.device("cuda:0")
+    C, L, n = w.extra["chunk_len"], w.context, w.q_len
+    log(f"[dca] generating {w.name}")
+    K = logical_bits(w, L, synth.S_K)
+    V = logical_bits(w, L, synth.S_V)
+    table_h, nblocks = synth.block_table(w)
+    table = torch.from_numpy(table_h).to(dev)
+    mask = w.retrieval_mask
+    tdt = torch_dtype(torch, w.dtype)
+    kp = torch.empty((nblocks, w.block_size, w.head_dim), dtype=tdt, device=dev)
+    vp = torch.empty((nblocks, w.head_dim, w.block_size), dtype=tdt, device=dev)
+    for s0 in range(0, L, n):
+        kn = to_dev(torch, K[:, :, s0:s0 + n].transpose(0, 2, 1, 3), w.dtype, dev)
+        vn = to_dev(torch, V[:, :, s0:s0 + n].transpose(0, 2, 1, 3), w.dtype, dev)
+        lb = torch.full((w.batch,), s0, dtype=torch.int32, device=dev)
+        la = torch.full((w.batch,), s0 + n, dtype=torch.int32, device=dev)
+        duo.kv_append_circular(kp, vp, table, kn, vn, lb, la, mask, w.sink, w.recent,
+                               w.ring_blocks)
+    del K, V
+    lens = torch.full((w.batch,), L, dtype=torch.int32, device=dev)
+    qs = [to_dev(torch, synth.f32_to_storage(synth.queries(w, 3 * (w.steps - 1) + k), w.dtype),
+                 w.dtype, dev) for k in range(3)]
+    ms = torch.from_numpy(synth.row_scales(w, w.steps - 1, n)).to(dev)
+    out = torch.empty_like(qs[0])
+    ws = duo.dca_prefill_workspace(qs[0], table)
+    torch.cuda.synchronize()
+    for _ in range(args.prefill_warmup):
+        duo.dca_attn_prefill(*qs, ms, C, kp, vp, table, lens, w.scale, out, ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_passes)]
+    for a, b in evs:
+        a.record()
+        duo.dca_attn_prefill(*qs, ms, C, kp, vp, table, lens, w.scale, out, ws)
+        b.record()
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in evs]))
+    flops = dca_flops(w, L, n)
+    ach = flops / t / 1e12
+    res = {"workload": w.name, "value": round(ach, 2), "unit": "TFLOP/s",
+           "ms_per_call": round(t * 1e3, 3), "flops_per_call": flops, "chunk_len": C,
+           "context": L, "q_len": n,
+           "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic("dca"),
+                        "kernel": "duo::prefill_kernel<bf16,128,dca>"}}
+    log(f"[dca] {t * 1e3:.3f} ms per call, {ach:.1f} TFLOP/s")
+    return res
+
+
 # ---- CPU baseline: the oracle on a bounded sample ----------------------------------------------
 def cpu_baseline(dec, budget_s: float):
     import oracle
@@ -433,7 +495,7 @@ def _read_counter_csv(path):
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: str, command: str):
-    """Per-launch HBM bytes of the decode and prefill kernels from two rocprofv3 --pmc runs
+    """Per-launch HBM bytes of the decode, prefill and Dual Chunk kernels from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), scaled by what the same counters read for a
     copy of copy_mib MiB. Writes profiles/counters.json keyed by kernel, with the source hash."""
     def per_kernel(path, counter):
@@ -448,7 +510,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
             elif "decode_kernel" in name:
                 acc.setdefault("decode", []).append(val)
             elif "prefill_kernel" in name:
-                acc.setdefault("prefill", []).append(val)
+                # the Dual Chunk Attention instantiation has its bool template argument set
+                dca = "Lb1E" in name or ", true>" in name
+                acc.setdefault("dca" if dca else "prefill", []).append(val)
             elif COPY_KERNEL_HINT in name.lower():
                 copies.append((int(r["Dispatch_Id"]), val))
         # the calibration copies are the last CALIBRATION_REPS copy dispatches of the run
@@ -464,7 +528,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
     out = {"calibration": {"copy_bytes": known, "fetch_raw": fetch.get("copy"),
                            "write_raw": write.get("copy"), "fetch_scale": f_scale,
                            "write_scale": w_scale, "command": command}}
-    for k in ("decode", "decode_int8", "prefill"):
+    for k in ("decode", "decode_int8", "prefill", "dca"):
         if k in fetch and k in write:
             out[k] = {"source_sha": source_sha(k),
                       "fetch_bytes_per_launch": fetch[k] * f_scale,
@@ -484,7 +548,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="decode caches rotated across steps")
     ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=1)
-    ap.add_argument("--legs", default="decode,decode_int8,prefill")
+    ap.add_argument("--legs", default="decode,decode_int8,prefill,dca")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -512,6 +576,7 @@ def main():
     dec = decode_leg(args, torch, duo) if legs & {"decode", "decode_int8"} else None
     dq = decode_int8_leg(args, torch, duo, dec) if "decode_int8" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
+    dca = dca_leg(args, torch, duo) if "dca" in legs else None
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
     cpu = None
@@ -537,6 +602,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": pre,
         "decode_int8": dq,
+        "dca_prefill": dca,
     }
     print(json.dumps(line), flush=True)
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 4
+#define DUO_ATTN_ABI_VERSION 5
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -261,6 +261,55 @@ int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* 
                              int32_t recent_size, int32_t ring_blocks, float softmax_scale,
                              void* out, void* workspace, size_t workspace_bytes,
                              int32_t split_tokens, void* stream);
+
+/*
+ * Dual Chunk Attention -- the prefill of the vLLM PR "[Model] Implement DualChunkAttention for Qwen2
+ * Models" over this library's paged cache, in one launch (the PR's brute-force form calls an
+ * attention kernel three times per chunk and merges the results).
+ *
+ * Source: that PR's description (the rotary layer hands attention three query vectors per token:
+ * intra-, succ- and inter-chunk) and review thread (the brute-force prefill swaps q for q_succ or
+ * q_inter by the chunk relation of query and key; every chunk but the query's own is chunk_len long;
+ * the weight is (q . k) * softmax_scale * mscale with an fp32 mscale per query position, applied in
+ * fp32; the partial results are merged by their log-sum-exp, i.e. one softmax over all keys j <= p).
+ * With chunk(t) = t / chunk_len, the query at position p uses against key j <= p:
+ *   q        if chunk(j) == chunk(p);
+ *   q_succ   if chunk(j) == chunk(p) - 1;
+ *   q_inter  if chunk(j) <  chunk(p) - 1.
+ * Every kv head is a full causal head (no streaming heads), bounded by the sequence's valid length,
+ * so the cache is filled with kv_append_circular with every kv head marked retrieval.
+ */
+
+/*
+ * dca_attn_prefill_workspace_size -- bytes of device workspace dca_attn_prefill needs (the
+ * duo_attn_prefill workspace with every kv head a retrieval head); zero-fill it once after
+ * allocation. Returns 0 for invalid sizes.
+ */
+size_t dca_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
+/*
+ * dca_attn_prefill -- q_len query rows per sequence (appended to the cache already) attend over
+ * positions 0..p of their kv head with the query vector the chunk relation selects.
+ *
+ *   q, q_succ, q_inter  device [batch][q_len][num_q_heads][head_dim] of dtype (16-byte aligned):
+ *                       the intra-, succ- and inter-chunk query vectors of each row.
+ *   mscale              device float [batch][q_len]: the row's factor on softmax_scale; it must be
+ *                       positive and finite (other values give wrong rows, never a fault).
+ *   chunk_len           chunk length in tokens, a multiple of 64 (so a 64-key tile lies in one chunk).
+ *   seq_lens, out, workspace, the pool, table and stream arguments: as for duo_attn_prefill (row i
+ *                       at position seq_lens[b] - q_len + i).
+ * Supported: dtype DUO_F16 or DUO_BF16, head_dim 64 or 128.
+ * Errors: INVALID_ARG (a missing or misaligned pointer, chunk_len < 1, sizes as duo_attn_prefill),
+ *         UNSUPPORTED (chunk_len not a multiple of 64, dtype, head_dim, block_size), WORKSPACE.
+ */
+int32_t dca_attn_prefill(const void* q, const void* q_succ, const void* q_inter,
+                         const float* mscale, int32_t chunk_len, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table, int32_t num_blocks,
+                         int32_t block_size, int32_t max_blocks_per_head, const int32_t* seq_lens,
+                         int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, float softmax_scale, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* duo_status_string(int32_t status);

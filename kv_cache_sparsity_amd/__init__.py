@@ -11,6 +11,7 @@ Tensor layouts (all contiguous, on the GPU, one dtype per call: float32, float16
   append:  k_new, v_new [batch][t_new][num_kv_heads][head_dim]
   decode:  q, out [batch][num_q_heads][head_dim]
   prefill: q, out [batch][q_len][num_q_heads][head_dim]
+  dca:     q, q_succ, q_inter, out [batch][q_len][num_q_heads][head_dim], mscale float32 [batch][q_len]
 """
 from __future__ import annotations
 
@@ -26,7 +27,8 @@ STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "D
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
            "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
            "kv_append_circular_int8",
-           "duo_attn_decode_int8", "duo_status_string", "duo_abi_version")
+           "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
+           "duo_status_string", "duo_abi_version")
 
 
 class DuoAttnError(RuntimeError):
@@ -75,6 +77,11 @@ def lib() -> ctypes.CDLL:
                                            _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
                                            _I32, _P]
         L.duo_status_string.restype = ctypes.c_char_p
+        L.dca_attn_prefill_workspace_size.restype = _SZ
+        L.dca_attn_prefill_workspace_size.argtypes = [_I32] * 6
+        L.dca_attn_prefill.restype = _I32
+        L.dca_attn_prefill.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32,
+                                       _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _SZ, _P]
         L.duo_status_string.argtypes = [_I32]
         L.duo_abi_version.restype = _I32
         L.duo_abi_version.argtypes = []
@@ -285,9 +292,45 @@ def duo_attn_decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_l
     _check("duo_attn_decode_int8", st)
 
 
+def dca_attn_prefill_workspace_size(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, dtype: int) -> int:
+    return int(lib().dca_attn_prefill_workspace_size(batch, q_len, num_q_heads, num_kv_heads,
+                                                     head_dim, dtype))
+
+
+def dca_prefill_workspace(q, block_table):
+    """Zero-filled workspace for dca_attn_prefill (q: [B][q_len][Hq][D])."""
+    import torch
+    batch, q_len, num_q_heads, d = q.shape
+    n = dca_attn_prefill_workspace_size(batch, q_len, num_q_heads, block_table.shape[1], d,
+                                        _dtype_tag(q))
+    if n == 0:
+        raise ValueError("invalid sizes for the Dual Chunk Attention workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
+def dca_attn_prefill(q, q_succ, q_inter, mscale, chunk_len: int, k_pool, v_pool, block_table,
+                     seq_lens, softmax_scale: float, out, workspace, stream=None) -> None:
+    """Dual Chunk Attention prefill: q, q_succ, q_inter, out [B][q_len][Hq][D] (float16 or
+    bfloat16); mscale float32 [B][q_len]; the cache filled with every kv head a retrieval head."""
+    import torch
+    if mscale.dtype != torch.float32:
+        raise TypeError("mscale must be torch.float32")
+    num_blocks, block_size, head_dim = k_pool.shape
+    batch, q_len, num_q_heads, _ = q.shape
+    st = lib().dca_attn_prefill(
+        _ptr(q), _ptr(q_succ), _ptr(q_inter), _ptr(mscale), chunk_len, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch,
+        q_len, num_q_heads, block_table.shape[1], head_dim, _dtype_tag(q), softmax_scale,
+        _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dca_attn_prefill", st)
+
+
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
-           "prefill_varlen_workspace",
+           "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size",
+           "dca_prefill_workspace",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",
            "prefill_workspace", "status_string", "abi_version",
            "DuoAttnError", "lib", "LIB_PATH", "SYMBOLS", "DUO_F32", "DUO_F16", "DUO_BF16"]

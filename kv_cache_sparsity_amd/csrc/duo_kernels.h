@@ -68,6 +68,13 @@ struct PrefillParams {
   float scale_log2;
   uint8_t ret_heads[kMaxKvHeads];
   uint8_t str_heads[kMaxKvHeads];
+  // Dual Chunk Attention only: the query vectors for keys of the preceding chunk (q_succ) and of
+  // earlier chunks (q_inter), laid out like q; one fp32 mscale per query row; the chunk length in
+  // 64-key tiles
+  const void* q_succ;
+  const void* q_inter;
+  const float* mscale;
+  int32_t chunk_tiles;
 };
 
 // Launchers (return the HIP launch status). dtype: 0 f32, 1 f16, 2 bf16.
@@ -77,6 +84,9 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool in
                          hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid,
                           hipStream_t stream);
+hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t stream);
+constexpr int kPrefillKeyTile = 64;   // keys per prefill K/V tile (Dual Chunk lengths are multiples)
 
 // Decode planning shared by the workspace-size query and the call.
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,

@@ -40,6 +40,15 @@
 //                                                     B = P^T taken from the S^T accumulators.
 // K rows sit in LDS in a permuted order so that the eight S^T accumulators a lane holds per
 // 16-key chunk are the chunk's keys 8*(lane/32) .. +7, the k-group of its P^T operand.
+//
+// Dual Chunk Attention (vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models", review
+// thread on the brute-force prefill and on mscale) is the same walk over a cache of full heads with
+// two changes. The query vector that meets a key depends on the chunks (chunk(t) = t / chunk_len)
+// of the two: the row's own q within its chunk, q_succ in the chunk before, q_inter further back.
+// Chunk lengths are multiples of the 64-key tile, so a tile lies in one chunk and each lane (one
+// query row of the B operand) picks its vector per tile; a lane reloads its Q^T registers only when
+// its kind changes, at most twice along the ascending walk. The scores scale is softmax_scale times
+// the row's fp32 mscale, applied to the fp32 accumulators.
 #include "duo_common.h"
 #include "duo_kernels.h"
 
@@ -50,7 +59,7 @@ __device__ __attribute__((aligned(64))) uint32_t g_prefill_zero_chunk[16];
 
 namespace {
 
-constexpr int kKeys = 64;      // keys per K/V tile (four 16-key runs)
+constexpr int kKeys = kPrefillKeyTile;   // keys per K/V tile (four 16-key runs)
 constexpr int kLdsAhead = 4;   // LDS operand reads kept in flight ahead of the MFMAs
 
 // Row of the 32-key block that holds key r of the block (an involution: swaps the middle two
@@ -164,7 +173,7 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
 template <int bytes, bool used>
 struct StageBytes { static constexpr int value = used ? bytes : 16; };
 
-template <typename T, int D>
+template <typename T, int D, bool DCA>
 __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(const PrefillParams p) {
   using TG = TileGeo<T, D>;
   constexpr int kThreads = TG::kThreads;
@@ -311,6 +320,18 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     for (int j = 0; j < 16; ++j) oT[i][j] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int32_t my_p = p_lo + wrow0 + rcol;          // this lane's query position
+  // Scores scale (log2 domain) of this lane's row, and for Dual Chunk Attention the first tiles of
+  // the row's own chunk and of the chunk before it (tiles below t_succ take q_inter). Rows before
+  // the sequence start (p < 0) see no key; they keep kind 0.
+  float sl2 = p.scale_log2;
+  int32_t t_intra = 0, t_succ = 0;
+  int q_kind = 0;                                    // the vector held in qT: 0 q, 1 q_succ, 2 q_inter
+  if constexpr (DCA) {
+    if (qrow < qn) sl2 *= p.mscale[q0 + qrow];
+    const int32_t cq = my_p >= 0 ? my_p / (p.chunk_tiles * kKeys) : -1;
+    t_intra = cq * p.chunk_tiles;
+    t_succ = t_intra - p.chunk_tiles;
+  }
 
   // Loop-invariant per-lane copy offsets (elements): this wave copies part (wave / 4) of run
   // (wave mod 4) of every tile.
@@ -404,7 +425,19 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     // The weights of one tile: S^T, the element mask when `mask`, online softmax; the tile's P^T
     // operands (one per 16-key chunk) go to `P`. (One body for both cases: two inlined copies
     // would each hoist their own LDS addresses out of the loop and run out of registers.)
-    auto scores = [&](bool mask, const Run* runs, const char* k_st, v8<T> (&P)[4]) {
+    auto scores = [&](int tile, bool mask, const Run* runs, const char* k_st, v8<T> (&P)[4]) {
+      if constexpr (DCA) {
+        const int need = tile >= t_intra ? 0 : tile >= t_succ ? 1 : 2;
+        if (__any(need != q_kind)) {
+          if (need != q_kind && qrow < qn) {
+            const void* base = need == 0 ? p.q : need == 1 ? p.q_succ : p.q_inter;
+            const T* src = static_cast<const T*>(base) + ((q0 + qrow) * p.num_q_heads + hq) * D;
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) qT[dc] = load8(src + dc * 16 + half * 8);
+          }
+          q_kind = need;
+        }
+      }
       // All K operands of the tile are read first, then the MFMAs run back to back: the LDS
       // latency is paid once per tile instead of once per MFMA.
       v8<T> ka[2][DC];
@@ -458,7 +491,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
 #pragma unroll
         for (int k = 0; k < w; ++k) t16[k] = __builtin_elementwise_maximum(t16[k], t16[k + w]);
       float mx = t16[0];
-      mx = max_xor32(mx) * p.scale_log2;
+      mx = max_xor32(mx) * (DCA ? sl2 : p.scale_log2);
       // Lazy reference max: it moves only when some row of the wave exceeds it by more than 8
       // (log2 units), so p <= 256 and O / l are rescaled on few tiles. The final O / l is exact
       // whatever reference was used. O holds every earlier tile's PV at this point.
@@ -475,7 +508,8 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
       for (int c = 0; c < 4; ++c) {
         float x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + k], p.scale_log2, -m_use));
+        for (int k = 0; k < 8; ++k)
+          x[k] = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + k], DCA ? sl2 : p.scale_log2, -m_use));
         P[c] = pack8<T>(x);
         l_run = sum8(P[c], l_run);
       }
@@ -539,7 +573,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
 #pragma unroll
         for (int i = 0; i < 4; ++i) runs[i] = run_pos(tile * 4 + i);
       }
-      scores(!all_full, runs, k_st, P);
+      scores(tile, !all_full, runs, k_st, P);
       return true;
     };
 
@@ -690,23 +724,36 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DCA>
 void launch_d(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<T, D>), dim3(grid), dim3(TileGeo<T, D>::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<T, D, DCA>), dim3(grid), dim3(TileGeo<T, D>::kThreads), 0,
+                     stream, p);
 }
 
 template <typename T>
 hipError_t launch_t(const PrefillParams& p, int head_dim, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's status
   switch (head_dim) {
-    case 64: launch_d<T, 64>(p, grid, stream); break;
-    case 128: launch_d<T, 128>(p, grid, stream); break;
+    case 64: launch_d<T, 64, false>(p, grid, stream); break;
+    case 128: launch_d<T, 128, false>(p, grid, stream); break;
     case 256:
       if constexpr (sizeof(T) == 2) {
-        launch_d<T, 256>(p, grid, stream);
+        launch_d<T, 256, false>(p, grid, stream);
         break;
       }
       return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Dual Chunk Attention: 16-bit queries and caches, head dims 64 and 128.
+template <typename T>
+hipError_t launch_dca_t(const PrefillParams& p, int head_dim, int grid, hipStream_t stream) {
+  (void)hipGetLastError();
+  switch (head_dim) {
+    case 64: launch_d<T, 64, true>(p, grid, stream); break;
+    case 128: launch_d<T, 128, true>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -719,6 +766,13 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
   if (dtype == 0) return launch_t<float>(p, head_dim, grid, stream);
   if (dtype == 1) return launch_t<_Float16>(p, head_dim, grid, stream);
   return launch_t<__bf16>(p, head_dim, grid, stream);
+}
+
+hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t stream) {
+  if (dtype == 1) return launch_dca_t<_Float16>(p, head_dim, grid, stream);
+  if (dtype == 2) return launch_dca_t<__bf16>(p, head_dim, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace duo

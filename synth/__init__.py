@@ -23,7 +23,7 @@ DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2}
 
 # Stream ids for the counter-based generator.
-S_HEADS, S_LENS, S_K, S_V, S_Q, S_TABLE, S_GARBAGE, S_KSTEP, S_VSTEP = range(9)
+S_HEADS, S_LENS, S_K, S_V, S_Q, S_TABLE, S_GARBAGE, S_KSTEP, S_VSTEP, S_ROWSCALE = range(10)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -187,6 +187,20 @@ def long_context_decode(context: int = 1 << 20, steps: int = 64) -> Workload:
                     steps=steps)
 
 
+def qwen2_72b_dca_prefill(chunk: int = 32768, chunks: int = 4, chunk_len: int = 32768) -> Workload:
+    """Qwen2-72B-shaped Dual Chunk Attention prefill, one GPU's share at tensor parallelism 4 (the
+    DualChunkAttention PR's usage example: chunk_size 32768, chunked prefill of 32768 batched
+    tokens, tensor_parallel_size 4): 64 / 4 = 16 q heads over 8 / 4 = 2 kv heads, D 128, bf16,
+    batch 1; four 32768-token chunks build a 131072-token context, so the last chunk's queries meet
+    intra-, succ- and inter-chunk keys. Every kv head is a full head."""
+    bs = 16
+    ctx = chunk * chunks
+    return Workload(f"qwen2-72b-tp4-dca-prefill-{chunks}x{chunk}-c{chunk_len}", 1, 16, 2, 128, BF16,
+                    bs, 0, 1, (0, 1), context=ctx, q_len=chunk, ring_blocks=1,
+                    max_blocks_per_head=_max_blocks(ctx, 0, 1, bs), seed=6, steps=chunks,
+                    extra={"chunk_len": chunk_len})
+
+
 def small(name: str, *, batch=2, q_heads=4, kv_heads=2, head_dim=64, dtype=BF16, block_size=16,
           sink=4, recent=24, retrieval=(0,), context=100, q_len=1, seed=11, ring_blocks=None,
           capacity=None) -> Workload:
@@ -204,6 +218,7 @@ ALL = {
     "llama2-7b-chunked-prefill": llama2_7b_chunked_prefill,
     "gemma-2b-static-decode": gemma_2b_static_decode,
     "long-context-decode": long_context_decode,
+    "qwen2-72b-dca-prefill": qwen2_72b_dca_prefill,
 }
 
 
@@ -271,6 +286,13 @@ def queries(w: Workload, step: int, q_len: int | None = None) -> np.ndarray:
     """Query rows for one attention call: float32 [batch][q_len][q_heads][D]."""
     q_len = w.q_len if q_len is None else q_len
     return normal(w.seed, S_Q, step, shape=(w.batch, q_len, w.num_q_heads, w.head_dim))
+
+
+def row_scales(w: Workload, step: int, q_len: int, lo: float = 1.0, hi: float = 1.4) -> np.ndarray:
+    """One positive float32 factor per query row, uniform in [lo, hi): float32 [batch][q_len] (the
+    per-position scale factor Dual Chunk Attention takes; synthetic values, no method arithmetic)."""
+    rng = np.random.default_rng([w.seed, S_ROWSCALE, step])
+    return rng.uniform(lo, hi, size=(w.batch, q_len)).astype(np.float32)
 
 
 def valid_lengths(w: Workload, lo: int, hi: int) -> np.ndarray:

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 4
+    assert duo.abi_version() == 5
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -235,3 +235,38 @@ def test_prefill_workspace_size_query():
 def test_all_retrieval_prefill_ignores_ring_geometry_but_checks_the_rest():
     mask = ctypes.cast(MASK_R, ctypes.c_void_p)
     assert prefill(mask=mask, rb=0, recent=0, d=96) == UNSUPPORTED
+
+
+# ---- dca_attn_prefill ----------------------------------------------------------------------------
+def dca(**kw):
+    a = dict(q=FAKE, qs=FAKE, qi=FAKE, ms=FAKE, chunk=256, k_pool=FAKE, v_pool=FAKE, table=FAKE,
+             num_blocks=64, bs=16, mbph=20, lens=FAKE, batch=1, q_len=32, hq=4, hkv=2, d=128,
+             dtype=2, scale=0.1, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return duo.lib().dca_attn_prefill(a["q"], a["qs"], a["qi"], a["ms"], a["chunk"], a["k_pool"],
+                                      a["v_pool"], a["table"], a["num_blocks"], a["bs"], a["mbph"],
+                                      a["lens"], a["batch"], a["q_len"], a["hq"], a["hkv"], a["d"],
+                                      a["dtype"], a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), INVALID), (dict(qi=None), INVALID), (dict(ms=None), INVALID),
+    (dict(qi=FAKE + 8), INVALID), (dict(ms=FAKE + 2), INVALID), (dict(q=None), INVALID),
+    (dict(chunk=0), INVALID), (dict(q_len=0), INVALID), (dict(lens=None), INVALID),
+    (dict(hkv=0), INVALID), (dict(scale=0.0), INVALID), (dict(hq=5), INVALID),
+    (dict(chunk=100), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(bs=8), UNSUPPORTED), (dict(hkv=65, hq=65), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE),
+])
+def test_dca_prefill_rejects(kw, status):
+    assert dca(**kw) == status
+
+
+def test_dca_workspace_is_the_all_retrieval_prefill_workspace():
+    L = duo.lib()
+    r_only = ctypes.cast(MASK_R, ctypes.c_void_p)
+    n = L.dca_attn_prefill_workspace_size(1, 32, 4, 2, 128, 2)
+    assert n == L.duo_attn_prefill_workspace_size(1, 32, 4, 2, 128, 2, r_only) > 256
+    assert L.dca_attn_prefill_workspace_size(1, 32, 4, 0, 128, 2) == 0
+    assert L.dca_attn_prefill_workspace_size(1, 32, 4, 65, 128, 2) == 0
+    assert dca(ws_bytes=n - 1) == WORKSPACE
