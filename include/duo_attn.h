@@ -40,6 +40,12 @@
  *                     with SB = ceil(sink_size / block_size) sink pages in front of the ring.
  *   A streaming head uses table columns [0, SB + ring_blocks); a retrieval head uses every column.
  *   Page ids outside [0, num_blocks) are clamped into range by the kernels (wrong results, no fault).
+ *   Shared sink pages (vLLM attention-sink issue, sh1ng's option 3: the sink block can serve every
+ *   request that starts with the same sink tokens): the rows of several sequences may point a
+ *   streaming head's sink columns [0, SB) at the same pages when their first sink_size tokens are
+ *   identical. Sink pages hold nothing but positions < sink_size, so every sequence that appends
+ *   those positions writes the same bits there; attention reads them through each row. Ring pages
+ *   and retrieval rows must stay private to one sequence.
  */
 #ifndef DUO_ATTN_H
 #define DUO_ATTN_H

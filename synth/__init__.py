@@ -233,14 +233,21 @@ def pages_needed(w: Workload, kv_head: int) -> int:
     return w.sink_blocks + w.ring_blocks
 
 
-def block_table(w: Workload, *, shuffle: bool = True, identity: bool = False):
+def block_table(w: Workload, *, shuffle: bool = True, identity: bool = False,
+                share_sinks: bool = False):
     """Block table [batch][kv_heads][max_blocks_per_head] int32 and the pool size in pages.
 
     Every (sequence, kv head) gets its own pages. Physical page ids are a seeded permutation (or the
     identity when ``identity``); unused columns hold 0, a valid page id that no kernel may read.
+    With ``share_sinks`` a streaming kv head's sink pages are allocated once and every sequence's
+    row points at them (sequences whose first sink tokens are the same; the ring stays private).
     """
-    need = [[pages_needed(w, h) for h in range(w.num_kv_heads)] for _ in range(w.batch)]
-    total = int(sum(sum(r) for r in need))
+    sb = w.sink_blocks
+    def own(b, h):
+        if share_sinks and h not in w.retrieval and b > 0:
+            return pages_needed(w, h) - sb
+        return pages_needed(w, h)
+    total = int(sum(own(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)))
     ids = np.arange(total, dtype=np.int64)
     if shuffle and not identity:
         ids = np.random.default_rng([w.seed, S_TABLE]).permutation(total)
@@ -248,8 +255,12 @@ def block_table(w: Workload, *, shuffle: bool = True, identity: bool = False):
     pos = 0
     for b in range(w.batch):
         for h in range(w.num_kv_heads):
-            n = need[b][h]
-            table[b, h, :n] = ids[pos:pos + n]
+            n = own(b, h)
+            if n < pages_needed(w, h):       # shared sink pages: those of sequence 0
+                table[b, h, :sb] = table[0, h, :sb]
+                table[b, h, sb:sb + n] = ids[pos:pos + n]
+            else:
+                table[b, h, :n] = ids[pos:pos + n]
             pos += n
     return table, total
 

@@ -61,10 +61,11 @@ class Cache:
     """Device pools + block table + lengths for one workload, filled through kv_append_circular."""
 
     def __init__(self, w: synth.Workload, fill: str = "nan", identity: bool = False,
-                 mask=None):
+                 mask=None, share_sinks: bool = False):
         self.w = w
         self.mask = np.asarray(mask if mask is not None else w.retrieval_mask, dtype=np.uint8)
-        self.table_h, self.num_blocks = synth.block_table(w, identity=identity)
+        self.table_h, self.num_blocks = synth.block_table(w, identity=identity,
+                                                          share_sinks=share_sinks)
         self.table = torch.from_numpy(self.table_h).cuda()
         ks, vs = oracle.pool_shapes(self.num_blocks, w.block_size, w.head_dim)
         fv = fill_bits(w.dtype, fill)

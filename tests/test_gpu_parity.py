@@ -238,6 +238,41 @@ def test_prefill_parity(case):
         check_close(got, want, w.dtype, f"{case['name']} chunk {ci}")
 
 
+def test_shared_sink_pages_across_sequences():
+    """Streaming heads of every sequence point at one set of sink pages (option 3 of the vLLM
+    attention-sink issue: sinks in blocks of their own, reusable by every request that starts with
+    the same sink tokens). Every sequence appends its own positions, so the shared pages receive the
+    same bits from each; decode and prefill read them through the table."""
+    say("shared sink pages")
+    w = synth.small("shared-sinks", batch=4, q_heads=8, kv_heads=4, head_dim=128,
+                    dtype=synth.BF16, block_size=16, sink=20, recent=64, retrieval=(0, 2),
+                    context=600, q_len=64, seed=47)
+    cache = Cache(w, fill="nan", share_sinks=True)
+    t = cache.table_h
+    for h in (1, 3):                       # streaming heads share their two sink pages
+        assert (t[:, h, :w.sink_blocks] == t[0, h, :w.sink_blocks]).all()
+    K = logical_kv(w, 600, synth.S_K)
+    V = logical_kv(w, 600, synth.S_V)
+    K[:, :, :w.sink] = K[0:1, :, :w.sink]  # the same first sink tokens in every sequence
+    V[:, :, :w.sink] = V[0:1, :, :w.sink]
+    cache.append_logical(K, V, 0, 536)
+    cache.append_logical(K, V, 536, 600)
+    torch.cuda.synchronize()
+    kp = to_host_bits(cache.k_pool, w.dtype)
+    for h in (1, 3):
+        for s in range(w.sink):
+            assert np.array_equal(kp[t[0, h, s // 16], s % 16], K[0, h, s])
+    lens = np.full(w.batch, 600)
+    q = q_prefill(w, 0, 64)
+    got = to_host_f64(cache.prefill(q), w.dtype)
+    want = oracle.attend(q, K, V, lens, cache.mask, sink=w.sink, recent=w.recent, scale=w.scale,
+                         dtype=w.dtype)
+    check_close(got, want, w.dtype, "shared sinks prefill")
+    qd = q_decode(w, 1)
+    got = to_host_f64(cache.decode(qd), w.dtype)
+    check_close(got, oracle_decode(w, qd, K, V, lens, cache.mask), w.dtype, "shared sinks decode")
+
+
 VARLEN_CASES = [
     dict(name="bf16-d128-gqa2", dtype=synth.BF16, head_dim=128, group=2, kv=2, ret=(0,),
          block_size=16, sink=4, recent=64, rows=[300, 1, 0, 37], lens=[700, 512, 100, 37]),

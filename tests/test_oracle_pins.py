@@ -293,6 +293,53 @@ def test_circular_paged_layout_equals_contiguous(calls, ring_blocks, q_len, bs):
     np.testing.assert_allclose(paged, contiguous, atol=1e-12)
 
 
+def test_shared_sink_pages_equal_private_ones_when_the_sinks_match():
+    """Option 3 of the vLLM attention-sink issue keeps the sinks in blocks of their own and suggests
+    reusing that block for every request that starts with the same sink tokens. Streaming heads of
+    all sequences share sink pages here; with identical first sink tokens the paged result equals the
+    contiguous attention, and the shared pages hold those tokens."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, D, bs, sink, ring_blocks, recent = 3, 4, 2, 8, 4, 6, 3, 9
+    total = 40
+    sb = -(-sink // bs)
+    mbph = max(-(-total // bs), sb + ring_blocks)
+    ret = (1,)
+    k = rng.standard_normal((B, Hkv, total, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, total, D)).astype(np.float32)
+    k[:, :, :sink] = k[0:1, :, :sink]                 # every sequence starts with the same sinks
+    v[:, :, :sink] = v[0:1, :, :sink]
+    table = np.zeros((B, Hkv, mbph), np.int32)
+    nxt = 0
+    for h in range(Hkv):
+        if h in ret:
+            continue
+        table[:, h, :sb] = np.arange(nxt, nxt + sb)   # one set of sink pages per streaming kv head
+        nxt += sb
+    for b in range(B):
+        for h in range(Hkv):
+            lo, n = (0, mbph) if h in ret else (sb, ring_blocks)
+            table[b, h, lo:lo + n] = np.arange(nxt, nxt + n)
+            nxt += n
+    kp, vp = ocache.new_pools(nxt, bs, D, np.float32, np.nan)
+    mask = np.zeros(Hkv, np.uint8)
+    mask[list(ret)] = 1
+    lens = np.zeros(B, np.int64)
+    for n in (5, 17, 1, 17):
+        kn = np.ascontiguousarray(k[:, :, lens[0]:lens[0] + n].transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(v[:, :, lens[0]:lens[0] + n].transpose(0, 2, 1, 3))
+        lens = ocache.append(kp, vp, table, kn, vn, lens, mask, sink=sink, block_size=bs,
+                             ring_blocks=ring_blocks, max_blocks_per_head=mbph)
+    q = rng.standard_normal((B, 2, Hq, D)).astype(np.float32)
+    paged = oracle.attend_paged(q, kp, vp, table, lens, mask, sink=sink, recent=recent, scale=0.3,
+                                dtype=0, block_size=bs, ring_blocks=ring_blocks)
+    contiguous = oracle.attend(q, k, v, lens, mask, sink=sink, recent=recent, scale=0.3, dtype=0)
+    np.testing.assert_allclose(paged, contiguous, atol=1e-12)
+    # the shared pages hold the sink tokens, one copy for all sequences
+    for t in range(sink):
+        assert np.array_equal(kp[table[0, 0, t // bs], t % bs], k[0, 0, t])
+    assert nxt == sb + B * (mbph + ring_blocks)      # private sinks would take B * sb
+
+
 def test_slots_beyond_valid_length_have_no_effect():
     rng = np.random.default_rng(11)
     L, Lcap = 29, 64
