@@ -431,14 +431,39 @@ def dca_leg(args, torch, duo):
     t = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in evs]))
     flops = dca_flops(w, L, n)
     ach = flops / t / 1e12
+    # the decode of the next token over the same cache (batch 1): every kv head's K/V is read once
+    qd = [x[:, -1].contiguous() for x in qs]     # [batch][Hq][D]: the chunk's last row
+    msd = ms[:, -1].contiguous()
+    outd = torch.empty_like(qd[0])
+    wsd = duo.decode_workspace(qd[0], table, w.block_size)
+    for _ in range(10):
+        duo.dca_attn_decode(*qd, msd, C, kp, vp, table, lens, w.scale, outd, wsd)
+    torch.cuda.synchronize()
+    devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(50)]
+    for a, b in devs:
+        a.record()
+        duo.dca_attn_decode(*qd, msd, C, kp, vp, table, lens, w.scale, outd, wsd)
+        b.record()
+    torch.cuda.synchronize()
+    td = float(np.median([a.elapsed_time(b) * 1e-3 for a, b in devs]))
+    dbytes = (2 * w.num_kv_heads * L * w.head_dim * w.elem_bytes
+              + 4 * w.num_kv_heads * (-(-L // w.block_size))
+              + 4 * w.num_q_heads * w.head_dim * w.elem_bytes)    # K/V, tables, three q + out
     res = {"workload": w.name, "value": round(ach, 2), "unit": "TFLOP/s",
            "ms_per_call": round(t * 1e3, 3), "flops_per_call": flops, "chunk_len": C,
            "context": L, "q_len": n,
            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": measured_traffic("dca"),
-                        "kernel": "duo::prefill_kernel<bf16,128,dca>"}}
-    log(f"[dca] {t * 1e3:.3f} ms per call, {ach:.1f} TFLOP/s")
+                        "kernel": "duo::prefill_kernel<bf16,128,dca>"},
+           "decode": {"batch": w.batch, "us_per_call": round(td * 1e6, 2),
+                      "algorithmic_bytes": dbytes, "GB/s": round(dbytes / td / 1e9, 1),
+                      "frac_hbm": round(dbytes / td / 1e9 / HBM_PEAK_GBS, 4),
+                      "kernel": "duo::decode_dca_kernel<bf16,128>",
+                      "note": "batch 1 over 134 MB: too small to fill the chip; context only"}}
+    log(f"[dca] prefill {t * 1e3:.3f} ms per call, {ach:.1f} TFLOP/s; decode {td * 1e6:.1f} us, "
+        f"{dbytes / td / 1e9:.0f} GB/s")
     return res
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 5
+#define DUO_ATTN_ABI_VERSION 6
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -269,9 +269,9 @@ int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* 
                              int32_t split_tokens, void* stream);
 
 /*
- * Dual Chunk Attention -- the prefill of the vLLM PR "[Model] Implement DualChunkAttention for Qwen2
- * Models" over this library's paged cache, in one launch (the PR's brute-force form calls an
- * attention kernel three times per chunk and merges the results).
+ * Dual Chunk Attention -- the prefill and decode of the vLLM PR "[Model] Implement DualChunkAttention
+ * for Qwen2 Models" over this library's paged cache, each in one launch (the PR's brute-force form
+ * calls an attention kernel three times per chunk and merges the results).
  *
  * Source: that PR's description (the rotary layer hands attention three query vectors per token:
  * intra-, succ- and inter-chunk) and review thread (the brute-force prefill swaps q for q_succ or
@@ -316,6 +316,28 @@ int32_t dca_attn_prefill(const void* q, const void* q_succ, const void* q_inter,
                          int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, float softmax_scale, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dca_attn_decode -- Dual Chunk Attention for one query per sequence (the PR's paged decode beside
+ * its prefill): the query at position seq_lens[b] - 1 attends over positions 0..seq_lens[b]-1 of its
+ * kv head, choosing q, q_succ or q_inter for each key as above.
+ *
+ *   q, q_succ, q_inter, out  device [batch][num_q_heads][head_dim] of dtype (16-byte aligned).
+ *   mscale              device float [batch]: the sequence's factor on softmax_scale (positive,
+ *                       finite).
+ *   chunk_len, pools, table, seq_lens: as for dca_attn_prefill.
+ *   workspace, split_tokens: as for duo_attn_decode (duo_attn_decode_workspace_size for the same
+ *                       sizes and split_tokens).
+ * Supported: dtype DUO_F16 or DUO_BF16, head_dim 64 or 128, num_q_heads / num_kv_heads <= 16.
+ * Errors: as dca_attn_prefill and duo_attn_decode.
+ */
+int32_t dca_attn_decode(const void* q, const void* q_succ, const void* q_inter,
+                        const float* mscale, int32_t chunk_len, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, int32_t num_blocks,
+                        int32_t block_size, int32_t max_blocks_per_head, const int32_t* seq_lens,
+                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t dtype, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t split_tokens, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* duo_status_string(int32_t status);

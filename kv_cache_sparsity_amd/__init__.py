@@ -12,6 +12,7 @@ Tensor layouts (all contiguous, on the GPU, one dtype per call: float32, float16
   decode:  q, out [batch][num_q_heads][head_dim]
   prefill: q, out [batch][q_len][num_q_heads][head_dim]
   dca:     q, q_succ, q_inter, out [batch][q_len][num_q_heads][head_dim], mscale float32 [batch][q_len]
+           (decode: [batch][num_q_heads][head_dim] and mscale [batch])
 """
 from __future__ import annotations
 
@@ -28,6 +29,7 @@ SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_dec
            "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
            "kv_append_circular_int8",
            "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
+           "dca_attn_decode",
            "duo_status_string", "duo_abi_version")
 
 
@@ -82,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.dca_attn_prefill.restype = _I32
         L.dca_attn_prefill.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32,
                                        _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _SZ, _P]
+        L.dca_attn_decode.restype = _I32
+        L.dca_attn_decode.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32,
+                                      _I32, _I32, _I32, _I32, _F, _P, _P, _SZ, _I32, _P]
         L.duo_status_string.argtypes = [_I32]
         L.duo_abi_version.restype = _I32
         L.duo_abi_version.argtypes = []
@@ -327,9 +332,28 @@ def dca_attn_prefill(q, q_succ, q_inter, mscale, chunk_len: int, k_pool, v_pool,
     _check("dca_attn_prefill", st)
 
 
+def dca_attn_decode(q, q_succ, q_inter, mscale, chunk_len: int, k_pool, v_pool, block_table,
+                    seq_lens, softmax_scale: float, out, workspace, split_tokens: int = 0,
+                    stream=None) -> None:
+    """Dual Chunk Attention decode: q, q_succ, q_inter, out [B][Hq][D] (float16 or bfloat16);
+    mscale float32 [B]; workspace as for duo_attn_decode (decode_workspace)."""
+    import torch
+    if mscale.dtype != torch.float32:
+        raise TypeError("mscale must be torch.float32")
+    num_blocks, block_size, head_dim = k_pool.shape
+    batch, num_q_heads, _ = q.shape
+    st = lib().dca_attn_decode(
+        _ptr(q), _ptr(q_succ), _ptr(q_inter), _ptr(mscale), chunk_len, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch,
+        num_q_heads, block_table.shape[1], head_dim, _dtype_tag(q), softmax_scale, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), split_tokens,
+        _stream(stream))
+    _check("dca_attn_decode", st)
+
+
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
-           "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size",
+           "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
            "dca_prefill_workspace",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",
            "prefill_workspace", "status_string", "abi_version",

@@ -217,6 +217,15 @@ size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_
 }
 
 // The decode behind both caches: int8 = codes in the pools plus one scale per slot for K and V.
+// The extra inputs of Dual Chunk Attention (checked by the dca_* entry points).
+struct DcaArgs {
+  const void* q_succ;
+  const void* q_inter;
+  const float* mscale;
+  int32_t chunk_len;
+};
+
+// The decode behind both caches; dca != nullptr: Dual Chunk Attention (16-bit cache, full heads).
 static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const void* v_pool,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
                            int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
@@ -224,7 +233,8 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
                            int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                            const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                            int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
-                           size_t workspace_bytes, int32_t split_tokens, void* stream) {
+                           size_t workspace_bytes, int32_t split_tokens, void* stream,
+                           const DcaArgs* dca = nullptr) {
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);
@@ -280,6 +290,16 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
   for (int32_t i = 0; i < n_str; ++i) p.str_heads[i] = str[i];
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  if (dca) {
+    p.q_succ = dca->q_succ;
+    p.q_inter = dca->q_inter;
+    p.mscale = dca->mscale;
+    p.chunk_len = dca->chunk_len;
+    if (launch_decode_dca(p, dtype, head_dim, (int)grid, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+      return DUO_ERR_HIP;
+    return DUO_OK;
+  }
   if (launch_decode(p, dtype, head_dim, int8, (int)grid, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DUO_ERR_HIP;
@@ -331,14 +351,6 @@ size_t duo_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num
                &bytes);
   return bytes > 0 ? bytes : 256;   // 0 means invalid arguments
 }
-
-// The extra inputs of Dual Chunk Attention (checked by the caller of prefill_impl).
-struct DcaArgs {
-  const void* q_succ;
-  const void* q_inter;
-  const float* mscale;
-  int32_t chunk_len;
-};
 
 // The prefill behind both layouts of the queries: q_start == nullptr: [batch][q_len] rows;
 // otherwise packed rows, sequence b's at [q_start[b], q_start[b+1]) of total_q, at most q_len each.
@@ -466,6 +478,39 @@ size_t dca_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num
                                          all);
 }
 
+// Checks shared by the two Dual Chunk Attention calls (before the common ones).
+static int32_t check_dca(const void* q_succ, const void* q_inter, const float* mscale,
+                         int32_t chunk_len, int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (!q_succ || !q_inter || !mscale || !aligned(q_succ, 16) || !aligned(q_inter, 16) ||
+      !aligned(mscale, 4))
+    return DUO_ERR_INVALID_ARG;
+  if (chunk_len < 1) return DUO_ERR_INVALID_ARG;
+  if (chunk_len % kPrefillKeyTile != 0) return DUO_ERR_UNSUPPORTED;
+  if (dtype != DUO_F16 && dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return DUO_ERR_UNSUPPORTED;
+  if (num_kv_heads < 1) return DUO_ERR_INVALID_ARG;
+  if (num_kv_heads > kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
+  return DUO_OK;
+}
+
+int32_t dca_attn_decode(const void* q, const void* q_succ, const void* q_inter,
+                        const float* mscale, int32_t chunk_len, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, int32_t num_blocks,
+                        int32_t block_size, int32_t max_blocks_per_head, const int32_t* seq_lens,
+                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t dtype, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t split_tokens, void* stream) {
+  const int32_t st = check_dca(q_succ, q_inter, mscale, chunk_len, num_kv_heads, head_dim, dtype);
+  if (st != DUO_OK) return st;
+  uint8_t all[kMaxKvHeads];
+  for (int32_t h = 0; h < num_kv_heads; ++h) all[h] = 1;
+  const DcaArgs dca{q_succ, q_inter, mscale, chunk_len};
+  return decode_impl(false, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
+                     block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, all, 0, 1, 0, softmax_scale, out, workspace, workspace_bytes,
+                     split_tokens, stream, &dca);
+}
+
 int32_t dca_attn_prefill(const void* q, const void* q_succ, const void* q_inter,
                          const float* mscale, int32_t chunk_len, const void* k_pool,
                          const void* v_pool, const int32_t* block_table, int32_t num_blocks,
@@ -473,15 +518,9 @@ int32_t dca_attn_prefill(const void* q, const void* q_succ, const void* q_inter,
                          int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, float softmax_scale, void* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q_succ || !q_inter || !mscale || !aligned(q_succ, 16) || !aligned(q_inter, 16) ||
-      !aligned(mscale, 4))
-    return DUO_ERR_INVALID_ARG;
-  if (q_len < 1 || (int64_t)batch * q_len > INT32_MAX || chunk_len < 1) return DUO_ERR_INVALID_ARG;
-  if (chunk_len % kPrefillKeyTile != 0) return DUO_ERR_UNSUPPORTED;
-  if (dtype != DUO_F16 && dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return DUO_ERR_UNSUPPORTED;
-  if (num_kv_heads < 1) return DUO_ERR_INVALID_ARG;
-  if (num_kv_heads > kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
+  if (q_len < 1 || (int64_t)batch * q_len > INT32_MAX) return DUO_ERR_INVALID_ARG;
+  const int32_t st = check_dca(q_succ, q_inter, mscale, chunk_len, num_kv_heads, head_dim, dtype);
+  if (st != DUO_OK) return st;
   uint8_t all[kMaxKvHeads];
   for (int32_t h = 0; h < num_kv_heads; ++h) all[h] = 1;
   const DcaArgs dca{q_succ, q_inter, mscale, chunk_len};

@@ -30,6 +30,15 @@
 // Split merge: each retrieval item writes (m, l, O) for its G q heads to the workspace, then takes a
 // ticket on the (b, h) counter; the last item merges the partials, writes the output and resets the
 // counter to zero for the next call.
+//
+// Dual Chunk Attention (vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models": the paged
+// decode beside the prefill; review thread on the query swap and on mscale): every kv head is a full
+// head, and the query vector that meets a key depends on the chunk (t / chunk_len) of the key
+// against the chunk of the decoded position: q in the same chunk, q_succ in the one before, q_inter
+// further back. A wave step (32 keys) lies in one chunk (chunk_len is a multiple of 64), and every
+// lane of an item shares the query position, so the choice is uniform per step; the Q^T registers
+// are reloaded when it changes, at most twice per item. The scale is softmax_scale times the
+// sequence's fp32 mscale.
 #include "duo_common.h"
 #include "duo_kernels.h"
 
@@ -44,7 +53,7 @@ template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
 // The decode body. Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
 // (k_scale, v_scale [num_blocks][block_size]); a score is (codes . q) * k_scale of its key, and a
 // key's weight enters PV as p * v_scale of the key (the row sum l takes p itself).
-template <typename T, int D, bool Q8>
+template <typename T, int D, bool Q8, bool DCA = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int kDecodeWaves = decode_waves<D>();
   constexpr int kThreads = kDecodeWaves * kWave;
@@ -137,6 +146,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
     for (int i = 0; i < DT; ++i) oT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    // Dual Chunk Attention: the chunk of the decoded position, the vector held in qT (0 q,
+    // 1 q_succ, 2 q_inter) and the scale with the sequence's mscale
+    int32_t cq = 0;
+    int q_kind = 0;
+    float sl2 = p.scale_log2;
+    if constexpr (DCA) {
+      cq = (L - 1) / p.chunk_len;
+      sl2 *= p.mscale[b];
+    }
 
     // A wave step covers kChunks 32-key chunks (4 runs of 16 keys). In chunk c, K tile t' (two
     // per chunk) puts key 8*(r/4) + 4*t' + r%4 of the chunk in MFMA row r, so the S^T accumulator
@@ -224,6 +242,18 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       for (; step < n_steps; step += kDecodeWaves) {
         const int nxt = step + kDecodeWaves;
         const bool has_next = nxt < n_steps;
+        if constexpr (DCA) {
+          // all keys of the step share one chunk: choose the query vector for it (uniform)
+          const int32_t ck = (rl.first + seg0 + kRunsPerStep * step) * 16 / p.chunk_len;
+          const int need = ck == cq ? 0 : ck == cq - 1 ? 1 : 2;
+          if (need != q_kind) {
+            q_kind = need;
+            const void* base = need == 0 ? p.q : need == 1 ? p.q_succ : p.q_inter;
+            const T* qrow = static_cast<const T*>(base) + ((int64_t)b * p.num_q_heads + h * G + col) * D;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) qT[c] = (col < G) ? load8(qrow + c * 32 + quad * 8) : zero8<T>();
+          }
+        }
         f32x4 s[kChunks][2];
 #pragma unroll
         for (int c = 0; c < kChunks; ++c)
@@ -274,7 +304,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
             mloc = fmaxf(mloc, e);
           }
         }
-        mloc *= p.scale_log2;   // softmax_scale > 0: max commutes with the scale
+        mloc *= DCA ? sl2 : p.scale_log2;   // softmax_scale > 0: max commutes with the scale
         // Lazy reference max, shared by the four lanes of a column: it moves only when a score
         // exceeds it by more than 8 (log2 units), so the cross-lane max and the O rescale run on
         // few steps; p = 2^(x - m_run) <= 256 in between.
@@ -294,7 +324,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
           float x[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            x[i] = fast_exp2(fmaf(s[c][i >> 2][i & 3], p.scale_log2, -m_use));
+            x[i] = fast_exp2(fmaf(s[c][i >> 2][i & 3], DCA ? sl2 : p.scale_log2, -m_use));
             l_run += x[i];
           }
           v8<T> pB;
@@ -427,6 +457,12 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_ke
   decode_body<T, D, true>(p);
 }
 
+// Dual Chunk Attention decode (16-bit cache, every kv head a full head).
+template <typename T, int D>
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_dca_kernel(const DecodeParams p) {
+  decode_body<T, D, false, true>(p);
+}
+
 template <typename T, int D>
 void launch_d(const DecodeParams& p, bool int8_cache, int grid, hipStream_t stream) {
   if (int8_cache)
@@ -454,6 +490,22 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool in
   if (dtype == 0) return launch_t<float>(p, head_dim, int8_cache, grid, stream);
   if (dtype == 1) return launch_t<_Float16>(p, head_dim, int8_cache, grid, stream);
   return launch_t<__bf16>(p, head_dim, int8_cache, grid, stream);
+}
+
+hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int grid,
+                             hipStream_t stream) {
+  (void)hipGetLastError();
+  if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
+  if (head_dim == 64) {
+    if (dtype == 1) hipLaunchKernelGGL((decode_dca_kernel<_Float16, 64>), dim3(grid), dim3(decode_waves<64>() * kWave), 0, stream, p);
+    else hipLaunchKernelGGL((decode_dca_kernel<__bf16, 64>), dim3(grid), dim3(decode_waves<64>() * kWave), 0, stream, p);
+  } else if (head_dim == 128) {
+    if (dtype == 1) hipLaunchKernelGGL((decode_dca_kernel<_Float16, 128>), dim3(grid), dim3(decode_waves<128>() * kWave), 0, stream, p);
+    else hipLaunchKernelGGL((decode_dca_kernel<__bf16, 128>), dim3(grid), dim3(decode_waves<128>() * kWave), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,

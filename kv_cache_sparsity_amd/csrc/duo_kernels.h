@@ -46,6 +46,12 @@ struct DecodeParams {
   float scale_log2;  // softmax_scale * log2(e)
   uint8_t ret_heads[kMaxKvHeads];
   uint8_t str_heads[kMaxKvHeads];
+  // Dual Chunk Attention only: the succ / inter query vectors (laid out like q), one fp32 mscale
+  // per sequence (its query row), and the chunk length in tokens (a multiple of 64)
+  const void* q_succ;
+  const void* q_inter;
+  const float* mscale;
+  int32_t chunk_len;
 };
 
 struct PrefillParams {
@@ -82,6 +88,8 @@ hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stre
 hipError_t launch_append_int8(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8_cache, int grid,
                          hipStream_t stream);
+hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int grid,
+                             hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid,
                           hipStream_t stream);
 hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,

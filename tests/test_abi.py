@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 5
+    assert duo.abi_version() == 6
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -270,3 +270,27 @@ def test_dca_workspace_is_the_all_retrieval_prefill_workspace():
     assert L.dca_attn_prefill_workspace_size(1, 32, 4, 0, 128, 2) == 0
     assert L.dca_attn_prefill_workspace_size(1, 32, 4, 65, 128, 2) == 0
     assert dca(ws_bytes=n - 1) == WORKSPACE
+
+
+def dca_dec(**kw):
+    a = dict(q=FAKE, qs=FAKE, qi=FAKE, ms=FAKE, chunk=256, k_pool=FAKE, v_pool=FAKE, table=FAKE,
+             num_blocks=64, bs=16, mbph=20, lens=FAKE, batch=2, hq=8, hkv=2, d=128, dtype=2,
+             scale=0.1, out=FAKE, ws=FAKE, ws_bytes=1 << 30, split=0)
+    a.update(kw)
+    return duo.lib().dca_attn_decode(a["q"], a["qs"], a["qi"], a["ms"], a["chunk"], a["k_pool"],
+                                     a["v_pool"], a["table"], a["num_blocks"], a["bs"], a["mbph"],
+                                     a["lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["dtype"],
+                                     a["scale"], a["out"], a["ws"], a["ws_bytes"], a["split"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), INVALID), (dict(qi=FAKE + 4), INVALID), (dict(ms=None), INVALID),
+    (dict(chunk=-64), INVALID), (dict(q=None), INVALID), (dict(out=FAKE + 2), INVALID),
+    (dict(batch=0), INVALID), (dict(hkv=0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(split=100), INVALID),
+    (dict(chunk=96), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(hq=34), UNSUPPORTED),                 # GQA group of 17 > 16
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
+])
+def test_dca_decode_rejects(kw, status):
+    assert dca_dec(**kw) == status

@@ -1,4 +1,5 @@
-"""GPU parity of Dual Chunk Attention (dca_attn_prefill) against the CPU oracle (oracle.dca).
+"""GPU parity of Dual Chunk Attention (dca_attn_prefill, dca_attn_decode) against the CPU oracle
+(oracle.dca).
 
 The cache is filled through kv_append_circular with every kv head a full head; the three query sets
 and the per-row mscale are seeded. Bar: max abs error <= 2e-2 (bf16 / fp16) against fp64. Pools
@@ -125,3 +126,83 @@ def test_dca_qwen2_72b_tp4_share_last_chunk_sampled_rows():
     idx = tuple(np.array(rows).T)
     check_close(got_h[idx[0], idx[1], idx[2]], want[idx[0], idx[1], idx[2]], w.dtype,
                 f"{w.name} ({len(rows)} sampled rows)")
+
+
+# ------------------------------------------------------------------------------------------------
+# dca_attn_decode
+# ------------------------------------------------------------------------------------------------
+def _fill_per_sequence(cache, K, V, lens):
+    """Sequence b holds positions [0, lens[b]) (batch-1 appends on table row slices)."""
+    w = cache.w
+    final = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+    for b in range(w.batch):
+        L = int(lens[b])
+        kn = np.ascontiguousarray(K[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(V[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        before = torch.zeros(1, dtype=torch.int32, device="cuda")
+        after = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, cache.table[b:b + 1],
+                               to_dev(kn, w.dtype), to_dev(vn, w.dtype), before, after,
+                               cache.mask, w.sink, w.recent, w.ring_blocks)
+        final[b] = after[0]
+    cache.lens = final
+
+
+def _run_dca_decode(cache, qs, ms, chunk_len, split_tokens=0):
+    w = cache.w
+    q, q_succ, q_inter = (to_dev(x, w.dtype) for x in qs)
+    out = torch.empty_like(q)
+    ws = duo.decode_workspace(q, cache.table, w.block_size, split_tokens)
+    duo.dca_attn_decode(q, q_succ, q_inter, torch.from_numpy(ms).cuda(), chunk_len, cache.k_pool,
+                        cache.v_pool, cache.table, cache.lens, w.scale, out, ws, split_tokens)
+    return out
+
+
+DECODE_CASES = [
+    dict(name="bf16-d128-gqa4-c64", dtype=synth.BF16, head_dim=128, group=4, kv=2, block_size=16,
+         chunk_len=64, lens=[1, 63, 64, 65, 1000], splits=[128, 0]),
+    dict(name="f16-d64-mha-c256-bs64", dtype=synth.F16, head_dim=64, group=1, kv=3, block_size=64,
+         chunk_len=256, lens=[300, 4000, 257], splits=[512, 0]),
+    dict(name="bf16-d64-gqa16-c128", dtype=synth.BF16, head_dim=64, group=16, kv=1, block_size=16,
+         chunk_len=128, lens=[129, 2500], splits=[256, 0]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c["name"] for c in DECODE_CASES])
+def test_dca_decode_parity(case):
+    say(f"dca decode {case['name']}")
+    lens = np.asarray(case["lens"])
+    kv = case["kv"]
+    w = synth.small(case["name"], batch=len(lens), q_heads=kv * case["group"], kv_heads=kv,
+                    head_dim=case["head_dim"], dtype=case["dtype"], block_size=case["block_size"],
+                    sink=0, recent=1, retrieval=tuple(range(kv)), context=int(lens.max()),
+                    q_len=1, seed=63)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, int(lens.max()), synth.S_K)
+    V = logical_kv(w, int(lens.max()), synth.S_V)
+    _fill_per_sequence(cache, K, V, lens)
+    q4, ms = _queries(w, 0, 1)
+    qs = [x[:, 0] for x in q4]
+    want = oracle.attend_dca(*q4, K, V, lens, ms, chunk_len=case["chunk_len"], scale=w.scale,
+                             dtype=w.dtype)[:, 0]
+    for split in case["splits"]:
+        got = to_host_f64(_run_dca_decode(cache, qs, ms[:, 0].copy(), case["chunk_len"], split),
+                          w.dtype)
+        check_close(got, want, w.dtype, f"{case['name']} split {split}")
+
+
+def test_dca_decode_qwen2_72b_tp4_share():
+    """Decode of the Qwen2-72B one-GPU share after the 131072-token context: batch 4, every row
+    checked (chunk_len 32768, so each query meets all three kinds)."""
+    w = synth.replace(synth.qwen2_72b_dca_prefill(), batch=4)
+    C, L = w.extra["chunk_len"], w.context
+    say(f"dca decode {w.name} batch 4: filling {L} tokens")
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, L, synth.S_K)
+    V = logical_kv(w, L, synth.S_V)
+    cache.append_logical(K, V, 0, L)
+    q4, ms = _queries(w, 9, 1)
+    got = to_host_f64(_run_dca_decode(cache, [x[:, 0] for x in q4], ms[:, 0].copy(), C), w.dtype)
+    want = oracle.attend_dca(*q4, K, V, np.full(4, L), ms, chunk_len=C, scale=w.scale,
+                             dtype=w.dtype)[:, 0]
+    check_close(got, want, w.dtype, f"{w.name} decode")
