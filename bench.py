@@ -21,6 +21,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -598,12 +599,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     legs = set(args.legs.split(","))
+    # No cyclic garbage collection while GPU work is timed: a collection pause on the host while
+    # the GPU queue has drained would land between a launch's start and stop events.
+    gc.collect()
+    gc.disable()
     dec = decode_leg(args, torch, duo) if legs & {"decode", "decode_int8"} else None
     dq = decode_int8_leg(args, torch, duo, dec) if "decode_int8" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
     dca = dca_leg(args, torch, duo) if "dca" in legs else None
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
+    gc.enable()
     cpu = None
     if dec is not None and not args.no_cpu_baseline:
         log("[cpu] timing the oracle")
