@@ -14,7 +14,8 @@
 // item's key tiles are split in n_split contiguous ranges, one workgroup each; the workgroups write
 // partial softmax states (m, l, O) to the workspace and the last to arrive merges them through
 // their log-sum-exp (vLLM DualChunkAttention PR, review thread) and writes the output. Retrieval
-// items come first in the grid, latest rows first (they scan the most keys).
+// items come first in the grid, latest rows first (they scan the most keys); within a row tile the
+// kv head varies fastest, so that a GQA group's workgroups share XCDs.
 //
 // Inside a workgroup every wave owns 32 rows and all waves work on the same 64-key tile, so each
 // K/V byte brought into LDS serves all R rows: copy traffic per MFMA is what the L2 -> LDS path
@@ -233,7 +234,9 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     int r = item % per_tile_r;
     b = r / (p.n_ret * G);
     r %= p.n_ret * G;
-    hq = p.ret_heads[r / G] * G + r % G;
+    // kv head fastest: workgroup i runs on XCD i mod 8, so the q heads that read one kv head's
+    // keys gather on the same XCDs (and L2s) instead of every XCD reading every kv head
+    hq = p.ret_heads[r % p.n_ret] * G + r / p.n_ret;
     ret = true;
   } else {
     const int per_tile_s = p.batch * p.n_str * G;
@@ -242,7 +245,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     int r = it % per_tile_s;
     b = r / (p.n_str * G);
     r %= p.n_str * G;
-    hq = p.str_heads[r / G] * G + r % G;
+    hq = p.str_heads[r % p.n_str] * G + r / p.n_str;
     ret = false;
   }
   const int h = hq / G;
