@@ -226,6 +226,93 @@ def decode_leg(args, torch, duo):
     return res
 
 
+def decode_shape_leg(args, torch, duo, w, lens_seq, n_layers, steps, tag):
+    """Timing of append (one token per sequence) + decode on another decode workload.
+
+    The pools are filled on the device with N(0,1) values (the workloads' distribution; the scores
+    must be realistic, since the online softmax rescales only when the running max moves). Parity
+    at these shapes, garbage past the valid lengths included, is covered by the GPU tests.
+    lens_seq[k] = the lengths after step k's append. n_layers caches are rotated so that every
+    step reads lines the Infinity Cache does not hold."""
+    dev = torch.device("cuda:0")
+    log(f"[{tag}] {w.name}: {n_layers} layer caches")
+    identity = w.sink == 0 and len(w.retrieval) == w.num_kv_heads and w.num_kv_heads == 1
+    table_h, nblocks = synth.block_table(w, identity=identity)
+    table = torch.from_numpy(table_h).to(dev)
+    mask = w.retrieval_mask
+    tdt = torch_dtype(torch, w.dtype)
+    layers = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    for _ in range(n_layers):
+        kp = torch.randn((nblocks, w.block_size, w.head_dim), generator=g, device=dev).to(tdt)
+        vp = torch.randn((nblocks, w.head_dim, w.block_size), generator=g, device=dev).to(tdt)
+        layers.append((kp, vp))
+    k_tok = torch.randn((w.batch, 1, w.num_kv_heads, w.head_dim), generator=g, device=dev).to(tdt)
+    v_tok = torch.randn((w.batch, 1, w.num_kv_heads, w.head_dim), generator=g, device=dev).to(tdt)
+    q = torch.randn((w.batch, w.num_q_heads, w.head_dim), generator=g, device=dev).to(tdt)
+    out = torch.empty_like(q)
+    ws = duo.decode_workspace(q, table, w.block_size)
+    after = [torch.from_numpy(np.asarray(x, dtype=np.int32)).to(dev) for x in lens_seq]
+    before = [a - 1 for a in after]
+    lens_tmp = torch.empty_like(after[0])
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kp, vp = layers[i % n_layers]
+        j = i % len(after)
+        duo.kv_append_circular(kp, vp, table, k_tok, v_tok, before[j], lens_tmp, mask, w.sink,
+                               w.recent, w.ring_blocks)
+        if ev is not None:
+            ev[0].record()
+        duo.duo_attn_decode(q, kp, vp, table, after[j], mask, w.sink, w.recent, w.ring_blocks,
+                            w.scale, out, ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(min(args.warmup, steps)):
+        step(i)
+    torch.cuda.synchronize()
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in range(0, steps, EVENT_EVERY // 2)}
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs.get(i))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / steps
+    kern = {i: a.elapsed_time(b) * 1e-3 for i, (a, b) in evs.items()}
+    kern_s = float(np.mean(list(kern.values())))
+    nbytes = float(np.mean([decode_bytes(w, lens_seq[i % len(lens_seq)]) for i in kern]))
+    res = {"workload": w.name, "value": round(nbytes / step_s / 1e9, 1), "unit": "GB/s",
+           "us_per_step": round(step_s * 1e6, 2), "steps": steps,
+           "step": "kv_append_circular(1 token/seq) + duo_attn_decode",
+           "algorithmic_bytes_per_launch": int(nbytes),
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / kern_s / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": f"duo::decode_kernel<{synth.DTYPE_NAMES[w.dtype]},{w.head_dim}>",
+                        "kernel_us": round(kern_s * 1e6, 2)}}
+    log(f"[{tag}] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
+        f"{nbytes / kern_s / 1e9:.0f} GB/s kernel ({nbytes / 1e6:.1f} MB per launch)")
+    return res
+
+
+def gemma_leg(args, torch, duo):
+    """Gemma-2b static-cache decode: batch 16, MQA, D 256, fp16, valid lengths U[1024, 8192]."""
+    w = synth.gemma_2b_static_decode()
+    lens = synth.valid_lengths(w, 1024, 8192)
+    return decode_shape_leg(args, torch, duo, w, [lens], 4, args.steps, "gemma")
+
+
+def long_context_leg(args, torch, duo):
+    """1M-token decode: batch 1, Llama-3-8B GQA shape; step k appends one token and attends over
+    1,048,576 + k positions (k = 1..64)."""
+    w = synth.long_context_decode()
+    seq = [np.array([w.context + k]) for k in range(1, w.steps + 1)]
+    return decode_shape_leg(args, torch, duo, w, seq, 2, w.steps, "1m")
+
+
 def decode_int8_leg(args, torch, duo, dec):
     """The decode workload over the int8 cache, on the bf16 leg's K/V bits (quantized by the
     library's own append)."""
@@ -574,7 +661,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="decode caches rotated across steps")
     ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=1)
-    ap.add_argument("--legs", default="decode,decode_int8,prefill,dca")
+    ap.add_argument("--legs", default="decode,decode_int8,prefill,dca,gemma,1m")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -607,6 +694,8 @@ def main():
     dq = decode_int8_leg(args, torch, duo, dec) if "decode_int8" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
     dca = dca_leg(args, torch, duo) if "dca" in legs else None
+    gem = gemma_leg(args, torch, duo) if "gemma" in legs else None
+    lng = long_context_leg(args, torch, duo) if "1m" in legs else None
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
     gc.enable()
@@ -634,6 +723,8 @@ def main():
         "prefill": pre,
         "decode_int8": dq,
         "dca_prefill": dca,
+        "decode_gemma_2b_static": gem,
+        "decode_1m_context": lng,
     }
     print(json.dumps(line), flush=True)
 

@@ -62,12 +62,14 @@ int32_t check_stream_geometry(int32_t n_str, int32_t sink, int32_t recent, int32
   return DUO_OK;
 }
 
+// rows: (sequence, retrieval kv head) pairs the split is sized for. The workspace-size query passes
+// batch (one retrieval head per sequence: the smallest split and the most partials any mask needs).
 int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbph,
-                    int32_t bs, int32_t split_req, int32_t* split_tokens, int32_t* n_split,
-                    size_t* ws_bytes) {
+                    int32_t bs, int32_t rows, int32_t split_req, int32_t* split_tokens,
+                    int32_t* n_split, size_t* ws_bytes) {
   if (split_req < 0 || (split_req % 128) != 0) return DUO_ERR_INVALID_ARG;
   const int32_t cap = mbph * bs;
-  const int32_t S = decode_split_tokens(batch, hkv, cap, split_req);
+  const int32_t S = decode_split_tokens(rows, cap, split_req);
   const int32_t ns = (cap + S - 1) / S;
   const int32_t G = hq / hkv;
   *split_tokens = S;
@@ -211,7 +213,7 @@ size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_
   int32_t S, ns;
   size_t bytes;
   if (decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
-                  split_tokens, &S, &ns, &bytes) != DUO_OK)
+                  batch, split_tokens, &S, &ns, &bytes) != DUO_OK)
     return 0;
   return bytes;
 }
@@ -254,7 +256,7 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
   int32_t S, ns;
   size_t need;
   st = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
-                   split_tokens, &S, &ns, &need);
+                   batch * (n_ret > 0 ? n_ret : 1), split_tokens, &S, &ns, &need);
   if (st != DUO_OK) return st;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return DUO_ERR_WORKSPACE;
   const int64_t grid = (int64_t)batch * n_ret * ns + (int64_t)batch * n_str;

@@ -50,6 +50,17 @@ namespace {
 // eight waves' merge buffers would not fit in LDS next to a second workgroup.
 template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
 
+// Split merge: up to kFastMergeSplits splits per (sequence, kv head) take the two-phase merge
+// (weights in LDS, then the partial outputs with kMergeLoads 8-byte loads in flight per thread).
+constexpr int kFastMergeSplits = 256;
+constexpr int kMergeLoads = 32;
+
+// Two consecutive floats (8-byte aligned) read at device coherence, as the single floats are.
+__device__ __forceinline__ uint64_t load_coherent_pair(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The decode body. Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
 // (k_scale, v_scale [num_blocks][block_size]); a score is (codes . q) * k_scale of its key, and a
 // key's weight enters PV as p * v_scale of the key (the row sum l takes p itself).
@@ -151,6 +162,11 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     int32_t cq = 0;
     int q_kind = 0;
     float sl2 = p.scale_log2;
+    // the three query bases as values (selecting among the parameter fields themselves would take
+    // their addresses and copy the parameter block to scratch)
+    const void* const q_intra = p.q;
+    const void* const q_succ = p.q_succ;
+    const void* const q_inter = p.q_inter;
     if constexpr (DCA) {
       cq = (L - 1) / p.chunk_len;
       sl2 *= p.mscale[b];
@@ -248,7 +264,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
           const int need = ck == cq ? 0 : ck == cq - 1 ? 1 : 2;
           if (need != q_kind) {
             q_kind = need;
-            const void* base = need == 0 ? p.q : need == 1 ? p.q_succ : p.q_inter;
+            const void* base = need == 0 ? q_intra : need == 1 ? q_succ : q_inter;
             const T* qrow = static_cast<const T*>(base) + ((int64_t)b * p.num_q_heads + h * G + col) * D;
 #pragma unroll
             for (int c = 0; c < KC; ++c) qT[c] = (col < G) ? load8(qrow + c * 32 + quad * 8) : zero8<T>();
@@ -411,37 +427,120 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sm_ticket != p.n_split - 1) return;
-  // One pass over the partials, online: a chunk of kMergeChunk splits is loaded at once (one
-  // round trip per chunk), then folded into the running (M, num, den) of each (q head, channel).
-  constexpr int kMergeChunk = 16;
   const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
   const float* base = p.partial + (((int64_t)b * p.num_kv_heads + h) * p.n_split) * G * (D + 2);
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx % D;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < n_act; s0 += kMergeChunk) {
-      float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
+  T* const obase = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G) * D;
+  if (n_act <= kFastMergeSplits) {
+    // (1) Per q head g, one wave folds the splits' (m, l) into the merged max and denominator and
+    // leaves each split's normalised weight in LDS (the wave buffers are free by now).
+    float* sm_w = &sm_o[0][0][0];   // [n_act][G]
+    constexpr int kR = kFastMergeSplits / kWave;
+    for (int g = wave; g < G; g += kDecodeWaves) {
+      float mv[kR], lv[kR];
+      float M = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kMergeChunk; ++i) {
-        const float* rec = base + (int64_t)(min(s0 + i, n_act - 1) * G + g) * (D + 2);
-        mv[i] = load_coherent(rec + D);
-        lv[i] = load_coherent(rec + D + 1);
-        ov[i] = load_coherent(rec + d);
+      for (int i = 0; i < kR; ++i) {
+        const int sp = lane + i * kWave;
+        const float* rec = base + (int64_t)(min(sp, n_act - 1) * G + g) * (D + 2);
+        mv[i] = sp < n_act ? load_coherent(rec + D) : -INFINITY;
+        lv[i] = sp < n_act ? load_coherent(rec + D + 1) : 0.f;
+        M = fmaxf(M, mv[i]);
       }
 #pragma unroll
-      for (int i = 0; i < kMergeChunk; ++i) {
-        if (s0 + i < n_act) {
-          const float mn = fmaxf(M, mv[i]);
-          const float keep = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
-          const float c = fast_exp2(mv[i] - mn);
-          num = num * keep + c * ov[i];
-          den = den * keep + c * lv[i];
-          M = mn;
-        }
+      for (int o = kWave / 2; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float den = 0.f;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) den += (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * lv[i];
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) den += shfl_xor(den, o);
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int sp = lane + i * kWave;
+        if (sp < n_act) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
       }
     }
-    T* o = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G + g) * D;
-    o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+    __syncthreads();
+    // (2) out[g][d] = sum_s w[s][g] O_s[g][d]: two channels per 8-byte load, and every thread keeps
+    // kMergeLoads loads in flight across its outputs and the splits, so the partials come back in
+    // few round trips.
+    const int pairs = G * D / 2;
+    auto fold = [&](auto KP) {
+      constexpr int kP = decltype(KP)::value;        // channel pairs per thread
+      constexpr int kCS = kMergeLoads / kP;          // splits per round
+      float acc0[kP], acc1[kP];
+      int gk[kP];
+      int64_t off[kP];
+#pragma unroll
+      for (int k = 0; k < kP; ++k) {
+        const int pr = min(tid + k * kThreads, pairs - 1);
+        gk[k] = pr / (D / 2);
+        off[k] = (int64_t)gk[k] * (D + 2) + (pr % (D / 2)) * 2;
+        acc0[k] = acc1[k] = 0.f;
+      }
+      for (int s0 = 0; s0 < n_act; s0 += kCS) {
+        uint64_t v[kP][kCS];
+#pragma unroll
+        for (int k = 0; k < kP; ++k)
+#pragma unroll
+          for (int i = 0; i < kCS; ++i)
+            v[k][i] = load_coherent_pair(base + (int64_t)min(s0 + i, n_act - 1) * G * (D + 2) + off[k]);
+#pragma unroll
+        for (int k = 0; k < kP; ++k)
+#pragma unroll
+          for (int i = 0; i < kCS; ++i) {
+            const float wgt = (s0 + i < n_act) ? sm_w[(s0 + i) * G + gk[k]] : 0.f;
+            acc0[k] += wgt * __uint_as_float((uint32_t)v[k][i]);
+            acc1[k] += wgt * __uint_as_float((uint32_t)(v[k][i] >> 32));
+          }
+      }
+#pragma unroll
+      for (int k = 0; k < kP; ++k) {
+        const int pr = tid + k * kThreads;
+        if (pr < pairs) {
+          const int d = (pr % (D / 2)) * 2;
+          obase[gk[k] * D + d] = from_f32<T>(acc0[k]);
+          obase[gk[k] * D + d + 1] = from_f32<T>(acc1[k]);
+        }
+      }
+    };
+    const int ppt = (pairs + kThreads - 1) / kThreads;
+    if (ppt <= 1) fold(std::integral_constant<int, 1>{});
+    else if (ppt <= 2) fold(std::integral_constant<int, 2>{});
+    else if (ppt <= 4) fold(std::integral_constant<int, 4>{});
+    else fold(std::integral_constant<int, 8>{});
+  } else {
+    // Many splits (a small split_tokens on a long context): one pass over the partials, online;
+    // a chunk of kMergeChunk splits is loaded at once, then folded into the running (M, num, den)
+    // of each (q head, channel).
+    constexpr int kMergeChunk = 16;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, d = idx % D;
+      float M = -INFINITY, num = 0.f, den = 0.f;
+      for (int s0 = 0; s0 < n_act; s0 += kMergeChunk) {
+        float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+          const float* rec = base + (int64_t)(min(s0 + i, n_act - 1) * G + g) * (D + 2);
+          mv[i] = load_coherent(rec + D);
+          lv[i] = load_coherent(rec + D + 1);
+          ov[i] = load_coherent(rec + d);
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+          if (s0 + i < n_act) {
+            const float mn = fmaxf(M, mv[i]);
+            const float keep = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
+            const float c = fast_exp2(mv[i] - mn);
+            num = num * keep + c * ov[i];
+            den = den * keep + c * lv[i];
+            M = mn;
+          }
+        }
+      }
+      obase[g * D + d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+    }
   }
   if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -508,16 +607,16 @@ hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int
   return hipGetLastError();
 }
 
-int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
-                            int32_t requested) {
+int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested) {
   if (requested > 0) return requested;
-  // About 512 work items if every kv head were a retrieval head (so about one workgroup per CU at
-  // the usual mixes: fewer, longer items amortise each item's start-up round trips), but at most 64
-  // splits per (sequence, kv head), which keeps the fused merge at the tail short. Between 256 and
-  // 65536 keys per item.
-  const int64_t total = (int64_t)batch * num_kv_heads * capacity_tokens;
+  // rows = (sequence, retrieval kv head) pairs. About one retrieval item per CU (256 on MI355X)
+  // at full capacity; but no item longer than 8192 keys (one long item per CU streams slower than
+  // two shorter ones that the dispatcher balances), and at most kFastMergeSplits splits per row, so
+  // that the fused merge takes its fast path. Between 256 and 65536 keys per item.
+  const int64_t r = rows > 0 ? rows : 1;
+  auto n_split = [&](int64_t s) { return (capacity_tokens + s - 1) / s; };
   int64_t s = 256;
-  while (s < 65536 && (s * 512 < total || capacity_tokens > 64 * s)) s *= 2;
+  while (s < 65536 && ((s < 8192 && r * n_split(s) > 256) || n_split(s) > kFastMergeSplits)) s *= 2;
   return (int32_t)s;
 }
 

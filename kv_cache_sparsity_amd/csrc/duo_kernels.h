@@ -96,9 +96,9 @@ hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, i
                               hipStream_t stream);
 constexpr int kPrefillKeyTile = 64;   // keys per prefill K/V tile (Dual Chunk lengths are multiples)
 
-// Decode planning shared by the workspace-size query and the call.
-int32_t decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t capacity_tokens,
-                            int32_t requested);
+// Decode split size (keys per retrieval item) from static sizes: rows = batch x retrieval kv heads.
+// Shared by the workspace-size query and the call.
+int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested);
 // Prefill workgroup shape: eight waves (two per SIMD, 32 query rows each) while one 64-key K+V tile
 // takes at most 32 KiB, so that four tile stages fit in LDS; four waves otherwise.
 constexpr int prefill_waves(int elem_bytes, int head_dim) {
