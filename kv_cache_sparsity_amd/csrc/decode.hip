@@ -441,7 +441,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
       for (int i = 0; i < kR; ++i) {
         const int sp = lane + i * kWave;
-        const float* rec = base + (int64_t)(min(sp, n_act - 1) * G + g) * (D + 2);
+        const float* rec = base + (int64_t)(max(min(sp, n_act - 1), 0) * G + g) * (D + 2);
         mv[i] = sp < n_act ? load_coherent(rec + D) : -INFINITY;
         lv[i] = sp < n_act ? load_coherent(rec + D + 1) : 0.f;
         M = fmaxf(M, mv[i]);
