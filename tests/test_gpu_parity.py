@@ -172,6 +172,24 @@ def test_decode_split_count_invariance(split):
     check_close(got, want, w.dtype, f"split={split}")
 
 
+@pytest.mark.parametrize("L", [32768, 32769, 40000])
+def test_decode_merge_at_and_past_256_splits(L):
+    """128-key splits: 256 live splits take the two-phase merge (weights in LDS), 257 and more the
+    one-pass online merge."""
+    say(f"decode 128-key splits, L={L}")
+    w = synth.small(f"many-splits-{L}", batch=1, q_heads=8, kv_heads=2, head_dim=128,
+                    dtype=synth.BF16, block_size=16, sink=4, recent=64, retrieval=(1,), context=L,
+                    seed=33)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, L, synth.S_K)
+    V = logical_kv(w, L, synth.S_V)
+    cache.append_logical(K, V, 0, L)
+    q = q_decode(w, 0)
+    got = to_host_f64(cache.decode(q, split_tokens=128), w.dtype)
+    want = oracle_decode(w, q, K, V, np.array([L]), cache.mask)
+    check_close(got, want, w.dtype, f"L={L} split=128")
+
+
 def test_decode_is_deterministic_and_workspace_reusable():
     case = DECODE_CASES[0]
     w, cache, K, V, q = _decode_case(case)
