@@ -9,7 +9,7 @@
 // the fp32 scale). Partial results over disjoint key ranges are merged through their log-sum-exp
 // (same review thread).
 //
-// Work decomposition. One workgroup (4 waves) = one work item:
+// Work decomposition. One workgroup (eight waves up to D = 128, four at D = 256) = one work item:
 //   retrieval head: (b, h, split s) over keys [s*S, (s+1)*S), S = split_tokens;
 //   streaming head: (b, h) over its sink runs and the ring runs that meet the recent window.
 // The grid comes from static capacities only (no host read of the lengths); items past the valid
@@ -29,7 +29,9 @@
 //
 // Split merge: each retrieval item writes (m, l, O) for its G q heads to the workspace, then takes a
 // ticket on the (b, h) counter; the last item merges the partials, writes the output and resets the
-// counter to zero for the next call.
+// counter to zero for the next call. Up to 256 splits it merges in two phases (per q head the
+// merged max, denominator and each split's weight, then the weighted partial outputs with many
+// loads in flight), since each of its loads is a round trip to another XCD's writes.
 //
 // Dual Chunk Attention (vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models": the paged
 // decode beside the prefill; review thread on the query swap and on mscale): every kv head is a full
