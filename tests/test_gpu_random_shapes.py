@@ -1,0 +1,99 @@
+"""GPU parity on seeded random shapes: decode and prefill against the CPU oracle.
+
+Each case draws a dtype, head dim, kv-head count, GQA group, page size, sink and recent sizes, a
+retrieval mask, per-sequence lengths and (for prefill) a chunk length, all within the documented
+limits of the calls, fills the cache one sequence at a time through kv_append_circular and compares
+every output row with the oracle. Bars as everywhere: 1e-4 (fp32), 2e-2 (fp16 / bf16).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_sparsity_amd as duo
+import oracle
+import synth
+from tests.gpu_harness import (Cache, check_close, logical_kv, oracle_decode, q_decode, q_prefill,
+                               say, to_dev, to_host_f64)
+
+N_CASES = 36
+
+
+@pytest.fixture(scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(duo.LIB_PATH):
+        pytest.fail("libduoattn.so is not built; the GPU tests need the HIP library")
+
+
+def draw_case(i: int) -> dict:
+    """The i-th seeded case (host-only; also usable without a GPU)."""
+    rng = np.random.default_rng([2024, i])
+    dtype = (synth.F32, synth.F16, synth.BF16)[rng.integers(3)]
+    D = (64, 128, 256)[rng.integers(3)]
+    if dtype == synth.F32 and D == 256:
+        D = 128                                  # fp32 prefill is limited to D <= 128
+    kv = int(rng.integers(1, 4))
+    return dict(dtype=dtype, D=D, kv=kv, G=(1, 2, 4, 8)[rng.integers(4)],
+                bs=(16, 32, 64)[rng.integers(3)], sink=int(rng.integers(0, 40)),
+                recent=int(rng.integers(1, 200)),
+                ret=tuple(h for h in range(kv) if rng.random() < 0.5),
+                lens=[int(x) for x in rng.integers(1, 1500, int(rng.integers(1, 4)))],
+                mode="decode" if rng.random() < 0.5 else "prefill", rng=rng)
+
+
+def test_cases_are_valid_calls():
+    """Host check: every drawn case fits the cache it builds (ring and row capacity)."""
+    for i in range(N_CASES):
+        c = draw_case(i)
+        q_len = 1 if c["mode"] == "decode" else int(c["rng"].integers(1, min(min(c["lens"]), 400) + 1))
+        w = synth.small("x", batch=len(c["lens"]), q_heads=c["kv"] * c["G"], kv_heads=c["kv"],
+                        head_dim=c["D"], dtype=c["dtype"], block_size=c["bs"], sink=c["sink"],
+                        recent=c["recent"], retrieval=c["ret"], context=max(c["lens"]),
+                        q_len=q_len)
+        assert w.ring_blocks * c["bs"] >= c["recent"] + q_len - 1
+        assert w.max_blocks_per_head * c["bs"] >= max(c["lens"])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape_parity(i, _need_gpu):
+    c = draw_case(i)
+    lens = np.asarray(c["lens"])
+    q_len = 1 if c["mode"] == "decode" else int(c["rng"].integers(1, min(lens.min(), 400) + 1))
+    name = (f"{i}: {c['mode']} dtype {c['dtype']} D {c['D']} kv {c['kv']} G {c['G']} bs {c['bs']} "
+            f"sink {c['sink']} recent {c['recent']} ret {c['ret']} lens {c['lens']} q_len {q_len}")
+    say(name)
+    B, dtype = len(lens), c["dtype"]
+    w = synth.small(f"rand{i}", batch=B, q_heads=c["kv"] * c["G"], kv_heads=c["kv"],
+                    head_dim=c["D"], dtype=dtype, block_size=c["bs"], sink=c["sink"],
+                    recent=c["recent"], retrieval=c["ret"], context=int(lens.max()), q_len=q_len,
+                    seed=100 + i)
+    cache = Cache(w, fill="nan")
+    Lm = int(lens.max())
+    K = logical_kv(w, Lm, synth.S_K)
+    V = logical_kv(w, Lm, synth.S_V)
+    final = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for b in range(B):
+        L = int(lens[b])
+        kn = np.ascontiguousarray(K[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(V[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        before = torch.zeros(1, dtype=torch.int32, device="cuda")
+        after = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, cache.table[b:b + 1],
+                               to_dev(kn, dtype), to_dev(vn, dtype), before, after, cache.mask,
+                               w.sink, w.recent, w.ring_blocks)
+        final[b] = after[0]
+    cache.lens = final
+    if c["mode"] == "decode":
+        q = q_decode(w, 0)
+        got = to_host_f64(cache.decode(q), dtype)
+        want = oracle_decode(w, q, K, V, lens, cache.mask)
+    else:
+        q = q_prefill(w, 0, q_len)
+        got = to_host_f64(cache.prefill(q), dtype)
+        want = oracle.attend(q, K, V, lens, cache.mask, sink=w.sink, recent=w.recent,
+                             scale=w.scale, dtype=dtype)
+    check_close(got, want, dtype, name)
