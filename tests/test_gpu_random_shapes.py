@@ -1,4 +1,5 @@
-"""GPU parity on seeded random shapes: decode and prefill against the CPU oracle.
+"""GPU parity on seeded random shapes: decode, prefill, the int8 decode and Dual Chunk Attention
+against the CPU oracle.
 
 Each case draws a dtype, head dim, kv-head count, GQA group, page size, sink and recent sizes, a
 retrieval mask, per-sequence lengths and (for prefill) a chunk length, all within the documented
@@ -96,4 +97,106 @@ def test_random_shape_parity(i, _need_gpu):
         got = to_host_f64(cache.prefill(q), dtype)
         want = oracle.attend(q, K, V, lens, cache.mask, sink=w.sink, recent=w.recent,
                              scale=w.scale, dtype=dtype)
+    check_close(got, want, dtype, name)
+
+
+# ------------------------------------------------------------------------------------------------
+# the int8 cache and Dual Chunk Attention on seeded random shapes
+# ------------------------------------------------------------------------------------------------
+N_INT8 = 12
+N_DCA = 12
+
+
+def _fill(cache_append, K, V, lens, table):
+    """Fill sequence b with positions [0, lens[b]) through batch-1 appends on table row slices."""
+    final = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    for b, L in enumerate(lens):
+        kn = np.ascontiguousarray(K[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        vn = np.ascontiguousarray(V[b:b + 1, :, :L].transpose(0, 2, 1, 3))
+        before = torch.zeros(1, dtype=torch.int32, device="cuda")
+        final[b] = cache_append(kn, vn, table[b:b + 1], before)[0]
+    return final
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_INT8))
+def test_random_shape_int8_decode_parity(i, _need_gpu):
+    from tests.test_gpu_int8 import Int8Cache, _logical_codes
+    rng = np.random.default_rng([2025, i])
+    dtype = (synth.F32, synth.F16, synth.BF16)[rng.integers(3)]
+    D = (64, 128, 256)[rng.integers(3)]
+    kv = int(rng.integers(1, 4))
+    G = (1, 2, 4, 8)[rng.integers(4)]
+    bs = (16, 32, 64)[rng.integers(3)]
+    sink, recent = int(rng.integers(0, 40)), int(rng.integers(1, 200))
+    ret = tuple(h for h in range(kv) if rng.random() < 0.5)
+    lens = [int(x) for x in rng.integers(1, 1500, int(rng.integers(1, 4)))]
+    split = (0, 128, 256)[rng.integers(3)]
+    name = (f"int8 {i}: dtype {dtype} D {D} kv {kv} G {G} bs {bs} sink {sink} recent {recent} "
+            f"ret {ret} lens {lens} split {split}")
+    say(name)
+    w = synth.small(f"rand8-{i}", batch=len(lens), q_heads=kv * G, kv_heads=kv, head_dim=D,
+                    dtype=dtype, block_size=bs, sink=sink, recent=recent, retrieval=ret,
+                    context=max(lens), q_len=1, seed=300 + i)
+    cache = Int8Cache(w)
+    K = logical_kv(w, max(lens), synth.S_K)
+    V = logical_kv(w, max(lens), synth.S_V)
+    cache.lens = _fill(lambda kn, vn, t, bf: cache.append(kn, vn, table=t, before=bf), K, V, lens,
+                       cache.table)
+    kc, ks, vc, vs = _logical_codes(K, V, dtype)
+    q = q_decode(w, 0)
+    want = oracle.attend_int8(q[:, None], kc, ks, vc, vs, np.asarray(lens), cache.mask,
+                              sink=sink, recent=recent, scale=w.scale, dtype=dtype)[:, 0]
+    got = to_host_f64(cache.decode(q, split_tokens=split), dtype)
+    check_close(got, want, dtype, name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_DCA))
+def test_random_shape_dca_parity(i, _need_gpu):
+    rng = np.random.default_rng([2026, i])
+    dtype = (synth.F16, synth.BF16)[rng.integers(2)]
+    D = (64, 128)[rng.integers(2)]
+    kv = int(rng.integers(1, 4))
+    G = (1, 2, 4, 8)[rng.integers(4)]
+    bs = (16, 32, 64)[rng.integers(3)]
+    chunk_len = (64, 128, 192, 256, 512)[rng.integers(5)]
+    lens = [int(x) for x in rng.integers(1, 1500, int(rng.integers(1, 4)))]
+    decode = rng.random() < 0.4
+    q_len = 1 if decode else int(rng.integers(1, min(lens) + 1))
+    name = (f"dca {i}: {'decode' if decode else 'prefill'} dtype {dtype} D {D} kv {kv} G {G} "
+            f"bs {bs} chunk {chunk_len} lens {lens} q_len {q_len}")
+    say(name)
+    w = synth.small(f"randdca-{i}", batch=len(lens), q_heads=kv * G, kv_heads=kv, head_dim=D,
+                    dtype=dtype, block_size=bs, sink=0, recent=1, retrieval=tuple(range(kv)),
+                    context=max(lens), q_len=q_len, seed=400 + i)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, max(lens), synth.S_K)
+    V = logical_kv(w, max(lens), synth.S_V)
+
+    def app(kn, vn, t, before):
+        after = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, t, to_dev(kn, dtype), to_dev(vn, dtype),
+                               before, after, cache.mask, w.sink, w.recent, w.ring_blocks)
+        return after
+    cache.lens = _fill(app, K, V, lens, cache.table)
+    qs = [synth.f32_to_storage(synth.queries(w, k, q_len=q_len), dtype) for k in range(3)]
+    ms = synth.row_scales(w, 0, q_len)
+    want = oracle.attend_dca(*qs, K, V, np.asarray(lens), ms, chunk_len=chunk_len, scale=w.scale,
+                             dtype=dtype)
+    qd = [to_dev(x, dtype) for x in qs]
+    if decode:
+        qd = [x[:, 0].contiguous() for x in qd]
+        out = torch.empty_like(qd[0])
+        ws = duo.decode_workspace(qd[0], cache.table, bs)
+        duo.dca_attn_decode(*qd, torch.from_numpy(ms[:, 0].copy()).cuda(), chunk_len, cache.k_pool,
+                            cache.v_pool, cache.table, cache.lens, w.scale, out, ws)
+        got = to_host_f64(out, dtype)
+        want = want[:, 0]
+    else:
+        out = torch.empty_like(qd[0])
+        ws = duo.dca_prefill_workspace(qd[0], cache.table)
+        duo.dca_attn_prefill(*qd, torch.from_numpy(ms).cuda(), chunk_len, cache.k_pool,
+                             cache.v_pool, cache.table, cache.lens, w.scale, out, ws)
+        got = to_host_f64(out, dtype)
     check_close(got, want, dtype, name)
