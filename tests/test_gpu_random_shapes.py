@@ -200,3 +200,59 @@ def test_random_shape_dca_parity(i, _need_gpu):
                              cache.v_pool, cache.table, cache.lens, w.scale, out, ws)
         got = to_host_f64(out, dtype)
     check_close(got, want, dtype, name)
+
+
+N_VARLEN = 8
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_VARLEN))
+def test_random_shape_varlen_prefill_parity(i, _need_gpu):
+    """Packed batches: every sequence brings 0..len rows (a chunk, a single decode row or none)."""
+    rng = np.random.default_rng([2027, i])
+    dtype = (synth.F32, synth.F16, synth.BF16)[rng.integers(3)]
+    D = (64, 128)[rng.integers(2)] if dtype == synth.F32 else (64, 128, 256)[rng.integers(3)]
+    kv = int(rng.integers(1, 4))
+    G = (1, 2, 4)[rng.integers(3)]
+    bs = (16, 32, 64)[rng.integers(3)]
+    sink, recent = int(rng.integers(0, 30)), int(rng.integers(1, 150))
+    ret = tuple(h for h in range(kv) if rng.random() < 0.5)
+    B = int(rng.integers(2, 5))
+    lens = [int(x) for x in rng.integers(1, 1200, B)]
+    rows = [int(rng.choice([0, 1, int(rng.integers(1, min(L, 300) + 1))])) for L in lens]
+    rows = [min(r, L) for r, L in zip(rows, lens)]
+    if sum(rows) == 0:
+        rows[0] = 1
+    max_q = max(rows)
+    name = (f"varlen {i}: dtype {dtype} D {D} kv {kv} G {G} bs {bs} sink {sink} recent {recent} "
+            f"ret {ret} lens {lens} rows {rows}")
+    say(name)
+    w = synth.small(f"randvl-{i}", batch=B, q_heads=kv * G, kv_heads=kv, head_dim=D, dtype=dtype,
+                    block_size=bs, sink=sink, recent=recent, retrieval=ret, context=max(lens),
+                    q_len=max_q, seed=500 + i)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, max(lens), synth.S_K)
+    V = logical_kv(w, max(lens), synth.S_V)
+
+    def app(kn, vn, t, before):
+        after = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, t, to_dev(kn, dtype), to_dev(vn, dtype),
+                               before, after, cache.mask, w.sink, w.recent, w.ring_blocks)
+        return after
+    cache.lens = _fill(app, K, V, lens, cache.table)
+    qs = [q_prefill(w, b, n)[b:b + 1] for b, n in enumerate(rows)]
+    packed = np.concatenate([q[0] for q in qs], axis=0)
+    q_start = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    qd = to_dev(packed, dtype)
+    out = torch.full_like(qd, float("nan"))
+    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, max_q, B)
+    duo.duo_attn_prefill_varlen(qd, cache.k_pool, cache.v_pool, cache.table, cache.lens,
+                                torch.from_numpy(q_start).cuda(), max_q, cache.mask, w.sink,
+                                w.recent, w.ring_blocks, w.scale, out, ws)
+    got = to_host_f64(out, dtype)
+    for b, n in enumerate(rows):
+        if n == 0:
+            continue
+        want = oracle.attend(qs[b], K[b:b + 1], V[b:b + 1], np.asarray(lens[b:b + 1]), cache.mask,
+                             sink=w.sink, recent=w.recent, scale=w.scale, dtype=dtype)[0]
+        check_close(got[q_start[b]:q_start[b + 1]], want, dtype, f"{name} sequence {b}")
