@@ -121,6 +121,15 @@ def prefill_flops(w: synth.Workload, L: int, q_len: int) -> int:
 
 
 # ---- device helpers --------------------------------------------------------------------------
+def event_pair(torch):
+    """Two timing events, recorded once so that they exist, to hand to duo.profile_next_launch:
+    the library's next attention launch records them at its kernel's own start and end."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    return a, b
+
+
 def to_dev(torch, arr, dtype, device):
     if dtype == synth.F32:
         return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
@@ -188,19 +197,17 @@ def decode_leg(args, torch, duo):
         duo.kv_append_circular(kp, vp, table, k_tok, v_tok, lens_before, lens, mask, w.sink,
                                w.recent, w.ring_blocks)
         if ev is not None:
-            ev[0].record()
+            duo.profile_next_launch(ev[0], ev[1])
         duo.duo_attn_decode(q, kp, vp, table, lens, mask, w.sink, w.recent, w.ring_blocks,
                             w.scale, out, ws)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # The decode launch is bracketed by HIP events on every EVENT_EVERY-th timed step only: each
-    # event record costs a few microseconds of queue time, which would otherwise inflate the step.
+    # The decode launch of every EVENT_EVERY-th timed step carries HIP events on its dispatch (its
+    # kernel's own start and end); the other steps run without, as a serving loop would.
     sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = {i: event_pair(torch)
            for i in sampled}
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -264,16 +271,14 @@ def decode_shape_leg(args, torch, duo, w, lens_seq, n_layers, steps, tag):
         duo.kv_append_circular(kp, vp, table, k_tok, v_tok, before[j], lens_tmp, mask, w.sink,
                                w.recent, w.ring_blocks)
         if ev is not None:
-            ev[0].record()
+            duo.profile_next_launch(ev[0], ev[1])
         duo.duo_attn_decode(q, kp, vp, table, after[j], mask, w.sink, w.recent, w.ring_blocks,
                             w.scale, out, ws)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(min(args.warmup, steps)):
         step(i)
     torch.cuda.synchronize()
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = {i: event_pair(torch)
            for i in range(0, steps, EVENT_EVERY // 2)}
     t0 = time.perf_counter()
     for i in range(steps):
@@ -360,17 +365,15 @@ def decode_int8_leg(args, torch, duo, dec):
         duo.kv_append_circular_int8(*pools, table, k_tok, v_tok, lens_before, lens, mask, w.sink,
                                     w.recent, w.ring_blocks)
         if ev is not None:
-            ev[0].record()
+            duo.profile_next_launch(ev[0], ev[1])
         duo.duo_attn_decode_int8(q, *pools, table, lens, mask, w.sink, w.recent, w.ring_blocks,
                                  w.scale, out, ws)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = {i: event_pair(torch)
            for i in sampled}
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -432,16 +435,14 @@ def prefill_leg(args, torch, duo):
             duo.kv_append_circular(kp, vp, table, kn, vn, lb, la, mask, w.sink, w.recent,
                                    w.ring_blocks)
             if evs is not None:
-                evs[c][0].record()
+                duo.profile_next_launch(evs[c][0], evs[c][1])
             duo.duo_attn_prefill(q, kp, vp, table, la, mask, w.sink, w.recent, w.ring_blocks,
                                  w.scale, out, ws)
-            if evs is not None:
-                evs[c][1].record()
 
     for _ in range(args.prefill_warmup):
         one_pass()
     torch.cuda.synchronize()
-    all_evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    all_evs = [[event_pair(torch)
                 for _ in chunks] for _ in range(args.prefill_passes)]
     t0 = time.perf_counter()
     for p in range(args.prefill_passes):
@@ -509,12 +510,11 @@ def dca_leg(args, torch, duo):
     for _ in range(args.prefill_warmup):
         duo.dca_attn_prefill(*qs, ms, C, kp, vp, table, lens, w.scale, out, ws)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [event_pair(torch)
            for _ in range(args.prefill_passes)]
     for a, b in evs:
-        a.record()
+        duo.profile_next_launch(a, b)
         duo.dca_attn_prefill(*qs, ms, C, kp, vp, table, lens, w.scale, out, ws)
-        b.record()
     torch.cuda.synchronize()
     t = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in evs]))
     flops = dca_flops(w, L, n)
@@ -527,12 +527,11 @@ def dca_leg(args, torch, duo):
     for _ in range(10):
         duo.dca_attn_decode(*qd, msd, C, kp, vp, table, lens, w.scale, outd, wsd)
     torch.cuda.synchronize()
-    devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    devs = [event_pair(torch)
             for _ in range(50)]
     for a, b in devs:
-        a.record()
+        duo.profile_next_launch(a, b)
         duo.dca_attn_decode(*qd, msd, C, kp, vp, table, lens, w.scale, outd, wsd)
-        b.record()
     torch.cuda.synchronize()
     td = float(np.median([a.elapsed_time(b) * 1e-3 for a, b in devs]))
     dbytes = (2 * w.num_kv_heads * L * w.head_dim * w.elem_bytes

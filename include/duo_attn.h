@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 6
+#define DUO_ATTN_ABI_VERSION 7
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -339,6 +339,17 @@ int32_t dca_attn_decode(const void* q, const void* q_succ, const void* q_inter,
                         int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t dtype, float softmax_scale, void* out, void* workspace,
                         size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/*
+ * duo_profile_next_launch -- a profiling hook for the caller's own timing. The next attention call
+ * (duo_attn_decode, duo_attn_decode_int8, duo_attn_prefill, duo_attn_prefill_varlen,
+ * dca_attn_prefill, dca_attn_decode) made from this host thread launches its kernel with
+ * start_event and stop_event attached to the dispatch itself: the events take the kernel's own
+ * start and end times, without the queue's gap before the dispatch. The events (hipEvent_t, timing
+ * enabled) are created and owned by the caller; either may be NULL. The hook applies to that one
+ * call, which takes it even when it returns an error, and then clears. Always returns DUO_OK.
+ */
+int32_t duo_profile_next_launch(void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static storage). */
 const char* duo_status_string(int32_t status);

@@ -29,7 +29,7 @@ SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_dec
            "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
            "kv_append_circular_int8",
            "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
-           "dca_attn_decode",
+           "dca_attn_decode", "duo_profile_next_launch",
            "duo_status_string", "duo_abi_version")
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.dca_attn_decode.restype = _I32
         L.dca_attn_decode.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32,
                                       _I32, _I32, _I32, _I32, _F, _P, _P, _SZ, _I32, _P]
+        L.duo_profile_next_launch.restype = _I32
+        L.duo_profile_next_launch.argtypes = [_P, _P]
         L.duo_status_string.argtypes = [_I32]
         L.duo_abi_version.restype = _I32
         L.duo_abi_version.argtypes = []
@@ -351,9 +353,25 @@ def dca_attn_decode(q, q_succ, q_inter, mscale, chunk_len: int, k_pool, v_pool, 
     _check("dca_attn_decode", st)
 
 
+def profile_next_launch(start_event=None, stop_event=None) -> None:
+    """The next attention call on this thread records start_event / stop_event at its kernel's
+    own start and end (torch.cuda.Event with timing, already recorded once so that it exists, or a
+    raw hipEvent_t handle)."""
+    def handle(e):
+        if e is None:
+            return None
+        h = int(getattr(e, "cuda_event", e))
+        if h == 0:
+            raise ValueError("the event does not exist yet: record it once first")
+        return h
+    _check("duo_profile_next_launch",
+           lib().duo_profile_next_launch(handle(start_event), handle(stop_event)))
+
+
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
            "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
+           "profile_next_launch",
            "dca_prefill_workspace",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",
            "prefill_workspace", "status_string", "abi_version",

@@ -93,9 +93,31 @@ void prefill_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t n_ret_kv, in
                 (size_t)*ret_items * kPrefillSplits * prefill_partial_floats(eb, head_dim) * sizeof(float);
 }
 
+// The profiling hook: events set by duo_profile_next_launch wait here until the next attention call
+// on this thread takes them; that call's launch sees them through current_launch_events().
+thread_local LaunchEvents t_pending_events{nullptr, nullptr};
+thread_local LaunchEvents t_call_events{nullptr, nullptr};
+struct CallEvents {   // one attention call: take the pending events, drop them when the call returns
+  CallEvents() {
+    t_call_events = t_pending_events;
+    t_pending_events = LaunchEvents{nullptr, nullptr};
+  }
+  ~CallEvents() { t_call_events = LaunchEvents{nullptr, nullptr}; }
+};
+
 }  // namespace
 
+namespace duo {
+LaunchEvents current_launch_events() { return t_call_events; }
+}  // namespace duo
+
 extern "C" {
+
+int32_t duo_profile_next_launch(void* start_event, void* stop_event) {
+  t_pending_events = LaunchEvents{static_cast<hipEvent_t>(start_event),
+                                  static_cast<hipEvent_t>(stop_event)};
+  return DUO_OK;
+}
 
 int32_t duo_abi_version(void) { return DUO_ATTN_ABI_VERSION; }
 
@@ -237,6 +259,7 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
                            int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
                            size_t workspace_bytes, int32_t split_tokens, void* stream,
                            const DcaArgs* dca = nullptr) {
+  const CallEvents events;
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);
@@ -366,6 +389,7 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
                             int32_t recent_size, int32_t ring_blocks, float softmax_scale,
                             void* out, void* workspace, size_t workspace_bytes, void* stream,
                             const DcaArgs* dca = nullptr) {
+  const CallEvents events;
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);

@@ -41,6 +41,8 @@
 // lane of an item shares the query position, so the choice is uniform per step; the Q^T registers
 // are reloaded when it changes, at most twice per item. The scale is softmax_scale times the
 // sequence's fp32 mscale.
+#include <hip/hip_ext.h>
+
 #include "duo_common.h"
 #include "duo_kernels.h"
 
@@ -566,10 +568,20 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_dca_ker
 
 template <typename T, int D>
 void launch_d(const DecodeParams& p, bool int8_cache, int grid, hipStream_t stream) {
+  const LaunchEvents ev = current_launch_events();
   if (int8_cache)
-    hipLaunchKernelGGL((decode_int8_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0, stream, p);
+    hipExtLaunchKernelGGL((decode_int8_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0,
+                          stream, ev.start, ev.stop, 0, p);
   else
-    hipLaunchKernelGGL((decode_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0, stream, p);
+    hipExtLaunchKernelGGL((decode_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0,
+                          stream, ev.start, ev.stop, 0, p);
+}
+
+template <typename T, int D>
+void launch_dca_d(const DecodeParams& p, int grid, hipStream_t stream) {
+  const LaunchEvents ev = current_launch_events();
+  hipExtLaunchKernelGGL((decode_dca_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0,
+                        stream, ev.start, ev.stop, 0, p);
 }
 
 template <typename T>
@@ -598,11 +610,11 @@ hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int
   (void)hipGetLastError();
   if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
   if (head_dim == 64) {
-    if (dtype == 1) hipLaunchKernelGGL((decode_dca_kernel<_Float16, 64>), dim3(grid), dim3(decode_waves<64>() * kWave), 0, stream, p);
-    else hipLaunchKernelGGL((decode_dca_kernel<__bf16, 64>), dim3(grid), dim3(decode_waves<64>() * kWave), 0, stream, p);
+    if (dtype == 1) launch_dca_d<_Float16, 64>(p, grid, stream);
+    else launch_dca_d<__bf16, 64>(p, grid, stream);
   } else if (head_dim == 128) {
-    if (dtype == 1) hipLaunchKernelGGL((decode_dca_kernel<_Float16, 128>), dim3(grid), dim3(decode_waves<128>() * kWave), 0, stream, p);
-    else hipLaunchKernelGGL((decode_dca_kernel<__bf16, 128>), dim3(grid), dim3(decode_waves<128>() * kWave), 0, stream, p);
+    if (dtype == 1) launch_dca_d<_Float16, 128>(p, grid, stream);
+    else launch_dca_d<__bf16, 128>(p, grid, stream);
   } else {
     return hipErrorInvalidValue;
   }

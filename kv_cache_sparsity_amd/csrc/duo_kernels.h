@@ -83,6 +83,14 @@ struct PrefillParams {
   int32_t chunk_tiles;
 };
 
+// Events the attention kernel launched by the current C-ABI call records at its start and its end
+// (null when the caller set none; see duo_profile_next_launch).
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchEvents current_launch_events();
+
 // Launchers (return the HIP launch status). dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream);
 hipError_t launch_append_int8(const AppendParams& p, hipStream_t stream);

@@ -50,6 +50,8 @@
 // query row of the B operand) picks its vector per tile; a lane reloads its Q^T registers only when
 // its kind changes, at most twice along the ascending walk. The scores scale is softmax_scale times
 // the row's fp32 mscale, applied to the fp32 accumulators.
+#include <hip/hip_ext.h>
+
 #include "duo_common.h"
 #include "duo_kernels.h"
 
@@ -729,8 +731,9 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
 
 template <typename T, int D, bool DCA>
 void launch_d(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<T, D, DCA>), dim3(grid), dim3(TileGeo<T, D>::kThreads), 0,
-                     stream, p);
+  const LaunchEvents ev = current_launch_events();
+  hipExtLaunchKernelGGL((prefill_kernel<T, D, DCA>), dim3(grid), dim3(TileGeo<T, D>::kThreads), 0,
+                        stream, ev.start, ev.stop, 0, p);
 }
 
 template <typename T>

@@ -190,6 +190,26 @@ def test_decode_merge_at_and_past_256_splits(L):
     check_close(got, want, w.dtype, f"L={L} split=128")
 
 
+def test_profile_hook_times_one_kernel_then_clears():
+    """duo_profile_next_launch: the next call's kernel records the events on its dispatch; the call
+    after it leaves them alone."""
+    case = DECODE_CASES[0]
+    w, cache, K, V, q = _decode_case(case)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    duo.profile_next_launch(a, b)
+    got = to_host_f64(cache.decode(q), w.dtype)
+    torch.cuda.synchronize()
+    t1 = a.elapsed_time(b)
+    assert 0.0 < t1 < 100.0, t1
+    cache.decode(q)
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == t1
+    want = oracle_decode(w, q, K, V, np.asarray(case["lens"]), cache.mask)
+    check_close(got, want, w.dtype, "decode with launch events")
+
+
 def test_decode_is_deterministic_and_workspace_reusable():
     case = DECODE_CASES[0]
     w, cache, K, V, q = _decode_case(case)
