@@ -150,6 +150,13 @@ def torch_dtype(torch, dtype):
 
 
 # ---- decode leg ------------------------------------------------------------------------------
+def spread_us(times_s):
+    """Median and 90th percentile of sampled kernel durations (seconds in, microseconds out)."""
+    return {"kernel_us_median": round(float(np.median(times_s)) * 1e6, 2),
+            "kernel_us_p90": round(float(np.percentile(times_s, 90)) * 1e6, 2),
+            "kernel_samples": len(times_s)}
+
+
 def decode_leg(args, torch, duo):
     w = synth.llama3_8b_decode()
     dev = torch.device("cuda:0")
@@ -215,7 +222,8 @@ def decode_leg(args, torch, duo):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs.values()])) * 1e-3
+    kern_all = [a.elapsed_time(b) * 1e-3 for a, b in evs.values()]
+    kern_s = float(np.mean(kern_all))
     nbytes = decode_bytes(w, np.full(w.batch, L))
     traffic = measured_traffic("decode")
     res = {
@@ -226,6 +234,7 @@ def decode_leg(args, torch, duo):
                      "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "duo::decode_kernel<bf16,128>",
                      "kernel_us": round(kern_s * 1e6, 2),
+                     **spread_us(kern_all),
                      "algorithmic_bytes_per_launch": nbytes},
     }
     log(f"[decode] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
@@ -381,7 +390,8 @@ def decode_int8_leg(args, torch, duo, dec):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs.values()])) * 1e-3
+    kern_all = [a.elapsed_time(b) * 1e-3 for a, b in evs.values()]
+    kern_s = float(np.mean(kern_all))
     nbytes = decode_bytes(w, np.full(w.batch, L), int8_cache=True)
     res = {
         "workload": w.name + "-int8-kv", "value": round(nbytes / step_s / 1e9, 1), "unit": "GB/s",
@@ -395,6 +405,7 @@ def decode_int8_leg(args, torch, duo, dec):
                      "traffic": measured_traffic("decode_int8"),
                      "kernel": "duo::decode_int8_kernel<bf16,128>",
                      "kernel_us": round(kern_s * 1e6, 2),
+                     **spread_us(kern_all),
                      "algorithmic_bytes_per_launch": nbytes},
     }
     log(f"[decode-int8] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
