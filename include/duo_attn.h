@@ -106,7 +106,9 @@ int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_tabl
  * sizes (split_tokens as passed to duo_attn_decode; 0 = the library's choice). The library's split
  * size depends on how many kv heads are retrieval heads; this size covers every retrieval/streaming
  * split of the heads. The caller zero-fills the workspace once after allocating it; every completed
- * decode call leaves it ready for the next. Returns 0 for invalid sizes.
+ * decode call leaves it ready for the next. It starts with the merge tickets (one per sequence and kv
+ * head, and one per group of 16 splits where a row has more than 16), at offsets fixed by these
+ * sizes, so one workspace serves calls with any split size or mask. Returns 0 for invalid sizes.
  */
 size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t max_blocks_per_head,

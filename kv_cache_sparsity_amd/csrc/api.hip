@@ -1,5 +1,6 @@
 // C ABI of libduoattn: argument validation, static work planning and kernel launches.
 // Every check runs before any HIP call, so invalid calls return an error without touching a device.
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -62,6 +63,17 @@ int32_t check_stream_geometry(int32_t n_str, int32_t sink, int32_t recent, int32
   return DUO_OK;
 }
 
+// The decode workspace starts with its tickets: one per (sequence, kv head), then one per merge
+// group for as many groups as any split of this capacity can have (splits are >= 128 tokens). The
+// region depends on the shapes only, so a workspace reused with other split sizes or masks still
+// finds every ticket at zero.
+size_t decode_counter_bytes(int32_t batch, int32_t hkv, int32_t cap) {
+  const int32_t most_splits = (int32_t)(((int64_t)cap + 127) / 128);
+  const int32_t groups = most_splits <= kMergeGroup
+                             ? 0 : std::min<int32_t>(kMaxMergeGroups, (most_splits + kMergeGroup - 1) / kMergeGroup);
+  return align256((size_t)batch * hkv * (1 + (size_t)groups) * sizeof(int32_t));
+}
+
 // rows: (sequence, retrieval kv head) pairs the split is sized for. The workspace-size query passes
 // batch (one retrieval head per sequence: the smallest split and the most partials any mask needs).
 int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbph,
@@ -74,8 +86,8 @@ int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, in
   const int32_t G = hq / hkv;
   *split_tokens = S;
   *n_split = ns;
-  *ws_bytes = align256((size_t)batch * hkv * sizeof(int32_t)) +
-              (size_t)batch * hkv * ns * G * (head_dim + 2) * sizeof(float);
+  *ws_bytes = decode_counter_bytes(batch, hkv, cap) +
+              (size_t)batch * hkv * (ns + decode_merge_groups(ns)) * G * (head_dim + 2) * sizeof(float);
   return DUO_OK;
 }
 
@@ -293,8 +305,13 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
   p.seq_lens = seq_lens;
   p.out = out;
   p.counter = static_cast<int32_t*>(workspace);
-  p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align256((size_t)batch * num_kv_heads * sizeof(int32_t)));
+  p.gcounter = p.counter + (size_t)batch * num_kv_heads;
+  p.partial = reinterpret_cast<float*>(
+      static_cast<char*>(workspace) +
+      decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size));
+  p.n_group = decode_merge_groups(ns);
+  p.gpartial = p.partial + (size_t)batch * num_kv_heads * ns * (num_q_heads / num_kv_heads) *
+                               (head_dim + 2);
   p.num_blocks = num_blocks;
   p.log2_bs = log2i(block_size);
   p.max_blocks_per_head = max_blocks_per_head;

@@ -420,24 +420,31 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     return;
   }
 
-  // ---- split merge: the last item of (b, h) to arrive reduces all partials ------------------
+  // ---- split merge ----------------------------------------------------------------------------
   // Partials were written with device-coherent (write-through) stores; waiting for them to
-  // complete before the ticket makes them visible to whichever workgroup, on any XCD, draws the
+  // complete before a ticket makes them visible to whichever workgroup, on any XCD, draws the
   // last ticket, which reads them back with device-coherent loads. No cache-wide write-back or
   // invalidate is needed, so other workgroups' cached K/V lines are left alone.
+  //
+  // Up to kMergeGroup splits per (b, h): the last item to arrive folds all partials into the
+  // output. More (n_group > 0): the last item of each group of kMergeGroup splits folds the
+  // group's partials into one record of the same form (unnormalised O, max, denominator), and the
+  // last group to finish folds the records into the output, so no single workgroup reads more than
+  // kMergeGroup partials per q head.
   wait_stores_complete();
   __syncthreads();
-  int32_t* ctr = p.counter + (int64_t)b * p.num_kv_heads + h;
-  if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (sm_ticket != p.n_split - 1) return;
+  const int64_t row = (int64_t)b * p.num_kv_heads + h;
   const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
-  const float* base = p.partial + (((int64_t)b * p.num_kv_heads + h) * p.n_split) * G * (D + 2);
   T* const obase = static_cast<T*>(p.out) + ((int64_t)b * p.num_q_heads + h * G) * D;
-  if (n_act <= kFastMergeSplits) {
-    // (1) Per q head g, one wave folds the splits' (m, l) into the merged max and denominator and
-    // leaves each split's normalised weight in LDS (the wave buffers are free by now).
-    float* sm_w = &sm_o[0][0][0];   // [n_act][G]
+  const int64_t rec_floats = (int64_t)G * (D + 2);
+
+  // Fold n_in records at src ([n_in][G][D + 2], all complete) into the output (rec == nullptr) or
+  // into the record rec: (1) per q head g, one wave reduces the records' (m, l) into the merged max
+  // and denominator and leaves each record's weight in LDS (the wave buffers are free by now);
+  // (2) out[g][d] = sum_s w[s][g] O_s[g][d], two channels per 8-byte load, each thread keeping
+  // kMergeLoads loads in flight across its outputs and the records.
+  auto fold_records = [&](const float* src, int n_in, float* rec) {
+    float* sm_w = &sm_o[0][0][0];   // [n_in][G]
     constexpr int kR = kFastMergeSplits / kWave;
     for (int g = wave; g < G; g += kDecodeWaves) {
       float mv[kR], lv[kR];
@@ -445,9 +452,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
       for (int i = 0; i < kR; ++i) {
         const int sp = lane + i * kWave;
-        const float* rec = base + (int64_t)(max(min(sp, n_act - 1), 0) * G + g) * (D + 2);
-        mv[i] = sp < n_act ? load_coherent(rec + D) : -INFINITY;
-        lv[i] = sp < n_act ? load_coherent(rec + D + 1) : 0.f;
+        const float* r = src + (int64_t)(max(min(sp, n_in - 1), 0) * G + g) * (D + 2);
+        mv[i] = sp < n_in ? load_coherent(r + D) : -INFINITY;
+        lv[i] = sp < n_in ? load_coherent(r + D + 1) : 0.f;
         M = fmaxf(M, mv[i]);
       }
 #pragma unroll
@@ -458,21 +465,23 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       for (int i = 0; i < kR; ++i) den += (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * lv[i];
 #pragma unroll
       for (int o = kWave / 2; o >= 1; o >>= 1) den += shfl_xor(den, o);
-      const float inv = den > 0.f ? 1.f / den : 0.f;
+      // the output is normalised; a record keeps its max and denominator
+      const float inv = rec ? 1.f : (den > 0.f ? 1.f / den : 0.f);
+      if (rec && lane == 0) {
+        store_coherent(rec + g * (D + 2) + D, M);
+        store_coherent(rec + g * (D + 2) + D + 1, den);
+      }
 #pragma unroll
       for (int i = 0; i < kR; ++i) {
         const int sp = lane + i * kWave;
-        if (sp < n_act) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
+        if (sp < n_in) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
       }
     }
     __syncthreads();
-    // (2) out[g][d] = sum_s w[s][g] O_s[g][d]: two channels per 8-byte load, and every thread keeps
-    // kMergeLoads loads in flight across its outputs and the splits, so the partials come back in
-    // few round trips.
     const int pairs = G * D / 2;
     auto fold = [&](auto KP) {
       constexpr int kP = decltype(KP)::value;        // channel pairs per thread
-      constexpr int kCS = kMergeLoads / kP;          // splits per round
+      constexpr int kCS = kMergeLoads / kP;          // records per round
       float acc0[kP], acc1[kP];
       int gk[kP];
       int64_t off[kP];
@@ -483,18 +492,18 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         off[k] = (int64_t)gk[k] * (D + 2) + (pr % (D / 2)) * 2;
         acc0[k] = acc1[k] = 0.f;
       }
-      for (int s0 = 0; s0 < n_act; s0 += kCS) {
+      for (int s0 = 0; s0 < n_in; s0 += kCS) {
         uint64_t v[kP][kCS];
 #pragma unroll
         for (int k = 0; k < kP; ++k)
 #pragma unroll
           for (int i = 0; i < kCS; ++i)
-            v[k][i] = load_coherent_pair(base + (int64_t)min(s0 + i, n_act - 1) * G * (D + 2) + off[k]);
+            v[k][i] = load_coherent_pair(src + (int64_t)min(s0 + i, n_in - 1) * rec_floats + off[k]);
 #pragma unroll
         for (int k = 0; k < kP; ++k)
 #pragma unroll
           for (int i = 0; i < kCS; ++i) {
-            const float wgt = (s0 + i < n_act) ? sm_w[(s0 + i) * G + gk[k]] : 0.f;
+            const float wgt = (s0 + i < n_in) ? sm_w[(s0 + i) * G + gk[k]] : 0.f;
             acc0[k] += wgt * __uint_as_float((uint32_t)v[k][i]);
             acc1[k] += wgt * __uint_as_float((uint32_t)(v[k][i] >> 32));
           }
@@ -504,8 +513,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         const int pr = tid + k * kThreads;
         if (pr < pairs) {
           const int d = (pr % (D / 2)) * 2;
-          obase[gk[k] * D + d] = from_f32<T>(acc0[k]);
-          obase[gk[k] * D + d + 1] = from_f32<T>(acc1[k]);
+          if (rec) {
+            store_coherent(rec + off[k], acc0[k]);
+            store_coherent(rec + off[k] + 1, acc1[k]);
+          } else {
+            obase[gk[k] * D + d] = from_f32<T>(acc0[k]);
+            obase[gk[k] * D + d + 1] = from_f32<T>(acc1[k]);
+          }
         }
       }
     };
@@ -514,6 +528,38 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     else if (ppt <= 2) fold(std::integral_constant<int, 2>{});
     else if (ppt <= 4) fold(std::integral_constant<int, 4>{});
     else fold(std::integral_constant<int, 8>{});
+  };
+
+  int32_t* ctr = p.counter + row;
+  if (p.n_group > 0) {
+    const int grp = split / kMergeGroup;
+    const int first = grp * kMergeGroup;
+    const int members = min(kMergeGroup, p.n_split - first);
+    int32_t* gctr = p.gcounter + row * p.n_group + grp;
+    if (tid == 0) sm_ticket = __hip_atomic_fetch_add(gctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sm_ticket != members - 1) return;
+    float* rec = p.gpartial + (row * p.n_group + grp) * rec_floats;
+    fold_records(p.partial + (row * p.n_split + first) * rec_floats,
+                 min(max(n_act - first, 0), kMergeGroup), rec);
+    if (tid == 0) __hip_atomic_store(gctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_stores_complete();
+    __syncthreads();
+    if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sm_ticket != p.n_group - 1) return;
+    // records of groups past the valid length hold max -inf and weigh nothing
+    fold_records(p.gpartial + row * p.n_group * rec_floats, (n_act + kMergeGroup - 1) / kMergeGroup,
+                 nullptr);
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sm_ticket != p.n_split - 1) return;
+  const float* base = p.partial + row * p.n_split * rec_floats;
+  if (n_act <= kFastMergeSplits) {
+    fold_records(base, n_act, nullptr);
   } else {
     // Many splits (a small split_tokens on a long context): one pass over the partials, online;
     // a chunk of kMergeChunk splits is loaded at once, then folded into the running (M, num, den)
@@ -624,13 +670,13 @@ hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int
 int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested) {
   if (requested > 0) return requested;
   // rows = (sequence, retrieval kv head) pairs. About one retrieval item per CU (256 on MI355X)
-  // at full capacity; but no item longer than 8192 keys (one long item per CU streams slower than
-  // two shorter ones that the dispatcher balances), and at most kFastMergeSplits splits per row, so
-  // that the fused merge takes its fast path. Between 256 and 65536 keys per item.
+  // at full capacity; but no item longer than 16384 keys (more, shorter items balance better than
+  // one very long one per CU), and at most kFastMergeSplits splits per row, so that the fused merge
+  // takes its fast path. Between 256 and 65536 keys per item.
   const int64_t r = rows > 0 ? rows : 1;
   auto n_split = [&](int64_t s) { return (capacity_tokens + s - 1) / s; };
   int64_t s = 256;
-  while (s < 65536 && ((s < 8192 && r * n_split(s) > 256) || n_split(s) > kFastMergeSplits)) s *= 2;
+  while (s < 65536 && ((s < 16384 && r * n_split(s) > 256) || n_split(s) > kFastMergeSplits)) s *= 2;
   return (int32_t)s;
 }
 

@@ -39,6 +39,9 @@ struct DecodeParams {
   const float* v_scale;   // and of V
   float* partial;     // [batch][num_kv_heads][n_split][group][head_dim + 2]
   int32_t* counter;   // [batch][num_kv_heads]
+  float* gpartial;    // [batch][num_kv_heads][n_group][group][head_dim + 2] (n_group > 0)
+  int32_t* gcounter;  // [batch][num_kv_heads][n_group]
+  int32_t n_group;    // groups of kMergeGroup splits merged first; 0: one-level merge
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t sink, recent, sink_blocks, ring_slots;
@@ -106,6 +109,14 @@ constexpr int kPrefillKeyTile = 64;   // keys per prefill K/V tile (Dual Chunk l
 
 // Decode split size (keys per retrieval item) from static sizes: rows = batch x retrieval kv heads.
 // Shared by the workspace-size query and the call.
+// Decode split merge in two levels when a (sequence, kv head) has more than kMergeGroup splits
+// (and at most kMergeGroup * kMaxMergeGroups): groups of kMergeGroup splits, then the groups.
+constexpr int32_t kMergeGroup = 16;
+constexpr int32_t kMaxMergeGroups = 256;
+inline int32_t decode_merge_groups(int32_t n_split) {
+  return (n_split > kMergeGroup && n_split <= kMergeGroup * kMaxMergeGroups)
+             ? (n_split + kMergeGroup - 1) / kMergeGroup : 0;
+}
 int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested);
 // Prefill workgroup shape: eight waves (two per SIMD, 32 query rows each) while one 64-key K+V tile
 // takes at most 32 KiB, so that four tile stages fit in LDS; four waves otherwise.

@@ -190,6 +190,30 @@ def test_decode_merge_at_and_past_256_splits(L):
     check_close(got, want, w.dtype, f"L={L} split=128")
 
 
+TWO_LEVEL_CASE = dict(name="bf16-d128-g4-two-level-merge", dtype=synth.BF16, head_dim=128, group=4,
+                      kv=2, ret=(0, 1), block_size=16, sink=4, recent=24, ring_blocks=2,
+                      lens=[0, 1, 2047, 2048, 2049, 5120])
+
+
+def test_decode_two_level_merge_ragged_rows_and_workspace_reuse():
+    """More than 16 splits per row merge in two levels (groups of 16 splits, then the groups). With
+    128-key splits over 5120 keys of capacity a row has 40 splits in 3 groups; the ragged lengths
+    leave whole groups empty (length 1, 2047, 2048) or cut one inside (2049), and length 0 leaves
+    every group empty. One workspace serves 128-, 256- and automatic splits in turn, twice, so every
+    ticket must be back at zero after each call."""
+    case = TWO_LEVEL_CASE
+    say(f"decode {case['name']}")
+    w, cache, K, V, q = _decode_case(case)
+    want = oracle_decode(w, q, K, V, np.asarray(case["lens"]), cache.mask)
+    qd = to_dev(q, w.dtype)
+    ws = duo.decode_workspace(qd, cache.table, w.block_size, 128)
+    for rep in range(2):
+        for split in (128, 256, 0):
+            got = to_host_f64(cache.decode(q, split_tokens=split, workspace=ws), w.dtype)
+            check_close(got, want, w.dtype, f"{case['name']} split {split} pass {rep}")
+            assert (got[0] == 0).all()
+
+
 def test_profile_hook_times_one_kernel_then_clears():
     """duo_profile_next_launch: the next call's kernel records the events on its dispatch; the call
     after it leaves them alone."""
