@@ -186,6 +186,22 @@ def test_decode_workspace_size_query():
     assert decode(ws_bytes=L.duo_attn_decode_workspace_size(2, 8, 2, 128, 20, 16, 0) - 1) == WORKSPACE
 
 
+def test_decode_workspace_holds_two_level_merge_records():
+    """Past 16 splits per row the decode merges in two levels: the workspace then holds, beside the
+    tickets, every split's partial and one record per group of 16 splits (G x (D + 2) floats each)."""
+    L = duo.lib()
+    B, hq, hkv, D, mbph, bs = 6, 8, 2, 128, 320, 16          # 5120 keys of capacity
+    G = hq // hkv
+    rec = G * (D + 2) * 4
+    for split, n_split in ((128, 40), (256, 20), (512, 10)):
+        groups = -(-n_split // 16) if n_split > 16 else 0
+        n = L.duo_attn_decode_workspace_size(B, hq, hkv, D, mbph, bs, split)
+        assert n >= B * hkv * (n_split + groups) * rec + B * hkv * 4, (split, n)
+    # the ticket region does not move with the split size: a smaller split only adds partials
+    sizes = [L.duo_attn_decode_workspace_size(B, hq, hkv, D, mbph, bs, s) for s in (128, 256, 512)]
+    assert sizes[0] > sizes[1] > sizes[2]
+
+
 # ---- prefill ---------------------------------------------------------------------------------
 def prefill(**kw):
     a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, table=FAKE, num_blocks=64, bs=16, mbph=20,
