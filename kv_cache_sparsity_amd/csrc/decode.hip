@@ -78,6 +78,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ int sm_ticket;
+  __shared__ int sm_next_step;   // the segment's next unclaimed wave step
   __shared__ int32_t sm_page[kRunSeg + 4];
 
   const int tid = threadIdx.x;
@@ -252,6 +253,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       load_pages<kThreads>(sm_page, geo, rl, seg0, nseg);
       // runs past the end of the list read page 0 (valid memory, fully masked)
       for (int i = nseg + (int)threadIdx.x; i < nseg + kRunsPerStep; i += kThreads) sm_page[i] = 0;
+      if (threadIdx.x == 0) sm_next_step = kDecodeWaves;
       __syncthreads();
       const int n_steps = (nseg + kRunsPerStep - 1) / kRunsPerStep;
       int step = wave;
@@ -259,8 +261,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         load_k(seg0, step);
         load_v(seg0, step);
       }
-      for (; step < n_steps; step += kDecodeWaves) {
-        const int nxt = step + kDecodeWaves;
+      // Wave w starts with step w; after that each wave claims the next unclaimed step, so waves
+      // that run ahead take more steps and all of them finish together.
+      while (step < n_steps) {
+        int nxt = 0;
+        if (lane == 0) nxt = atomicAdd(&sm_next_step, 1);
+        nxt = __builtin_amdgcn_readfirstlane(nxt);
         const bool has_next = nxt < n_steps;
         if constexpr (DCA) {
           // all keys of the step share one chunk: choose the query vector for it (uniform)
@@ -368,6 +374,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
           }
         }
         if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
+        step = nxt;
       }
     }
     // lanes sharing a column hold partial sums over disjoint keys
