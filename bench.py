@@ -39,12 +39,15 @@ METRIC = "decode attn HBM GB/s + prefill TFLOP/s (% of MI355X roofline), mixed h
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-EVENT_EVERY = 8                  # decode launches timed with HIP events: one step in eight
+KERNEL_SAMPLES = 32              # decode launches timed with HIP events, in a pass of their own
+FLUSH_BYTES = 1 << 30            # read before each sampled launch: more than L2 + Infinity Cache
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "decode_int8": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "prefill": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
     "dca": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
+    "gemma": ["decode.hip", "duo_common.h", "duo_kernels.h"],
+    "1m": ["decode.hip", "duo_common.h", "duo_kernels.h"],
 }
 
 
@@ -157,6 +160,30 @@ def spread_us(times_s):
             "kernel_samples": len(times_s)}
 
 
+class Flusher:
+    """Reads FLUSH_BYTES of device memory (a reduction over a buffer no leg uses), which pushes the
+    decode's earlier lines out of the L2s and the 256 MB Infinity Cache. A read leaves no dirty
+    lines behind, so the next kernel pays no write-backs of the flush."""
+
+    def __init__(self, torch):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = None
+
+    def __call__(self):
+        self.sink = self.buf.sum()
+
+
+def sample_kernels(torch, step, first: int, n: int, flush):
+    """n steps, each preceded by a flush (outside the events) and with HIP events attached to its
+    attention dispatch; returns the kernel durations in seconds, in step order."""
+    evs = [event_pair(torch) for _ in range(n)]
+    for i, ev in enumerate(evs):
+        flush()
+        step(first + i, ev)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+
+
 def decode_leg(args, torch, duo):
     w = synth.llama3_8b_decode()
     dev = torch.device("cuda:0")
@@ -211,18 +238,16 @@ def decode_leg(args, torch, duo):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # The decode launch of every EVENT_EVERY-th timed step carries HIP events on its dispatch (its
-    # kernel's own start and end); the other steps run without, as a serving loop would.
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: event_pair(torch)
-           for i in sampled}
+    # The timed steps run back to back without events, as a serving loop would; the kernel's own
+    # duration comes from a separate pass of KERNEL_SAMPLES steps with HIP events on the decode
+    # dispatch, each after a flush.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs.get(i))
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    kern_all = [a.elapsed_time(b) * 1e-3 for a, b in evs.values()]
+    kern_all = sample_kernels(torch, step, args.warmup + args.steps, KERNEL_SAMPLES, args.flush)
     kern_s = float(np.mean(kern_all))
     nbytes = decode_bytes(w, np.full(w.batch, L))
     traffic = measured_traffic("decode")
@@ -235,6 +260,7 @@ def decode_leg(args, torch, duo):
                      "traffic": traffic, "kernel": "duo::decode_kernel<bf16,128>",
                      "kernel_us": round(kern_s * 1e6, 2),
                      **spread_us(kern_all),
+                     "cold": f"{FLUSH_BYTES >> 20} MiB read before each sampled launch",
                      "algorithmic_bytes_per_launch": nbytes},
     }
     log(f"[decode] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
@@ -287,26 +313,29 @@ def decode_shape_leg(args, torch, duo, w, lens_seq, n_layers, steps, tag):
     for i in range(min(args.warmup, steps)):
         step(i)
     torch.cuda.synchronize()
-    evs = {i: event_pair(torch)
-           for i in range(0, steps, EVENT_EVERY // 2)}
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, evs.get(i))
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / steps
-    kern = {i: a.elapsed_time(b) * 1e-3 for i, (a, b) in evs.items()}
-    kern_s = float(np.mean(list(kern.values())))
-    nbytes = float(np.mean([decode_bytes(w, lens_seq[i % len(lens_seq)]) for i in kern]))
-    res = {"workload": w.name, "value": round(nbytes / step_s / 1e9, 1), "unit": "GB/s",
-           "us_per_step": round(step_s * 1e6, 2), "steps": steps,
+    step_bytes = float(np.mean([decode_bytes(w, lens_seq[i % len(lens_seq)]) for i in range(steps)]))
+    kern_all = sample_kernels(torch, step, steps, KERNEL_SAMPLES, args.flush)
+    kern_s = float(np.mean(kern_all))
+    # bytes of the sampled launches (the 1M context grows by one token per step)
+    nbytes = float(np.mean([decode_bytes(w, lens_seq[(steps + i) % len(lens_seq)])
+                            for i in range(KERNEL_SAMPLES)]))
+    res = {"workload": w.name, "value": round(step_bytes / step_s / 1e9, 1), "unit": "GB/s",
+           "us_per_step": round(step_s * 1e6, 2), "steps": steps, "layers_rotated": n_layers,
            "step": "kv_append_circular(1 token/seq) + duo_attn_decode",
            "algorithmic_bytes_per_launch": int(nbytes),
            "roofline": {"bound": "hbm", "achieved": round(nbytes / kern_s / 1e9, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                        "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(tag),
                         "kernel": f"duo::decode_kernel<{synth.DTYPE_NAMES[w.dtype]},{w.head_dim}>",
-                        "kernel_us": round(kern_s * 1e6, 2)}}
+                        "kernel_us": round(kern_s * 1e6, 2), **spread_us(kern_all),
+                        "cold": f"{FLUSH_BYTES >> 20} MiB read before each sampled launch"}}
     log(f"[{tag}] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
         f"{nbytes / kern_s / 1e9:.0f} GB/s kernel ({nbytes / 1e6:.1f} MB per launch)")
     return res
@@ -316,7 +345,7 @@ def gemma_leg(args, torch, duo):
     """Gemma-2b static-cache decode: batch 16, MQA, D 256, fp16, valid lengths U[1024, 8192]."""
     w = synth.gemma_2b_static_decode()
     lens = synth.valid_lengths(w, 1024, 8192)
-    return decode_shape_leg(args, torch, duo, w, [lens], 4, args.steps, "gemma")
+    return decode_shape_leg(args, torch, duo, w, [lens], 8, args.steps, "gemma")
 
 
 def long_context_leg(args, torch, duo):
@@ -381,16 +410,13 @@ def decode_int8_leg(args, torch, duo, dec):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: event_pair(torch)
-           for i in sampled}
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs.get(i))
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    kern_all = [a.elapsed_time(b) * 1e-3 for a, b in evs.values()]
+    kern_all = sample_kernels(torch, step, args.warmup + args.steps, KERNEL_SAMPLES, args.flush)
     kern_s = float(np.mean(kern_all))
     nbytes = decode_bytes(w, np.full(w.batch, L), int8_cache=True)
     res = {
@@ -617,10 +643,13 @@ def _read_counter_csv(path):
     return rows
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: str, command: str):
+def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: str, command: str,
+                       rename: dict | None = None):
     """Per-launch HBM bytes of the decode, prefill and Dual Chunk kernels from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), scaled by what the same counters read for a
-    copy of copy_mib MiB. Writes profiles/counters.json keyed by kernel, with the source hash."""
+    copy of copy_mib MiB in the same run. Merges the results into profiles/counters.json, keyed by
+    leg, with the source hash. rename maps a kernel key to the leg it measured in this run (a run
+    of the Gemma-2b leg alone: decode -> gemma)."""
     def per_kernel(path, counter):
         acc, copies = {}, []
         for r in _read_counter_csv(path):
@@ -648,16 +677,23 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
     known = float(copy_mib << 20)
     f_scale = known / fetch["copy"] if fetch.get("copy") else 1.0
     w_scale = known / write["copy"] if write.get("copy") else 1.0
-    out = {"calibration": {"copy_bytes": known, "fetch_raw": fetch.get("copy"),
-                           "write_raw": write.get("copy"), "fetch_scale": f_scale,
-                           "write_scale": w_scale, "command": command}}
+    try:
+        with open(out_path) as fh:
+            out = json.load(fh)
+    except (OSError, ValueError):
+        out = {}
+    out.pop("calibration", None)   # older layout: one calibration for the whole file
+    calib = {"copy_bytes": known, "fetch_raw": fetch.get("copy"), "write_raw": write.get("copy"),
+             "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
+    rename = rename or {}
     for k in ("decode", "decode_int8", "prefill", "dca"):
         if k in fetch and k in write:
-            out[k] = {"source_sha": source_sha(k),
-                      "fetch_bytes_per_launch": fetch[k] * f_scale,
-                      "write_bytes_per_launch": write[k] * w_scale,
-                      "hbm_bytes_per_launch": fetch[k] * f_scale + write[k] * w_scale,
-                      "dispatches": [nf.get(k), nw.get(k)]}
+            leg = rename.get(k, k)
+            out[leg] = {"source_sha": source_sha(leg),
+                        "fetch_bytes_per_launch": fetch[k] * f_scale,
+                        "write_bytes_per_launch": write[k] * w_scale,
+                        "hbm_bytes_per_launch": fetch[k] * f_scale + write[k] * w_scale,
+                        "dispatches": [nf.get(k), nw.get(k)], "calibration": calib}
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -679,10 +715,13 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs into profiles/counters.json")
     ap.add_argument("--counters-command", default="", help="command recorded with the summary")
+    ap.add_argument("--counters-as", default="", metavar="KERNEL=LEG,...",
+                    help="record a kernel's counters under another leg (decode=gemma)")
     args = ap.parse_args()
     if args.summarize_counters:
+        rename = dict(x.split("=", 1) for x in args.counters_as.split(",") if x)
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1],
-                           args.calibrate_copy, COUNTERS, args.counters_command)
+                           args.calibrate_copy, COUNTERS, args.counters_command, rename)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its "
@@ -700,6 +739,7 @@ def main():
     # the GPU queue has drained would land between a launch's start and stop events.
     gc.collect()
     gc.disable()
+    args.flush = Flusher(torch)
     dec = decode_leg(args, torch, duo) if legs & {"decode", "decode_int8"} else None
     dq = decode_int8_leg(args, torch, duo, dec) if "decode_int8" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None

@@ -128,17 +128,92 @@ def _stream(stream) -> int | None:
     return getattr(stream, "cuda_stream", stream) or None
 
 
-class _HostMask:
-    """head_is_retrieval as a host uint8 array kept alive for the call."""
+# Argument checks. The C ABI takes raw pointers, so a tensor of the wrong dtype, shape or device
+# would be read or written past its end; every wrapper checks its tensors here first.
+def _fail_type(msg: str):
+    raise TypeError(msg)
 
-    def __init__(self, mask):
+
+def _fail(msg: str):
+    raise ValueError(msg)
+
+
+def _check_tensor(t, name: str, dtype=None, shape=None, ndim=None, like=None):
+    """t has `dtype` (or like's dtype), `shape` (None entries free) / `ndim`, and like's device."""
+    if t is None:
+        _fail(f"{name} is required")
+    want = like.dtype if like is not None and dtype is None else dtype
+    if want is not None and t.dtype != want:
+        _fail_type(f"{name} must be {want}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                        for g, w in zip(t.shape, shape)):
+            _fail(f"{name} must have shape {tuple('*' if x is None else x for x in shape)}, "
+                  f"got {tuple(t.shape)}")
+    elif ndim is not None and t.dim() != ndim:
+        _fail(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if like is not None and t.device != like.device:
+        _fail(f"{name} is on {t.device}, expected {like.device}")
+
+
+def _check_gpu(t, name: str):
+    if not t.is_cuda:
+        _fail(f"{name} must be a GPU tensor (device pointers only)")
+
+
+def _int32():
+    import torch
+    return torch.int32
+
+
+class _HostMask:
+    """head_is_retrieval as a host uint8 array kept alive for the call (num_kv_heads entries, each
+    0 or 1)."""
+
+    def __init__(self, mask, num_kv_heads: int | None = None):
         vals = [int(x) for x in (mask.tolist() if hasattr(mask, "tolist") else mask)]
         self.n = len(vals)
+        if num_kv_heads is not None and self.n != num_kv_heads:
+            _fail(f"head_is_retrieval has {self.n} entries, expected num_kv_heads = {num_kv_heads}")
+        if any(v not in (0, 1) for v in vals):
+            _fail("head_is_retrieval entries must be 0 or 1")
         self.buf = (ctypes.c_uint8 * max(1, self.n))(*vals)
 
     @property
     def ptr(self):
         return ctypes.cast(self.buf, ctypes.c_void_p)
+
+
+def _check_tables(block_table, seq_lens, batch: int, num_kv_heads: int, like, lens_name="seq_lens"):
+    _check_tensor(block_table, "block_table", dtype=_int32(), shape=(batch, num_kv_heads, None),
+                  like=like)
+    _check_tensor(seq_lens, lens_name, dtype=_int32(), shape=(batch,), like=like)
+
+
+def _kv_heads(block_table) -> int:
+    """num_kv_heads from an int32 block table [batch][num_kv_heads][max_blocks_per_head]."""
+    _check_tensor(block_table, "block_table", dtype=_int32(), ndim=3)
+    return int(block_table.shape[1])
+
+
+def _check_workspace(workspace, like, required: bool = True):
+    if workspace is None:
+        if required:
+            _fail("workspace is required")
+        return
+    if workspace.device != like.device:
+        _fail(f"workspace is on {workspace.device}, expected {like.device}")
+    if not workspace.is_contiguous():
+        _fail("workspace must be contiguous")
+
+
+def _check_cache16(q, k_pool, v_pool, head_dim_axis=-1):
+    """16-bit / fp32 pools of q's dtype: k [NB][bs][D], v [NB][D][bs]."""
+    _check_tensor(k_pool, "k_pool", ndim=3, like=q)
+    nb, bs, d = k_pool.shape
+    if int(q.shape[head_dim_axis]) != int(d):
+        _fail(f"q has head_dim {q.shape[head_dim_axis]}, the pools {d}")
+    _check_tensor(v_pool, "v_pool", shape=(nb, d, bs), like=q)
 
 
 def _check(fn: str, status: int) -> None:
@@ -149,9 +224,19 @@ def _check(fn: str, status: int) -> None:
 def kv_append_circular(k_pool, v_pool, block_table, k_new, v_new, seq_lens_before, seq_lens_after,
                        head_is_retrieval, sink_size: int, recent_size: int, ring_blocks: int,
                        stream=None) -> None:
+    _check_tensor(k_pool, "k_pool", ndim=3)
     num_blocks, block_size, head_dim = k_pool.shape
+    _check_tensor(v_pool, "v_pool", shape=(num_blocks, head_dim, block_size), like=k_pool)
+    _check_tensor(k_new, "k_new", ndim=4, like=k_pool)
     batch, t_new, num_kv_heads, _ = k_new.shape
-    mask = _HostMask(head_is_retrieval)
+    _check_tensor(k_new, "k_new", shape=(batch, t_new, num_kv_heads, head_dim), like=k_pool)
+    _check_tensor(v_new, "v_new", shape=tuple(k_new.shape), like=k_pool)
+    _check_tables(block_table, seq_lens_before, batch, num_kv_heads, k_pool, "seq_lens_before")
+    if seq_lens_after is not None:
+        _check_tensor(seq_lens_after, "seq_lens_after", dtype=_int32(), shape=(batch,), like=k_pool)
+    for t, n in ((k_pool, "k_pool"),):
+        _check_gpu(t, n)
+    mask = _HostMask(head_is_retrieval, num_kv_heads)
     st = lib().kv_append_circular(
         _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
         block_table.shape[2], _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
@@ -181,9 +266,15 @@ def decode_workspace(q, block_table, block_size: int, split_tokens: int = 0):
 def duo_attn_decode(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval, sink_size: int,
                     recent_size: int, ring_blocks: int, softmax_scale: float, out, workspace,
                     split_tokens: int = 0, stream=None) -> None:
+    _check_tensor(q, "q", ndim=3)
+    _check_cache16(q, k_pool, v_pool)
     num_blocks, block_size, head_dim = k_pool.shape
     batch, num_q_heads, _ = q.shape
-    mask = _HostMask(head_is_retrieval)
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, block_table.shape[1])
     st = lib().duo_attn_decode(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
         block_table.shape[2], _ptr(seq_lens), batch, num_q_heads, block_table.shape[1], head_dim,
@@ -195,7 +286,7 @@ def duo_attn_decode(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval,
 
 def duo_attn_prefill_workspace_size(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
                                     head_dim: int, dtype: int, head_is_retrieval) -> int:
-    mask = _HostMask(head_is_retrieval)
+    mask = _HostMask(head_is_retrieval, num_kv_heads)
     return lib().duo_attn_prefill_workspace_size(batch, q_len, num_q_heads, num_kv_heads, head_dim,
                                                  dtype, mask.ptr)
 
@@ -214,9 +305,15 @@ def prefill_workspace(q, block_table, head_is_retrieval, head_dim: int | None = 
 def duo_attn_prefill(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval, sink_size: int,
                      recent_size: int, ring_blocks: int, softmax_scale: float, out, workspace,
                      stream=None) -> None:
+    _check_tensor(q, "q", ndim=4)
+    _check_cache16(q, k_pool, v_pool)
     num_blocks, block_size, head_dim = k_pool.shape
     batch, q_len, num_q_heads, _ = q.shape
-    mask = _HostMask(head_is_retrieval)
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q, required=False)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, block_table.shape[1])
     st = lib().duo_attn_prefill(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
         block_table.shape[2], _ptr(seq_lens), batch, q_len, num_q_heads, block_table.shape[1],
@@ -232,10 +329,19 @@ def duo_attn_prefill_varlen(q, k_pool, v_pool, block_table, seq_lens, q_start, m
     """Prefill of a packed batch: q, out [total_q][Hq][D]; q_start int32 [batch + 1] (device) gives
     each sequence's rows; max_q_len bounds any sequence's rows (the workspace is
     prefill_workspace for q_len = max_q_len)."""
+    _check_tensor(q, "q", ndim=3)
+    _check_cache16(q, k_pool, v_pool)
     num_blocks, block_size, head_dim = k_pool.shape
     total_q, num_q_heads, _ = q.shape
+    _check_tensor(q_start, "q_start", dtype=_int32(), ndim=1, like=q)
     batch = q_start.shape[0] - 1
-    mask = _HostMask(head_is_retrieval)
+    if batch < 1:
+        _fail("q_start must hold batch + 1 >= 2 offsets")
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q, required=False)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, block_table.shape[1])
     st = lib().duo_attn_prefill_varlen(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
         block_table.shape[2], _ptr(seq_lens), _ptr(q_start), batch, total_q, max_q_len,
@@ -257,11 +363,13 @@ def prefill_varlen_workspace(q, block_table, head_is_retrieval, max_q_len: int, 
 
 
 def _int8_pools(k_pool, v_pool, k_scale, v_scale):
+    """int8 codes k [NB][bs][D], v [NB][D][bs] and float32 scales [NB][bs], on one device."""
     import torch
-    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
-        raise TypeError("int8 cache pools must be torch.int8")
-    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
-        raise TypeError("int8 cache scales must be torch.float32")
+    _check_tensor(k_pool, "k_pool", dtype=torch.int8, ndim=3)
+    nb, bs, d = k_pool.shape
+    _check_tensor(v_pool, "v_pool", dtype=torch.int8, shape=(nb, d, bs), like=k_pool)
+    _check_tensor(k_scale, "k_scale", dtype=torch.float32, shape=(nb, bs), like=k_pool)
+    _check_tensor(v_scale, "v_scale", dtype=torch.float32, shape=(nb, bs), like=k_pool)
 
 
 def kv_append_circular_int8(k_pool, v_pool, k_scale, v_scale, block_table, k_new, v_new,
@@ -271,8 +379,17 @@ def kv_append_circular_int8(k_pool, v_pool, k_scale, v_scale, block_table, k_new
     [NB][D][bs], k_scale / v_scale float32 [NB][bs]; k_new / v_new [B][t_new][Hkv][D]."""
     _int8_pools(k_pool, v_pool, k_scale, v_scale)
     num_blocks, block_size, head_dim = k_pool.shape
+    _check_tensor(k_new, "k_new", ndim=4)
     batch, t_new, num_kv_heads, _ = k_new.shape
-    mask = _HostMask(head_is_retrieval)
+    _check_tensor(k_new, "k_new", shape=(batch, t_new, num_kv_heads, head_dim))
+    _check_tensor(v_new, "v_new", shape=tuple(k_new.shape), like=k_new)
+    if k_new.device != k_pool.device:
+        _fail(f"k_new is on {k_new.device}, the pools on {k_pool.device}")
+    _check_tables(block_table, seq_lens_before, batch, num_kv_heads, k_pool, "seq_lens_before")
+    if seq_lens_after is not None:
+        _check_tensor(seq_lens_after, "seq_lens_after", dtype=_int32(), shape=(batch,), like=k_pool)
+    _check_gpu(k_pool, "k_pool")
+    mask = _HostMask(head_is_retrieval, num_kv_heads)
     st = lib().kv_append_circular_int8(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), num_blocks,
         block_size, block_table.shape[2], _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
@@ -288,8 +405,15 @@ def duo_attn_decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_l
     """duo_attn_decode over the int8 cache (pools and scales as for kv_append_circular_int8)."""
     _int8_pools(k_pool, v_pool, k_scale, v_scale)
     num_blocks, block_size, head_dim = k_pool.shape
+    _check_tensor(q, "q", shape=(None, None, head_dim))
+    if q.device != k_pool.device:
+        _fail(f"q is on {q.device}, the pools on {k_pool.device}")
     batch, num_q_heads, _ = q.shape
-    mask = _HostMask(head_is_retrieval)
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, block_table.shape[1])
     st = lib().duo_attn_decode_int8(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
         num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch, num_q_heads,
@@ -321,10 +445,17 @@ def dca_attn_prefill(q, q_succ, q_inter, mscale, chunk_len: int, k_pool, v_pool,
     """Dual Chunk Attention prefill: q, q_succ, q_inter, out [B][q_len][Hq][D] (float16 or
     bfloat16); mscale float32 [B][q_len]; the cache filled with every kv head a retrieval head."""
     import torch
-    if mscale.dtype != torch.float32:
-        raise TypeError("mscale must be torch.float32")
+    _check_tensor(q, "q", ndim=4)
+    _check_cache16(q, k_pool, v_pool)
     num_blocks, block_size, head_dim = k_pool.shape
     batch, q_len, num_q_heads, _ = q.shape
+    _check_tensor(q_succ, "q_succ", shape=tuple(q.shape), like=q)
+    _check_tensor(q_inter, "q_inter", shape=tuple(q.shape), like=q)
+    _check_tensor(mscale, "mscale", dtype=torch.float32, shape=(batch, q_len), like=q)
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q, required=False)
+    _check_gpu(q, "q")
     st = lib().dca_attn_prefill(
         _ptr(q), _ptr(q_succ), _ptr(q_inter), _ptr(mscale), chunk_len, _ptr(k_pool), _ptr(v_pool),
         _ptr(block_table), num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch,
@@ -340,10 +471,17 @@ def dca_attn_decode(q, q_succ, q_inter, mscale, chunk_len: int, k_pool, v_pool, 
     """Dual Chunk Attention decode: q, q_succ, q_inter, out [B][Hq][D] (float16 or bfloat16);
     mscale float32 [B]; workspace as for duo_attn_decode (decode_workspace)."""
     import torch
-    if mscale.dtype != torch.float32:
-        raise TypeError("mscale must be torch.float32")
+    _check_tensor(q, "q", ndim=3)
+    _check_cache16(q, k_pool, v_pool)
     num_blocks, block_size, head_dim = k_pool.shape
     batch, num_q_heads, _ = q.shape
+    _check_tensor(q_succ, "q_succ", shape=tuple(q.shape), like=q)
+    _check_tensor(q_inter, "q_inter", shape=tuple(q.shape), like=q)
+    _check_tensor(mscale, "mscale", dtype=torch.float32, shape=(batch,), like=q)
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q)
+    _check_gpu(q, "q")
     st = lib().dca_attn_decode(
         _ptr(q), _ptr(q_succ), _ptr(q_inter), _ptr(mscale), chunk_len, _ptr(k_pool), _ptr(v_pool),
         _ptr(block_table), num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch,

@@ -296,6 +296,7 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return DUO_ERR_WORKSPACE;
   const int64_t grid = (int64_t)batch * n_ret * ns + (int64_t)batch * n_str;
   if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
+  const size_t ticket_bytes = decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size);
 
   DecodeParams p{};
   p.q = q;
@@ -306,9 +307,7 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
   p.out = out;
   p.counter = static_cast<int32_t*>(workspace);
   p.gcounter = p.counter + (size_t)batch * num_kv_heads;
-  p.partial = reinterpret_cast<float*>(
-      static_cast<char*>(workspace) +
-      decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size));
+  p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + ticket_bytes);
   p.n_group = decode_merge_groups(ns);
   p.gpartial = p.partial + (size_t)batch * num_kv_heads * ns * (num_q_heads / num_kv_heads) *
                                (head_dim + 2);

@@ -43,6 +43,8 @@
 // sequence's fp32 mscale.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "duo_common.h"
 #include "duo_kernels.h"
 
@@ -56,7 +58,6 @@ template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
 
 // Split merge: up to kFastMergeSplits splits per (sequence, kv head) take the two-phase merge
 // (weights in LDS, then the partial outputs with kMergeLoads 8-byte loads in flight per thread).
-constexpr int kFastMergeSplits = 256;
 constexpr int kMergeLoads = 32;
 
 // Two consecutive floats (8-byte aligned) read at device coherence, as the single floats are.
@@ -67,13 +68,18 @@ __device__ __forceinline__ uint64_t load_coherent_pair(const float* p) {
 
 // The decode body. Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
 // (k_scale, v_scale [num_blocks][block_size]); a score is (codes . q) * k_scale of its key, and a
-// key's weight enters PV as p * v_scale of the key (the row sum l takes p itself).
+// key's weight enters PV as p * v_scale of the key (the row sum l takes p itself). Otherwise the row
+// sum l adds the weights as rounded for PV.
 template <typename T, int D, bool Q8, bool DCA = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int kDecodeWaves = decode_waves<D>();
   constexpr int kThreads = kDecodeWaves * kWave;
   constexpr int KC = D / 32;  // k-steps of S^T over the head dim
   constexpr int DT = D / 16;  // 16-row tiles of O^T
+  // PV operand type. An fp16 call over the int8 cache takes PV in bf16: a weight (up to 2^8 under
+  // the lazy max) times a V scale (up to 65504 / 127) can pass fp16's range, and every code is
+  // exact in bf16 as well.
+  using PT = typename std::conditional<Q8 && std::is_same<T, _Float16>::value, __bf16, T>::type;
   __shared__ float sm_o[kDecodeWaves][16][D];
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
@@ -349,28 +355,30 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         for (int c = 0; c < kChunks; ++c) {
           float x[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < 8; ++i)
             x[i] = fast_exp2(fmaf(s[c][i >> 2][i & 3], DCA ? sl2 : p.scale_log2, -m_use));
-            l_run += x[i];
-          }
-          v8<T> pB;
           if constexpr (Q8) {
-            // weights times the keys' V scales; absent keys (whose scale may be anything) give 0
+            // weights times the keys' V scales; absent keys (whose scale may be anything) give 0.
+            // The row sum takes the fp32 weights: PV multiplies each one by its key's scale first.
             float xv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = ((keep[c] >> i) & 1u) ? x[i] * vS[c][i >> 2][i & 3] : 0.f;
-            pB = pack8<T>(xv);
+            for (int i = 0; i < 8; ++i) {
+              l_run += x[i];
+              xv[i] = ((keep[c] >> i) & 1u) ? x[i] * vS[c][i >> 2][i & 3] : 0.f;
+            }
+            const v8<PT> pB = pack8<PT>(xv);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(codes_to_v8<PT>(vR[c][dt]), pB, oT[dt]);
           } else {
-            pB = pack8<T>(x);
+            // the row sum adds exactly the rounded weights that PV multiplies
+            const v8<T> pB = pack8<T>(x);
+            l_run = sum8(pB, l_run);
             if (!full) {
 #pragma unroll
               for (int dt = 0; dt < DT; ++dt) vA[c][dt] = select8<T>(vA[c][dt], keep[c]);
             }
-          }
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            if constexpr (Q8) oT[dt] = mfma16(codes_to_v8<T>(vR[c][dt]), pB, oT[dt]);
-            else oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
+            for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
           }
         }
         if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
@@ -672,19 +680,6 @@ hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested) {
-  if (requested > 0) return requested;
-  // rows = (sequence, retrieval kv head) pairs. About one retrieval item per CU (256 on MI355X)
-  // at full capacity; but no item longer than 16384 keys (more, shorter items balance better than
-  // one very long one per CU), and at most kFastMergeSplits splits per row, so that the fused merge
-  // takes its fast path. Between 256 and 65536 keys per item.
-  const int64_t r = rows > 0 ? rows : 1;
-  auto n_split = [&](int64_t s) { return (capacity_tokens + s - 1) / s; };
-  int64_t s = 256;
-  while (s < 65536 && ((s < 16384 && r * n_split(s) > 256) || n_split(s) > kFastMergeSplits)) s *= 2;
-  return (int32_t)s;
 }
 
 }  // namespace duo

@@ -105,10 +105,9 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
                           hipStream_t stream);
 hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
                               hipStream_t stream);
+
 constexpr int kPrefillKeyTile = 64;   // keys per prefill K/V tile (Dual Chunk lengths are multiples)
 
-// Decode split size (keys per retrieval item) from static sizes: rows = batch x retrieval kv heads.
-// Shared by the workspace-size query and the call.
 // Decode split merge in two levels when a (sequence, kv head) has more than kMergeGroup splits
 // (and at most kMergeGroup * kMaxMergeGroups): groups of kMergeGroup splits, then the groups.
 constexpr int32_t kMergeGroup = 16;
@@ -117,7 +116,23 @@ inline int32_t decode_merge_groups(int32_t n_split) {
   return (n_split > kMergeGroup && n_split <= kMergeGroup * kMaxMergeGroups)
              ? (n_split + kMergeGroup - 1) / kMergeGroup : 0;
 }
-int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested);
+// Up to this many splits per (sequence, kv head) the fused merge takes its two-phase fast path.
+constexpr int32_t kFastMergeSplits = 256;
+// Decode split size (keys per retrieval item) from static sizes: rows = batch x retrieval kv heads.
+// Shared by the workspace-size query and the call.
+inline int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested) {
+  if (requested > 0) return requested;
+  // rows = (sequence, retrieval kv head) pairs. About one retrieval item per CU (256 on MI355X)
+  // at full capacity; but no item longer than 16384 keys (more, shorter items balance better than
+  // one very long one per CU), and at most kFastMergeSplits splits per row, so that the fused merge
+  // takes its fast path. Between 256 and 65536 keys per item.
+  const int64_t r = rows > 0 ? rows : 1;
+  auto n_split = [&](int64_t s) { return (capacity_tokens + s - 1) / s; };
+  int64_t s = 256;
+  while (s < 65536 && ((s < 16384 && r * n_split(s) > 256) || n_split(s) > kFastMergeSplits)) s *= 2;
+  return (int32_t)s;
+}
+
 // Prefill workgroup shape: eight waves (two per SIMD, 32 query rows each) while one 64-key K+V tile
 // takes at most 32 KiB, so that four tile stages fit in LDS; four waves otherwise.
 constexpr int prefill_waves(int elem_bytes, int head_dim) {

@@ -26,11 +26,13 @@ the grouping of q heads onto kv heads (contiguous, hq // (Hq / Hkv); pinned only
 """
 from .cache import (slot_of, table_position, append, gather, pool_shapes, to_f64,
                     new_pools, ring_capacity)
-from .attention import visible_positions, attend_row, attend, attend_paged
+from .attention import (visible_positions, visible_mask, attend_row, attend_rows, attend,
+                        attend_paged)
 from .quant import quantize_rows, dequantize, scale_pool_shape, append_int8, attend_int8
-from .dca import query_kind, attend_dca_row, attend_dca
+from .dca import query_kind, attend_dca_row, attend_dca, attend_dca_rows
 
 __all__ = ["slot_of", "table_position", "append", "gather", "pool_shapes", "to_f64", "new_pools",
-           "ring_capacity", "visible_positions", "attend_row", "attend", "attend_paged",
+           "ring_capacity", "visible_positions", "visible_mask", "attend_row", "attend_rows",
+           "attend", "attend_paged",
            "quantize_rows", "dequantize", "scale_pool_shape", "append_int8", "attend_int8",
-           "query_kind", "attend_dca_row", "attend_dca"]
+           "query_kind", "attend_dca_row", "attend_dca", "attend_dca_rows"]

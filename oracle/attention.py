@@ -47,6 +47,42 @@ def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.
     return (w @ V) / w.sum()
 
 
+def visible_mask(p_rows, key_pos, *, retrieval: bool, sink: int, recent: int) -> np.ndarray:
+    """Boolean [R][N]: may a query at position p_rows[r] attend the key at position key_pos[n]?
+
+    The rule of ``visible_positions``, applied to every (query, key) pair at once: the key is at or
+    before the query, and for a streaming head it is a sink (j < sink) or in the recent window
+    (p - j < recent).
+    """
+    p = np.asarray(p_rows, dtype=np.int64)[:, None]
+    j = np.asarray(key_pos, dtype=np.int64)[None, :]
+    ok = (j >= 0) & (j <= p)
+    if not retrieval:
+        ok = ok & ((j < sink) | (p - j < recent))
+    return ok
+
+
+def attend_rows(q_rows, p_rows, K, V, key_pos, *, retrieval: bool, sink: int, recent: int,
+                scale: float) -> np.ndarray:
+    """Several query rows of one (sequence, kv head) at once, float64: the same softmax attention
+    as ``attend_row`` over ``visible_positions``, with the scores of all rows taken in one matrix
+    product and the invisible ones set to -inf.
+
+    q_rows [R][D] and p_rows [R] (positions); K, V [N][D] float64 rows held at the distinct key
+    positions key_pos [N], which must include every key any of the rows can see (keys no row sees
+    may be left out). Rows with nothing visible give zeros. Returns [R][D].
+    """
+    ok = visible_mask(p_rows, key_pos, retrieval=retrieval, sink=sink, recent=recent)
+    s = np.where(ok, scale * (np.asarray(q_rows, dtype=np.float64) @ K.T), -np.inf)
+    seen = ok.any(axis=1)
+    m = np.where(seen, s.max(axis=1), 0.0)
+    w = np.where(ok, np.exp(s - m[:, None]), 0.0)
+    den = w.sum(axis=1)
+    out = (w @ V) / np.where(seen, den, 1.0)[:, None]
+    out[~seen] = 0.0
+    return out
+
+
 def attend(q, k, v, seq_lens, retrieval_mask, *, sink, recent, scale, dtype, rows=None):
     """Reference output for every (or the selected) query rows, float64.
 

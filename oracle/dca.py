@@ -83,3 +83,34 @@ def attend_dca(q, q_succ, q_inter, k, v, seq_lens, mscale, *, chunk_len, scale, 
         out[b, i, hq] = attend_dca_row(qs, Kf, Vf, p, chunk_len, scale,
                                        float(np.float32(mscale[b, i])))
     return out
+
+
+def attend_dca_rows(qs, p_rows, K: np.ndarray, V: np.ndarray, chunk_len: int, scale: float,
+                    mscale_rows) -> np.ndarray:
+    """Several query rows of one (sequence, kv head) at once, float64: ``attend_dca_row`` for each
+    row, with the scores of the three query sets taken as three matrix products over keys
+    0..max(p) and each (row, key) score taken from the set ``query_kind`` names for it.
+
+    qs = (q, q_succ, q_inter), each float64 [R][D]; p_rows [R] positions; K, V float64 [>= max p + 1]
+    rows; mscale_rows [R] (float32 values). Rows at p < 0 give zeros. Returns [R][D].
+    """
+    p = np.asarray(p_rows, dtype=np.int64)
+    R, D = len(p), V.shape[1]
+    out = np.zeros((R, D), dtype=np.float64)
+    live = p >= 0
+    if not live.any():
+        return out
+    n = int(p.max()) + 1
+    j = np.arange(n, dtype=np.int64)
+    kind = query_kind(p[:, None], j[None, :], chunk_len)
+    Kp = K[:n]
+    s = np.where(kind == 0, qs[0] @ Kp.T, np.where(kind == 1, qs[1] @ Kp.T, qs[2] @ Kp.T))
+    s = s * (scale * np.asarray(mscale_rows, dtype=np.float64))[:, None]
+    ok = j[None, :] <= p[:, None]
+    s = np.where(ok, s, -np.inf)
+    m = np.where(live, s.max(axis=1), 0.0)
+    w = np.where(ok, np.exp(s - m[:, None]), 0.0)
+    den = w.sum(axis=1)
+    res = (w @ V[:n]) / np.where(live, den, 1.0)[:, None]
+    out[live] = res[live]
+    return out

@@ -1,0 +1,317 @@
+// Host-side checks of the C ABI layer (api.hip) under AddressSanitizer and UndefinedBehaviorSanitizer.
+//
+// api.hip is compiled for the host only and linked against the stubs below in place of the kernel
+// launchers: each stub records what the layer would launch and returns success, so every entry
+// point runs its argument checks and launch planning on the CPU with no GPU and no device memory.
+// Device pointers are fake addresses that nothing dereferences; host inputs (the retrieval masks)
+// are heap arrays of exactly num_kv_heads bytes, so a read past one is reported.
+//
+// Exit status 0 and no sanitizer report: every case returned the documented status, and every
+// accepted call planned the launch the layer documents.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/duo_attn.h"
+#include "../../kv_cache_sparsity_amd/csrc/duo_kernels.h"
+
+namespace {
+
+struct Launch {
+  int kind = 0;           // 0 none, 1 append, 2 append int8, 3 decode, 4 decode dca, 5 prefill,
+                          // 6 prefill dca
+  int grid = 0, dtype = -1, head_dim = 0;
+  bool int8 = false;
+  duo::AppendParams ap{};
+  duo::DecodeParams dp{};
+  duo::PrefillParams pp{};
+  duo::LaunchEvents ev{nullptr, nullptr};
+};
+std::vector<Launch> g_launches;
+int g_failures = 0;
+
+void record(Launch l) {
+  l.ev = duo::current_launch_events();
+  g_launches.push_back(l);
+}
+
+#define CHECK(cond)                                                              \
+  do {                                                                           \
+    if (!(cond)) {                                                               \
+      std::fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #cond); \
+      ++g_failures;                                                              \
+    }                                                                            \
+  } while (0)
+
+}  // namespace
+
+// ---- stubs of the kernel side ------------------------------------------------------------------
+namespace duo {
+hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t) {
+  Launch l; l.kind = 1; l.ap = p; l.dtype = elem_bytes; record(l); return hipSuccess;
+}
+hipError_t launch_append_int8(const AppendParams& p, hipStream_t) {
+  Launch l; l.kind = 2; l.ap = p; record(l); return hipSuccess;
+}
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8, int grid,
+                         hipStream_t) {
+  Launch l; l.kind = 3; l.dp = p; l.dtype = dtype; l.head_dim = head_dim; l.int8 = int8;
+  l.grid = grid; record(l); return hipSuccess;
+}
+hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int grid, hipStream_t) {
+  Launch l; l.kind = 4; l.dp = p; l.dtype = dtype; l.head_dim = head_dim; l.grid = grid;
+  record(l); return hipSuccess;
+}
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid, hipStream_t) {
+  Launch l; l.kind = 5; l.pp = p; l.dtype = dtype; l.head_dim = head_dim; l.grid = grid;
+  record(l); return hipSuccess;
+}
+hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t) {
+  Launch l; l.kind = 6; l.pp = p; l.dtype = dtype; l.head_dim = head_dim; l.grid = grid;
+  record(l); return hipSuccess;
+}
+}  // namespace duo
+
+namespace {
+
+void* fake(uintptr_t off = 0) { return reinterpret_cast<void*>(uintptr_t(0x100000) + off); }
+
+struct Mask {   // exactly n host bytes
+  explicit Mask(int n, int ret_every = 2) : n(n), p(new uint8_t[n]) {
+    for (int i = 0; i < n; ++i) p[i] = (i % ret_every == 0) ? 1 : 0;
+  }
+  ~Mask() { delete[] p; }
+  int n;
+  uint8_t* p;
+};
+
+size_t launches_of(int kind) {
+  size_t c = 0;
+  for (const Launch& l : g_launches) c += l.kind == kind;
+  return c;
+}
+
+// ---- kv_append_circular -------------------------------------------------------------------------
+void append_cases() {
+  for (int hkv : {1, 2, 7, 64}) {
+    Mask m(hkv);
+    g_launches.clear();
+    const int32_t st = kv_append_circular(fake(), fake(), (const int32_t*)fake(), 1000, 16, 40,
+                                          fake(), fake(), (const int32_t*)fake(),
+                                          (int32_t*)fake(256), 3, 70, hkv, 128, DUO_BF16, m.p, 4,
+                                          16, 2, nullptr);
+    CHECK(st == DUO_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].kind == 1);
+    if (!g_launches.empty()) {
+      const duo::AppendParams& p = g_launches[0].ap;
+      uint64_t bits = 0;
+      for (int h = 0; h < hkv; ++h) bits |= (uint64_t)m.p[h] << h;
+      CHECK(p.retrieval_bits == bits);
+      const bool streaming = hkv > 1;   // heads 1, 3, ... are streaming heads
+      CHECK(p.sink_blocks == 1 && p.log2_bs == 4 && p.ring_slots == (streaming ? 32 : 1));
+    }
+  }
+  Mask m(2);
+  g_launches.clear();
+  CHECK(kv_append_circular(nullptr, fake(), (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                           (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16, m.p, 4, 16, 2,
+                           nullptr) == DUO_ERR_INVALID_ARG);
+  CHECK(kv_append_circular(fake(), fake(), (const int32_t*)fake(), 64, 16, 8, fake(8), fake(),
+                           (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16, m.p, 4, 16, 2,
+                           nullptr) == DUO_ERR_INVALID_ARG);
+  CHECK(kv_append_circular(fake(), fake(), (const int32_t*)fake(), 64, 12, 8, fake(), fake(),
+                           (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16, m.p, 4, 16, 2,
+                           nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(kv_append_circular(fake(), fake(), (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                           (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16, m.p, 4, 16, 8,
+                           nullptr) == DUO_ERR_CAPACITY);
+  // sizes at the edges of int32 arithmetic
+  CHECK(kv_append_circular(fake(), fake(), (const int32_t*)fake(), 64, 256, INT32_MAX, fake(),
+                           fake(), (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16, m.p, 4,
+                           16, 2, nullptr) == DUO_ERR_INVALID_ARG);
+  CHECK(kv_append_circular(fake(), fake(), (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                           (const int32_t*)fake(), nullptr, 2, INT32_MAX, 2, 128, DUO_BF16, m.p, 4,
+                           16, 2, nullptr) == DUO_ERR_INVALID_ARG);
+  CHECK(kv_append_circular(fake(), fake(), (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                           (const int32_t*)fake(), nullptr, 65536, 5, 2, 128, DUO_BF16, m.p, 4, 16,
+                           2, nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(launches_of(1) == 0);
+  // int8: scale pools required and distinct
+  CHECK(kv_append_circular_int8((int8_t*)fake(), (int8_t*)fake(), (float*)fake(), (float*)fake(),
+                                (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                                (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_F16, m.p, 4, 16,
+                                2, nullptr) == DUO_ERR_INVALID_ARG);
+  CHECK(kv_append_circular_int8((int8_t*)fake(), (int8_t*)fake(), (float*)fake(), (float*)fake(4096),
+                                (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                                (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_F16, m.p, 4, 16,
+                                2, nullptr) == DUO_OK);
+  CHECK(launches_of(2) == 1);
+}
+
+// ---- decode ---------------------------------------------------------------------------------------
+int32_t decode(const Mask& m, int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t mbph,
+               size_t ws_bytes, int32_t split, int32_t dtype = DUO_BF16, int32_t bs = 16) {
+  return duo_attn_decode(fake(), fake(), fake(), (const int32_t*)fake(), 100000, bs, mbph,
+                         (const int32_t*)fake(), batch, hq, hkv, d, dtype, m.p, 64, 256, 16,
+                         0.088f, fake(), fake(), ws_bytes, split, nullptr);
+}
+
+void decode_cases() {
+  // the Llama-3-8B decode shape: 4 of 8 kv heads retrieval
+  Mask m(8);
+  const size_t ws = duo_attn_decode_workspace_size(8, 32, 8, 128, 2048, 16, 0);
+  CHECK(ws > 0);
+  g_launches.clear();
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 0) == DUO_OK);
+  CHECK(g_launches.size() == 1);
+  if (g_launches.size() == 1) {
+    const Launch& l = g_launches[0];
+    const duo::DecodeParams& p = l.dp;
+    CHECK(l.kind == 3 && !l.int8 && l.head_dim == 128 && l.dtype == DUO_BF16);
+    CHECK(p.n_ret == 4 && p.n_str == 4 && p.group == 4);
+    CHECK(p.split_tokens == 4096 && p.n_split == 8);
+    CHECK(l.grid == 8 * 4 * 8 + 8 * 4);
+    for (int i = 0; i < p.n_ret; ++i) CHECK(m.p[p.ret_heads[i]] == 1);
+    for (int i = 0; i < p.n_str; ++i) CHECK(m.p[p.str_heads[i]] == 0);
+    // partials sit past the tickets and inside the workspace
+    const size_t part_off = (const char*)p.partial - (const char*)fake();
+    const size_t part_bytes = (size_t)8 * 8 * (p.n_split + p.n_group) * 4 * (128 + 2) * 4;
+    CHECK(part_off > 0 && part_off % 256 == 0 && part_off + part_bytes <= ws);
+  }
+  // the size query without a mask covers the smallest split any mask gives; with the split given,
+  // it is exactly what the call needs
+  const size_t ws4096 = duo_attn_decode_workspace_size(8, 32, 8, 128, 2048, 16, 4096);
+  CHECK(ws4096 > 0 && ws4096 <= ws);
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws4096, 4096) == DUO_OK);
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws4096 - 1, 4096) == DUO_ERR_WORKSPACE);
+  CHECK(decode(m, 8, 32, 8, 128, 2048, 0, 0) == DUO_ERR_WORKSPACE);
+  CHECK(decode(m, 8, 128, 4, 128, 2048, ws, 0) == DUO_ERR_UNSUPPORTED);    // group 32
+  CHECK(decode(m, 8, 32, 8, 96, 2048, ws, 0) == DUO_ERR_UNSUPPORTED);
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 100) == DUO_ERR_INVALID_ARG);  // not a multiple of 128
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 0, 9) == DUO_ERR_UNSUPPORTED);
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 0, DUO_BF16, 8) == DUO_ERR_UNSUPPORTED);
+  // every split size a caller may ask for fits the workspace sized for it
+  for (int32_t split : {128, 256, 1024, 4096, 16384, 65536}) {
+    const size_t w2 = duo_attn_decode_workspace_size(8, 32, 8, 128, 65540, 16, split);
+    CHECK(w2 > 0);
+    CHECK(decode(m, 8, 32, 8, 128, 65540, w2, split) == DUO_OK);
+  }
+  // 64 kv heads, all streaming but one
+  Mask m64(64, 64);
+  const size_t w64 = duo_attn_decode_workspace_size(2, 64, 64, 64, 100, 16, 0);
+  CHECK(decode(m64, 2, 64, 64, 64, 100, w64, 0) == DUO_OK);
+  // the profiling hook applies to the next call only
+  g_launches.clear();
+  duo_profile_next_launch(fake(1), fake(2));
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 0) == DUO_OK);
+  CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 0) == DUO_OK);
+  CHECK(g_launches.size() == 2);
+  if (g_launches.size() == 2) {
+    CHECK(g_launches[0].ev.start == (hipEvent_t)fake(1) && g_launches[0].ev.stop == (hipEvent_t)fake(2));
+    CHECK(g_launches[1].ev.start == nullptr && g_launches[1].ev.stop == nullptr);
+  }
+  // workspace-size queries reject sizes whose products would overflow
+  CHECK(duo_attn_decode_workspace_size(8, 32, 8, 128, INT32_MAX, 16, 0) == 0);
+  CHECK(duo_attn_decode_workspace_size(0, 32, 8, 128, 2048, 16, 0) == 0);
+  // int8 decode needs its scale pools
+  CHECK(duo_attn_decode_int8(fake(), (const int8_t*)fake(), (const int8_t*)fake(), nullptr,
+                             (const float*)fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                             (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16, m.p, 64, 256, 16,
+                             0.088f, fake(), fake(), ws, 0, nullptr) == DUO_ERR_INVALID_ARG);
+  g_launches.clear();
+  CHECK(duo_attn_decode_int8(fake(), (const int8_t*)fake(), (const int8_t*)fake(),
+                             (const float*)fake(), (const float*)fake(), (const int32_t*)fake(),
+                             100000, 16, 2048, (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16,
+                             m.p, 64, 256, 16, 0.088f, fake(), fake(), ws, 0, nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 1 && g_launches[0].int8);
+}
+
+// ---- prefill ----------------------------------------------------------------------------------------
+void prefill_cases() {
+  Mask m(32, 4);   // 8 of 32 heads retrieval (the Llama-2-7B shape)
+  const size_t ws = duo_attn_prefill_workspace_size(1, 4096, 32, 32, 128, DUO_BF16, m.p);
+  CHECK(ws > 0);
+  g_launches.clear();
+  CHECK(duo_attn_prefill(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                         (const int32_t*)fake(), 1, 4096, 32, 32, 128, DUO_BF16, m.p, 128, 1024,
+                         320, 0.088f, fake(), fake(), ws, nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 1);
+  if (g_launches.size() == 1) {
+    const Launch& l = g_launches[0];
+    CHECK(l.kind == 5 && l.pp.n_ret == 8 && l.pp.n_str == 24 && l.pp.n_qtiles == 16);
+    CHECK(l.grid == 8 * 16 * 2 + 24 * 16);
+  }
+  CHECK(duo_attn_prefill(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                         (const int32_t*)fake(), 1, 4096, 32, 32, 128, DUO_BF16, m.p, 128, 1024,
+                         300, 0.088f, fake(), fake(), ws, nullptr) == DUO_ERR_CAPACITY);
+  CHECK(duo_attn_prefill(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                         (const int32_t*)fake(), 1, 4096, 32, 32, 128, DUO_BF16, m.p, 128, 1024,
+                         320, 0.088f, fake(), fake(), ws - 1, nullptr) == DUO_ERR_WORKSPACE);
+  CHECK(duo_attn_prefill(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                         (const int32_t*)fake(), 1, 4096, 32, 32, 256, DUO_F32, m.p, 128, 1024,
+                         320, 0.088f, fake(), fake(), ws, nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(duo_attn_prefill(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                         (const int32_t*)fake(), 2, INT32_MAX / 2 + 1, 32, 32, 128, DUO_BF16, m.p,
+                         128, 1024, 320, 0.088f, fake(), fake(), ws, nullptr) == DUO_ERR_INVALID_ARG);
+  // varlen: needs its offsets
+  CHECK(duo_attn_prefill_varlen(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                                (const int32_t*)fake(), nullptr, 4, 5000, 4096, 32, 32, 128,
+                                DUO_BF16, m.p, 128, 1024, 320, 0.088f, fake(), fake(), ws,
+                                nullptr) == DUO_ERR_INVALID_ARG);
+  CHECK(duo_attn_prefill_varlen(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                                (const int32_t*)fake(), (const int32_t*)fake(), 1, 5000, 4096, 32,
+                                32, 128, DUO_BF16, m.p, 128, 1024, 320, 0.088f, fake(), fake(), ws,
+                                nullptr) == DUO_OK);
+  // all streaming: no workspace needed
+  Mask none(32, 1000);
+  none.p[0] = 0;
+  CHECK(duo_attn_prefill_workspace_size(1, 4096, 32, 32, 128, DUO_BF16, none.p) == 256);
+  CHECK(duo_attn_prefill(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                         (const int32_t*)fake(), 1, 4096, 32, 32, 128, DUO_BF16, none.p, 128, 1024,
+                         320, 0.088f, fake(), nullptr, 0, nullptr) == DUO_OK);
+}
+
+// ---- Dual Chunk Attention -------------------------------------------------------------------------
+void dca_cases() {
+  const size_t ws = dca_attn_prefill_workspace_size(1, 32768, 16, 2, 128, DUO_BF16);
+  CHECK(ws > 0);
+  g_launches.clear();
+  CHECK(dca_attn_prefill(fake(), fake(), fake(), (const float*)fake(), 32768, fake(), fake(),
+                         (const int32_t*)fake(), 100000, 16, 8192, (const int32_t*)fake(), 1, 32768,
+                         16, 2, 128, DUO_BF16, 0.088f, fake(), fake(), ws, nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 1 && g_launches[0].kind == 6 && g_launches[0].pp.chunk_tiles == 512);
+  CHECK(dca_attn_prefill(fake(), fake(), fake(), (const float*)fake(), 100, fake(), fake(),
+                         (const int32_t*)fake(), 100000, 16, 8192, (const int32_t*)fake(), 1, 32768,
+                         16, 2, 128, DUO_BF16, 0.088f, fake(), fake(), ws, nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(dca_attn_prefill(fake(), nullptr, fake(), (const float*)fake(), 32768, fake(), fake(),
+                         (const int32_t*)fake(), 100000, 16, 8192, (const int32_t*)fake(), 1, 32768,
+                         16, 2, 128, DUO_BF16, 0.088f, fake(), fake(), ws, nullptr) == DUO_ERR_INVALID_ARG);
+  const size_t wd = duo_attn_decode_workspace_size(1, 16, 2, 128, 8192, 16, 0);
+  g_launches.clear();
+  CHECK(dca_attn_decode(fake(), fake(), fake(), (const float*)fake(), 32768, fake(), fake(),
+                        (const int32_t*)fake(), 100000, 16, 8192, (const int32_t*)fake(), 1, 16, 2,
+                        128, DUO_BF16, 0.088f, fake(), fake(), wd, 0, nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 1 && g_launches[0].kind == 4 && g_launches[0].dp.n_ret == 2);
+  CHECK(dca_attn_decode(fake(), fake(), fake(), (const float*)fake(), 32768, fake(), fake(),
+                        (const int32_t*)fake(), 100000, 16, 8192, (const int32_t*)fake(), 1, 16, 2,
+                        128, DUO_F32, 0.088f, fake(), fake(), wd, 0, nullptr) == DUO_ERR_UNSUPPORTED);
+}
+
+}  // namespace
+
+int main() {
+  CHECK(duo_abi_version() == DUO_ATTN_ABI_VERSION);
+  for (int s = 0; s <= 6; ++s) CHECK(std::strlen(duo_status_string(s)) > 0);
+  append_cases();
+  decode_cases();
+  prefill_cases();
+  dca_cases();
+  if (g_failures) {
+    std::fprintf(stderr, "%d check(s) failed\n", g_failures);
+    return 1;
+  }
+  std::printf("host ABI checks passed\n");
+  return 0;
+}

@@ -202,3 +202,32 @@ def test_llama3_8b_gqa_decode_int8_batch8_ctx32768():
     full = oracle.attend(q[:, None], K, V, np.full(w.batch, L), cache.mask, sink=w.sink,
                          recent=w.recent, scale=w.scale, dtype=w.dtype)[:, 0]
     assert float(np.max(np.abs(got - full))) < 0.05
+
+
+def test_decode_int8_f16_large_value_rows_stay_finite():
+    """fp16 calls over the int8 cache with V rows near fp16's largest magnitude (scales near
+    65504 / 127): a weight times such a scale passes fp16's range, so the decode must not form that
+    product in fp16. K rows are ordinary, so the weights spread over many keys."""
+    w = synth.small("f16-int8-large-v", batch=2, q_heads=8, kv_heads=2, head_dim=128,
+                    dtype=synth.F16, block_size=16, sink=4, recent=64, retrieval=(0,),
+                    context=900, q_len=1, seed=53)
+    say(f"decode int8 {w.name}")
+    lens = np.array([900, 421])
+    K = logical_kv(w, 900, synth.S_K)
+    Vf = synth.normal(w.seed, 77, 0, shape=(w.batch, w.num_kv_heads, 900, w.head_dim))
+    Vf *= np.float32(20000.0)                         # |v| up to ~65000: fp16's top binade
+    V = synth.f32_to_storage(np.clip(Vf, -65000, 65000), w.dtype)
+    cache = Int8Cache(w)
+    cache.fill_per_sequence(K, V, lens)
+    kc, ks, vc, vs = _logical_codes(K, V, w.dtype)
+    assert float(vs.max()) > 256.0
+    q = q_decode(w, 0)
+    want = oracle.attend_int8(q[:, None], kc, ks, vc, vs, lens, cache.mask, sink=w.sink,
+                              recent=w.recent, scale=w.scale, dtype=w.dtype)[:, 0]
+    for split in (0, 128):
+        got = to_host_f64(cache.decode(q, split_tokens=split), w.dtype)
+        # outputs are of order 1e4 here: the bound scales with the values' magnitude
+        assert np.isfinite(got).all()
+        err = float(np.max(np.abs(got - want) / np.maximum(1.0, np.abs(want).max())))
+        say(f"  split {split}: max |gpu - oracle| / max |oracle| = {err:.3e}")
+        assert err <= 2e-2

@@ -11,6 +11,8 @@
 * invariants: a chunk covering the whole sequence leaves only the intra query (q_succ and q_inter
   have no effect, and the result is the ordinary attention of ``oracle.attend``); slots past the
   valid length have no effect;
+* the row-block form (``attend_dca_rows``: the rows of one head against all keys in three matrix
+  products) against the same brute force;
 * planted mistakes in the oracle (wrong chunk of the succ query, succ and inter swapped, chunks
   counted from the query backwards, mscale dropped) must each fail a pin.
 """
@@ -50,6 +52,42 @@ def test_matches_three_attentions_merged_by_lse(B, q_len, Hq, Hkv, D, lens, C):
     lens = np.array(lens)
     scale = 1 / np.sqrt(D)
     got = _run(q, qs, qi, k, v, lens, ms, C, scale)
+    f = lambda a: a.astype(np.float64)
+    want = brute_force_dca(f(q), f(qs), f(qi), f(k), f(v), lens, f(ms), C, scale)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def _rows_form(q, qs, qi, k, v, lens, ms, C, scale):
+    """attend_dca_rows over every (sequence, q head): all rows of a head at once."""
+    B, q_len, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros(q.shape)
+    f = lambda a: a.astype(np.float64)
+    for b in range(B):
+        p = int(lens[b]) - q_len + np.arange(q_len)
+        for hq in range(Hq):
+            h = hq // G
+            out[b, :, hq] = odca.attend_dca_rows((f(q[b, :, hq]), f(qs[b, :, hq]), f(qi[b, :, hq])),
+                                                 p, f(k[b, h]), f(v[b, h]), C, scale, ms[b])
+    return out
+
+
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,D,lens,C", [
+    (1, 24, 2, 2, 8, [24], 8),
+    (2, 5, 4, 2, 16, [37, 21], 8),
+    (1, 40, 2, 1, 8, [40], 16),
+    (1, 7, 2, 2, 8, [50], 7),
+    (2, 3, 2, 2, 8, [3, 9], 64),
+    (1, 33, 1, 1, 4, [33], 1),
+    (1, 6, 2, 2, 8, [4], 4),          # two rows before the sequence start
+])
+def test_row_blocks_match_three_attentions_merged_by_lse(B, q_len, Hq, Hkv, D, lens, C):
+    rng = np.random.default_rng(23 + C)
+    q, qs, qi, k, v = _case(rng, B, q_len, Hq, Hkv, D, max(lens))
+    ms = rng.uniform(0.5, 1.5, (B, q_len)).astype(np.float32)
+    lens = np.array(lens)
+    scale = 1 / np.sqrt(D)
+    got = _rows_form(q, qs, qi, k, v, lens, ms, C, scale)
     f = lambda a: a.astype(np.float64)
     want = brute_force_dca(f(q), f(qs), f(qi), f(k), f(v), lens, f(ms), C, scale)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
@@ -173,3 +211,12 @@ def test_planted_mistakes_fail_a_pin(monkeypatch, mistake):
         test_matches_three_attentions_merged_by_lse(2, 5, 4, 2, 16, [37, 21], 8)
     caught += 1
     assert caught == 2
+
+
+@pytest.mark.parametrize("mistake", ["succ_two_back", "swapped", "from_query"])
+def test_planted_kind_mistakes_fail_the_row_block_pin(monkeypatch, mistake):
+    fns = {"succ_two_back": _kind_succ_two_back, "swapped": _kind_swapped,
+           "from_query": _kind_from_query}
+    monkeypatch.setattr(odca, "query_kind", fns[mistake])
+    with pytest.raises(AssertionError):
+        test_row_blocks_match_three_attentions_merged_by_lse(2, 5, 4, 2, 16, [37, 21], 8)

@@ -10,6 +10,8 @@
   the circular paged layout gives the same outputs as the contiguous cache; cache slots beyond the
   valid length (NaN there) have no effect; repeating kv heads turns GQA into MHA without changing
   outputs.
+* the row-block form (``attend_rows``, all rows of a head in one score matrix, optionally over a
+  subset of the keys) against the same brute force and closed forms;
 * planted mistakes: a few plausible bugs injected into a copy of the oracle must each fail a pin.
 """
 import os
@@ -375,6 +377,66 @@ def test_dtype_widening_is_exact():
 
 
 # ------------------------------------------------------------------------------------------------
+# Row blocks (oracle.attend_rows): several rows of one head in one score matrix
+# ------------------------------------------------------------------------------------------------
+def _rows_by_blocks(q, k, v, lens, mask, sink, recent, scale, subset=False):
+    """oracle.attend_rows over every (sequence, q head): all rows of a head at once. With subset,
+    streaming heads get only the keys some row can see (the sinks and the union of the windows)."""
+    B, q_len, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros(q.shape)
+    for b in range(B):
+        L = int(lens[b])
+        p = L - q_len + np.arange(q_len)
+        for hq in range(Hq):
+            h = hq // G
+            ret = bool(mask[h])
+            keys = np.arange(L)
+            if subset and not ret:
+                keys = np.union1d(np.arange(min(sink, L)),
+                                  np.arange(max(0, p[0] - recent + 1), L))
+            out[b, :, hq] = oracle.attend_rows(q[b, :, hq], p, k[b, h, keys], v[b, h, keys], keys,
+                                               retrieval=ret, sink=sink, recent=recent,
+                                               scale=scale)
+    return out
+
+
+@pytest.mark.parametrize("L,q_len,sink,recent,Hq,Hkv,ret", SWEEP)
+@pytest.mark.parametrize("subset", [False, True])
+def test_row_blocks_match_brute_force(L, q_len, sink, recent, Hq, Hkv, ret, subset):
+    rng = np.random.default_rng(L * 1000 + q_len + 17)
+    B, D = 2, 8
+    q, k, v = _rand_case(rng, B, q_len, Hq, Hkv, D, L + 5)
+    lens = np.array([L, max(q_len, L - 2)])
+    mask = np.zeros(Hkv, np.uint8)
+    mask[list(ret)] = 1
+    got = _rows_by_blocks(q, k, v, lens, mask, sink, recent, 0.3, subset)
+    want = brute_force(q, k, v, lens, mask, sink, recent, 0.3)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,q_len,sink,recent,ret,sets", HAND)
+def test_row_blocks_zero_query_average_exactly_the_visible_rows(L, q_len, sink, recent, ret, sets):
+    D = 16
+    v = np.zeros((L, D))
+    v[np.arange(L), np.arange(L)] = 1.0
+    k = np.random.default_rng(1).standard_normal((L, D))
+    got = oracle.attend_rows(np.zeros((q_len, D)), L - q_len + np.arange(q_len), k, v,
+                             np.arange(L), retrieval=ret, sink=sink, recent=recent, scale=0.5)
+    for i, s in enumerate(sets):
+        want = np.zeros(D)
+        want[sorted(s)] = 1.0 / len(s)
+        np.testing.assert_allclose(got[i], want, atol=1e-15)
+
+
+def test_row_blocks_rows_before_the_start_are_zero():
+    got = oracle.attend_rows(np.ones((3, 4)), np.array([-2, -1, 0]), np.ones((1, 4)),
+                             np.full((1, 4), 2.0), np.array([0]), retrieval=True, sink=0, recent=1,
+                             scale=1.0)
+    assert (got[:2] == 0).all() and np.allclose(got[2], 2.0)
+
+
+# ------------------------------------------------------------------------------------------------
 # Planted mistakes: each must be caught by one of the pins above
 # ------------------------------------------------------------------------------------------------
 def _window_off_by_one(p, *, retrieval, sink, recent):
@@ -426,6 +488,37 @@ def test_planted_softmax_bugs_are_caught(monkeypatch, bug):
     monkeypatch.setattr(oatt, "attend_row", bug)
     with pytest.raises(AssertionError):
         test_oracle_matches_brute_force(*SWEEP[3])
+
+
+def _mask_window_off_by_one(p_rows, key_pos, *, retrieval, sink, recent):
+    p, j = np.asarray(p_rows)[:, None], np.asarray(key_pos)[None, :]
+    ok = (j >= 0) & (j <= p)
+    return ok if retrieval else ok & ((j < sink) | (p - j <= recent))
+
+
+def _mask_sink_dropped(p_rows, key_pos, *, retrieval, sink, recent):
+    p, j = np.asarray(p_rows)[:, None], np.asarray(key_pos)[None, :]
+    ok = (j >= 0) & (j <= p)
+    return ok if retrieval else ok & (p - j < recent)
+
+
+def _mask_future_leak(p_rows, key_pos, *, retrieval, sink, recent):
+    p, j = np.asarray(p_rows)[:, None], np.asarray(key_pos)[None, :]
+    ok = (j >= 0) & (j <= p + 1)
+    return ok if retrieval else ok & ((j < sink) | (p - j < recent))
+
+
+@pytest.mark.parametrize("bug", [_mask_window_off_by_one, _mask_sink_dropped, _mask_future_leak])
+def test_planted_row_block_mask_bugs_are_caught(monkeypatch, bug):
+    monkeypatch.setattr(oatt, "visible_mask", bug)
+    caught = False
+    for case in SWEEP:
+        try:
+            test_row_blocks_match_brute_force(*case, False)
+        except AssertionError:
+            caught = True
+            break
+    assert caught
 
 
 def test_planted_ring_index_bug_is_caught(monkeypatch):
