@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 7
+#define DUO_ATTN_ABI_VERSION 8
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -145,6 +145,32 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                         const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                         int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
                         size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/*
+ * duo_attn_decode_noalloc -- duo_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It takes no
+ * workspace: the library keeps one in a static device array of DUO_NOALLOC_SCRATCH_BYTES, one copy
+ * on each GPU it runs on, held until the process ends. The call allocates nothing and frees nothing.
+ *
+ *   Arguments: those of duo_attn_decode without workspace and workspace_bytes; the same semantics,
+ *   kernels and results.
+ * Each call clears the merge tickets it uses (a fill kernel on `stream`, ahead of the decode), so
+ * the array needs no setup; the first call on a device looks up that device's copy. Calls on one
+ * GPU share the array: calls that may overlap on one GPU (other streams, other host threads) race
+ * and give wrong results; order them on one stream.
+ * Errors: as duo_attn_decode; DUO_ERR_WORKSPACE when the shapes need more than
+ * DUO_NOALLOC_SCRATCH_BYTES (duo_attn_decode_workspace_size with the same split_tokens bounds what
+ * a call needs); DUO_ERR_HIP when the device's copy cannot be found.
+ */
+#define DUO_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t duo_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const int32_t* seq_lens,
+                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                float softmax_scale, void* out, int32_t split_tokens,
+                                void* stream);
 
 /*
  * duo_attn_prefill_workspace_size -- bytes of device workspace duo_attn_prefill needs for these

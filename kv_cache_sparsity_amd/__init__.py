@@ -26,6 +26,7 @@ DUO_F32, DUO_F16, DUO_BF16 = 0, 1, 2
 STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "DUO_ERR_CAPACITY",
           4: "DUO_ERR_WORKSPACE", 5: "DUO_ERR_HIP"}
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
+           "duo_attn_decode_noalloc",
            "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
            "kv_append_circular_int8",
            "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.duo_attn_decode.restype = _I32
         L.duo_attn_decode.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                       _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ, _I32, _P]
+        L.duo_attn_decode_noalloc.restype = _I32
+        L.duo_attn_decode_noalloc.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32,
+                                              _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P,
+                                              _I32, _P]
         L.duo_attn_prefill_workspace_size.restype = _SZ
         L.duo_attn_prefill_workspace_size.argtypes = [_I32] * 6 + [_P]
         L.duo_attn_prefill.restype = _I32
@@ -284,6 +289,30 @@ def duo_attn_decode(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval,
     _check("duo_attn_decode", st)
 
 
+NOALLOC_SCRATCH_BYTES = 16 << 20   # DUO_NOALLOC_SCRATCH_BYTES
+
+
+def duo_attn_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, head_is_retrieval,
+                            sink_size: int, recent_size: int, ring_blocks: int,
+                            softmax_scale: float, out, split_tokens: int = 0, stream=None) -> None:
+    """duo_attn_decode without a workspace argument: the library's static per-GPU scratch serves
+    instead, and the call allocates no device memory. Calls that overlap on one GPU race."""
+    _check_tensor(q, "q", ndim=3)
+    _check_cache16(q, k_pool, v_pool)
+    num_blocks, block_size, head_dim = k_pool.shape
+    batch, num_q_heads, _ = q.shape
+    _check_tables(block_table, seq_lens, batch, _kv_heads(block_table), q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, block_table.shape[1])
+    st = lib().duo_attn_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), num_blocks, block_size,
+        block_table.shape[2], _ptr(seq_lens), batch, num_q_heads, block_table.shape[1], head_dim,
+        _dtype_tag(q), mask.ptr, sink_size, recent_size, ring_blocks, softmax_scale, _ptr(out),
+        split_tokens, _stream(stream))
+    _check("duo_attn_decode_noalloc", st)
+
+
 def duo_attn_prefill_workspace_size(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
                                     head_dim: int, dtype: int, head_is_retrieval) -> int:
     mask = _HostMask(head_is_retrieval, num_kv_heads)
@@ -506,7 +535,8 @@ def profile_next_launch(start_event=None, stop_event=None) -> None:
            lib().duo_profile_next_launch(handle(start_event), handle(stop_event)))
 
 
-__all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill",
+__all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill", "duo_attn_decode_noalloc",
+           "NOALLOC_SCRATCH_BYTES",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
            "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
            "profile_next_launch",

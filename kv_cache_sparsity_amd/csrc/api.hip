@@ -7,6 +7,9 @@
 #include "../../include/duo_attn.h"
 #include "duo_kernels.h"
 
+static_assert(DUO_NOALLOC_SCRATCH_BYTES == duo::kNoAllocScratchBytes,
+              "the header states the scratch size of duo_attn_decode_noalloc");
+
 namespace {
 
 using namespace duo;
@@ -270,7 +273,7 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
                            const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                            int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
                            size_t workspace_bytes, int32_t split_tokens, void* stream,
-                           const DcaArgs* dca = nullptr) {
+                           const DcaArgs* dca = nullptr, bool noalloc = false) {
   const CallEvents events;
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
@@ -293,10 +296,23 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
   st = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
                    batch * (n_ret > 0 ? n_ret : 1), split_tokens, &S, &ns, &need);
   if (st != DUO_OK) return st;
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return DUO_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes) return DUO_ERR_WORKSPACE;
+  } else if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) {
+    return DUO_ERR_WORKSPACE;
+  }
   const int64_t grid = (int64_t)batch * n_ret * ns + (int64_t)batch * n_str;
   if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
   const size_t ticket_bytes = decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size);
+  if (noalloc) {
+    // every check has passed: take this device's scratch and clear its tickets (a fill kernel on
+    // the call's stream, ahead of the decode)
+    if (noalloc_scratch(&workspace) != hipSuccess) return DUO_ERR_HIP;
+    workspace_bytes = kNoAllocScratchBytes;
+    if (launch_zero_words(static_cast<uint32_t*>(workspace), ticket_bytes / 4,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+      return DUO_ERR_HIP;
+  }
 
   DecodeParams p{};
   p.q = q;
@@ -358,6 +374,20 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                      softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+int32_t duo_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const int32_t* seq_lens,
+                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                float softmax_scale, void* out, int32_t split_tokens,
+                                void* stream) {
+  return decode_impl(false, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
+                     block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                     softmax_scale, out, nullptr, 0, split_tokens, stream, nullptr, true);
 }
 
 int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* v_pool,

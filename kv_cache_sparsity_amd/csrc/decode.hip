@@ -43,6 +43,8 @@
 // sequence's fp32 mscale.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "duo_common.h"
@@ -657,7 +659,45 @@ hipError_t launch_t(const DecodeParams& p, int head_dim, bool int8_cache, int gr
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
+
+// ---- scratch of the no-alloc decode ------------------------------------------------------------
+// Callers that cannot allocate device memory (graph capture, serving loops, harnesses that forbid
+// it) get the decode workspace from this array instead. Every GPU the library runs on holds its own
+// copy until the process ends; calls on one GPU share it.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  // The symbol's address differs per device: look it up once per device, with that device
+  // current, and keep it. The array's name in host code is only a stand-in for the symbol.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t stream) {
+  (void)hipGetLastError();
+  const size_t blocks = std::min<size_t>((n_words + 255) / 256, 1024);
+  if (blocks > 0) hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n_words);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8_cache, int grid,
                          hipStream_t stream) {

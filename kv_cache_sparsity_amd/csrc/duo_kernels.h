@@ -106,6 +106,12 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
 hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
                               hipStream_t stream);
 
+// The decode scratch of duo_attn_decode_noalloc: a device array of kNoAllocScratchBytes in the
+// library's code object (one copy per GPU). noalloc_scratch gives the current device's address of
+// it (looked up once per device); launch_zero_words clears n_words 32-bit words with a fill kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
+hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t stream);
 constexpr int kPrefillKeyTile = 64;   // keys per prefill K/V tile (Dual Chunk lengths are multiples)
 
 // Decode split merge in two levels when a (sequence, kv head) has more than kMergeGroup splits

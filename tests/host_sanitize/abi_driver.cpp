@@ -20,13 +20,14 @@ namespace {
 
 struct Launch {
   int kind = 0;           // 0 none, 1 append, 2 append int8, 3 decode, 4 decode dca, 5 prefill,
-                          // 6 prefill dca
+                          // 6 prefill dca, 7 zero words
   int grid = 0, dtype = -1, head_dim = 0;
   bool int8 = false;
   duo::AppendParams ap{};
   duo::DecodeParams dp{};
   duo::PrefillParams pp{};
   duo::LaunchEvents ev{nullptr, nullptr};
+  size_t zero_words = 0;
 };
 std::vector<Launch> g_launches;
 int g_failures = 0;
@@ -71,6 +72,13 @@ hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, i
                               hipStream_t) {
   Launch l; l.kind = 6; l.pp = p; l.dtype = dtype; l.head_dim = head_dim; l.grid = grid;
   record(l); return hipSuccess;
+}
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>(uintptr_t(0x7f0000000000));
+  return hipSuccess;
+}
+hipError_t launch_zero_words(uint32_t*, size_t n_words, hipStream_t) {
+  Launch l; l.kind = 7; l.zero_words = n_words; record(l); return hipSuccess;
 }
 }  // namespace duo
 
@@ -228,6 +236,26 @@ void decode_cases() {
   CHECK(g_launches.size() == 1 && g_launches[0].int8);
 }
 
+void noalloc_cases() {
+  Mask m(8);
+  g_launches.clear();
+  CHECK(duo_attn_decode_noalloc(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                                (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16, m.p, 64, 256, 16,
+                                0.088f, fake(), 0, nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 2 && g_launches[0].kind == 7 && g_launches[1].kind == 3);
+  if (g_launches.size() == 2) {
+    const size_t tickets = (const char*)g_launches[1].dp.partial - (const char*)g_launches[1].dp.counter;
+    CHECK(g_launches[0].zero_words * 4 == tickets);
+  }
+  // shapes whose workspace passes the scratch: refused before anything is launched
+  Mask m64(64);
+  g_launches.clear();
+  CHECK(duo_attn_decode_noalloc(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 65540,
+                                (const int32_t*)fake(), 64, 256, 64, 256, DUO_BF16, m64.p, 64, 256,
+                                16, 0.0625f, fake(), 128, nullptr) == DUO_ERR_WORKSPACE);
+  CHECK(g_launches.empty());
+}
+
 // ---- prefill ----------------------------------------------------------------------------------------
 void prefill_cases() {
   Mask m(32, 4);   // 8 of 32 heads retrieval (the Llama-2-7B shape)
@@ -306,6 +334,7 @@ int main() {
   for (int s = 0; s <= 6; ++s) CHECK(std::strlen(duo_status_string(s)) > 0);
   append_cases();
   decode_cases();
+  noalloc_cases();
   prefill_cases();
   dca_cases();
   if (g_failures) {

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 7
+    assert duo.abi_version() == 8
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -149,6 +149,42 @@ def append_int8(**kw):
 ])
 def test_append_int8_rejects(kw, status):
     assert append_int8(**kw) == status
+
+
+def decode_noalloc(**kw):
+    a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, table=FAKE, num_blocks=64, bs=16, mbph=20,
+             lens=FAKE, batch=2, hq=8, hkv=2, d=128, dtype=2,
+             mask=ctypes.cast(MASK_RS, ctypes.c_void_p), sink=4, recent=16, rb=2, scale=0.1,
+             out=FAKE, split=0)
+    a.update(kw)
+    return duo.lib().duo_attn_decode_noalloc(
+        a["q"], a["k_pool"], a["v_pool"], a["table"], a["num_blocks"], a["bs"], a["mbph"],
+        a["lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["dtype"], a["mask"], a["sink"],
+        a["recent"], a["rb"], a["scale"], a["out"], a["split"], None)
+
+
+MASK_64 = (ctypes.c_uint8 * 64)(*([1] * 64))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(hq=40, hkv=2), UNSUPPORTED), (dict(recent=33), CAPACITY),
+    (dict(split=100), INVALID), (dict(mask=ctypes.cast(MASK_BAD, ctypes.c_void_p)), INVALID),
+    # 64 sequences x 64 kv heads x 128-key splits over 1M slots: more than the scratch holds
+    (dict(batch=64, hq=256, hkv=64, d=256, mbph=65540, split=128,
+          mask=ctypes.cast(MASK_64, ctypes.c_void_p)), WORKSPACE),
+])
+def test_decode_noalloc_rejects(kw, status):
+    """Every check runs before the call touches a device (this container has none)."""
+    assert decode_noalloc(**kw) == status
+
+
+def test_decode_noalloc_scratch_bounds_the_workspace_of_the_workloads():
+    """The workloads' decode workspaces (library split, worst mask) fit the no-alloc scratch."""
+    sizes = [duo.duo_attn_decode_workspace_size(8, 32, 8, 128, 2048, 16, 0),      # Llama-3-8B
+             duo.duo_attn_decode_workspace_size(16, 8, 1, 256, 512, 16, 0),       # Gemma-2b
+             duo.duo_attn_decode_workspace_size(1, 32, 8, 128, 65540, 16, 0),     # 1M context
+             duo.duo_attn_decode_workspace_size(1, 16, 2, 128, 8192, 16, 0)]      # Qwen2-72B share
+    assert all(0 < s <= duo.NOALLOC_SCRATCH_BYTES for s in sizes), sizes
 
 
 def decode_int8(**kw):
