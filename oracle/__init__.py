@@ -14,6 +14,9 @@ Sources (the four web pages on KV-cache sparsity):
     streamed tokens).
   * transformers PR "[WIP] Dynamic length in static cache", description: a new position only needs
     attention against the positions up to itself, not the whole static cache.
+  * DuoAttention README, installation and efficiency sections: the method paired with a quantized
+    KV cache (8-bit codes with a scale per stored row, ``quant``; 4-bit codes with a static scale
+    per kv head and channel, ``quant4``, after the pages' "kv4-per-channel" demo models).
   * vLLM PR "[Model] Implement DualChunkAttention for Qwen2 Models", review thread: the softmax
     scale is applied in fp32 to the q.k product; Dual Chunk Attention itself (``dca``): three query
     vectors chosen by the chunk relation of query and key, a float32 mscale per query position.
@@ -30,9 +33,12 @@ from .attention import (visible_positions, visible_mask, attend_row, attend_rows
                         attend_paged)
 from .quant import quantize_rows, dequantize, scale_pool_shape, append_int8, attend_int8
 from .dca import query_kind, attend_dca_row, attend_dca, attend_dca_rows
+from .quant4 import (quantize_rows4, dequantize4, pack4, unpack4, pool4_shapes, append_int4,
+                     attend_int4)
 
 __all__ = ["slot_of", "table_position", "append", "gather", "pool_shapes", "to_f64", "new_pools",
            "ring_capacity", "visible_positions", "visible_mask", "attend_row", "attend_rows",
            "attend", "attend_paged",
            "quantize_rows", "dequantize", "scale_pool_shape", "append_int8", "attend_int8",
-           "query_kind", "attend_dca_row", "attend_dca", "attend_dca_rows"]
+           "query_kind", "attend_dca_row", "attend_dca", "attend_dca_rows", "quantize_rows4",
+           "dequantize4", "pack4", "unpack4", "pool4_shapes", "append_int4", "attend_int4"]

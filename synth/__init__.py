@@ -23,7 +23,7 @@ DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2}
 
 # Stream ids for the counter-based generator.
-S_HEADS, S_LENS, S_K, S_V, S_Q, S_TABLE, S_GARBAGE, S_KSTEP, S_VSTEP, S_ROWSCALE = range(10)
+S_HEADS, S_LENS, S_K, S_V, S_Q, S_TABLE, S_GARBAGE, S_KSTEP, S_VSTEP, S_ROWSCALE, S_CHSCALE = range(11)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -304,6 +304,14 @@ def row_scales(w: Workload, step: int, q_len: int, lo: float = 1.0, hi: float = 
     per-position scale factor Dual Chunk Attention takes; synthetic values, no method arithmetic)."""
     rng = np.random.default_rng([w.seed, S_ROWSCALE, step])
     return rng.uniform(lo, hi, size=(w.batch, q_len)).astype(np.float32)
+
+
+def channel_scales(w: Workload, which: int, lo: float = 0.45, hi: float = 0.65) -> np.ndarray:
+    """Per-(kv head, channel) scales float32 [Hkv][D] for a 4-bit cache of K (which = S_K) or V
+    (S_V): seeded draws in [lo, hi), standing in for scales calibrated offline on N(0, 1) data
+    (7 steps of 0.45-0.65 reach 3.2-4.6 standard deviations)."""
+    rng = np.random.default_rng([w.seed, S_CHSCALE, which])
+    return rng.uniform(lo, hi, (w.num_kv_heads, w.head_dim)).astype(np.float32)
 
 
 def valid_lengths(w: Workload, lo: int, hi: int) -> np.ndarray:
