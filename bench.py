@@ -7,9 +7,10 @@ per sequence (kv_append_circular) + duo_attn_decode. Four layers' caches are rot
 step reads cache lines last touched >1.5 GB earlier (the 256 MB Infinity Cache cannot serve them).
 value = algorithmic decode bytes per step / wall time per step.
 
-Int8 decode leg: the same decode workload over the int8 cache (kv_append_circular_int8 +
-duo_attn_decode_int8; 8-bit codes plus one fp32 scale per slot for K and V), reported in the same
-algorithmic GB/s (codes + scales + block table + q/out) and as its step-time speedup over bf16.
+Int8 and 4-bit decode legs: the same decode workload over the int8 cache (kv_append_circular_int8 +
+duo_attn_decode_int8; 8-bit codes plus one fp32 scale per slot for K and V) and over the 4-bit cache
+(kv_append_circular_int4 + duo_attn_decode_int4; 4-bit codes with per-channel scales), reported in
+the same algorithmic GB/s (codes + scales + block table + q/out) and as step-time speedups over bf16.
 
 Prefill leg: Llama-2-7B-shaped MHA chunked prefill, eight 4096-token chunks building a 32768-token
 context, 8 of 32 heads retrieval, sink 128 / recent 1024. One pass = 8 x (append chunk + prefill).
@@ -44,6 +45,7 @@ FLUSH_BYTES = 1 << 30            # read before each sampled launch: more than L2
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "decode_int8": ["decode.hip", "duo_common.h", "duo_kernels.h"],
+    "decode_int4": ["decode.hip", "duo_common.h", "duo_kernels.h"],
     "prefill": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
     "dca": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
     "gemma": ["decode.hip", "duo_common.h", "duo_kernels.h"],
@@ -89,10 +91,18 @@ def visible_count(p: np.ndarray, retrieval: bool, sink: int, recent: int) -> np.
     return a + b - overlap
 
 
-def decode_bytes(w: synth.Workload, lens: np.ndarray, int8_cache: bool = False) -> int:
+def decode_bytes(w: synth.Workload, lens: np.ndarray, int8_cache: bool = False,
+                 int4_cache: bool = False) -> int:
     """K+V rows each head must read + q + out + block-table entries. With the int8 cache a key's
-    K+V row is 2 * head_dim one-byte codes plus its two fp32 scales."""
-    row = 2 * w.head_dim + 2 * 4 if int8_cache else 2 * w.head_dim * w.elem_bytes
+    K+V row is 2 * head_dim one-byte codes plus its two fp32 scales; with the 4-bit cache it is
+    head_dim bytes of codes, and the per-channel scales (2 * head_dim fp32 per kv head) are read
+    once per call."""
+    if int4_cache:
+        row = w.head_dim
+    elif int8_cache:
+        row = 2 * w.head_dim + 2 * 4
+    else:
+        row = 2 * w.head_dim * w.elem_bytes
     total = 0
     for b in range(w.batch):
         L = int(lens[b])
@@ -111,6 +121,8 @@ def decode_bytes(w: synth.Workload, lens: np.ndarray, int8_cache: bool = False) 
                 pages = sink_pages + ring_pages
             total += pages * 4
     total += 2 * w.batch * w.num_q_heads * w.head_dim * w.elem_bytes
+    if int4_cache:
+        total += 2 * w.num_kv_heads * w.head_dim * 4
     return total
 
 
@@ -356,38 +368,54 @@ def long_context_leg(args, torch, duo):
     return decode_shape_leg(args, torch, duo, w, seq, 2, w.steps, "1m")
 
 
-def decode_int8_leg(args, torch, duo, dec):
-    """The decode workload over the int8 cache, on the bf16 leg's K/V bits (quantized by the
-    library's own append)."""
+def decode_quant_leg(args, torch, duo, dec, bits: int):
+    """The decode workload over the int8 (bits = 8) or 4-bit (bits = 4) cache, on the bf16 leg's K/V
+    bits (quantized by the library's own append; the 4-bit cache's per-channel scales are seeded
+    stand-ins for calibrated ones)."""
     w = dec["w"]
     K, V = dec["K"], dec["V"]
     dev = torch.device("cuda:0")
     L = w.context
-    log("[decode-int8] filling the int8 cache")
+    tag = f"decode-int{bits}"
+    log(f"[{tag}] filling the cache")
     table_h, nblocks = synth.block_table(w)
     table = torch.from_numpy(table_h).to(dev)
     mask = w.retrieval_mask
-    ks = (nblocks, w.block_size, w.head_dim)
-    vs = (nblocks, w.head_dim, w.block_size)
-    ss = (nblocks, w.block_size)
+    if bits == 8:
+        append, decode = duo.kv_append_circular_int8, duo.duo_attn_decode_int8
+        ss = (nblocks, w.block_size)
+
+        def new_pools():
+            return (torch.empty((nblocks, w.block_size, w.head_dim), dtype=torch.int8, device=dev),
+                    torch.empty((nblocks, w.head_dim, w.block_size), dtype=torch.int8, device=dev),
+                    torch.empty(ss, dtype=torch.float32, device=dev),
+                    torch.empty(ss, dtype=torch.float32, device=dev))
+    else:
+        append, decode = duo.kv_append_circular_int4, duo.duo_attn_decode_int4
+        ks = torch.from_numpy(synth.channel_scales(w, synth.S_K)).to(dev)
+        vs = torch.from_numpy(synth.channel_scales(w, synth.S_V)).to(dev)
+
+        def new_pools():
+            return (torch.empty((nblocks, w.block_size, w.head_dim // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((nblocks, w.head_dim, w.block_size // 2), dtype=torch.uint8, device=dev),
+                    ks, vs)
     after = torch.empty(w.batch, dtype=torch.int32, device=dev)
     layers = []
     for li in range(args.layers):
-        pools = (torch.empty(ks, dtype=torch.int8, device=dev),
-                 torch.empty(vs, dtype=torch.int8, device=dev),
-                 torch.empty(ss, dtype=torch.float32, device=dev),
-                 torch.empty(ss, dtype=torch.float32, device=dev))
+        pools = new_pools()
         if li == 0:
             for s0 in range(0, L - 1, 8192):
                 e = min(L - 1, s0 + 8192)
                 kn = to_dev(torch, K[:, :, s0:e].transpose(0, 2, 1, 3), w.dtype, dev)
                 vn = to_dev(torch, V[:, :, s0:e].transpose(0, 2, 1, 3), w.dtype, dev)
                 lb = torch.full((w.batch,), s0, dtype=torch.int32, device=dev)
-                duo.kv_append_circular_int8(*pools, table, kn, vn, lb, after, mask, w.sink,
-                                            w.recent, w.ring_blocks)
+                append(*pools, table, kn, vn, lb, after, mask, w.sink, w.recent, w.ring_blocks)
         else:
-            for dst, src in zip(pools, layers[0]):
+            for dst, src in zip(pools[:2], layers[0][:2]):
                 dst.copy_(src)
+            if bits == 8:
+                for dst, src in zip(pools[2:], layers[0][2:]):
+                    dst.copy_(src)
         layers.append(pools)
     k_tok = to_dev(torch, K[:, :, L - 1:L].transpose(0, 2, 1, 3), w.dtype, dev)
     v_tok = to_dev(torch, V[:, :, L - 1:L].transpose(0, 2, 1, 3), w.dtype, dev)
@@ -400,12 +428,11 @@ def decode_int8_leg(args, torch, duo, dec):
 
     def step(i, ev=None):
         pools = layers[i % len(layers)]
-        duo.kv_append_circular_int8(*pools, table, k_tok, v_tok, lens_before, lens, mask, w.sink,
-                                    w.recent, w.ring_blocks)
+        append(*pools, table, k_tok, v_tok, lens_before, lens, mask, w.sink, w.recent,
+               w.ring_blocks)
         if ev is not None:
             duo.profile_next_launch(ev[0], ev[1])
-        duo.duo_attn_decode_int8(q, *pools, table, lens, mask, w.sink, w.recent, w.ring_blocks,
-                                 w.scale, out, ws)
+        decode(q, *pools, table, lens, mask, w.sink, w.recent, w.ring_blocks, w.scale, out, ws)
 
     for i in range(args.warmup):
         step(i)
@@ -418,23 +445,24 @@ def decode_int8_leg(args, torch, duo, dec):
     step_s = (t1 - t0) / args.steps
     kern_all = sample_kernels(torch, step, args.warmup + args.steps, KERNEL_SAMPLES, args.flush)
     kern_s = float(np.mean(kern_all))
-    nbytes = decode_bytes(w, np.full(w.batch, L), int8_cache=True)
+    nbytes = decode_bytes(w, np.full(w.batch, L), int8_cache=bits == 8, int4_cache=bits == 4)
     res = {
-        "workload": w.name + "-int8-kv", "value": round(nbytes / step_s / 1e9, 1), "unit": "GB/s",
-        "ms_per_step": round(step_s * 1e3, 4),
-        "step": "kv_append_circular_int8(1 token/seq) + duo_attn_decode_int8",
+        "workload": w.name + f"-int{bits}-kv", "value": round(nbytes / step_s / 1e9, 1),
+        "unit": "GB/s", "ms_per_step": round(step_s * 1e3, 4),
+        "step": f"kv_append_circular_int{bits}(1 token/seq) + duo_attn_decode_int{bits}",
         "algorithmic_bytes_per_step": nbytes,
         "step_speedup_vs_bf16": round(dec["ms_per_step"] / (step_s * 1e3), 3),
         "roofline": {"bound": "hbm", "achieved": round(nbytes / kern_s / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("decode_int8"),
-                     "kernel": "duo::decode_int8_kernel<bf16,128>",
+                     "traffic": measured_traffic(f"decode_int{bits}"),
+                     "kernel": f"duo::decode_int{bits}_kernel<bf16,128>",
                      "kernel_us": round(kern_s * 1e6, 2),
                      **spread_us(kern_all),
+                     "cold": f"{FLUSH_BYTES >> 20} MiB read before each sampled launch",
                      "algorithmic_bytes_per_launch": nbytes},
     }
-    log(f"[decode-int8] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
+    log(f"[{tag}] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
         f"{res['value']:.0f} GB/s per step, {nbytes / kern_s / 1e9:.0f} GB/s kernel, "
         f"{res['step_speedup_vs_bf16']}x the bf16 step")
     return res
@@ -659,6 +687,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
             val = float(r["Counter_Value"]) * 1024.0          # counters are KiB per dispatch
             if "decode_int8_kernel" in name:
                 acc.setdefault("decode_int8", []).append(val)
+            elif "decode_int4_kernel" in name:
+                acc.setdefault("decode_int4", []).append(val)
             elif "decode_kernel" in name:
                 acc.setdefault("decode", []).append(val)
             elif "prefill_kernel" in name:
@@ -686,7 +716,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
     calib = {"copy_bytes": known, "fetch_raw": fetch.get("copy"), "write_raw": write.get("copy"),
              "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
     rename = rename or {}
-    for k in ("decode", "decode_int8", "prefill", "dca"):
+    for k in ("decode", "decode_int8", "decode_int4", "prefill", "dca"):
         if k in fetch and k in write:
             leg = rename.get(k, k)
             out[leg] = {"source_sha": source_sha(leg),
@@ -707,7 +737,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="decode caches rotated across steps")
     ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=1)
-    ap.add_argument("--legs", default="decode,decode_int8,prefill,dca,gemma,1m")
+    ap.add_argument("--legs", default="decode,decode_int8,decode_int4,prefill,dca,gemma,1m")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -740,8 +770,9 @@ def main():
     gc.collect()
     gc.disable()
     args.flush = Flusher(torch)
-    dec = decode_leg(args, torch, duo) if legs & {"decode", "decode_int8"} else None
-    dq = decode_int8_leg(args, torch, duo, dec) if "decode_int8" in legs else None
+    dec = decode_leg(args, torch, duo) if legs & {"decode", "decode_int8", "decode_int4"} else None
+    dq = decode_quant_leg(args, torch, duo, dec, 8) if "decode_int8" in legs else None
+    d4 = decode_quant_leg(args, torch, duo, dec, 4) if "decode_int4" in legs else None
     pre = prefill_leg(args, torch, duo) if "prefill" in legs else None
     dca = dca_leg(args, torch, duo) if "dca" in legs else None
     gem = gemma_leg(args, torch, duo) if "gemma" in legs else None
@@ -772,6 +803,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": pre,
         "decode_int8": dq,
+        "decode_int4": d4,
         "dca_prefill": dca,
         "decode_gemma_2b_static": gem,
         "decode_1m_context": lng,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 8
+#define DUO_ATTN_ABI_VERSION 9
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -298,6 +298,63 @@ int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* 
                              int32_t split_tokens, void* stream);
 
 /*
+ * The 4-bit cache -- the same paged, per-head circular layout with 4-bit codes and one fp32 scale
+ * per kv head and channel for K and one for V.
+ *
+ * Source: DuoAttention README, installation section (the "w8a8kv4-per-channel" demo models) and
+ * efficiency section (8-bit weights and a 4-bit KV cache hold 3.3 million tokens of Llama-3-8B on
+ * one A100-80G). The pages fix no scheme beyond "4-bit" and "per channel"; this library's is:
+ *   scales   k_scale, v_scale float [num_kv_heads][head_dim], set by the caller (calibrated
+ *            offline) and the same for every token, so a new row is quantized on its own;
+ *   code     = x / s (a correctly rounded fp32 division) rounded half to even, clamped to [-7, 7];
+ *            a channel whose scale is 0 stores code 0. The row's value is code * s.
+ *   storage  a code c is the 4-bit number u = c + 8. Eight consecutive codes e0..e7 of a row form a
+ *            little-endian 32-bit word: bits 4i..4i+3 hold u(e_2i), bits 16+4i..16+4i+3 hold
+ *            u(e_2i+1), i = 0..3.
+ * Layout:
+ *   k_pool  uint8 [num_blocks][block_size][head_dim / 2]  (token-major: a row is head_dim / 8 words
+ *                                                          over channels 0, 1, ...)
+ *   v_pool  uint8 [num_blocks][head_dim][block_size / 2]  (channel-major: a row is block_size / 8
+ *                                                          words over slots 0, 1, ...)
+ * Block table, slots, lengths and every other convention are those of the 16-bit calls. q / out and
+ * the new rows are DUO_F16 or DUO_BF16; block_size is at least 16. The new rows must be finite and
+ * the scales finite and non-negative.
+ */
+
+/*
+ * kv_append_circular_int4 -- as kv_append_circular, quantizing each new K and V row with its kv
+ * head's scales (the scheme above) into the 4-bit pages. Codes are bit-exact functions of the row
+ * and the scales; the other codes of a word (other tokens of a V page row) are left as they were.
+ * Errors: as kv_append_circular, INVALID_ARG for a missing or misaligned scale array, UNSUPPORTED
+ * for DUO_F32 or block_size < 16.
+ */
+int32_t kv_append_circular_int4(uint8_t* k_pool, uint8_t* v_pool, const float* k_scale,
+                                const float* v_scale, const int32_t* block_table,
+                                int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                                int32_t batch, int32_t t_new, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                void* stream);
+
+/*
+ * duo_attn_decode_int4 -- as duo_attn_decode over the 4-bit cache: a score is softmax_scale times
+ * the sum over channels of q * k_scale * code, and a value row is code * v_scale per channel. The
+ * workspace is the one duo_attn_decode_workspace_size gives for the same sizes. Errors: as
+ * duo_attn_decode, INVALID_ARG for a missing or misaligned scale array, UNSUPPORTED for DUO_F32.
+ */
+int32_t duo_attn_decode_int4(const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                             int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, const uint8_t* head_is_retrieval, int32_t sink_size,
+                             int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             int32_t split_tokens, void* stream);
+
+/*
  * Dual Chunk Attention -- the prefill and decode of the vLLM PR "[Model] Implement DualChunkAttention
  * for Qwen2 Models" over this library's paged cache, each in one launch (the PR's brute-force form
  * calls an attention kernel three times per chunk and merges the results).
@@ -370,8 +427,8 @@ int32_t dca_attn_decode(const void* q, const void* q_succ, const void* q_inter,
 
 /*
  * duo_profile_next_launch -- a profiling hook for the caller's own timing. The next attention call
- * (duo_attn_decode, duo_attn_decode_int8, duo_attn_prefill, duo_attn_prefill_varlen,
- * dca_attn_prefill, dca_attn_decode) made from this host thread launches its kernel with
+ * (duo_attn_decode, duo_attn_decode_noalloc, duo_attn_decode_int8, duo_attn_decode_int4,
+ * duo_attn_prefill, duo_attn_prefill_varlen, dca_attn_prefill, dca_attn_decode) made from this host thread launches its kernel with
  * start_event and stop_event attached to the dispatch itself: the events take the kernel's own
  * start and end times, without the queue's gap before the dispatch. The events (hipEvent_t, timing
  * enabled) are created and owned by the caller; either may be NULL. The hook applies to that one

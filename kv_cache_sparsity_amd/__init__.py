@@ -28,7 +28,7 @@ STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "D
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
            "duo_attn_decode_noalloc",
            "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
-           "kv_append_circular_int8",
+           "kv_append_circular_int8", "kv_append_circular_int4", "duo_attn_decode_int4",
            "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
            "dca_attn_decode", "duo_profile_next_launch",
            "duo_status_string", "duo_abi_version")
@@ -81,6 +81,14 @@ def lib() -> ctypes.CDLL:
                                               _P]
         L.duo_attn_decode_int8.restype = _I32
         L.duo_attn_decode_int8.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32,
+                                           _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
+                                           _I32, _P]
+        L.kv_append_circular_int4.restype = _I32
+        L.kv_append_circular_int4.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                                              _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
+                                              _P]
+        L.duo_attn_decode_int4.restype = _I32
+        L.duo_attn_decode_int4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32,
                                            _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
                                            _I32, _P]
         L.duo_status_string.restype = ctypes.c_char_p
@@ -452,6 +460,74 @@ def duo_attn_decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_l
     _check("duo_attn_decode_int8", st)
 
 
+def _int4_pools(k_pool, v_pool, k_scale, v_scale):
+    """4-bit codes k uint8 [NB][bs][D/2], v uint8 [NB][D][bs/2]; float32 scales [Hkv][D]. Returns
+    (num_blocks, block_size, head_dim)."""
+    import torch
+    _check_tensor(k_pool, "k_pool", dtype=torch.uint8, ndim=3)
+    nb, bs, half_d = k_pool.shape
+    d = 2 * int(half_d)
+    _check_tensor(v_pool, "v_pool", dtype=torch.uint8, shape=(nb, d, bs // 2), like=k_pool)
+    _check_tensor(k_scale, "k_scale", dtype=torch.float32, shape=(None, d), like=k_pool)
+    _check_tensor(v_scale, "v_scale", dtype=torch.float32, shape=tuple(k_scale.shape), like=k_pool)
+    return int(nb), int(bs), d
+
+
+def kv_append_circular_int4(k_pool, v_pool, k_scale, v_scale, block_table, k_new, v_new,
+                            seq_lens_before, seq_lens_after, head_is_retrieval, sink_size: int,
+                            recent_size: int, ring_blocks: int, stream=None) -> None:
+    """Quantize and append new rows into the 4-bit cache: k_pool uint8 [NB][bs][D/2], v_pool uint8
+    [NB][D][bs/2], k_scale / v_scale float32 [Hkv][D] (per kv head and channel, read);
+    k_new / v_new [B][t_new][Hkv][D] float16 or bfloat16."""
+    num_blocks, block_size, head_dim = _int4_pools(k_pool, v_pool, k_scale, v_scale)
+    _check_tensor(k_new, "k_new", ndim=4)
+    batch, t_new, num_kv_heads, _ = k_new.shape
+    _check_tensor(k_new, "k_new", shape=(batch, t_new, num_kv_heads, head_dim))
+    _check_tensor(v_new, "v_new", shape=tuple(k_new.shape), like=k_new)
+    if k_new.device != k_pool.device:
+        _fail(f"k_new is on {k_new.device}, the pools on {k_pool.device}")
+    if int(k_scale.shape[0]) != num_kv_heads:
+        _fail(f"k_scale has {k_scale.shape[0]} kv heads, k_new {num_kv_heads}")
+    _check_tables(block_table, seq_lens_before, batch, num_kv_heads, k_pool, "seq_lens_before")
+    if seq_lens_after is not None:
+        _check_tensor(seq_lens_after, "seq_lens_after", dtype=_int32(), shape=(batch,), like=k_pool)
+    _check_gpu(k_pool, "k_pool")
+    mask = _HostMask(head_is_retrieval, num_kv_heads)
+    st = lib().kv_append_circular_int4(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), num_blocks,
+        block_size, block_table.shape[2], _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
+        _ptr(seq_lens_after), batch, t_new, num_kv_heads, head_dim, _dtype_tag(k_new), mask.ptr,
+        sink_size, recent_size, ring_blocks, _stream(stream))
+    _check("kv_append_circular_int4", st)
+
+
+def duo_attn_decode_int4(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                         head_is_retrieval, sink_size: int, recent_size: int, ring_blocks: int,
+                         softmax_scale: float, out, workspace, split_tokens: int = 0,
+                         stream=None) -> None:
+    """duo_attn_decode over the 4-bit cache (pools and scales as for kv_append_circular_int4)."""
+    num_blocks, block_size, head_dim = _int4_pools(k_pool, v_pool, k_scale, v_scale)
+    _check_tensor(q, "q", shape=(None, None, head_dim))
+    if q.device != k_pool.device:
+        _fail(f"q is on {q.device}, the pools on {k_pool.device}")
+    batch, num_q_heads, _ = q.shape
+    hkv = _kv_heads(block_table)
+    if int(k_scale.shape[0]) != hkv:
+        _fail(f"k_scale has {k_scale.shape[0]} kv heads, the block table {hkv}")
+    _check_tables(block_table, seq_lens, batch, hkv, q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, hkv)
+    st = lib().duo_attn_decode_int4(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        num_blocks, block_size, block_table.shape[2], _ptr(seq_lens), batch, num_q_heads, hkv,
+        head_dim, _dtype_tag(q), mask.ptr, sink_size, recent_size, ring_blocks, softmax_scale,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), split_tokens,
+        _stream(stream))
+    _check("duo_attn_decode_int4", st)
+
+
 def dca_attn_prefill_workspace_size(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int,
                                     head_dim: int, dtype: int) -> int:
     return int(lib().dca_attn_prefill_workspace_size(batch, q_len, num_q_heads, num_kv_heads,
@@ -538,7 +614,7 @@ def profile_next_launch(start_event=None, stop_event=None) -> None:
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill", "duo_attn_decode_noalloc",
            "NOALLOC_SCRATCH_BYTES",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
-           "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
+           "kv_append_circular_int4", "duo_attn_decode_int4", "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
            "profile_next_launch",
            "dca_prefill_workspace",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",

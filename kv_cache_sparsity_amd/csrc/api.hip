@@ -148,8 +148,9 @@ const char* duo_status_string(int32_t s) {
   }
 }
 
-// The append behind both caches: int8 = quantize each new row into codes + one scale per slot.
-static int32_t append_impl(bool int8, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+// The append behind the three caches. quant 8: each new row quantized into int8 codes + one scale
+// per slot (written); quant 4: 4-bit codes with the caller's per-(kv head, channel) scales (read).
+static int32_t append_impl(int quant, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                            const int32_t* block_table, int32_t num_blocks, int32_t block_size,
                            int32_t max_blocks_per_head, const void* k_new, const void* v_new,
                            const int32_t* seq_lens_before, int32_t* seq_lens_after, int32_t batch,
@@ -160,8 +161,8 @@ static int32_t append_impl(bool int8, void* k_pool, void* v_pool, float* k_scale
   if (!k_pool || !v_pool || !block_table || !k_new || !v_new || !seq_lens_before ||
       !head_is_retrieval)
     return DUO_ERR_INVALID_ARG;
-  if (int8 && (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16) ||
-               k_scale == v_scale))
+  if (quant != 0 && (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16) ||
+                     (quant == 8 && k_scale == v_scale)))
     return DUO_ERR_INVALID_ARG;
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens_before, 4) ||
@@ -173,6 +174,8 @@ static int32_t append_impl(bool int8, void* k_pool, void* v_pool, float* k_scale
   if (batch > 65535 || num_kv_heads > kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return DUO_ERR_UNSUPPORTED;
   if (!is_pow2(block_size) || block_size > 256) return DUO_ERR_UNSUPPORTED;
+  // a 4-bit V page row packs 8 slots to a word, and a run of 16 slots must sit in one page
+  if (quant == 4 && (block_size < 16 || dtype == DUO_F32)) return DUO_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_head * block_size > INT32_MAX) return DUO_ERR_INVALID_ARG;
   if (t_new > INT32_MAX - 64 * 16) return DUO_ERR_INVALID_ARG;
   uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
@@ -208,8 +211,10 @@ static int32_t append_impl(bool int8, void* k_pool, void* v_pool, float* k_scale
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   p.dtype = dtype;
-  const hipError_t e = int8 ? launch_append_int8(p, static_cast<hipStream_t>(stream))
-                            : launch_append(p, elem_bytes(dtype), static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = quant == 8 ? launch_append_int8(p, st)
+                       : quant == 4 ? launch_append_int4(p, st)
+                                    : launch_append(p, elem_bytes(dtype), st);
   return e == hipSuccess ? DUO_OK : DUO_ERR_HIP;
 }
 
@@ -220,7 +225,7 @@ int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_tabl
                            int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                            const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                            int32_t ring_blocks, void* stream) {
-  return append_impl(false, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks, block_size,
+  return append_impl(0, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks, block_size,
                      max_blocks_per_head, k_new, v_new, seq_lens_before, seq_lens_after, batch,
                      t_new, num_kv_heads, head_dim, dtype, head_is_retrieval, sink_size,
                      recent_size, ring_blocks, stream);
@@ -234,10 +239,25 @@ int32_t kv_append_circular_int8(int8_t* k_pool, int8_t* v_pool, float* k_scale, 
                                 int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
                                 int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
                                 void* stream) {
-  return append_impl(true, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks, block_size,
+  return append_impl(8, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks, block_size,
                      max_blocks_per_head, k_new, v_new, seq_lens_before, seq_lens_after, batch,
                      t_new, num_kv_heads, head_dim, dtype, head_is_retrieval, sink_size,
                      recent_size, ring_blocks, stream);
+}
+
+int32_t kv_append_circular_int4(uint8_t* k_pool, uint8_t* v_pool, const float* k_scale,
+                                const float* v_scale, const int32_t* block_table,
+                                int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_head, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                                int32_t batch, int32_t t_new, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                                int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                                void* stream) {
+  return append_impl(4, k_pool, v_pool, const_cast<float*>(k_scale), const_cast<float*>(v_scale),
+                     block_table, num_blocks, block_size, max_blocks_per_head, k_new, v_new,
+                     seq_lens_before, seq_lens_after, batch, t_new, num_kv_heads, head_dim, dtype,
+                     head_is_retrieval, sink_size, recent_size, ring_blocks, stream);
 }
 
 size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -264,8 +284,10 @@ struct DcaArgs {
   int32_t chunk_len;
 };
 
-// The decode behind both caches; dca != nullptr: Dual Chunk Attention (16-bit cache, full heads).
-static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const void* v_pool,
+// The decode behind the three caches (quant 0: 16-bit or fp32, 8: int8 codes + per-slot scales,
+// 4: 4-bit codes + per-(kv head, channel) scales); dca != nullptr: Dual Chunk Attention (16-bit
+// cache, full heads).
+static int32_t decode_impl(int quant, const void* q, const void* k_pool, const void* v_pool,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
                            int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
                            const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
@@ -279,8 +301,9 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                            head_is_retrieval);
   if (st != DUO_OK) return st;
-  if (int8 && (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16)))
+  if (quant != 0 && (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16)))
     return DUO_ERR_INVALID_ARG;
+  if (quant == 4 && dtype == DUO_F32) return DUO_ERR_UNSUPPORTED;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
   if (num_q_heads / num_kv_heads > 16) return DUO_ERR_UNSUPPORTED;
@@ -357,7 +380,7 @@ static int32_t decode_impl(bool int8, const void* q, const void* k_pool, const v
       return DUO_ERR_HIP;
     return DUO_OK;
   }
-  if (launch_decode(p, dtype, head_dim, int8, (int)grid, static_cast<hipStream_t>(stream)) !=
+  if (launch_decode(p, dtype, head_dim, quant, (int)grid, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DUO_ERR_HIP;
   return DUO_OK;
@@ -370,7 +393,7 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                         const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                         int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
                         size_t workspace_bytes, int32_t split_tokens, void* stream) {
-  return decode_impl(false, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
+  return decode_impl(0, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                      softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
@@ -384,7 +407,7 @@ int32_t duo_attn_decode_noalloc(const void* q, const void* k_pool, const void* v
                                 int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
                                 float softmax_scale, void* out, int32_t split_tokens,
                                 void* stream) {
-  return decode_impl(false, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
+  return decode_impl(0, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                      softmax_scale, out, nullptr, 0, split_tokens, stream, nullptr, true);
@@ -399,7 +422,22 @@ int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* 
                              int32_t recent_size, int32_t ring_blocks, float softmax_scale,
                              void* out, void* workspace, size_t workspace_bytes,
                              int32_t split_tokens, void* stream) {
-  return decode_impl(true, q, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks,
+  return decode_impl(8, q, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks,
+                     block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                     softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+int32_t duo_attn_decode_int4(const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t num_blocks, int32_t block_size,
+                             int32_t max_blocks_per_head, const int32_t* seq_lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, const uint8_t* head_is_retrieval, int32_t sink_size,
+                             int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             int32_t split_tokens, void* stream) {
+  return decode_impl(4, q, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks,
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                      softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
@@ -577,7 +615,7 @@ int32_t dca_attn_decode(const void* q, const void* q_succ, const void* q_inter,
   uint8_t all[kMaxKvHeads];
   for (int32_t h = 0; h < num_kv_heads; ++h) all[h] = 1;
   const DcaArgs dca{q_succ, q_inter, mscale, chunk_len};
-  return decode_impl(false, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
+  return decode_impl(0, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks,
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, all, 0, 1, 0, softmax_scale, out, workspace, workspace_bytes,
                      split_tokens, stream, &dca);

@@ -257,7 +257,108 @@ __global__ void __launch_bounds__(kAppendThreads) append_int8_kernel(const Appen
   }
 }
 
+// 4-bit code of x with a per-channel scale s (0 -> code 0): x / s correctly rounded, rounded half
+// to even and clamped to [-7, 7]; stored as u = code + 8.
+__device__ __forceinline__ uint32_t quant4_u(float x, float s) {
+  if (!(s > 0.f)) return 8u;
+  const float c = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -7.f), 7.f);
+  return (uint32_t)((int32_t)c + 8);
+}
+
+// Position of element e (0..7) of a run of 8 codes in its 32-bit word: even elements in the low
+// half, odd ones in the high half, 4 bits each, the first lowest.
+__device__ __forceinline__ int nibble_shift(int e) { return (e & 1) * 16 + (e >> 1) * 4; }
+
+// 4-bit cache: every new K and V row is quantized with the static scales of its kv head
+// (k_scale, v_scale [num_kv_heads][head_dim]). K rows (head_dim / 8 words, token-major) are written
+// whole. A V page row holds the block_size codes of one channel, 8 tokens to a word, so a token
+// changes half a byte of each channel's row: the run's codes are staged in LDS, and each word of
+// the run is written whole when this workgroup owns all 8 of its tokens, else merged with atomic
+// AND / OR on its own fields only (the other tokens of the word may belong to an earlier call, or
+// to another workgroup of this call when the ring window starts inside the run).
+__global__ void __launch_bounds__(kAppendThreads) append_int4_kernel(const AppendParams p) {
+  __shared__ uint8_t vstage[16][kMaxHeadDim];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int D = p.head_dim;
+  const AppendRun run = append_run(p, blockIdx.x, h, b);
+  const int32_t L0 = run.L0, t_lo = run.t_lo, t_hi = run.t_hi;
+  if (t_lo >= t_hi) return;
+  const int n_tok = t_hi - t_lo;
+  const int32_t bs_mask = (1 << p.log2_bs) - 1;
+  const int words = D / 8;   // words of a K row; one thread per word and token
+  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new);
+  uint8_t* kq = static_cast<uint8_t*>(p.k_pool);
+  uint32_t* vq = static_cast<uint32_t*>(p.v_pool);
+  const float* ks = p.k_scale + (int64_t)h * D;
+  const float* vs = p.v_scale + (int64_t)h * D;
+  const int64_t tok_stride = (int64_t)p.num_kv_heads * D;
+  const int64_t src0 = ((int64_t)b * p.t_new) * tok_stride + (int64_t)h * D;
+
+  for (int idx = threadIdx.x; idx < n_tok * words; idx += kAppendThreads) {
+    const int r = idx / words, j = idx % words;
+    const int32_t t = t_lo + r;
+    const int64_t src = src0 + (int64_t)(t - L0) * tok_stride + j * 8;
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(kn + src);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(vn + src);
+    const f32x4 ks0 = *reinterpret_cast<const f32x4*>(ks + j * 8);
+    const f32x4 ks1 = *reinterpret_cast<const f32x4*>(ks + j * 8 + 4);
+    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(vs + j * 8);
+    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(vs + j * 8 + 4);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t kb = (kw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const uint32_t vb = (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const float sk = e < 4 ? ks0[e] : ks1[e - 4];
+      const float sv = e < 4 ? vs0[e] : vs1[e - 4];
+      word |= quant4_u(elem_to_f32<uint16_t>(kb, p.dtype), sk) << nibble_shift(e);
+      vstage[r][j * 8 + e] = (uint8_t)quant4_u(elem_to_f32<uint16_t>(vb, p.dtype), sv);
+    }
+    const int32_t slot = run.slot_of(p, t);
+    const int64_t row = (run.page_of(p, slot) << p.log2_bs) + (slot & bs_mask);
+    *reinterpret_cast<uint32_t*>(kq + row * (D / 2) + j * 4) = word;
+  }
+  __syncthreads();
+  // V: the run's slots are consecutive inside one 16-slot-aligned run of one page (pages hold >= 16
+  // slots); this workgroup owns offsets [o_lo, o_lo + n_tok) of it.
+  const int32_t s_first = run.slot_of(p, t_lo);
+  const int32_t sr = s_first & ~15;
+  const int o_lo = s_first - sr;
+  const int64_t page = run.page_of(p, sr);
+  // channel d's row of the page: bs / 8 words; the run's two words start at word (sr % bs) / 8
+  uint32_t* vrow0 = vq + page * D * ((int64_t)1 << p.log2_bs) / 8 + (sr & bs_mask) / 8;
+  for (int idx = threadIdx.x; idx < 2 * D; idx += kAppendThreads) {
+    const int d = idx >> 1, w = idx & 1;
+    uint32_t val = 0, mask = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int o = 8 * w + e;
+      if (o >= o_lo && o < o_lo + n_tok) {
+        val |= (uint32_t)vstage[o - o_lo][d] << nibble_shift(e);
+        mask |= 0xFu << nibble_shift(e);
+      }
+    }
+    if (mask == 0) continue;
+    uint32_t* dst = vrow0 + (int64_t)d * ((int64_t)1 << p.log2_bs) / 8 + w;
+    if (mask == 0xffffffffu) {
+      *dst = val;
+    } else {
+      atomicAnd(dst, ~mask);
+      atomicOr(dst, val);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_int4(const AppendParams& p, hipStream_t stream) {
+  const int groups = p.t_new == 1 ? 1 : (p.t_new + 15) / 16 + 3;
+  const dim3 grid(groups, p.num_kv_heads, p.batch);
+  (void)hipGetLastError();  // report only this launch's status
+  hipLaunchKernelGGL(append_int4_kernel, grid, dim3(kAppendThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_int8(const AppendParams& p, hipStream_t stream) {
   const int groups = p.t_new == 1 ? 1 : (p.t_new + 15) / 16 + 3;

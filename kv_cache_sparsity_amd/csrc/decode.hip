@@ -68,11 +68,16 @@ __device__ __forceinline__ uint64_t load_coherent_pair(const float* p) {
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The decode body. Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
+// The decode body. Q4: the cache holds 4-bit codes (two per byte, in words of 8) with one fp32
+// scale per kv head and channel for K and for V ([num_kv_heads][head_dim]); the K scales multiply q
+// once per item, each code enters its MFMA as 24 + code (nib8_plus24), the 24 of a score is the same
+// for every key of a q head (softmax ignores it), and the output of a wave is
+// (O - 24 l) * v_scale per channel, with l the sum of the rounded weights PV multiplied.
+// Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
 // (k_scale, v_scale [num_blocks][block_size]); a score is (codes . q) * k_scale of its key, and a
 // key's weight enters PV as p * v_scale of the key (the row sum l takes p itself). Otherwise the row
 // sum l adds the weights as rounded for PV.
-template <typename T, int D, bool Q8, bool DCA = false>
+template <typename T, int D, bool Q8, bool DCA = false, bool Q4 = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int kDecodeWaves = decode_waves<D>();
   constexpr int kThreads = kDecodeWaves * kWave;
@@ -87,7 +92,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ int sm_ticket;
   __shared__ int sm_next_step;   // the segment's next unclaimed wave step
-  __shared__ int32_t sm_page[kRunSeg + 4];
+  __shared__ int32_t sm_page[kRunSeg + 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,6 +154,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const T* kpool = static_cast<const T*>(p.k_pool);
   const T* vpool = static_cast<const T*>(p.v_pool);
   const int8_t* kq = static_cast<const int8_t*>(p.k_pool);   // the int8 cache's codes (Q8)
+  const uint8_t* k4 = static_cast<const uint8_t*>(p.k_pool);  // the 4-bit cache's codes (Q4)
+  const uint8_t* v4 = static_cast<const uint8_t*>(p.v_pool);
   const int8_t* vq = static_cast<const int8_t*>(p.v_pool);
   const int64_t page_elems = (int64_t)D << p.log2_bs;
   const int bs = 1 << p.log2_bs;
@@ -162,8 +169,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       for (int c = 0; c < KC; ++c) {
         // Q8 takes each lane's K codes 16 at a time, so its k-step c pairs lane quad with head
         // dims (c / 2) * 64 + 16 * quad + 8 * (c % 2) .. +7; q must follow the same order
-        const int d0 = Q8 ? (c >> 1) * 64 + quad * 16 + (c & 1) * 8 : c * 32 + quad * 8;
-        qT[c] = (col < G) ? load8(qrow + d0) : zero8<T>();
+        // Q4 takes a lane's K codes D / 8 bytes at a time: k-step c pairs lane quad with head dims
+        // quad * D / 4 + 8 c .. +7, and q is taken times those channels' K scales
+        const int d0 = Q8 ? (c >> 1) * 64 + quad * 16 + (c & 1) * 8
+                          : Q4 ? quad * (D / 4) + c * 8 : c * 32 + quad * 8;
+        if constexpr (Q4) {
+          const T* qq = qrow + d0;
+          const float* ksc = p.k_scale + (int64_t)h * D + d0;
+          float qs[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qs[i] = (col < G) ? (float)qq[i] * ksc[i] : 0.f;
+          qT[c] = pack8<T>(qs);
+        } else {
+          qT[c] = (col < G) ? load8(qrow + d0) : zero8<T>();
+        }
       }
     }
     f32x4 oT[DT];
@@ -189,12 +208,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     // per chunk) puts key 8*(r/4) + 4*t' + r%4 of the chunk in MFMA row r, so the S^T accumulator
     // a lane holds for chunk c is keys 8*quad .. 8*quad+7 of the chunk: exactly the keys of its
     // V^T operand (channel dt*16 + col) and of its P^T operand.
-    constexpr int kChunks = 1;   // one 32-key chunk per step (measured best: two waves per SIMD)
+    // One 32-key chunk per step for 16-bit and int8 caches (measured best: two waves per SIMD).
+    // A 4-bit step moves a quarter of the bytes, so it takes four chunks (two at D = 256).
+    constexpr int kChunks = Q4 ? (D <= 128 ? 4 : 2) : 1;
     constexpr int kRunsPerStep = 2 * kChunks;
     v8<T> kA[kChunks][2][KC], vA[kChunks][DT];
     // Q8: the raw code words, converted only where the MFMAs take them, so that the look-ahead
     // loads are waited for at their use and not at their issue
     u32x2 kR[kChunks][2][KC], vR[kChunks][DT];
+    uint32_t kW[kChunks][2][KC], vW[kChunks][DT];   // Q4: the code words
     f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
     // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
     // S^T accumulators and of its P^T operand.
@@ -219,7 +241,23 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
-          if constexpr (Q8) {
+          if constexpr (Q4) {
+            // the lane's D / 8 bytes of the row: KC words, one per k-step
+            const uint8_t* src = k4 + (packed_page(pr) * page_elems + ((int64_t)packed_row0(pr) + krow) * D) / 2 +
+                                 quad * (D / 8);
+            if constexpr (KC == 2) {
+              const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+              kW[c][t][0] = w[0];
+              kW[c][t][1] = w[1];
+            } else {
+#pragma unroll
+              for (int i = 0; i < KC / 4; ++i) {
+                const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kW[c][t][4 * i + e] = w[e];
+              }
+            }
+          } else if constexpr (Q8) {
             // 16 codes per load: head dims 64 i + 16 quad .. +15, the lane's slots of k-steps
             // 2i and 2i + 1
 #pragma unroll
@@ -246,7 +284,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         const int64_t base = packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          if constexpr (Q8)
+          if constexpr (Q4)   // the lane's 8 slots of channel dt * 16 + col: one word
+            vW[c][dt] = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t*>(v4 + (base + (int64_t)(dt * 16 + col) * bs) / 2));
+          else if constexpr (Q8)
             vR[c][dt] = load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs);
           else
             vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
@@ -296,7 +337,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
             s[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-              if constexpr (Q8) s[c][t] = mfma16(codes_to_v8<T>(kR[c][t][kc]), qT[kc], s[c][t]);
+              if constexpr (Q4) s[c][t] = mfma16(nib8_plus24<T>(kW[c][t][kc]), qT[kc], s[c][t]);
+              else if constexpr (Q8) s[c][t] = mfma16(codes_to_v8<T>(kR[c][t][kc]), qT[kc], s[c][t]);
               else s[c][t] = mfma16(kA[c][t][kc], qT[kc], s[c][t]);
             }
           }
@@ -371,6 +413,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
             const v8<PT> pB = pack8<PT>(xv);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(codes_to_v8<PT>(vR[c][dt]), pB, oT[dt]);
+          } else if constexpr (Q4) {
+            // codes are always finite and absent keys weigh 0: no selection needed
+            const v8<T> pB = pack8<T>(x);
+            l_run = sum8(pB, l_run);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(nib8_plus24<T>(vW[c][dt]), pB, oT[dt]);
           } else {
             // the row sum adds exactly the rounded weights that PV multiplies
             const v8<T> pB = pack8<T>(x);
@@ -390,6 +438,16 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     // lanes sharing a column hold partial sums over disjoint keys
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
+    if constexpr (Q4) {
+      // every V operand was 24 + code: take 24 times the weights back out, then the channel scale
+      const float* vsc = p.v_scale + (int64_t)h * D + quad * 4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(vsc + dt * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oT[dt][j] = (oT[dt][j] - 24.f * l_run) * sc[j];
+      }
+    }
     if (quad == 0) {
       sm_m[wave][col] = m_run;
       sm_l[wave][col] = l_run;
@@ -623,6 +681,12 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_ke
   decode_body<T, D, true>(p);
 }
 
+// Decode over the 4-bit cache (one fp32 scale per kv head and channel for K and for V).
+template <typename T, int D>
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int4_kernel(const DecodeParams p) {
+  decode_body<T, D, false, false, true>(p);
+}
+
 // Dual Chunk Attention decode (16-bit cache, every kv head a full head).
 template <typename T, int D>
 __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_dca_kernel(const DecodeParams p) {
@@ -630,9 +694,16 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_dca_ker
 }
 
 template <typename T, int D>
-void launch_d(const DecodeParams& p, bool int8_cache, int grid, hipStream_t stream) {
+void launch_d(const DecodeParams& p, int quant, int grid, hipStream_t stream) {
   const LaunchEvents ev = current_launch_events();
-  if (int8_cache)
+  if constexpr (!std::is_same<T, float>::value) {
+    if (quant == 4) {
+      hipExtLaunchKernelGGL((decode_int4_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave),
+                            0, stream, ev.start, ev.stop, 0, p);
+      return;
+    }
+  }
+  if (quant == 8)
     hipExtLaunchKernelGGL((decode_int8_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0,
                           stream, ev.start, ev.stop, 0, p);
   else
@@ -648,12 +719,13 @@ void launch_dca_d(const DecodeParams& p, int grid, hipStream_t stream) {
 }
 
 template <typename T>
-hipError_t launch_t(const DecodeParams& p, int head_dim, bool int8_cache, int grid, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, int head_dim, int quant, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // report only this launch's status
+  if (quant == 4 && std::is_same<T, float>::value) return hipErrorInvalidValue;
   switch (head_dim) {
-    case 64: launch_d<T, 64>(p, int8_cache, grid, stream); break;
-    case 128: launch_d<T, 128>(p, int8_cache, grid, stream); break;
-    case 256: launch_d<T, 256>(p, int8_cache, grid, stream); break;
+    case 64: launch_d<T, 64>(p, quant, grid, stream); break;
+    case 128: launch_d<T, 128>(p, quant, grid, stream); break;
+    case 256: launch_d<T, 256>(p, quant, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -699,11 +771,11 @@ hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8_cache, int grid,
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int quant, int grid,
                          hipStream_t stream) {
-  if (dtype == 0) return launch_t<float>(p, head_dim, int8_cache, grid, stream);
-  if (dtype == 1) return launch_t<_Float16>(p, head_dim, int8_cache, grid, stream);
-  return launch_t<__bf16>(p, head_dim, int8_cache, grid, stream);
+  if (dtype == 0) return launch_t<float>(p, head_dim, quant, grid, stream);
+  if (dtype == 1) return launch_t<_Float16>(p, head_dim, quant, grid, stream);
+  return launch_t<__bf16>(p, head_dim, quant, grid, stream);
 }
 
 hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int grid,

@@ -74,6 +74,27 @@ __device__ __forceinline__ v8<T> codes_to_v8(u32x2 w) {
   return r;
 }
 
+// Eight 4-bit codes (one word of a 4-bit cache row: element 2i at bits 4i..4i+3, element 2i+1 at
+// bits 16+4i..16+4i+3, stored as u = code + 8) as an MFMA operand holding 16 + u = 24 + code for
+// every element, exactly: the bf16 with bits 0x4180 | (u << 3), the fp16 with bits 0x4C00 | (u << 6).
+// Two logic instructions per pair of elements; whoever multiplies the operand removes the offset 24.
+template <typename T>
+__device__ __forceinline__ v8<T> nib8_plus24(uint32_t w) {
+  u32x4 r;
+  if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+    r[0] = ((w << 3) & 0x00780078u) | 0x41804180u;
+    r[1] = ((w >> 1) & 0x00780078u) | 0x41804180u;
+    r[2] = ((w >> 5) & 0x00780078u) | 0x41804180u;
+    r[3] = ((w >> 9) & 0x00780078u) | 0x41804180u;
+  } else {
+    r[0] = ((w << 6) & 0x03C003C0u) | 0x4C004C00u;
+    r[1] = ((w << 2) & 0x03C003C0u) | 0x4C004C00u;
+    r[2] = ((w >> 2) & 0x03C003C0u) | 0x4C004C00u;
+    r[3] = ((w >> 6) & 0x03C003C0u) | 0x4C004C00u;
+  }
+  return __builtin_bit_cast(v8<T>, r);
+}
+
 template <typename T>
 __device__ __forceinline__ v8<T> pack8(const float* x) {
   v8<T> r;

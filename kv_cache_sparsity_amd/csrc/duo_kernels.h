@@ -21,8 +21,9 @@ struct AppendParams {
   int32_t batch, t_new, num_kv_heads, head_dim;
   int32_t sink, sink_blocks, ring_slots;
   uint64_t retrieval_bits;  // bit h set = kv head h is a retrieval head
-  // int8 cache only: one fp32 scale per slot ([num_blocks][block_size]) for K and for V, and the
-  // dtype of k_new / v_new
+  // int8 cache: one fp32 scale per slot ([num_blocks][block_size]) for K and for V (written);
+  // 4-bit cache: one per kv head and channel ([num_kv_heads][head_dim], read). Also the dtype of
+  // k_new / v_new.
   float* k_scale;
   float* v_scale;
   int32_t dtype;
@@ -35,8 +36,8 @@ struct DecodeParams {
   const int32_t* table;
   const int32_t* seq_lens;
   void* out;
-  const float* k_scale;   // int8 cache only: [num_blocks][block_size] per-slot scales of K
-  const float* v_scale;   // and of V
+  const float* k_scale;   // int8 cache: [num_blocks][block_size] per-slot scales of K;
+  const float* v_scale;   // and of V; 4-bit cache: [num_kv_heads][head_dim] per-channel scales
   float* partial;     // [batch][num_kv_heads][n_split][group][head_dim + 2]
   int32_t* counter;   // [batch][num_kv_heads]
   float* gpartial;    // [batch][num_kv_heads][n_group][group][head_dim + 2] (n_group > 0)
@@ -97,7 +98,9 @@ LaunchEvents current_launch_events();
 // Launchers (return the HIP launch status). dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t stream);
 hipError_t launch_append_int8(const AppendParams& p, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8_cache, int grid,
+hipError_t launch_append_int4(const AppendParams& p, hipStream_t stream);
+// quant: 0 = 16-bit / fp32 cache, 8 = int8 cache, 4 = 4-bit cache (dtype 1 or 2 only)
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int quant, int grid,
                          hipStream_t stream);
 hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int grid,
                              hipStream_t stream);

@@ -20,9 +20,9 @@ namespace {
 
 struct Launch {
   int kind = 0;           // 0 none, 1 append, 2 append int8, 3 decode, 4 decode dca, 5 prefill,
-                          // 6 prefill dca, 7 zero words
+                          // 6 prefill dca, 7 zero words, 8 append int4
   int grid = 0, dtype = -1, head_dim = 0;
-  bool int8 = false;
+  int quant = 0;
   duo::AppendParams ap{};
   duo::DecodeParams dp{};
   duo::PrefillParams pp{};
@@ -55,9 +55,12 @@ hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t) {
 hipError_t launch_append_int8(const AppendParams& p, hipStream_t) {
   Launch l; l.kind = 2; l.ap = p; record(l); return hipSuccess;
 }
-hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, bool int8, int grid,
+hipError_t launch_append_int4(const AppendParams& p, hipStream_t) {
+  Launch l; l.kind = 8; l.ap = p; record(l); return hipSuccess;
+}
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int quant, int grid,
                          hipStream_t) {
-  Launch l; l.kind = 3; l.dp = p; l.dtype = dtype; l.head_dim = head_dim; l.int8 = int8;
+  Launch l; l.kind = 3; l.dp = p; l.dtype = dtype; l.head_dim = head_dim; l.quant = quant;
   l.grid = grid; record(l); return hipSuccess;
 }
 hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int grid, hipStream_t) {
@@ -156,6 +159,24 @@ void append_cases() {
                                 (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_F16, m.p, 4, 16,
                                 2, nullptr) == DUO_OK);
   CHECK(launches_of(2) == 1);
+  // 4-bit append: bf16/fp16 rows, pages of at least 16 slots
+  CHECK(kv_append_circular_int4((uint8_t*)fake(), (uint8_t*)fake(), (const float*)fake(),
+                                (const float*)fake(4096), (const int32_t*)fake(), 64, 16, 8, fake(),
+                                fake(), (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16,
+                                m.p, 4, 16, 2, nullptr) == DUO_OK);
+  CHECK(launches_of(8) == 1);
+  CHECK(kv_append_circular_int4((uint8_t*)fake(), (uint8_t*)fake(), (const float*)fake(),
+                                (const float*)fake(4096), (const int32_t*)fake(), 64, 8, 16, fake(),
+                                fake(), (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16,
+                                m.p, 4, 16, 2, nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(kv_append_circular_int4((uint8_t*)fake(), (uint8_t*)fake(), (const float*)fake(),
+                                (const float*)fake(4096), (const int32_t*)fake(), 64, 16, 8, fake(),
+                                fake(), (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_F32,
+                                m.p, 4, 16, 2, nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(kv_append_circular_int4((uint8_t*)fake(), (uint8_t*)fake(), nullptr, (const float*)fake(),
+                                (const int32_t*)fake(), 64, 16, 8, fake(), fake(),
+                                (const int32_t*)fake(), nullptr, 2, 5, 2, 128, DUO_BF16, m.p, 4, 16,
+                                2, nullptr) == DUO_ERR_INVALID_ARG);
 }
 
 // ---- decode ---------------------------------------------------------------------------------------
@@ -177,7 +198,7 @@ void decode_cases() {
   if (g_launches.size() == 1) {
     const Launch& l = g_launches[0];
     const duo::DecodeParams& p = l.dp;
-    CHECK(l.kind == 3 && !l.int8 && l.head_dim == 128 && l.dtype == DUO_BF16);
+    CHECK(l.kind == 3 && l.quant == 0 && l.head_dim == 128 && l.dtype == DUO_BF16);
     CHECK(p.n_ret == 4 && p.n_str == 4 && p.group == 4);
     CHECK(p.split_tokens == 4096 && p.n_split == 8);
     CHECK(l.grid == 8 * 4 * 8 + 8 * 4);
@@ -233,7 +254,22 @@ void decode_cases() {
                              (const float*)fake(), (const float*)fake(), (const int32_t*)fake(),
                              100000, 16, 2048, (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16,
                              m.p, 64, 256, 16, 0.088f, fake(), fake(), ws, 0, nullptr) == DUO_OK);
-  CHECK(g_launches.size() == 1 && g_launches[0].int8);
+  CHECK(g_launches.size() == 1 && g_launches[0].quant == 8);
+  // 4-bit: per-channel scales required; 16-bit calls only
+  g_launches.clear();
+  CHECK(duo_attn_decode_int4(fake(), (const uint8_t*)fake(), (const uint8_t*)fake(),
+                             (const float*)fake(), (const float*)fake(4096), (const int32_t*)fake(),
+                             100000, 16, 2048, (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16,
+                             m.p, 64, 256, 16, 0.088f, fake(), fake(), ws, 0, nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 1 && g_launches[0].quant == 4);
+  CHECK(duo_attn_decode_int4(fake(), (const uint8_t*)fake(), (const uint8_t*)fake(),
+                             (const float*)fake(), (const float*)fake(4096), (const int32_t*)fake(),
+                             100000, 16, 2048, (const int32_t*)fake(), 8, 32, 8, 128, DUO_F32,
+                             m.p, 64, 256, 16, 0.088f, fake(), fake(), ws, 0, nullptr) == DUO_ERR_UNSUPPORTED);
+  CHECK(duo_attn_decode_int4(fake(), (const uint8_t*)fake(), (const uint8_t*)fake(), nullptr,
+                             (const float*)fake(4096), (const int32_t*)fake(), 100000, 16, 2048,
+                             (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16, m.p, 64, 256, 16,
+                             0.088f, fake(), fake(), ws, 0, nullptr) == DUO_ERR_INVALID_ARG);
 }
 
 void noalloc_cases() {
