@@ -77,20 +77,37 @@ __device__ __forceinline__ v8<T> codes_to_v8(u32x2 w) {
 // Eight 4-bit codes (one word of a 4-bit cache row: element 2i at bits 4i..4i+3, element 2i+1 at
 // bits 16+4i..16+4i+3, stored as u = code + 8) as an MFMA operand holding 16 + u = 24 + code for
 // every element, exactly: the bf16 with bits 0x4180 | (u << 3), the fp16 with bits 0x4C00 | (u << 6).
-// Two logic instructions per pair of elements; whoever multiplies the operand removes the offset 24.
+// Whoever multiplies the operand removes the offset 24. The mask and the exponent bits come in
+// registers (Nib4Consts, set once), so each pair is one shift and one fused AND-OR: a VOP3
+// instruction on gfx9 cannot carry the two 32-bit literals itself.
+struct Nib4Consts {
+  uint32_t mask, bits;
+};
 template <typename T>
-__device__ __forceinline__ v8<T> nib8_plus24(uint32_t w) {
-  u32x4 r;
-  if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
-    r[0] = ((w << 3) & 0x00780078u) | 0x41804180u;
-    r[1] = ((w >> 1) & 0x00780078u) | 0x41804180u;
-    r[2] = ((w >> 5) & 0x00780078u) | 0x41804180u;
-    r[3] = ((w >> 9) & 0x00780078u) | 0x41804180u;
+__device__ __forceinline__ Nib4Consts nib4_consts() {
+  Nib4Consts k;
+  if constexpr (__is_same(T, __bf16)) {
+    __asm__("v_mov_b32 %0, 0x00780078" : "=v"(k.mask));
+    __asm__("v_mov_b32 %0, 0x41804180" : "=v"(k.bits));
   } else {
-    r[0] = ((w << 6) & 0x03C003C0u) | 0x4C004C00u;
-    r[1] = ((w << 2) & 0x03C003C0u) | 0x4C004C00u;
-    r[2] = ((w >> 2) & 0x03C003C0u) | 0x4C004C00u;
-    r[3] = ((w >> 6) & 0x03C003C0u) | 0x4C004C00u;
+    __asm__("v_mov_b32 %0, 0x03C003C0" : "=v"(k.mask));
+    __asm__("v_mov_b32 %0, 0x4C004C00" : "=v"(k.bits));
+  }
+  return k;
+}
+template <typename T>
+__device__ __forceinline__ v8<T> nib8_plus24(uint32_t w, Nib4Consts k) {
+  u32x4 r;
+  if constexpr (__is_same(T, __bf16)) {
+    r[0] = ((w << 3) & k.mask) | k.bits;
+    r[1] = ((w >> 1) & k.mask) | k.bits;
+    r[2] = ((w >> 5) & k.mask) | k.bits;
+    r[3] = ((w >> 9) & k.mask) | k.bits;
+  } else {
+    r[0] = ((w << 6) & k.mask) | k.bits;
+    r[1] = ((w << 2) & k.mask) | k.bits;
+    r[2] = ((w >> 2) & k.mask) | k.bits;
+    r[3] = ((w >> 6) & k.mask) | k.bits;
   }
   return __builtin_bit_cast(v8<T>, r);
 }
