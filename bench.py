@@ -535,6 +535,100 @@ def prefill_leg(args, torch, duo):
     return res
 
 
+def continuous_batching_leg(args, torch, duo):
+    """A continuous-batching step (Llama-3-8B GQA shape, 32 sequences at 32768 tokens: one 4096-row
+    prompt chunk and 31 single decode rows) as one duo_attn_prefill_varlen launch, against the same
+    work as two calls (duo_attn_prefill on the chunk, duo_attn_decode on the 31 rows). The pools are
+    filled on the device with N(0,1) values; parity at this shape is in the GPU tests."""
+    w = synth.continuous_batching_step()
+    rows_n = w.extra["rows"]
+    dev = torch.device("cuda:0")
+    B, L, n0 = w.batch, w.context, rows_n[0]
+    log(f"[cb] {w.name}")
+    table_h, nblocks = synth.block_table(w)
+    table = torch.from_numpy(table_h).to(dev)
+    mask = w.retrieval_mask
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    kp = torch.randn((nblocks, w.block_size, w.head_dim), generator=g, device=dev).to(torch.bfloat16)
+    vp = torch.randn((nblocks, w.head_dim, w.block_size), generator=g, device=dev).to(torch.bfloat16)
+    total_q = sum(rows_n)
+    q = torch.randn((total_q, w.num_q_heads, w.head_dim), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    q_start = torch.from_numpy(np.concatenate([[0], np.cumsum(rows_n)]).astype(np.int32)).to(dev)
+    ws_mix = duo.prefill_varlen_workspace(q, table, mask, n0, B, w.block_size)
+    q_chunk = q[:n0].reshape(1, n0, w.num_q_heads, w.head_dim)
+    out_chunk = torch.empty_like(q_chunk)
+    ws_pre = duo.prefill_workspace(q_chunk, table[:1], mask)
+    q_dec = q[n0:].contiguous()
+    out_dec = torch.empty_like(q_dec)
+    ws_dec = duo.decode_workspace(q_dec, table[1:], w.block_size)
+
+    def mixed(ev=None):
+        if ev is not None:
+            duo.profile_next_launch(*ev)
+        duo.duo_attn_prefill_varlen(q, kp, vp, table, lens, q_start, n0, mask, w.sink, w.recent,
+                                    w.ring_blocks, w.scale, out, ws_mix)
+
+    def separate(ev=None):
+        if ev is not None:
+            duo.profile_next_launch(*ev[0])
+        duo.duo_attn_prefill(q_chunk, kp, vp, table[:1], lens[:1], mask, w.sink, w.recent,
+                             w.ring_blocks, w.scale, out_chunk, ws_pre)
+        if ev is not None:
+            duo.profile_next_launch(*ev[1])
+        duo.duo_attn_decode(q_dec, kp, vp, table[1:], lens[1:], mask, w.sink, w.recent,
+                            w.ring_blocks, w.scale, out_dec, ws_dec)
+
+    reps = max(4, args.prefill_passes * 2)
+    for _ in range(2):
+        mixed()
+        separate()
+    torch.cuda.synchronize()
+    res_m, res_p, res_d, wall_m, wall_s = [], [], [], [], []
+    for _ in range(reps):
+        e = event_pair(torch)
+        args.flush()
+        t0 = time.perf_counter()
+        mixed(e)
+        torch.cuda.synchronize()
+        wall_m.append(time.perf_counter() - t0)
+        res_m.append(e[0].elapsed_time(e[1]) * 1e-3)
+        e2 = (event_pair(torch), event_pair(torch))
+        args.flush()
+        t0 = time.perf_counter()
+        separate(e2)
+        torch.cuda.synchronize()
+        wall_s.append(time.perf_counter() - t0)
+        res_p.append(e2[0][0].elapsed_time(e2[0][1]) * 1e-3)
+        res_d.append(e2[1][0].elapsed_time(e2[1][1]) * 1e-3)
+    t_m = float(np.median(res_m))
+    t_p, t_d = float(np.median(res_p)), float(np.median(res_d))
+    w1 = synth.replace(w, batch=1)
+    flops = prefill_flops(w1, L, n0)
+    dbytes = decode_bytes(synth.replace(w, batch=B - 1), np.full(B - 1, L))
+    ideal = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) + dbytes / (HBM_PEAK_GBS * 1e9)
+    res = {"workload": w.name, "rows": f"1 x {n0} + {B - 1} x 1",
+           "one_launch_us": round(t_m * 1e6, 1),
+           "two_calls_us": {"prefill": round(t_p * 1e6, 1), "decode": round(t_d * 1e6, 1),
+                            "sum": round((t_p + t_d) * 1e6, 1)},
+           "one_launch_vs_two_calls": round((t_p + t_d) / t_m, 3),
+           "wall_us": {"one_launch": round(float(np.median(wall_m)) * 1e6, 1),
+                       "two_calls": round(float(np.median(wall_s)) * 1e6, 1)},
+           "roofline": {"bound": "mfma+hbm", "chunk_flops": flops, "decode_bytes": dbytes,
+                        "ideal_us": round(ideal * 1e6, 1),
+                        "achieved": round(ideal / t_m, 4), "peak": 1.0,
+                        "unit": "ideal time / kernel time",
+                        "frac": round(ideal / t_m, 4), "traffic": None,
+                        "kernel": "duo::prefill_kernel<bf16,128,mixed>",
+                        "note": "ideal = chunk FLOP at bf16 MFMA peak + decode-row bytes at HBM peak"},
+           "kernel_samples": reps}
+    log(f"[cb] one launch {t_m * 1e6:.1f} us; two calls {t_p * 1e6:.1f} + {t_d * 1e6:.1f} us; "
+        f"ideal {ideal * 1e6:.1f} us")
+    return res
+
+
 def dca_flops(w: synth.Workload, L: int, q_len: int) -> int:
     """4 D FLOP per (query, key) pair; every head sees keys 0..p (Dual Chunk Attention changes which
     query vector meets a key, not how many keys)."""
@@ -737,7 +831,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="decode caches rotated across steps")
     ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--prefill-warmup", type=int, default=1)
-    ap.add_argument("--legs", default="decode,decode_int8,decode_int4,prefill,dca,gemma,1m")
+    ap.add_argument("--legs", default="decode,decode_int8,decode_int4,prefill,dca,gemma,1m,cb")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -777,6 +871,7 @@ def main():
     dca = dca_leg(args, torch, duo) if "dca" in legs else None
     gem = gemma_leg(args, torch, duo) if "gemma" in legs else None
     lng = long_context_leg(args, torch, duo) if "1m" in legs else None
+    cbs = continuous_batching_leg(args, torch, duo) if "cb" in legs else None
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
     gc.enable()
@@ -807,6 +902,7 @@ def main():
         "dca_prefill": dca,
         "decode_gemma_2b_static": gem,
         "decode_1m_context": lng,
+        "continuous_batching": cbs,
     }
     print(json.dumps(line), flush=True)
 

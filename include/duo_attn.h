@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 9
+#define DUO_ATTN_ABI_VERSION 10
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -214,9 +214,23 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                          void* stream);
 
 /*
+ * duo_attn_prefill_varlen_workspace_size -- bytes of device workspace duo_attn_prefill_varlen needs
+ * for these sizes (total_q and max_q_len as passed to the call; max_blocks_per_head and block_size
+ * of the cache) and this retrieval/streaming split (head_is_retrieval: host, num_kv_heads bytes).
+ * It covers the prefill row tiles and, when num_q_heads / num_kv_heads <= 16, the split-K decode
+ * items of single-row sequences. Zero-fill it once after allocating; every completed call leaves it
+ * ready for the next. Returns 0 for invalid sizes.
+ */
+size_t duo_attn_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t dtype,
+                                              int32_t max_blocks_per_head, int32_t block_size,
+                                              const uint8_t* head_is_retrieval);
+
+/*
  * duo_attn_prefill_varlen -- duo_attn_prefill for a packed batch in which every sequence brings its
  * own number of query rows (prompt chunks and single decode tokens side by side, as a continuous-
- * batching step does).
+ * batching step does), in one launch.
  *
  * Source: as for duo_attn_prefill; the DualChunkAttention PR's description adds the per-sequence
  * prefill lengths to the attention metadata of a batched step, which is what q_start carries here.
@@ -229,9 +243,13 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
  *                       and to max_q_len rows, so malformed offsets give wrong rows, never a fault.
  *   seq_lens            device int32 [batch]: valid tokens AFTER the rows were appended; row i of
  *                       sequence b sits at position seq_lens[b] - n_b + i (n_b its number of rows).
- *   max_q_len           host bound on any sequence's rows: it sizes the launch (no host read of the
- *                       offsets), the workspace (duo_attn_prefill_workspace_size with
- *                       q_len = max_q_len) and the ring check.
+ *   max_q_len           host bound on any sequence's rows: with total_q it sizes the launch (no host
+ *                       read of the offsets) and it sets the ring check.
+ *   workspace           >= duo_attn_prefill_varlen_workspace_size(...) bytes, zero-filled once.
+ * The kernel numbers the row tiles the sequences actually have on the device (from q_start), so the
+ * launch holds about total_q / 256 + batch row tiles per head whatever the mix. A sequence with
+ * exactly one row (a decode step) is attended by split-K decode items in the same launch, as
+ * duo_attn_decode would (when num_q_heads / num_kv_heads <= 16; above that, by a row tile).
  * Everything else is as for duo_attn_prefill. Errors: as duo_attn_prefill, and INVALID_ARG for a
  * missing or misaligned q_start or total_q, max_q_len < 1.
  */

@@ -27,7 +27,7 @@ STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "D
           4: "DUO_ERR_WORKSPACE", 5: "DUO_ERR_HIP"}
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
            "duo_attn_decode_noalloc",
-           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen",
+           "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen", "duo_attn_prefill_varlen_workspace_size",
            "kv_append_circular_int8", "kv_append_circular_int4", "duo_attn_decode_int4",
            "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
            "dca_attn_decode", "duo_profile_next_launch",
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.duo_attn_prefill.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                        _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ,
                                        _P]
+        L.duo_attn_prefill_varlen_workspace_size.restype = _SZ
+        L.duo_attn_prefill_varlen_workspace_size.argtypes = [_I32] * 9 + [_P]
         L.duo_attn_prefill_varlen.restype = _I32
         L.duo_attn_prefill_varlen.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _I32,
                                               _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
@@ -388,14 +390,27 @@ def duo_attn_prefill_varlen(q, k_pool, v_pool, block_table, seq_lens, q_start, m
     _check("duo_attn_prefill_varlen", st)
 
 
-def prefill_varlen_workspace(q, block_table, head_is_retrieval, max_q_len: int, batch: int):
-    """Zero-filled workspace for duo_attn_prefill_varlen (q: [total_q][Hq][D])."""
+def duo_attn_prefill_varlen_workspace_size(batch: int, total_q: int, max_q_len: int,
+                                           num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                           dtype: int, max_blocks_per_head: int, block_size: int,
+                                           head_is_retrieval) -> int:
+    mask = _HostMask(head_is_retrieval, num_kv_heads)
+    return int(lib().duo_attn_prefill_varlen_workspace_size(
+        batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, dtype,
+        max_blocks_per_head, block_size, mask.ptr))
+
+
+def prefill_varlen_workspace(q, block_table, head_is_retrieval, max_q_len: int, batch: int,
+                             block_size: int):
+    """Zero-filled workspace for duo_attn_prefill_varlen (q: [total_q][Hq][D]; block_table
+    [batch][Hkv][max_blocks_per_head]; block_size of the cache)."""
     import torch
-    _, num_q_heads, d = q.shape
-    n = duo_attn_prefill_workspace_size(batch, max_q_len, num_q_heads, block_table.shape[1], d,
-                                        _dtype_tag(q), head_is_retrieval)
+    total_q, num_q_heads, d = q.shape
+    n = duo_attn_prefill_varlen_workspace_size(batch, total_q, max_q_len, num_q_heads,
+                                               block_table.shape[1], d, _dtype_tag(q),
+                                               block_table.shape[2], block_size, head_is_retrieval)
     if n == 0:
-        raise ValueError("invalid sizes for the prefill workspace")
+        raise ValueError("invalid sizes for the varlen prefill workspace")
     return torch.zeros(n, dtype=torch.uint8, device=q.device)
 
 
@@ -614,7 +629,8 @@ def profile_next_launch(start_event=None, stop_event=None) -> None:
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_prefill", "duo_attn_decode_noalloc",
            "NOALLOC_SCRATCH_BYTES",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",
-           "kv_append_circular_int4", "duo_attn_decode_int4", "prefill_varlen_workspace", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
+           "kv_append_circular_int4", "duo_attn_decode_int4", "prefill_varlen_workspace",
+           "duo_attn_prefill_varlen_workspace_size", "dca_attn_prefill", "dca_attn_prefill_workspace_size", "dca_attn_decode",
            "profile_next_launch",
            "dca_prefill_workspace",
            "duo_attn_decode_workspace_size", "decode_workspace", "duo_attn_prefill_workspace_size",

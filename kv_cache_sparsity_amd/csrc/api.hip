@@ -95,14 +95,25 @@ int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, in
 }
 
 // Prefill work layout: row tiles of prefill_rows() rows; retrieval items split their keys in
-// kPrefillSplits workgroups that merge through the workspace (tickets, then partials).
+// kPrefillSplits workgroups that merge through the workspace (tickets, then partials). Fixed-length
+// calls: n_qtiles tiles per sequence. Packed batches (total_q > 0): one list of the live tiles of
+// all sequences, at most ceil(total_q / rows) + batch - 1 long (each sequence leaves at most one
+// tile partly empty) and at most batch * ceil(q_len / rows).
 void prefill_plan(int32_t batch, int32_t q_len, int32_t hq, int32_t n_ret_kv, int32_t hkv,
                   int32_t head_dim, int32_t dtype, int32_t* n_qtiles, int64_t* ret_items,
-                  size_t* ws_bytes) {
+                  size_t* ws_bytes, int32_t total_q = 0) {
   const int eb = elem_bytes(dtype);
   const int rows = prefill_rows(eb, head_dim);
-  *n_qtiles = (q_len + rows - 1) / rows;
-  *ret_items = (int64_t)batch * n_ret_kv * (hq / hkv) * *n_qtiles;
+  const int64_t per_seq = (q_len + rows - 1) / rows;
+  if (total_q > 0) {
+    const int64_t bound = std::min<int64_t>((int64_t)batch * per_seq,
+                                            ((int64_t)total_q + rows - 1) / rows + batch - 1);
+    *n_qtiles = (int32_t)std::min<int64_t>(bound, INT32_MAX);
+    *ret_items = (int64_t)n_ret_kv * (hq / hkv) * *n_qtiles;
+  } else {
+    *n_qtiles = (int32_t)per_seq;
+    *ret_items = (int64_t)batch * n_ret_kv * (hq / hkv) * *n_qtiles;
+  }
   *ws_bytes = *ret_items == 0 ? 0
               : align256((size_t)*ret_items * sizeof(int32_t)) +
                 (size_t)*ret_items * kPrefillSplits * prefill_partial_floats(eb, head_dim) * sizeof(float);
@@ -489,15 +500,31 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
   st = check_stream_geometry(n_str, sink_size, recent_size, ring_blocks, block_size,
                              max_blocks_per_head, q_len);
   if (st != DUO_OK) return st;
+  const bool packed = q_start != nullptr;
   int32_t n_qt;
   int64_t ret_items;
   size_t need;
   prefill_plan(batch, q_len, num_q_heads, n_ret, num_kv_heads, head_dim, dtype, &n_qt, &ret_items,
-               &need);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+               &need, packed ? total_q : 0);
+  // Packed batches with a GQA group of at most 16 run their single-row sequences as split-K
+  // decode items in the same launch; their workspace follows the prefill's.
+  const bool mixed = packed && num_q_heads / num_kv_heads <= 16;
+  int32_t dS = 0, dns = 0;
+  size_t dneed = 0;
+  if (mixed) {
+    const int32_t st2 = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head,
+                                    block_size, batch * (n_ret > 0 ? n_ret : 1), 0, &dS, &dns, &dneed);
+    if (st2 != DUO_OK) return st2;
+  }
+  const size_t pneed = mixed ? align256(need) : need;
+  if (pneed + dneed > 0 &&
+      (!workspace || workspace_bytes < pneed + dneed || !aligned(workspace, 16)))
     return DUO_ERR_WORKSPACE;
-  const int64_t grid = ret_items * kPrefillSplits +
-                       (int64_t)batch * n_str * (num_q_heads / num_kv_heads) * n_qt;
+  const int64_t seqs = packed ? 1 : batch;
+  const int64_t n_prefill = ret_items * kPrefillSplits +
+                            seqs * n_str * (num_q_heads / num_kv_heads) * n_qt;
+  const int64_t n_decode = mixed ? (int64_t)batch * n_ret * dns + (int64_t)batch * n_str : 0;
+  const int64_t grid = n_prefill + n_decode;
   if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
 
   PrefillParams p{};
@@ -509,6 +536,7 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
   p.out = out;
   p.q_start = q_start;
   p.total_q = total_q;
+  p.skip_single_rows = mixed ? 1 : 0;
   p.counter = need > 0 ? static_cast<int32_t*>(workspace) : nullptr;
   p.partial = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                   align256((size_t)ret_items * sizeof(int32_t)))
@@ -539,6 +567,47 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
     p.chunk_tiles = dca->chunk_len / kPrefillKeyTile;
     if (launch_prefill_dca(p, dtype, head_dim, (int)grid, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
+      return DUO_ERR_HIP;
+    return DUO_OK;
+  }
+  if (mixed) {
+    DecodeParams d{};
+    d.q = q;
+    d.k_pool = k_pool;
+    d.v_pool = v_pool;
+    d.table = block_table;
+    d.seq_lens = seq_lens;
+    d.out = out;
+    d.q_start = q_start;
+    d.total_q = total_q;
+    char* dws = static_cast<char*>(workspace) + pneed;
+    const size_t ticket_bytes = decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size);
+    d.counter = reinterpret_cast<int32_t*>(dws);
+    d.gcounter = d.counter + (size_t)batch * num_kv_heads;
+    d.partial = reinterpret_cast<float*>(dws + ticket_bytes);
+    d.n_group = decode_merge_groups(dns);
+    d.gpartial = d.partial + (size_t)batch * num_kv_heads * dns * (num_q_heads / num_kv_heads) *
+                                 (head_dim + 2);
+    d.num_blocks = num_blocks;
+    d.log2_bs = p.log2_bs;
+    d.max_blocks_per_head = max_blocks_per_head;
+    d.batch = batch;
+    d.num_q_heads = num_q_heads;
+    d.num_kv_heads = num_kv_heads;
+    d.group = num_q_heads / num_kv_heads;
+    d.sink = sink_size;
+    d.recent = recent_size;
+    d.sink_blocks = p.sink_blocks;
+    d.ring_slots = p.ring_slots;
+    d.split_tokens = dS;
+    d.n_split = dns;
+    d.n_ret = n_ret;
+    d.n_str = n_str;
+    d.scale_log2 = p.scale_log2;
+    for (int32_t i = 0; i < n_ret; ++i) d.ret_heads[i] = ret[i];
+    for (int32_t i = 0; i < n_str; ++i) d.str_heads[i] = str[i];
+    if (launch_prefill_mixed(p, d, (int)n_prefill, dtype, head_dim, (int)grid,
+                             static_cast<hipStream_t>(stream)) != hipSuccess)
       return DUO_ERR_HIP;
     return DUO_OK;
   }
@@ -577,6 +646,35 @@ int32_t duo_attn_prefill_varlen(const void* q, const void* k_pool, const void* v
                       seq_lens, q_start, total_q, batch, max_q_len, num_q_heads, num_kv_heads,
                       head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                       softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+size_t duo_attn_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t dtype,
+                                              int32_t max_blocks_per_head, int32_t block_size,
+                                              const uint8_t* head_is_retrieval) {
+  if (batch < 1 || total_q < 1 || max_q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_kv_heads > kMaxKvHeads || num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) ||
+      !dtype_ok(dtype) || !head_is_retrieval || max_blocks_per_head < 1 || !is_pow2(block_size) ||
+      (int64_t)max_blocks_per_head * block_size > INT32_MAX)
+    return 0;
+  uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
+  int32_t n_ret, n_str;
+  if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str)) return 0;
+  int32_t n_qt;
+  int64_t ret_items;
+  size_t bytes;
+  prefill_plan(batch, max_q_len, num_q_heads, n_ret, num_kv_heads, head_dim, dtype, &n_qt,
+               &ret_items, &bytes, total_q);
+  if (num_q_heads / num_kv_heads <= 16) {
+    int32_t S, ns;
+    size_t dbytes;
+    if (decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
+                    batch * (n_ret > 0 ? n_ret : 1), 0, &S, &ns, &dbytes) != DUO_OK)
+      return 0;
+    bytes = align256(bytes) + dbytes;
+  }
+  return bytes > 0 ? bytes : 256;   // 0 means invalid arguments
 }
 
 size_t dca_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads,

@@ -1,0 +1,661 @@
+// The split-K decode work item, shared by the decode kernels (decode.hip) and the packed-batch
+// prefill kernel (prefill.hip), which runs decode items for its single-row sequences in the same
+// launch. What is computed, the work decomposition and the merge are described in decode.hip.
+#pragma once
+
+#include <type_traits>
+
+#include "duo_common.h"
+#include "duo_kernels.h"
+
+namespace duo {
+
+namespace {
+
+
+// Waves per workgroup: eight up to D = 128 (more loads in flight per CU); four at D = 256, where
+// eight waves' merge buffers would not fit in LDS next to a second workgroup.
+template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
+
+// Split merge: up to kFastMergeSplits splits per (sequence, kv head) take the two-phase merge
+// (weights in LDS, then the partial outputs with kMergeLoads 8-byte loads in flight per thread).
+constexpr int kMergeLoads = 32;
+
+// Two consecutive floats (8-byte aligned) read at device coherence, as the single floats are.
+__device__ __forceinline__ uint64_t load_coherent_pair(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The decode body. Q4: the cache holds 4-bit codes (two per byte, in words of 8) with one fp32
+// scale per kv head and channel for K and for V ([num_kv_heads][head_dim]); the K scales multiply q
+// once per item, each code enters its MFMA as 24 + code (nib8_plus24), the 24 of a score is the same
+// for every key of a q head (softmax ignores it), and the output of a wave is
+// (O - 24 l) * v_scale per channel, with l the sum of the rounded weights PV multiplied.
+// Q8: the cache holds int8 codes with one fp32 scale per slot and per K / V
+// (k_scale, v_scale [num_blocks][block_size]); a score is (codes . q) * k_scale of its key, and a
+// key's weight enters PV as p * v_scale of the key (the row sum l takes p itself). Otherwise the row
+// sum l adds the weights as rounded for PV.
+// LDS of one decode work item (decode_body's `lds`): per wave and q head the partial O, the max and
+// the row sum, then the staged page list, the merge ticket and the step counter.
+template <int kWaves, int D>
+struct DecodeLds {
+  static constexpr int kO = kWaves * 16 * D * 4;
+  static constexpr int kM = kWaves * 16 * 4;
+  static constexpr int kPage = (kRunSeg + 8) * 4;
+  static constexpr int kBytes = kO + 2 * kM + kPage + 16;
+};
+
+// One decode work item `blk` of the grid the host planned (see decode.hip), with `lds` pointing at
+// DecodeLds<kWavesT, D>::kBytes of LDS. kWavesT waves per workgroup.
+template <typename T, int D, bool Q8, bool DCA = false, bool Q4 = false, int kWavesT = decode_waves<D>()>
+__device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char* lds) {
+  constexpr int kDecodeWaves = kWavesT;
+  constexpr int kThreads = kDecodeWaves * kWave;
+  constexpr int KC = D / 32;  // k-steps of S^T over the head dim
+  constexpr int DT = D / 16;  // 16-row tiles of O^T
+  // PV operand type. An fp16 call over the int8 cache takes PV in bf16: a weight (up to 2^8 under
+  // the lazy max) times a V scale (up to 65504 / 127) can pass fp16's range, and every code is
+  // exact in bf16 as well.
+  using PT = typename std::conditional<Q8 && std::is_same<T, _Float16>::value, __bf16, T>::type;
+  using LB = DecodeLds<kDecodeWaves, D>;
+  float (*const sm_o)[16][D] = reinterpret_cast<float (*)[16][D]>(lds);
+  float (*const sm_m)[16] = reinterpret_cast<float (*)[16]>(lds + LB::kO);
+  float (*const sm_l)[16] = reinterpret_cast<float (*)[16]>(lds + LB::kO + LB::kM);
+  int32_t* const sm_page = reinterpret_cast<int32_t*>(lds + LB::kO + 2 * LB::kM);
+  int& sm_ticket = *reinterpret_cast<int*>(lds + LB::kO + 2 * LB::kM + LB::kPage);
+  int& sm_next_step = *reinterpret_cast<int*>(lds + LB::kO + 2 * LB::kM + LB::kPage + 4);  // the
+                                                         // segment's next unclaimed wave step
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int col = lane & 15;   // MFMA column = q head within the group
+  const int quad = lane >> 4;  // k-group of the lane
+  const int G = p.group;
+
+  // ---- which item -------------------------------------------------------------------------
+  const int n_ret_items = p.batch * p.n_ret * p.n_split;
+  int b, h, split;
+  bool ret;
+  if (blk < n_ret_items) {
+    split = blk % p.n_split;
+    const int bh = blk / p.n_split;
+    b = bh / p.n_ret;
+    h = p.ret_heads[bh % p.n_ret];
+    ret = true;
+  } else {
+    const int it = blk - n_ret_items;
+    b = it / p.n_str;
+    h = p.str_heads[it % p.n_str];
+    split = 0;
+    ret = false;
+  }
+  // The row of q and out: b, or in a packed batch the sequence's row when it has exactly one
+  // (a sequence with more rows is the prefill tiles' work: every item of it returns here, before
+  // any ticket).
+  int64_t qb = b;
+  if (p.q_start != nullptr) {
+    const int32_t s0 = min(max(p.q_start[b], 0), p.total_q);
+    const int32_t s1 = min(max(p.q_start[b + 1], s0), p.total_q);
+    if (s1 - s0 != 1) return;
+    qb = s0;
+  }
+  int32_t L = max(p.seq_lens[b], 0);
+  if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
+
+  HeadGeom geo;
+  geo.row = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
+  geo.num_blocks = p.num_blocks;
+  geo.log2_bs = p.log2_bs;
+  geo.sink = p.sink;
+  geo.sink_blocks = p.sink_blocks;
+  geo.ring_slots = p.ring_slots;
+
+  // ---- the item's runs ----------------------------------------------------------------------
+  RunList rl;
+  rl.ret = ret;
+  rl.L = L;
+  rl.first = rl.n_sink = rl.k_lo = rl.ring_lo = 0;
+  if (ret) {
+    const int32_t t0 = split * p.split_tokens;
+    const int32_t end = min(L, t0 + p.split_tokens);
+    rl.first = t0 / 16;
+    rl.n = end > t0 ? (end - t0 + 15) / 16 : 0;
+  } else {
+    rl.n_sink = (min(p.sink, L) + 15) / 16;
+    rl.ring_lo = max(p.sink, L - p.recent);
+    int32_t n_ring = 0;
+    if (L > p.sink) {
+      rl.k_lo = (rl.ring_lo - p.sink) / 16;
+      n_ring = (L - 1 - p.sink) / 16 - rl.k_lo + 1;
+    }
+    rl.n = rl.n_sink + n_ring;
+  }
+  const int32_t n_runs = rl.n;
+
+  const T* kpool = static_cast<const T*>(p.k_pool);
+  const T* vpool = static_cast<const T*>(p.v_pool);
+  const int8_t* kq = static_cast<const int8_t*>(p.k_pool);   // the int8 cache's codes (Q8)
+  const uint8_t* k4 = static_cast<const uint8_t*>(p.k_pool);  // the 4-bit cache's codes (Q4)
+  const uint8_t* v4 = static_cast<const uint8_t*>(p.v_pool);
+  const int8_t* vq = static_cast<const int8_t*>(p.v_pool);
+  const int64_t page_elems = (int64_t)D << p.log2_bs;
+  const int bs = 1 << p.log2_bs;
+
+  if (n_runs > 0) {
+    // ---- Q^T operand (B of S^T): column = q head, k = head-dim chunk ------------------------
+    v8<T> qT[KC];
+    {
+      const T* qrow = static_cast<const T*>(p.q) + (qb * p.num_q_heads + h * G + col) * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        // Q8 takes each lane's K codes 16 at a time, so its k-step c pairs lane quad with head
+        // dims (c / 2) * 64 + 16 * quad + 8 * (c % 2) .. +7; q must follow the same order
+        // Q4 takes a lane's K codes D / 8 bytes at a time: k-step c pairs lane quad with head dims
+        // quad * D / 4 + 8 c .. +7, and q is taken times those channels' K scales
+        const int d0 = Q8 ? (c >> 1) * 64 + quad * 16 + (c & 1) * 8
+                          : Q4 ? quad * (D / 4) + c * 8 : c * 32 + quad * 8;
+        if constexpr (Q4) {
+          const T* qq = qrow + d0;
+          const float* ksc = p.k_scale + (int64_t)h * D + d0;
+          float qs[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qs[i] = (col < G) ? (float)qq[i] * ksc[i] : 0.f;
+          qT[c] = pack8<T>(qs);
+        } else {
+          qT[c] = (col < G) ? load8(qrow + d0) : zero8<T>();
+        }
+      }
+    }
+    f32x4 oT[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) oT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    // Dual Chunk Attention: the chunk of the decoded position, the vector held in qT (0 q,
+    // 1 q_succ, 2 q_inter) and the scale with the sequence's mscale
+    int32_t cq = 0;
+    int q_kind = 0;
+    float sl2 = p.scale_log2;
+    // the three query bases as values (selecting among the parameter fields themselves would take
+    // their addresses and copy the parameter block to scratch)
+    const void* const q_intra = p.q;
+    const void* const q_succ = p.q_succ;
+    const void* const q_inter = p.q_inter;
+    if constexpr (DCA) {
+      cq = (L - 1) / p.chunk_len;
+      sl2 *= p.mscale[b];
+    }
+
+    // A wave step covers kChunks 32-key chunks (4 runs of 16 keys). In chunk c, K tile t' (two
+    // per chunk) puts key 8*(r/4) + 4*t' + r%4 of the chunk in MFMA row r, so the S^T accumulator
+    // a lane holds for chunk c is keys 8*quad .. 8*quad+7 of the chunk: exactly the keys of its
+    // V^T operand (channel dt*16 + col) and of its P^T operand.
+    const Nib4Consts n4 = Q4 ? nib4_consts<T>() : Nib4Consts{0u, 0u};
+    // One 32-key chunk per step for 16-bit and int8 caches (measured best: two waves per SIMD).
+    // A 4-bit step moves a quarter of the bytes, so it takes two chunks (measured on the
+    // Llama-3-8B shape: 36.0 us against 38.6 us with four chunks).
+    constexpr int kChunks = Q4 ? 2 : 1;
+    constexpr int kRunsPerStep = 2 * kChunks;
+    v8<T> kA[kChunks][2][KC], vA[kChunks][DT];
+    // Q8: the raw code words, converted only where the MFMAs take them, so that the look-ahead
+    // loads are waited for at their use and not at their issue
+    u32x2 kR[kChunks][2][KC], vR[kChunks][DT];
+    uint32_t kW[kChunks][2][KC], vW[kChunks][DT];   // Q4: the code words
+    f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
+    // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
+    // S^T accumulators and of its P^T operand.
+    auto load_scales = [&](const float* pool, int step, f32x4 (&dst)[kChunks][2]) {
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
+        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const f32x4* sp = reinterpret_cast<const f32x4*>(
+            pool + ((int64_t)packed_page(pr) << p.log2_bs) + packed_row0(pr) + (quad & 1) * 8);
+        dst[c][0] = __builtin_nontemporal_load(sp);
+        dst[c][1] = __builtin_nontemporal_load(sp + 1);
+      }
+    };
+    auto load_k = [&](int32_t seg0, int step) {
+      const int r = col;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int v = kRunsPerStep * step + 2 * c + (r >> 3);
+        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const int64_t base = packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+          if constexpr (Q4) {
+            // the lane's D / 8 bytes of the row: KC words, one per k-step
+            const uint8_t* src = k4 + (packed_page(pr) * page_elems + ((int64_t)packed_row0(pr) + krow) * D) / 2 +
+                                 quad * (D / 8);
+            if constexpr (KC == 2) {
+              const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+              kW[c][t][0] = w[0];
+              kW[c][t][1] = w[1];
+            } else {
+#pragma unroll
+              for (int i = 0; i < KC / 4; ++i) {
+                const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kW[c][t][4 * i + e] = w[e];
+              }
+            }
+          } else if constexpr (Q8) {
+            // 16 codes per load: head dims 64 i + 16 quad .. +15, the lane's slots of k-steps
+            // 2i and 2i + 1
+#pragma unroll
+            for (int i = 0; i < KC / 2; ++i) {
+              const u32x4 w = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4*>(kq + base + krow * D + i * 64 + quad * 16));
+              kR[c][t][2 * i] = u32x2{w[0], w[1]};
+              kR[c][t][2 * i + 1] = u32x2{w[2], w[3]};
+            }
+          } else {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+              kA[c][t][kc] = load8_stream(kpool + base + krow * D + kc * 32 + quad * 8);
+          }
+        }
+      }
+      if constexpr (Q8) load_scales(p.k_scale, step, kS);
+    };
+    auto load_v = [&](int32_t seg0, int step) {
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
+        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const int64_t base = packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          if constexpr (Q4)   // the lane's 8 slots of channel dt * 16 + col: one word
+            vW[c][dt] = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t*>(v4 + (base + (int64_t)(dt * 16 + col) * bs) / 2));
+          else if constexpr (Q8)
+            vR[c][dt] = load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs);
+          else
+            vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
+        }
+      }
+      if constexpr (Q8) load_scales(p.v_scale, step, vS);
+    };
+
+    for (int32_t seg0 = 0; seg0 < n_runs; seg0 += kRunSeg) {
+      const int32_t nseg = min(kRunSeg, n_runs - seg0);
+      if (seg0 > 0) __syncthreads();   // everyone is done with the previous segment's pages
+      load_pages<kThreads>(sm_page, geo, rl, seg0, nseg);
+      // runs past the end of the list read page 0 (valid memory, fully masked)
+      for (int i = nseg + (int)threadIdx.x; i < nseg + kRunsPerStep; i += kThreads) sm_page[i] = 0;
+      if (threadIdx.x == 0) sm_next_step = kDecodeWaves;
+      __syncthreads();
+      const int n_steps = (nseg + kRunsPerStep - 1) / kRunsPerStep;
+      int step = wave;
+      if (step < n_steps) {
+        load_k(seg0, step);
+        load_v(seg0, step);
+      }
+      // Wave w starts with step w; after that each wave claims the next unclaimed step, so waves
+      // that run ahead take more steps and all of them finish together.
+      while (step < n_steps) {
+        int nxt = 0;
+        if (lane == 0) nxt = atomicAdd(&sm_next_step, 1);
+        nxt = __builtin_amdgcn_readfirstlane(nxt);
+        const bool has_next = nxt < n_steps;
+        if constexpr (DCA) {
+          // all keys of the step share one chunk: choose the query vector for it (uniform)
+          const int32_t ck = (rl.first + seg0 + kRunsPerStep * step) * 16 / p.chunk_len;
+          const int need = ck == cq ? 0 : ck == cq - 1 ? 1 : 2;
+          if (need != q_kind) {
+            q_kind = need;
+            const void* base = need == 0 ? q_intra : need == 1 ? q_succ : q_inter;
+            const T* qrow = static_cast<const T*>(base) + (qb * p.num_q_heads + h * G + col) * D;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) qT[c] = (col < G) ? load8(qrow + c * 32 + quad * 8) : zero8<T>();
+          }
+        }
+        f32x4 s[kChunks][2];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            s[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+              if constexpr (Q4) s[c][t] = mfma16(nib8_plus24<T>(kW[c][t][kc], n4), qT[kc], s[c][t]);
+              else if constexpr (Q8) s[c][t] = mfma16(codes_to_v8<T>(kR[c][t][kc]), qT[kc], s[c][t]);
+              else s[c][t] = mfma16(kA[c][t][kc], qT[kc], s[c][t]);
+            }
+          }
+        f32x4 kS_cur[kChunks][2];   // this step's K scales (the next step's load replaces kS)
+        if constexpr (Q8) {
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c) {
+            kS_cur[c][0] = kS[c][0];
+            kS_cur[c][1] = kS[c][1];
+          }
+        }
+        if (has_next) load_k(seg0, nxt);   // next step's K streams in during this step's math
+        if constexpr (Q8) {   // scores of the int8 cache: (codes . q) * the key's K scale
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) s[c][t] *= kS_cur[c][t];
+        }
+
+        // Lane holds keys t0 + 8*(quad&1) + i of run 2c + quad/2, i = 4*t + j.
+        uint32_t keep[kChunks];
+        bool full = true;
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const Run rv = rl.at(geo, seg0 + kRunsPerStep * step + 2 * c + (quad >> 1));
+          const int32_t key0 = rv.t0 + (quad & 1) * 8;
+          keep[c] = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int32_t t = key0 + i;
+            keep[c] |= (uint32_t)((t >= rv.lo) && (t < rv.hi)) << i;
+          }
+          full = full && keep[c] == 0xFFu;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float e = ((keep[c] >> i) & 1u) ? s[c][i >> 2][i & 3] : -INFINITY;
+            s[c][i >> 2][i & 3] = e;
+            mloc = fmaxf(mloc, e);
+          }
+        }
+        mloc *= DCA ? sl2 : p.scale_log2;   // softmax_scale > 0: max commutes with the scale
+        // Lazy reference max, shared by the four lanes of a column: it moves only when a score
+        // exceeds it by more than 8 (log2 units), so the cross-lane max and the O rescale run on
+        // few steps; p = 2^(x - m_run) <= 256 in between.
+        if (__any(mloc > m_run + 8.f)) {
+          float mx = fmaxf(mloc, shfl_xor(mloc, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oT[dt] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            x[i] = fast_exp2(fmaf(s[c][i >> 2][i & 3], DCA ? sl2 : p.scale_log2, -m_use));
+          if constexpr (Q8) {
+            // weights times the keys' V scales; absent keys (whose scale may be anything) give 0.
+            // The row sum takes the fp32 weights: PV multiplies each one by its key's scale first.
+            float xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              l_run += x[i];
+              xv[i] = ((keep[c] >> i) & 1u) ? x[i] * vS[c][i >> 2][i & 3] : 0.f;
+            }
+            const v8<PT> pB = pack8<PT>(xv);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(codes_to_v8<PT>(vR[c][dt]), pB, oT[dt]);
+          } else if constexpr (Q4) {
+            // codes are always finite and absent keys weigh 0: no selection needed
+            const v8<T> pB = pack8<T>(x);
+            l_run = sum8(pB, l_run);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(nib8_plus24<T>(vW[c][dt], n4), pB, oT[dt]);
+          } else {
+            // the row sum adds exactly the rounded weights that PV multiplies
+            const v8<T> pB = pack8<T>(x);
+            l_run = sum8(pB, l_run);
+            if (!full) {
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) vA[c][dt] = select8<T>(vA[c][dt], keep[c]);
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
+          }
+        }
+        if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
+        step = nxt;
+      }
+    }
+    // lanes sharing a column hold partial sums over disjoint keys
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if constexpr (Q4) {
+      // every V operand was 24 + code: take 24 times the weights back out, then the channel scale
+      const float* vsc = p.v_scale + (int64_t)h * D + quad * 4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(vsc + dt * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oT[dt][j] = (oT[dt][j] - 24.f * l_run) * sc[j];
+      }
+    }
+    if (quad == 0) {
+      sm_m[wave][col] = m_run;
+      sm_l[wave][col] = l_run;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_o[wave][col][dt * 16 + quad * 4 + j] = oT[dt][j];
+    __syncthreads();
+
+    // ---- merge the waves; write the output (single item) or a partial -----------------------
+    const bool direct = !ret || p.n_split == 1;
+    float* part = p.partial + ((((int64_t)b * p.num_kv_heads + h) * p.n_split + split) * G) * (D + 2);
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, d = idx % D;
+      float M = sm_m[0][g];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float c = fast_exp2(sm_m[w][g] - Mu);
+        num += c * sm_o[w][g][d];
+        den += c * sm_l[w][g];
+      }
+      if (direct) {
+        T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + h * G + g) * D;
+        o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+      } else {
+        store_coherent(part + g * (D + 2) + d, num);
+        if (d == 0) {
+          store_coherent(part + g * (D + 2) + D, M);
+          store_coherent(part + g * (D + 2) + D + 1, den);
+        }
+      }
+    }
+    if (direct) return;
+  } else if (!ret || p.n_split == 1) {
+    // nothing visible (L == 0): zero output row(s)
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + h * G) * D;
+      o[idx] = from_f32<T>(0.f);
+    }
+    return;
+  }
+
+  // ---- split merge ----------------------------------------------------------------------------
+  // Partials were written with device-coherent (write-through) stores; waiting for them to
+  // complete before a ticket makes them visible to whichever workgroup, on any XCD, draws the
+  // last ticket, which reads them back with device-coherent loads. No cache-wide write-back or
+  // invalidate is needed, so other workgroups' cached K/V lines are left alone.
+  //
+  // Up to kMergeGroup splits per (b, h): the last item to arrive folds all partials into the
+  // output. More (n_group > 0): the last item of each group of kMergeGroup splits folds the
+  // group's partials into one record of the same form (unnormalised O, max, denominator), and the
+  // last group to finish folds the records into the output, so no single workgroup reads more than
+  // kMergeGroup partials per q head.
+  wait_stores_complete();
+  __syncthreads();
+  const int64_t row = (int64_t)b * p.num_kv_heads + h;
+  const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
+  T* const obase = static_cast<T*>(p.out) + (qb * p.num_q_heads + h * G) * D;
+  const int64_t rec_floats = (int64_t)G * (D + 2);
+
+  // Fold n_in records at src ([n_in][G][D + 2], all complete) into the output (rec == nullptr) or
+  // into the record rec: (1) per q head g, one wave reduces the records' (m, l) into the merged max
+  // and denominator and leaves each record's weight in LDS (the wave buffers are free by now);
+  // (2) out[g][d] = sum_s w[s][g] O_s[g][d], two channels per 8-byte load, each thread keeping
+  // kMergeLoads loads in flight across its outputs and the records.
+  auto fold_records = [&](const float* src, int n_in, float* rec) {
+    float* sm_w = &sm_o[0][0][0];   // [n_in][G]
+    constexpr int kR = kFastMergeSplits / kWave;
+    for (int g = wave; g < G; g += kDecodeWaves) {
+      float mv[kR], lv[kR];
+      float M = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int sp = lane + i * kWave;
+        const float* r = src + (int64_t)(max(min(sp, n_in - 1), 0) * G + g) * (D + 2);
+        mv[i] = sp < n_in ? load_coherent(r + D) : -INFINITY;
+        lv[i] = sp < n_in ? load_coherent(r + D + 1) : 0.f;
+        M = fmaxf(M, mv[i]);
+      }
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float den = 0.f;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) den += (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * lv[i];
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) den += shfl_xor(den, o);
+      // the output is normalised; a record keeps its max and denominator
+      const float inv = rec ? 1.f : (den > 0.f ? 1.f / den : 0.f);
+      if (rec && lane == 0) {
+        store_coherent(rec + g * (D + 2) + D, M);
+        store_coherent(rec + g * (D + 2) + D + 1, den);
+      }
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int sp = lane + i * kWave;
+        if (sp < n_in) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
+      }
+    }
+    __syncthreads();
+    const int pairs = G * D / 2;
+    auto fold = [&](auto KP) {
+      constexpr int kP = decltype(KP)::value;        // channel pairs per thread
+      constexpr int kCS = kMergeLoads / kP;          // records per round
+      float acc0[kP], acc1[kP];
+      int gk[kP];
+      int64_t off[kP];
+#pragma unroll
+      for (int k = 0; k < kP; ++k) {
+        const int pr = min(tid + k * kThreads, pairs - 1);
+        gk[k] = pr / (D / 2);
+        off[k] = (int64_t)gk[k] * (D + 2) + (pr % (D / 2)) * 2;
+        acc0[k] = acc1[k] = 0.f;
+      }
+      for (int s0 = 0; s0 < n_in; s0 += kCS) {
+        uint64_t v[kP][kCS];
+#pragma unroll
+        for (int k = 0; k < kP; ++k)
+#pragma unroll
+          for (int i = 0; i < kCS; ++i)
+            v[k][i] = load_coherent_pair(src + (int64_t)min(s0 + i, n_in - 1) * rec_floats + off[k]);
+#pragma unroll
+        for (int k = 0; k < kP; ++k)
+#pragma unroll
+          for (int i = 0; i < kCS; ++i) {
+            const float wgt = (s0 + i < n_in) ? sm_w[(s0 + i) * G + gk[k]] : 0.f;
+            acc0[k] += wgt * __uint_as_float((uint32_t)v[k][i]);
+            acc1[k] += wgt * __uint_as_float((uint32_t)(v[k][i] >> 32));
+          }
+      }
+#pragma unroll
+      for (int k = 0; k < kP; ++k) {
+        const int pr = tid + k * kThreads;
+        if (pr < pairs) {
+          const int d = (pr % (D / 2)) * 2;
+          if (rec) {
+            store_coherent(rec + off[k], acc0[k]);
+            store_coherent(rec + off[k] + 1, acc1[k]);
+          } else {
+            obase[gk[k] * D + d] = from_f32<T>(acc0[k]);
+            obase[gk[k] * D + d + 1] = from_f32<T>(acc1[k]);
+          }
+        }
+      }
+    };
+    const int ppt = (pairs + kThreads - 1) / kThreads;
+    if (ppt <= 1) fold(std::integral_constant<int, 1>{});
+    else if (ppt <= 2) fold(std::integral_constant<int, 2>{});
+    else if (ppt <= 4) fold(std::integral_constant<int, 4>{});
+    else fold(std::integral_constant<int, 8>{});
+  };
+
+  int32_t* ctr = p.counter + row;
+  if (p.n_group > 0) {
+    const int grp = split / kMergeGroup;
+    const int first = grp * kMergeGroup;
+    const int members = min(kMergeGroup, p.n_split - first);
+    int32_t* gctr = p.gcounter + row * p.n_group + grp;
+    if (tid == 0) sm_ticket = __hip_atomic_fetch_add(gctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sm_ticket != members - 1) return;
+    float* rec = p.gpartial + (row * p.n_group + grp) * rec_floats;
+    fold_records(p.partial + (row * p.n_split + first) * rec_floats,
+                 min(max(n_act - first, 0), kMergeGroup), rec);
+    if (tid == 0) __hip_atomic_store(gctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_stores_complete();
+    __syncthreads();
+    if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sm_ticket != p.n_group - 1) return;
+    // records of groups past the valid length hold max -inf and weigh nothing
+    fold_records(p.gpartial + row * p.n_group * rec_floats, (n_act + kMergeGroup - 1) / kMergeGroup,
+                 nullptr);
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (tid == 0) sm_ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sm_ticket != p.n_split - 1) return;
+  const float* base = p.partial + row * p.n_split * rec_floats;
+  if (n_act <= kFastMergeSplits) {
+    fold_records(base, n_act, nullptr);
+  } else {
+    // Many splits (a small split_tokens on a long context): one pass over the partials, online;
+    // a chunk of kMergeChunk splits is loaded at once, then folded into the running (M, num, den)
+    // of each (q head, channel).
+    constexpr int kMergeChunk = 16;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, d = idx % D;
+      float M = -INFINITY, num = 0.f, den = 0.f;
+      for (int s0 = 0; s0 < n_act; s0 += kMergeChunk) {
+        float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+          const float* rec = base + (int64_t)(min(s0 + i, n_act - 1) * G + g) * (D + 2);
+          mv[i] = load_coherent(rec + D);
+          lv[i] = load_coherent(rec + D + 1);
+          ov[i] = load_coherent(rec + d);
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+          if (s0 + i < n_act) {
+            const float mn = fmaxf(M, mv[i]);
+            const float keep = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
+            const float c = fast_exp2(mv[i] - mn);
+            num = num * keep + c * ov[i];
+            den = den * keep + c * lv[i];
+            M = mn;
+          }
+        }
+      }
+      obase[g * D + d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
+}  // namespace
+
+}  // namespace duo

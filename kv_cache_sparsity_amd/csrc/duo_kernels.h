@@ -56,6 +56,11 @@ struct DecodeParams {
   const void* q_inter;
   const float* mscale;
   int32_t chunk_len;
+  // packed batches (decode items inside the packed-batch prefill launch): sequence b's rows of q
+  // and out are [q_start[b], q_start[b+1]) clamped into [0, total_q); its items run only when it
+  // has exactly one row, which then takes the place of row b. null: row b.
+  const int32_t* q_start;
+  int32_t total_q;
 };
 
 struct PrefillParams {
@@ -68,9 +73,12 @@ struct PrefillParams {
   int32_t* counter;   // [retrieval items] arrival tickets (zero between calls)
   float* partial;     // [retrieval items][n_split] partial (m, l, O^T) of every row
   // packed (varlen) batches: rows [q_start[b], q_start[b+1]) of q / out belong to sequence b
-  // (at most q_len of them, clamped into [0, total_q)); null: b * q_len .. + q_len
+  // (at most q_len of them, clamped into [0, total_q)); null: b * q_len .. + q_len. Packed, the
+  // live row tiles of all sequences form one list of at most n_qtiles tiles.
   const int32_t* q_start;
   int32_t total_q;
+  // packed batches in one launch with decode items: a sequence with exactly one row is left to them
+  int32_t skip_single_rows;
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group;
   int32_t sink, recent, sink_blocks, ring_slots;
@@ -108,6 +116,10 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
                           hipStream_t stream);
 hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
                               hipStream_t stream);
+// The packed-batch prefill with split-K decode items for single-row sequences: blocks
+// [0, n_prefill) run prefill items, the rest decode items of dp.
+hipError_t launch_prefill_mixed(const PrefillParams& p, const DecodeParams& dp, int n_prefill,
+                                int dtype, int head_dim, int grid, hipStream_t stream);
 
 // The decode scratch of duo_attn_decode_noalloc: a device array of kNoAllocScratchBytes in the
 // library's code object (one copy per GPU). noalloc_scratch gives the current device's address of

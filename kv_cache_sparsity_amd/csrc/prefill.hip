@@ -52,6 +52,7 @@
 // the row's fp32 mscale, applied to the fp32 accumulators.
 #include <hip/hip_ext.h>
 
+#include "decode_body.h"
 #include "duo_common.h"
 #include "duo_kernels.h"
 
@@ -176,8 +177,78 @@ __device__ __forceinline__ void pipeline_lds_mfma() {
 template <int bytes, bool used>
 struct StageBytes { static constexpr int value = used ? bytes : 16; };
 
-template <typename T, int D, bool DCA>
-__global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(const PrefillParams p) {
+// Packed batches: the sequence and row tile of global row tile gt, where the live row tiles of the
+// sequences are numbered one after the other (sequence b owns ceil(n_b / rows) of them, or none
+// when its single row goes to a decode item). Every thread of the workgroup calls this; it returns
+// false when gt lies past the last live tile. The sequences are scanned kScan at a time (an
+// inclusive prefix sum in LDS); `scratch` holds kScan + 2 ints of LDS.
+template <int kThreads>
+__device__ __forceinline__ bool find_packed_tile(const PrefillParams& p, int rows, int gt, int* scratch,
+                                                 int* b_out, int* qt_out) {
+  constexpr int kScan = kThreads < 256 ? kThreads : 256;
+  const int tid = threadIdx.x;
+  int base = 0;   // live tiles of the sequences before this chunk
+  if (tid == 0) scratch[kScan] = -1;
+  for (int c0 = 0; c0 < p.batch; c0 += kScan) {
+    const int b = c0 + tid;
+    int tiles = 0;
+    if (tid < kScan && b < p.batch) {
+      const int32_t s0 = min(max(p.q_start[b], 0), p.total_q);
+      const int32_t s1 = min(max(p.q_start[b + 1], s0), p.total_q);
+      const int32_t n = min(s1 - s0, p.q_len);
+      tiles = (p.skip_single_rows && n == 1) ? 0 : (n + rows - 1) / rows;
+    }
+    __syncthreads();
+    if (tid < kScan) scratch[tid] = tiles;
+    __syncthreads();
+    for (int o = 1; o < kScan; o <<= 1) {
+      const int v = (tid < kScan && tid >= o) ? scratch[tid - o] : 0;
+      __syncthreads();
+      if (tid < kScan) scratch[tid] += v;
+      __syncthreads();
+    }
+    if (tid < kScan && tiles > 0) {
+      const int incl = base + scratch[tid];
+      if (gt < incl && gt >= incl - tiles) {
+        scratch[kScan] = b;
+        scratch[kScan + 1] = gt - (incl - tiles);
+      }
+    }
+    base += scratch[kScan - 1];
+    __syncthreads();
+    if (scratch[kScan] >= 0) break;
+  }
+  const int found = scratch[kScan];
+  *b_out = found;
+  *qt_out = scratch[kScan + 1];
+  __syncthreads();   // the scratch is the page list's: everybody has read it
+  return found >= 0;
+}
+
+// The stage ring as one block of LDS (the mixed kernel, whose decode items use its start).
+template <typename T, int D>
+struct PrefillLdsLayout {
+  using TG = TileGeo<T, D>;
+  static constexpr int kK23 = StageBytes<TG::kKBytes, TG::kStages == 4>::value;
+  static constexpr int kV23 = StageBytes<TG::kVBytes, TG::kStages == 4>::value;
+  static constexpr int kOffK0 = 0;
+  static constexpr int kOffV0 = TG::kKBytes;
+  static constexpr int kOffK1 = TG::kKBytes + TG::kVBytes;
+  static constexpr int kOffV1 = kOffK1 + TG::kKBytes;
+  static constexpr int kOffK2 = 2 * (TG::kKBytes + TG::kVBytes);
+  static constexpr int kOffV2 = kOffK2 + kK23;
+  static constexpr int kOffK3 = kOffV2 + kV23;
+  static constexpr int kOffV3 = kOffK3 + kK23;
+  static constexpr int kBytes = kOffV3 + kV23;
+};
+
+// MIX: a packed batch of prompt chunks and single decode rows in one launch. Blocks below
+// n_prefill are prefill items of the sequences with more than one row; the others are split-K
+// decode items (decode_body, the decode kernels' work item, over dp) that run for the sequences
+// with exactly one row. The stage ring is then one block of LDS, whose start the decode items use.
+template <typename T, int D, bool DCA, bool MIX>
+__global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(
+    const PrefillParams p, const DecodeParams dp, int n_prefill) {
   using TG = TileGeo<T, D>;
   constexpr int kThreads = TG::kThreads;
   constexpr int kWaves = TG::kWaves;
@@ -190,30 +261,55 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   // the stage ring (stages 2 and 3 only with four stages)
   constexpr int kK23 = StageBytes<TG::kKBytes, kStages == 4>::value;
   constexpr int kV23 = StageBytes<TG::kVBytes, kStages == 4>::value;
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TG::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TG::kVBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TG::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TG::kVBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds2[kK23];
-  __shared__ __attribute__((aligned(1024))) char v_lds2[kV23];
-  __shared__ __attribute__((aligned(1024))) char k_lds3[kK23];
-  __shared__ __attribute__((aligned(1024))) char v_lds3[kV23];
+  using LL = PrefillLdsLayout<T, D>;
+  constexpr int kSep = MIX ? 16 : 1;   // separate stage arrays (their size when unused: 16 bytes)
+  __shared__ __attribute__((aligned(1024))) char k_lds0[MIX ? 16 : TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[MIX ? 16 : TG::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[MIX ? 16 : TG::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[MIX ? 16 : TG::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[MIX ? 16 : kK23];
+  __shared__ __attribute__((aligned(1024))) char v_lds2[MIX ? 16 : kV23];
+  __shared__ __attribute__((aligned(1024))) char k_lds3[MIX ? 16 : kK23];
+  __shared__ __attribute__((aligned(1024))) char v_lds3[MIX ? 16 : kV23];
+  __shared__ __attribute__((aligned(1024))) char ring[MIX ? LL::kBytes : 16];
   __shared__ int32_t sm_run[kRunSeg];
   __shared__ int32_t sm_flags[kRunSeg / 4];   // per tile of the segment: see tile_flags
   __shared__ int sm_ticket;
+  (void)kSep;
+  if constexpr (MIX) {
+    static_assert(DecodeLds<TG::kWaves, D>::kBytes <= LL::kBytes, "decode items fit the ring");
+    if ((int)blockIdx.x >= n_prefill) {
+      decode_body<T, D, false, false, false, TG::kWaves>(dp, (int)blockIdx.x - n_prefill, ring);
+      return;
+    }
+  }
   auto kst = [&](auto C) -> char* {
     constexpr int c = decltype(C)::value;
-    if constexpr (c == 0) return k_lds0;
-    else if constexpr (c == 1) return k_lds1;
-    else if constexpr (c == 2) return k_lds2;
-    else return k_lds3;
+    if constexpr (MIX) {
+      if constexpr (c == 0) return ring + LL::kOffK0;
+      else if constexpr (c == 1) return ring + LL::kOffK1;
+      else if constexpr (c == 2) return ring + LL::kOffK2;
+      else return ring + LL::kOffK3;
+    } else {
+      if constexpr (c == 0) return k_lds0;
+      else if constexpr (c == 1) return k_lds1;
+      else if constexpr (c == 2) return k_lds2;
+      else return k_lds3;
+    }
   };
   auto vst = [&](auto C) -> char* {
     constexpr int c = decltype(C)::value;
-    if constexpr (c == 0) return v_lds0;
-    else if constexpr (c == 1) return v_lds1;
-    else if constexpr (c == 2) return v_lds2;
-    else return v_lds3;
+    if constexpr (MIX) {
+      if constexpr (c == 0) return ring + LL::kOffV0;
+      else if constexpr (c == 1) return ring + LL::kOffV1;
+      else if constexpr (c == 2) return ring + LL::kOffV2;
+      else return ring + LL::kOffV3;
+    } else {
+      if constexpr (c == 0) return v_lds0;
+      else if constexpr (c == 1) return v_lds1;
+      else if constexpr (c == 2) return v_lds2;
+      else return v_lds3;
+    }
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -223,8 +319,13 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   const int G = p.group;
 
   // ---- which item -------------------------------------------------------------------------------
+  // Row tiles come per sequence (fixed-length calls: sequence b's n_qtiles tiles), or, in a packed
+  // batch, as one list of the live tiles of all sequences (n_qtiles bounds its length), found on
+  // the device from q_start.
+  const bool packed = !DCA && p.q_start != nullptr;
   const int n_split = p.n_split;
-  const int per_tile_r = p.batch * p.n_ret * G;
+  const int seqs = packed ? 1 : p.batch;
+  const int per_tile_r = seqs * p.n_ret * G;
   const int ret_items = per_tile_r * p.n_qtiles;
   int b, hq, qt, split = 0, item = 0;
   bool ret;
@@ -241,7 +342,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     hq = p.ret_heads[r % p.n_ret] * G + r / p.n_ret;
     ret = true;
   } else {
-    const int per_tile_s = p.batch * p.n_str * G;
+    const int per_tile_s = seqs * p.n_str * G;
     const int it = blockIdx.x - ret_items * n_split;
     qt = p.n_qtiles - 1 - it / per_tile_s;
     int r = it % per_tile_s;
@@ -250,13 +351,18 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
     hq = p.str_heads[r % p.n_str] * G + r / p.n_str;
     ret = false;
   }
+  if constexpr (!DCA) {   // (Dual Chunk Attention takes no packed batches)
+    if (packed) {   // qt is the global live tile: which sequence and tile (the same for every split)
+      if (!find_packed_tile<kThreads>(p, kRows, qt, sm_run, &b, &qt)) return;
+    }
+  }
   const int h = hq / G;
   int32_t L = max(p.seq_lens[b], 0);
   if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
   // The sequence's query rows: rows [q0, q0 + qn) of q and out.
   int64_t q0;
   int32_t qn;
-  if (p.q_start != nullptr) {   // packed batch: bounds from the device, clamped into [0, total_q)
+  if (packed) {   // packed batch: bounds from the device, clamped into [0, total_q)
     const int32_t s0 = min(max(p.q_start[b], 0), p.total_q);
     const int32_t s1 = min(max(p.q_start[b + 1], s0), p.total_q);
     q0 = s0;
@@ -729,11 +835,31 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(c
   }
 }
 
-template <typename T, int D, bool DCA>
-void launch_d(const PrefillParams& p, int grid, hipStream_t stream) {
+template <typename T, int D, bool DCA, bool MIX = false>
+void launch_d(const PrefillParams& p, int grid, hipStream_t stream, const DecodeParams* dp = nullptr,
+              int n_prefill = 0) {
   const LaunchEvents ev = current_launch_events();
-  hipExtLaunchKernelGGL((prefill_kernel<T, D, DCA>), dim3(grid), dim3(TileGeo<T, D>::kThreads), 0,
-                        stream, ev.start, ev.stop, 0, p);
+  const DecodeParams none{};
+  hipExtLaunchKernelGGL((prefill_kernel<T, D, DCA, MIX>), dim3(grid), dim3(TileGeo<T, D>::kThreads),
+                        0, stream, ev.start, ev.stop, 0, p, dp ? *dp : none, n_prefill);
+}
+
+template <typename T>
+hipError_t launch_mixed_t(const PrefillParams& p, const DecodeParams& dp, int n_prefill,
+                          int head_dim, int grid, hipStream_t stream) {
+  (void)hipGetLastError();
+  switch (head_dim) {
+    case 64: launch_d<T, 64, false, true>(p, grid, stream, &dp, n_prefill); break;
+    case 128: launch_d<T, 128, false, true>(p, grid, stream, &dp, n_prefill); break;
+    case 256:
+      if constexpr (sizeof(T) == 2) {
+        launch_d<T, 256, false, true>(p, grid, stream, &dp, n_prefill);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -772,6 +898,13 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int g
   if (dtype == 0) return launch_t<float>(p, head_dim, grid, stream);
   if (dtype == 1) return launch_t<_Float16>(p, head_dim, grid, stream);
   return launch_t<__bf16>(p, head_dim, grid, stream);
+}
+
+hipError_t launch_prefill_mixed(const PrefillParams& p, const DecodeParams& dp, int n_prefill,
+                                int dtype, int head_dim, int grid, hipStream_t stream) {
+  if (dtype == 0) return launch_mixed_t<float>(p, dp, n_prefill, head_dim, grid, stream);
+  if (dtype == 1) return launch_mixed_t<_Float16>(p, dp, n_prefill, head_dim, grid, stream);
+  return launch_mixed_t<__bf16>(p, dp, n_prefill, head_dim, grid, stream);
 }
 
 hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,

@@ -201,6 +201,19 @@ def qwen2_72b_dca_prefill(chunk: int = 32768, chunks: int = 4, chunk_len: int = 
                     extra={"chunk_len": chunk_len})
 
 
+def continuous_batching_step(batch: int = 32, context: int = 32768, chunk: int = 4096) -> Workload:
+    """A continuous-batching step on the Llama-3-8B GQA shape (32 q / 8 kv heads, D 128, bf16, 4 of
+    8 kv heads retrieval, sink 64, recent 256, pages of 16): sequence 0 brings a 4096-row prompt
+    chunk that ends its 32768-token context, the other 31 sequences one decode row each at 32768
+    tokens. The ring holds a whole chunk's windows."""
+    bs, sink, recent = 16, 64, 256
+    rb = _ring_blocks_for(recent, chunk, bs)
+    return Workload(f"llama3-8b-gqa-continuous-batching-b{batch}-ctx{context}-chunk{chunk}", batch,
+                    32, 8, 128, BF16, bs, sink, recent, _pick_heads(2, 8, 4), context=context,
+                    q_len=chunk, ring_blocks=rb, max_blocks_per_head=_max_blocks(context, sink, rb, bs),
+                    seed=7, extra={"rows": [chunk] + [1] * (batch - 1)})
+
+
 def small(name: str, *, batch=2, q_heads=4, kv_heads=2, head_dim=64, dtype=BF16, block_size=16,
           sink=4, recent=24, retrieval=(0,), context=100, q_len=1, seed=11, ring_blocks=None,
           capacity=None) -> Workload:
@@ -219,6 +232,7 @@ ALL = {
     "gemma-2b-static-decode": gemma_2b_static_decode,
     "long-context-decode": long_context_decode,
     "qwen2-72b-dca-prefill": qwen2_72b_dca_prefill,
+    "continuous-batching-step": continuous_batching_step,
 }
 
 

@@ -20,7 +20,7 @@ namespace {
 
 struct Launch {
   int kind = 0;           // 0 none, 1 append, 2 append int8, 3 decode, 4 decode dca, 5 prefill,
-                          // 6 prefill dca, 7 zero words, 8 append int4
+                          // 6 prefill dca, 7 zero words, 8 append int4, 9 prefill + decode
   int grid = 0, dtype = -1, head_dim = 0;
   int quant = 0;
   duo::AppendParams ap{};
@@ -28,6 +28,7 @@ struct Launch {
   duo::PrefillParams pp{};
   duo::LaunchEvents ev{nullptr, nullptr};
   size_t zero_words = 0;
+  int n_prefill = 0;
 };
 std::vector<Launch> g_launches;
 int g_failures = 0;
@@ -70,6 +71,11 @@ hipError_t launch_decode_dca(const DecodeParams& p, int dtype, int head_dim, int
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int grid, hipStream_t) {
   Launch l; l.kind = 5; l.pp = p; l.dtype = dtype; l.head_dim = head_dim; l.grid = grid;
   record(l); return hipSuccess;
+}
+hipError_t launch_prefill_mixed(const PrefillParams& p, const DecodeParams& dp, int n_prefill,
+                                int dtype, int head_dim, int grid, hipStream_t) {
+  Launch l; l.kind = 9; l.pp = p; l.dp = dp; l.dtype = dtype; l.head_dim = head_dim; l.grid = grid;
+  l.n_prefill = n_prefill; record(l); return hipSuccess;
 }
 hipError_t launch_prefill_dca(const PrefillParams& p, int dtype, int head_dim, int grid,
                               hipStream_t) {
@@ -324,10 +330,33 @@ void prefill_cases() {
                                 (const int32_t*)fake(), nullptr, 4, 5000, 4096, 32, 32, 128,
                                 DUO_BF16, m.p, 128, 1024, 320, 0.088f, fake(), fake(), ws,
                                 nullptr) == DUO_ERR_INVALID_ARG);
+  // a continuous-batching step: one 4096-row chunk and 31 single rows, Llama-3-8B shape, one launch
+  Mask m8(8);
+  const size_t wv = duo_attn_prefill_varlen_workspace_size(32, 4127, 4096, 32, 8, 128, DUO_BF16, 2048,
+                                                           16, m8.p);
+  CHECK(wv > 0);
+  g_launches.clear();
   CHECK(duo_attn_prefill_varlen(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
-                                (const int32_t*)fake(), (const int32_t*)fake(), 1, 5000, 4096, 32,
-                                32, 128, DUO_BF16, m.p, 128, 1024, 320, 0.088f, fake(), fake(), ws,
+                                (const int32_t*)fake(), (const int32_t*)fake(), 32, 4127, 4096, 32,
+                                8, 128, DUO_BF16, m8.p, 64, 256, 272, 0.088f, fake(), fake(), wv,
                                 nullptr) == DUO_OK);
+  CHECK(g_launches.size() == 1);
+  if (g_launches.size() == 1) {
+    const Launch& l = g_launches[0];
+    // 48 live row tiles at most (17 for 4127 rows + 31); per tile 16 retrieval q heads x 2 splits
+    // and 16 streaming q heads; decode items: 32 sequences x 4 retrieval heads x 2 splits + 32 x 4
+    CHECK(l.kind == 9 && l.pp.n_qtiles == 48 && l.pp.skip_single_rows == 1);
+    CHECK(l.n_prefill == 48 * (16 * 2 + 16));
+    CHECK(l.grid == l.n_prefill + 32 * 4 * 2 + 32 * 4);
+    CHECK(l.dp.q_start == l.pp.q_start && l.dp.n_split == 2 && l.dp.split_tokens == 16384);
+    const size_t dec_off = (const char*)l.dp.counter - (const char*)fake();
+    CHECK(dec_off > 0 && dec_off % 256 == 0 && dec_off < wv);
+  }
+  CHECK(duo_attn_prefill_varlen(fake(), fake(), fake(), (const int32_t*)fake(), 100000, 16, 2048,
+                                (const int32_t*)fake(), (const int32_t*)fake(), 32, 4127, 4096, 32,
+                                8, 128, DUO_BF16, m8.p, 64, 256, 272, 0.088f, fake(), fake(), wv - 1,
+                                nullptr) == DUO_ERR_WORKSPACE);
+  CHECK(duo_attn_prefill_varlen_workspace_size(32, 0, 4096, 32, 8, 128, DUO_BF16, 2048, 16, m8.p) == 0);
   // all streaming: no workspace needed
   Mask none(32, 1000);
   none.p[0] = 0;

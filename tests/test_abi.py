@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 9
+    assert duo.abi_version() == 10
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"

@@ -376,7 +376,7 @@ def test_prefill_varlen_parity(case):
     q_start = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     qd = to_dev(packed, w.dtype)
     out = torch.full_like(qd, float("nan"))
-    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, max_q, B)
+    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, max_q, B, w.block_size)
     duo.duo_attn_prefill_varlen(qd, cache.k_pool, cache.v_pool, cache.table, cache.lens,
                                 torch.from_numpy(q_start).cuda(), max_q, cache.mask, w.sink,
                                 w.recent, w.ring_blocks, w.scale, out, ws)
@@ -549,6 +549,79 @@ def test_llama2_7b_mha_chunked_prefill_row_tiles():
         say(f"  chunk {c}: {len(rows)} rows x {w.num_q_heads} heads, max |gpu - oracle| = "
             f"{err:.3e} (tol {TOL[w.dtype]:.0e})")
         assert err <= TOL[w.dtype], (c, err)
+
+
+@pytest.mark.timeout(900)
+def test_continuous_batching_step_one_chunk_and_31_decode_rows():
+    """One packed call on the Llama-3-8B GQA shape at 32768 tokens: sequence 0 brings a 4096-row
+    chunk, sequences 1..31 one decode row each (run as split-K decode items in the same launch).
+    Every q head of every decode row is compared, and 512 rows of the chunk (32 in every 256-row
+    tile) on every q head. The oracle runs sequence by sequence while the cache is filled, so each
+    sequence's keys and values are drawn once."""
+    w = synth.continuous_batching_step()
+    rows_n = w.extra["rows"]
+    L = w.context
+    say(f"workload {w.name}")
+    cache = Cache(w, fill="nan")
+    B, Hq, G = w.batch, w.num_q_heads, w.group
+    q_start = np.concatenate([[0], np.cumsum(rows_n)]).astype(np.int32)
+    qs = [q_prefill(w, b, n)[b:b + 1] for b, n in enumerate(rows_n)]   # [1][n][Hq][D] each
+    packed = np.concatenate([q[0] for q in qs], axis=0)
+    rng = np.random.default_rng(17)
+    chunk_rows = _tile_rows(rows_n[0], 256, 32, rng)
+    want = {}
+    for b in range(B):
+        Kb = np.stack([synth.f32_to_storage(synth.kv_tokens(w, synth.S_K, b, h, 0, L), w.dtype)
+                       for h in range(w.num_kv_heads)])[None]
+        Vb = np.stack([synth.f32_to_storage(synth.kv_tokens(w, synth.S_V, b, h, 0, L), w.dtype)
+                       for h in range(w.num_kv_heads)])[None]
+        z = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, cache.table[b:b + 1],
+                               to_dev(np.ascontiguousarray(Kb.transpose(0, 2, 1, 3)), w.dtype),
+                               to_dev(np.ascontiguousarray(Vb.transpose(0, 2, 1, 3)), w.dtype),
+                               z, torch.empty_like(z), cache.mask, w.sink, w.recent, w.ring_blocks)
+        n = rows_n[b]
+        rows = chunk_rows if n > 1 else np.arange(1)
+        p = L - n + rows
+        for h in range(w.num_kv_heads):
+            ret = bool(cache.mask[h])
+            keys = (np.arange(L) if ret else
+                    np.union1d(np.arange(w.sink), np.arange(max(0, int(p.min()) - w.recent + 1), L)))
+            Kf = oracle.to_f64(Kb[0, h, keys], w.dtype)
+            Vf = oracle.to_f64(Vb[0, h, keys], w.dtype)
+            for hq in range(h * G, (h + 1) * G):
+                if ret or n == 1:
+                    want[(b, hq)] = oracle.attend_rows(oracle.to_f64(qs[b][0, rows, hq], w.dtype), p,
+                                                       Kf, Vf, keys, retrieval=ret, sink=w.sink,
+                                                       recent=w.recent, scale=w.scale)
+                else:   # a streaming head's chunk rows, tile by tile over their own windows
+                    out_rows = []
+                    for blk in np.array_split(np.arange(len(rows)), len(rows) // 32):
+                        pb = p[blk]
+                        kk = np.union1d(np.arange(w.sink),
+                                        np.arange(max(0, int(pb.min()) - w.recent + 1), int(pb.max()) + 1))
+                        sel = np.searchsorted(keys, kk)
+                        out_rows.append(oracle.attend_rows(
+                            oracle.to_f64(qs[b][0, rows[blk], hq], w.dtype), pb, Kf[sel], Vf[sel],
+                            kk, retrieval=False, sink=w.sink, recent=w.recent, scale=w.scale))
+                    want[(b, hq)] = np.concatenate(out_rows)
+    cache.set_lens(np.full(B, L))
+    say("  filled; oracle done")
+    qd = to_dev(packed, w.dtype)
+    out = torch.full_like(qd, float("nan"))
+    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, rows_n[0], B, w.block_size)
+    duo.duo_attn_prefill_varlen(qd, cache.k_pool, cache.v_pool, cache.table, cache.lens,
+                                torch.from_numpy(q_start).cuda(), rows_n[0], cache.mask, w.sink,
+                                w.recent, w.ring_blocks, w.scale, out, ws)
+    got = to_host_f64(out, w.dtype)
+    assert np.isfinite(got).all()
+    err_chunk = max(float(np.abs(got[q_start[0] + chunk_rows, hq] - want[(0, hq)]).max())
+                    for hq in range(Hq))
+    err_dec = max(float(np.abs(got[q_start[b], hq] - want[(b, hq)][0]).max())
+                  for b in range(1, B) for hq in range(Hq))
+    say(f"  chunk rows: max |gpu - oracle| = {err_chunk:.3e}; decode rows: {err_dec:.3e} "
+        f"(tol {TOL[w.dtype]:.0e})")
+    assert err_chunk <= TOL[w.dtype] and err_dec <= TOL[w.dtype]
 
 
 def test_gemma_2b_mqa_static_decode_with_garbage_past_lengths():

@@ -245,7 +245,7 @@ def test_random_shape_varlen_prefill_parity(i, _need_gpu):
     q_start = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     qd = to_dev(packed, dtype)
     out = torch.full_like(qd, float("nan"))
-    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, max_q, B)
+    ws = duo.prefill_varlen_workspace(qd, cache.table, cache.mask, max_q, B, w.block_size)
     duo.duo_attn_prefill_varlen(qd, cache.k_pool, cache.v_pool, cache.table, cache.lens,
                                 torch.from_numpy(q_start).cuda(), max_q, cache.mask, w.sink,
                                 w.recent, w.ring_blocks, w.scale, out, ws)
