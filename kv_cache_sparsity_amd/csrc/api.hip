@@ -77,14 +77,15 @@ size_t decode_counter_bytes(int32_t batch, int32_t hkv, int32_t cap) {
   return align256((size_t)batch * hkv * (1 + (size_t)groups) * sizeof(int32_t));
 }
 
-// rows: (sequence, retrieval kv head) pairs the split is sized for. The workspace-size query passes
-// batch (one retrieval head per sequence: the smallest split and the most partials any mask needs).
+// rows: (sequence, retrieval kv head) pairs the split is sized for; stream_window: sink + recent
+// when the call has streaming heads, else 0. The workspace-size queries pass rows = batch and no
+// window (one retrieval head per sequence: the smallest split and the most partials any mask needs).
 int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbph,
                     int32_t bs, int32_t rows, int32_t split_req, int32_t* split_tokens,
-                    int32_t* n_split, size_t* ws_bytes) {
+                    int32_t* n_split, size_t* ws_bytes, int32_t stream_window = 0) {
   if (split_req < 0 || (split_req % 128) != 0) return DUO_ERR_INVALID_ARG;
   const int32_t cap = mbph * bs;
-  const int32_t S = decode_split_tokens(rows, cap, split_req);
+  const int32_t S = decode_split_tokens(rows, cap, split_req, stream_window);
   const int32_t ns = (cap + S - 1) / S;
   const int32_t G = hq / hkv;
   *split_tokens = S;
@@ -327,8 +328,14 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   if (st != DUO_OK) return st;
   int32_t S, ns;
   size_t need;
+  // 16-bit caches: streaming items first, and the retrieval rows' last splits shortened by about
+  // one streaming item (for int8 and 4-bit caches a streaming item, bound by latency, is worth many
+  // more keys, and the streaming items keep their place after the retrieval items, where they
+  // overlap the merges)
+  const bool str_first = quant == 0 && n_str > 0 && split_tokens == 0;
   st = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
-                   batch * (n_ret > 0 ? n_ret : 1), split_tokens, &S, &ns, &need);
+                   batch * (n_ret > 0 ? n_ret : 1), split_tokens, &S, &ns, &need,
+                   str_first ? (int32_t)std::min<int64_t>((int64_t)sink_size + recent_size, INT32_MAX / 2) : 0);
   if (st != DUO_OK) return st;
   if (noalloc) {
     if (need > kNoAllocScratchBytes) return DUO_ERR_WORKSPACE;
@@ -376,6 +383,7 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   p.n_split = ns;
   p.n_ret = n_ret;
   p.n_str = n_str;
+  p.str_first = str_first ? 1 : 0;
   p.scale_log2 = softmax_scale * kLog2e;
   for (int32_t i = 0; i < n_ret; ++i) p.ret_heads[i] = ret[i];
   for (int32_t i = 0; i < n_str; ++i) p.str_heads[i] = str[i];

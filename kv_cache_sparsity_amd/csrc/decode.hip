@@ -13,8 +13,11 @@
 //   retrieval head: (b, h, split s) over keys [s*S, (s+1)*S), S = split_tokens;
 //   streaming head: (b, h) over its sink runs and the ring runs that meet the recent window.
 // The grid comes from static capacities only (no host read of the lengths); items past the valid
-// length exit at once. A wave processes steps of two 16-key runs (32 keys); waves take steps
-// round-robin and are merged in LDS at the end.
+// length exit at once. Streaming items come first in the grid and the last split of every
+// retrieval row last: with one workgroup per CU the streaming items run beside the first retrieval
+// splits, and the last splits, which the host makes shorter, start on the CUs they free. A wave
+// processes steps of two 16-key runs (32 keys; four runs for the 4-bit cache); wave w starts with
+// step w and then claims the next unclaimed step, and the waves are merged in LDS at the end.
 //
 // MFMA formulation (16x16x32, one k-step = 8 elements per lane). All q heads of a kv head (the GQA
 // group, G <= 16) ride in the 16 columns, so K and V are read once per kv head:

@@ -75,21 +75,38 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   const int G = p.group;
 
   // ---- which item -------------------------------------------------------------------------
-  const int n_ret_items = p.batch * p.n_ret * p.n_split;
+  // str_first: streaming items first, then the retrieval splits of every (sequence, retrieval
+  // head) row but its last, then the rows' last splits. With one workgroup per CU, the workgroups
+  // dispatched last start on the CUs that the short streaming items free, and the last splits are
+  // the shortest (the host sizes the splits for that). Otherwise the retrieval items (split
+  // fastest), then the streaming items, which start on the CUs of the first retrieval items done.
+  const int n_str_items = p.str_first ? p.batch * p.n_str : 0;
+  const int n_rows = p.batch * p.n_ret;
+  const int n_ret_items = n_rows * p.n_split;
   int b, h, split;
   bool ret;
-  if (blk < n_ret_items) {
-    split = blk % p.n_split;
-    const int bh = blk / p.n_split;
-    b = bh / p.n_ret;
-    h = p.ret_heads[bh % p.n_ret];
-    ret = true;
-  } else {
-    const int it = blk - n_ret_items;
+  if (blk < n_str_items || blk >= n_str_items + n_ret_items) {
+    const int it = blk < n_str_items ? blk : blk - n_ret_items;
     b = it / p.n_str;
     h = p.str_heads[it % p.n_str];
     split = 0;
     ret = false;
+  } else {
+    const int r = blk - n_str_items;
+    int row;
+    if (!p.str_first) {
+      split = r % p.n_split;
+      row = r / p.n_split;
+    } else if (r < n_rows * (p.n_split - 1)) {
+      split = r % (p.n_split - 1);
+      row = r / (p.n_split - 1);
+    } else {
+      split = p.n_split - 1;
+      row = r - n_rows * (p.n_split - 1);
+    }
+    b = row / p.n_ret;
+    h = p.ret_heads[row % p.n_ret];
+    ret = true;
   }
   // The row of q and out: b, or in a packed batch the sequence's row when it has exactly one
   // (a sequence with more rows is the prefill tiles' work: every item of it returns here, before

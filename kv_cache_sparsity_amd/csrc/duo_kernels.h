@@ -47,6 +47,9 @@ struct DecodeParams {
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t sink, recent, sink_blocks, ring_slots;
   int32_t split_tokens, n_split, n_ret, n_str;
+  // 1: streaming items first in the grid and the retrieval rows' last splits last (the host then
+  // shortens the last splits); 0: retrieval items (split fastest), then streaming items
+  int32_t str_first;
   float scale_log2;  // softmax_scale * log2(e)
   uint8_t ret_heads[kMaxKvHeads];
   uint8_t str_heads[kMaxKvHeads];
@@ -139,19 +142,31 @@ inline int32_t decode_merge_groups(int32_t n_split) {
 }
 // Up to this many splits per (sequence, kv head) the fused merge takes its two-phase fast path.
 constexpr int32_t kFastMergeSplits = 256;
-// Decode split size (keys per retrieval item) from static sizes: rows = batch x retrieval kv heads.
-// Shared by the workspace-size query and the call.
-inline int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested) {
+// Decode split size (keys per retrieval item) from static sizes. rows = (sequence, retrieval kv
+// head) pairs; stream_window = sink + recent when the call has streaming heads, else 0. Shared by
+// the workspace-size query (stream_window 0: the smallest split) and the call.
+//
+// About one retrieval item per CU (256 on MI355X): n = 256 / rows splits per row (at least 1, at
+// most kFastMergeSplits, so that the fused merge takes its fast path), S = capacity / n rounded up
+// to 64 keys, at least 256. With stream_window > 0 the streaming items come first in the grid and
+// the last split of every row comes last, so those last splits start on the CUs the streaming
+// items free: S grows by about one streaming item's keys (stream_window + 256) spread over the
+// row's splits, so that each last split is that much shorter and ends with the others.
+inline int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested,
+                                   int32_t stream_window = 0) {
   if (requested > 0) return requested;
-  // rows = (sequence, retrieval kv head) pairs. About one retrieval item per CU (256 on MI355X)
-  // at full capacity; but no item longer than 16384 keys (more, shorter items balance better than
-  // one very long one per CU), and at most kFastMergeSplits splits per row, so that the fused merge
-  // takes its fast path. Between 256 and 65536 keys per item.
   const int64_t r = rows > 0 ? rows : 1;
-  auto n_split = [&](int64_t s) { return (capacity_tokens + s - 1) / s; };
-  int64_t s = 256;
-  while (s < 65536 && ((s < 16384 && r * n_split(s) > 256) || n_split(s) > kFastMergeSplits)) s *= 2;
-  return (int32_t)s;
+  const int64_t cap = capacity_tokens > 0 ? capacity_tokens : 1;
+  int64_t n = 256 / r;
+  n = n < 1 ? 1 : n > kFastMergeSplits ? kFastMergeSplits : n;
+  int64_t s = ((cap + n - 1) / n + 63) / 64 * 64;
+  if (s < 256) s = 256;
+  if (stream_window > 0 && n > 1) {
+    // nearest multiple of 64; kept only while every split still holds keys
+    const int64_t st = ((cap + stream_window + 256 + n - 1) / n + 32) / 64 * 64;
+    if (st > s && (n - 1) * st < cap) s = st;
+  }
+  return (int32_t)(s < (int64_t)(INT32_MAX / 64) * 64 ? s : (int64_t)(INT32_MAX / 64) * 64);
 }
 
 // Prefill workgroup shape: eight waves (two per SIMD, 32 query rows each) while one 64-key K+V tile

@@ -206,7 +206,9 @@ void decode_cases() {
     const duo::DecodeParams& p = l.dp;
     CHECK(l.kind == 3 && l.quant == 0 && l.head_dim == 128 && l.dtype == DUO_BF16);
     CHECK(p.n_ret == 4 && p.n_str == 4 && p.group == 4);
-    CHECK(p.split_tokens == 4096 && p.n_split == 8);
+    // 8 splits per row; with streaming heads each split grows by (64 + 256 + 256) / 8 keys, to the
+    // nearest 64, so that the last splits (dispatched last) are shorter: 7 x 4160 + 3648
+    CHECK(p.split_tokens == 4160 && p.n_split == 8 && p.str_first == 1);
     CHECK(l.grid == 8 * 4 * 8 + 8 * 4);
     for (int i = 0; i < p.n_ret; ++i) CHECK(m.p[p.ret_heads[i]] == 1);
     for (int i = 0; i < p.n_str; ++i) CHECK(m.p[p.str_heads[i]] == 0);
@@ -219,7 +221,9 @@ void decode_cases() {
   // it is exactly what the call needs
   const size_t ws4096 = duo_attn_decode_workspace_size(8, 32, 8, 128, 2048, 16, 4096);
   CHECK(ws4096 > 0 && ws4096 <= ws);
+  g_launches.clear();
   CHECK(decode(m, 8, 32, 8, 128, 2048, ws4096, 4096) == DUO_OK);
+  CHECK(g_launches.size() == 1 && g_launches[0].dp.str_first == 0 && g_launches[0].dp.split_tokens == 4096);
   CHECK(decode(m, 8, 32, 8, 128, 2048, ws4096 - 1, 4096) == DUO_ERR_WORKSPACE);
   CHECK(decode(m, 8, 32, 8, 128, 2048, 0, 0) == DUO_ERR_WORKSPACE);
   CHECK(decode(m, 8, 128, 4, 128, 2048, ws, 0) == DUO_ERR_UNSUPPORTED);    // group 32
@@ -261,6 +265,8 @@ void decode_cases() {
                              100000, 16, 2048, (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16,
                              m.p, 64, 256, 16, 0.088f, fake(), fake(), ws, 0, nullptr) == DUO_OK);
   CHECK(g_launches.size() == 1 && g_launches[0].quant == 8);
+  if (g_launches.size() == 1)   // the int8 cache keeps the streaming items last and plain splits
+    CHECK(g_launches[0].dp.str_first == 0 && g_launches[0].dp.split_tokens == 4096);
   // 4-bit: per-channel scales required; 16-bit calls only
   g_launches.clear();
   CHECK(duo_attn_decode_int4(fake(), (const uint8_t*)fake(), (const uint8_t*)fake(),
