@@ -523,39 +523,43 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   auto fold_records = [&](const float* src, int n_in, float* rec) {
     float* sm_w = &sm_o[0][0][0];   // [n_in][G]
     constexpr int kR = kFastMergeSplits / kWave;
-    for (int g = wave; g < G; g += kDecodeWaves) {
-      float mv[kR], lv[kR];
-      float M = -INFINITY;
+    auto weights = [&]() {
+      for (int g = wave; g < G; g += kDecodeWaves) {
+        float mv[kR], lv[kR];
+        float M = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kR; ++i) {
-        const int sp = lane + i * kWave;
-        const float* r = src + (int64_t)(max(min(sp, n_in - 1), 0) * G + g) * (D + 2);
-        mv[i] = sp < n_in ? load_coherent(r + D) : -INFINITY;
-        lv[i] = sp < n_in ? load_coherent(r + D + 1) : 0.f;
-        M = fmaxf(M, mv[i]);
+        for (int i = 0; i < kR; ++i) {
+          const int sp = lane + i * kWave;
+          const float* r = src + (int64_t)(max(min(sp, n_in - 1), 0) * G + g) * (D + 2);
+          mv[i] = sp < n_in ? load_coherent(r + D) : -INFINITY;
+          lv[i] = sp < n_in ? load_coherent(r + D + 1) : 0.f;
+          M = fmaxf(M, mv[i]);
+        }
+#pragma unroll
+        for (int o = kWave / 2; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float den = 0.f;
+#pragma unroll
+        for (int i = 0; i < kR; ++i) den += (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * lv[i];
+#pragma unroll
+        for (int o = kWave / 2; o >= 1; o >>= 1) den += shfl_xor(den, o);
+        // the output is normalised; a record keeps its max and denominator
+        const float inv = rec ? 1.f : (den > 0.f ? 1.f / den : 0.f);
+        if (rec && lane == 0) {
+          store_coherent(rec + g * (D + 2) + D, M);
+          store_coherent(rec + g * (D + 2) + D + 1, den);
+        }
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          const int sp = lane + i * kWave;
+          if (sp < n_in) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
+        }
       }
-#pragma unroll
-      for (int o = kWave / 2; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
-      const float Mu = (M == -INFINITY) ? 0.f : M;
-      float den = 0.f;
-#pragma unroll
-      for (int i = 0; i < kR; ++i) den += (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * lv[i];
-#pragma unroll
-      for (int o = kWave / 2; o >= 1; o >>= 1) den += shfl_xor(den, o);
-      // the output is normalised; a record keeps its max and denominator
-      const float inv = rec ? 1.f : (den > 0.f ? 1.f / den : 0.f);
-      if (rec && lane == 0) {
-        store_coherent(rec + g * (D + 2) + D, M);
-        store_coherent(rec + g * (D + 2) + D + 1, den);
-      }
-#pragma unroll
-      for (int i = 0; i < kR; ++i) {
-        const int sp = lane + i * kWave;
-        if (sp < n_in) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
-      }
-    }
-    __syncthreads();
+      __syncthreads();
+    };
     const int pairs = G * D / 2;
+    // The first round of partial outputs is loaded before the weights, so that both round trips
+    // to the records (written from other XCDs) overlap.
     auto fold = [&](auto KP) {
       constexpr int kP = decltype(KP)::value;        // channel pairs per thread
       constexpr int kCS = kMergeLoads / kP;          // records per round
@@ -569,13 +573,18 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
         off[k] = (int64_t)gk[k] * (D + 2) + (pr % (D / 2)) * 2;
         acc0[k] = acc1[k] = 0.f;
       }
-      for (int s0 = 0; s0 < n_in; s0 += kCS) {
-        uint64_t v[kP][kCS];
+      uint64_t v[kP][kCS];
+      auto load_round = [&](int s0) {
 #pragma unroll
         for (int k = 0; k < kP; ++k)
 #pragma unroll
           for (int i = 0; i < kCS; ++i)
             v[k][i] = load_coherent_pair(src + (int64_t)min(s0 + i, n_in - 1) * rec_floats + off[k]);
+      };
+      if (n_in > 0) load_round(0);
+      weights();
+      for (int s0 = 0; s0 < n_in; s0 += kCS) {
+        if (s0 > 0) load_round(s0);
 #pragma unroll
         for (int k = 0; k < kP; ++k)
 #pragma unroll
