@@ -42,14 +42,17 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SAMPLES = 32              # decode launches timed with HIP events, in a pass of their own
 FLUSH_BYTES = 1 << 30            # read before each sampled launch: more than L2 + Infinity Cache
+_DECODE_SRC = ["decode.hip", "decode_body.h", "duo_common.h", "duo_kernels.h"]
+_PREFILL_SRC = ["prefill.hip", "decode_body.h", "duo_common.h", "duo_kernels.h"]
 KERNEL_SOURCES = {
-    "decode": ["decode.hip", "duo_common.h", "duo_kernels.h"],
-    "decode_int8": ["decode.hip", "duo_common.h", "duo_kernels.h"],
-    "decode_int4": ["decode.hip", "duo_common.h", "duo_kernels.h"],
-    "prefill": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
-    "dca": ["prefill.hip", "duo_common.h", "duo_kernels.h"],
-    "gemma": ["decode.hip", "duo_common.h", "duo_kernels.h"],
-    "1m": ["decode.hip", "duo_common.h", "duo_kernels.h"],
+    "decode": _DECODE_SRC,
+    "decode_int8": _DECODE_SRC,
+    "decode_int4": _DECODE_SRC,
+    "prefill": _PREFILL_SRC,
+    "dca": _PREFILL_SRC,
+    "gemma": _DECODE_SRC,
+    "1m": _DECODE_SRC,
+    "cb": _PREFILL_SRC,
 }
 
 
@@ -620,7 +623,7 @@ def continuous_batching_leg(args, torch, duo):
                         "ideal_us": round(ideal * 1e6, 1),
                         "achieved": round(ideal / t_m, 4), "peak": 1.0,
                         "unit": "ideal time / kernel time",
-                        "frac": round(ideal / t_m, 4), "traffic": None,
+                        "frac": round(ideal / t_m, 4), "traffic": measured_traffic("cb"),
                         "kernel": "duo::prefill_kernel<bf16,128,mixed>",
                         "note": "ideal = chunk FLOP at bf16 MFMA peak + decode-row bytes at HBM peak"},
            "kernel_samples": reps}
@@ -771,7 +774,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), scaled by what the same counters read for a
     copy of copy_mib MiB in the same run. Merges the results into profiles/counters.json, keyed by
     leg, with the source hash. rename maps a kernel key to the leg it measured in this run (a run
-    of the Gemma-2b leg alone: decode -> gemma)."""
+    of the Gemma-2b leg alone: decode -> gemma), or to "-" to leave it out (a run of the
+    continuous-batching leg alone also launches the plain prefill and decode kernels)."""
     def per_kernel(path, counter):
         acc, copies = {}, []
         for r in _read_counter_csv(path):
@@ -786,9 +790,14 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
             elif "decode_kernel" in name:
                 acc.setdefault("decode", []).append(val)
             elif "prefill_kernel" in name:
-                # the Dual Chunk Attention instantiation has its bool template argument set
-                dca = "Lb1E" in name or ", true>" in name
-                acc.setdefault("dca" if dca else "prefill", []).append(val)
+                # template arguments <T, D, DCA, MIX>: the Dual Chunk instantiation has DCA set, the
+                # packed-batch launch with decode items (continuous batching) MIX
+                if "Lb1ELb0E" in name or ", true, false>" in name:
+                    acc.setdefault("dca", []).append(val)
+                elif "Lb0ELb1E" in name or ", false, true>" in name:
+                    acc.setdefault("cb", []).append(val)
+                else:
+                    acc.setdefault("prefill", []).append(val)
             elif COPY_KERNEL_HINT in name.lower():
                 copies.append((int(r["Dispatch_Id"]), val))
         # the calibration copies are the last CALIBRATION_REPS copy dispatches of the run
@@ -810,9 +819,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_path: 
     calib = {"copy_bytes": known, "fetch_raw": fetch.get("copy"), "write_raw": write.get("copy"),
              "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
     rename = rename or {}
-    for k in ("decode", "decode_int8", "decode_int4", "prefill", "dca"):
+    for k in ("decode", "decode_int8", "decode_int4", "prefill", "dca", "cb"):
         if k in fetch and k in write:
             leg = rename.get(k, k)
+            if leg == "-":
+                continue
             out[leg] = {"source_sha": source_sha(leg),
                         "fetch_bytes_per_launch": fetch[k] * f_scale,
                         "write_bytes_per_launch": write[k] * w_scale,

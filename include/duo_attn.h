@@ -57,14 +57,14 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 10
+#define DUO_ATTN_ABI_VERSION 11
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
 typedef enum {
   DUO_OK = 0,
   DUO_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, non-positive size, bad mask value, aliasing */
-  DUO_ERR_UNSUPPORTED = 2,   /* head_dim not in {64,128,256}, block_size not supported, group > 16 */
+  DUO_ERR_UNSUPPORTED = 2,   /* head_dim not in {64,128,256}, block_size not supported */
   DUO_ERR_CAPACITY = 3,      /* ring or table too small for the requested window / chunk */
   DUO_ERR_WORKSPACE = 4,     /* workspace missing or smaller than the size query says */
   DUO_ERR_HIP = 5            /* a HIP launch failed */
@@ -106,9 +106,10 @@ int32_t kv_append_circular(void* k_pool, void* v_pool, const int32_t* block_tabl
  * sizes (split_tokens as passed to duo_attn_decode; 0 = the library's choice). The library's split
  * size depends on how many kv heads are retrieval heads; this size covers every retrieval/streaming
  * split of the heads. The caller zero-fills the workspace once after allocating it; every completed
- * decode call leaves it ready for the next. It starts with the merge tickets (one per sequence and kv
- * head, and one per group of 16 splits where a row has more than 16), at offsets fixed by these
- * sizes, so one workspace serves calls with any split size or mask. Returns 0 for invalid sizes.
+ * decode call leaves it ready for the next. It starts with the merge tickets (one per sequence, kv
+ * head and chunk of up to 16 q heads, and one per group of 16 splits where a row has more than 16),
+ * at offsets fixed by these sizes, so one workspace serves calls with any split size or mask.
+ * Returns 0 for invalid sizes.
  */
 size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t max_blocks_per_head,
@@ -132,9 +133,13 @@ size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  * Visible positions of the query at p = seq_lens[b] - 1: retrieval head j in [0, p]; streaming head
  * j < sink_size or p - j < recent_size (within [0, p]). seq_lens[b] = 0 yields a zero output row.
  * Retrieval lengths above max_blocks_per_head*block_size are clamped to it.
- * Calls sharing one workspace must not run concurrently.
- * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16,
- *         num_q_heads/num_kv_heads > 16), CAPACITY (streaming heads present and
+ * The q heads of a kv head are taken up to 16 at a time (a larger GQA group in chunks of 16, each
+ * reading the kv head's keys and values once).
+ * Calls sharing one workspace must not run concurrently. The waves of a work item take its key
+ * steps as they become free, so the order in which partial sums are added, and with it the last
+ * bits of the output, can differ from call to call (every call is within the stated tolerance).
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16),
+ *         CAPACITY (streaming heads present and
  *         ring_blocks*block_size < recent_size or SB + ring_blocks > max_blocks_per_head),
  *         WORKSPACE.
  */
@@ -217,8 +222,7 @@ int32_t duo_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
  * duo_attn_prefill_varlen_workspace_size -- bytes of device workspace duo_attn_prefill_varlen needs
  * for these sizes (total_q and max_q_len as passed to the call; max_blocks_per_head and block_size
  * of the cache) and this retrieval/streaming split (head_is_retrieval: host, num_kv_heads bytes).
- * It covers the prefill row tiles and, when num_q_heads / num_kv_heads <= 16, the split-K decode
- * items of single-row sequences. Zero-fill it once after allocating; every completed call leaves it
+ * It covers the prefill row tiles and the split-K decode items of single-row sequences. Zero-fill it once after allocating; every completed call leaves it
  * ready for the next. Returns 0 for invalid sizes.
  */
 size_t duo_attn_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
@@ -249,7 +253,7 @@ size_t duo_attn_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, in
  * The kernel numbers the row tiles the sequences actually have on the device (from q_start), so the
  * launch holds about total_q / 256 + batch row tiles per head whatever the mix. A sequence with
  * exactly one row (a decode step) is attended by split-K decode items in the same launch, as
- * duo_attn_decode would (when num_q_heads / num_kv_heads <= 16; above that, by a row tile).
+ * duo_attn_decode would.
  * Everything else is as for duo_attn_prefill. Errors: as duo_attn_prefill, and INVALID_ARG for a
  * missing or misaligned q_start or total_q, max_q_len < 1.
  */
@@ -432,7 +436,7 @@ int32_t dca_attn_prefill(const void* q, const void* q_succ, const void* q_inter,
  *   chunk_len, pools, table, seq_lens: as for dca_attn_prefill.
  *   workspace, split_tokens: as for duo_attn_decode (duo_attn_decode_workspace_size for the same
  *                       sizes and split_tokens).
- * Supported: dtype DUO_F16 or DUO_BF16, head_dim 64 or 128, num_q_heads / num_kv_heads <= 16.
+ * Supported: dtype DUO_F16 or DUO_BF16, head_dim 64 or 128.
  * Errors: as dca_attn_prefill and duo_attn_decode.
  */
 int32_t dca_attn_decode(const void* q, const void* q_succ, const void* q_inter,

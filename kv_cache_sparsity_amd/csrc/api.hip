@@ -66,32 +66,41 @@ int32_t check_stream_geometry(int32_t n_str, int32_t sink, int32_t recent, int32
   return DUO_OK;
 }
 
-// The decode workspace starts with its tickets: one per (sequence, kv head), then one per merge
-// group for as many groups as any split of this capacity can have (splits are >= 128 tokens). The
-// region depends on the shapes only, so a workspace reused with other split sizes or masks still
-// finds every ticket at zero.
-size_t decode_counter_bytes(int32_t batch, int32_t hkv, int32_t cap) {
+// Decode rows: a kv head's q heads ride in the 16 MFMA columns, so a group of more than 16 is taken
+// in chunks of 16 q heads, each chunk its own row of items; a merge record holds min(group, 16)
+// q heads.
+int32_t decode_group_chunks(int32_t hq, int32_t hkv) { return (hq / hkv + 15) / 16; }
+int32_t decode_record_heads(int32_t hq, int32_t hkv) { return std::min(hq / hkv, 16); }
+
+// The decode workspace starts with its tickets: one per row (sequence, kv head, chunk of q heads),
+// then one per merge group for as many groups as any split of this capacity can have (splits are
+// >= 128 tokens). The region depends on the shapes only, so a workspace reused with other split
+// sizes or masks still finds every ticket at zero.
+size_t decode_counter_bytes(int32_t batch, int32_t hkv, int32_t cap, int32_t gch = 1) {
   const int32_t most_splits = (int32_t)(((int64_t)cap + 127) / 128);
   const int32_t groups = most_splits <= kMergeGroup
                              ? 0 : std::min<int32_t>(kMaxMergeGroups, (most_splits + kMergeGroup - 1) / kMergeGroup);
-  return align256((size_t)batch * hkv * (1 + (size_t)groups) * sizeof(int32_t));
+  return align256((size_t)batch * hkv * gch * (1 + (size_t)groups) * sizeof(int32_t));
 }
 
-// rows: (sequence, retrieval kv head) pairs the split is sized for; stream_window: sink + recent
-// when the call has streaming heads, else 0. The workspace-size queries pass rows = batch and no
-// window (one retrieval head per sequence: the smallest split and the most partials any mask needs).
+// rows: (sequence, retrieval kv head) pairs the split is sized for (times the chunks of q heads);
+// stream_window: sink + recent when the call has streaming heads, else 0. The workspace-size
+// queries pass rows = batch and no window (one retrieval head per sequence: the smallest split and
+// the most partials any mask needs).
 int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbph,
                     int32_t bs, int32_t rows, int32_t split_req, int32_t* split_tokens,
                     int32_t* n_split, size_t* ws_bytes, int32_t stream_window = 0) {
   if (split_req < 0 || (split_req % 128) != 0) return DUO_ERR_INVALID_ARG;
   const int32_t cap = mbph * bs;
-  const int32_t S = decode_split_tokens(rows, cap, split_req, stream_window);
+  const int32_t gch = decode_group_chunks(hq, hkv);
+  const int32_t S = decode_split_tokens((int32_t)std::min<int64_t>((int64_t)rows * gch, INT32_MAX),
+                                        cap, split_req, stream_window);
   const int32_t ns = (cap + S - 1) / S;
-  const int32_t G = hq / hkv;
   *split_tokens = S;
   *n_split = ns;
-  *ws_bytes = decode_counter_bytes(batch, hkv, cap) +
-              (size_t)batch * hkv * (ns + decode_merge_groups(ns)) * G * (head_dim + 2) * sizeof(float);
+  *ws_bytes = decode_counter_bytes(batch, hkv, cap, gch) +
+              (size_t)batch * hkv * gch * (ns + decode_merge_groups(ns)) *
+                  decode_record_heads(hq, hkv) * (head_dim + 2) * sizeof(float);
   return DUO_OK;
 }
 
@@ -318,7 +327,6 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   if (quant == 4 && dtype == DUO_F32) return DUO_ERR_UNSUPPORTED;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
-  if (num_q_heads / num_kv_heads > 16) return DUO_ERR_UNSUPPORTED;
   uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
   int32_t n_ret, n_str;
   if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str))
@@ -342,9 +350,11 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   } else if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) {
     return DUO_ERR_WORKSPACE;
   }
-  const int64_t grid = (int64_t)batch * n_ret * ns + (int64_t)batch * n_str;
+  const int32_t gch = decode_group_chunks(num_q_heads, num_kv_heads);
+  const int64_t grid = ((int64_t)batch * n_ret * ns + (int64_t)batch * n_str) * gch;
   if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
-  const size_t ticket_bytes = decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size);
+  const size_t ticket_bytes =
+      decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size, gch);
   if (noalloc) {
     // every check has passed: take this device's scratch and clear its tickets (a fill kernel on
     // the call's stream, ahead of the decode)
@@ -363,11 +373,12 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   p.seq_lens = seq_lens;
   p.out = out;
   p.counter = static_cast<int32_t*>(workspace);
-  p.gcounter = p.counter + (size_t)batch * num_kv_heads;
+  p.gcounter = p.counter + (size_t)batch * num_kv_heads * gch;
   p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + ticket_bytes);
   p.n_group = decode_merge_groups(ns);
-  p.gpartial = p.partial + (size_t)batch * num_kv_heads * ns * (num_q_heads / num_kv_heads) *
-                               (head_dim + 2);
+  p.gpartial = p.partial + (size_t)batch * num_kv_heads * gch * ns *
+                               decode_record_heads(num_q_heads, num_kv_heads) * (head_dim + 2);
+  p.gchunks = gch;
   p.num_blocks = num_blocks;
   p.log2_bs = log2i(block_size);
   p.max_blocks_per_head = max_blocks_per_head;
@@ -514,9 +525,10 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
   size_t need;
   prefill_plan(batch, q_len, num_q_heads, n_ret, num_kv_heads, head_dim, dtype, &n_qt, &ret_items,
                &need, packed ? total_q : 0);
-  // Packed batches with a GQA group of at most 16 run their single-row sequences as split-K
-  // decode items in the same launch; their workspace follows the prefill's.
-  const bool mixed = packed && num_q_heads / num_kv_heads <= 16;
+  // Packed batches run their single-row sequences as split-K decode items in the same launch;
+  // their workspace follows the prefill's.
+  const bool mixed = packed;
+  const int32_t gch = decode_group_chunks(num_q_heads, num_kv_heads);
   int32_t dS = 0, dns = 0;
   size_t dneed = 0;
   if (mixed) {
@@ -531,7 +543,7 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
   const int64_t seqs = packed ? 1 : batch;
   const int64_t n_prefill = ret_items * kPrefillSplits +
                             seqs * n_str * (num_q_heads / num_kv_heads) * n_qt;
-  const int64_t n_decode = mixed ? (int64_t)batch * n_ret * dns + (int64_t)batch * n_str : 0;
+  const int64_t n_decode = mixed ? ((int64_t)batch * n_ret * dns + (int64_t)batch * n_str) * gch : 0;
   const int64_t grid = n_prefill + n_decode;
   if (grid > INT32_MAX) return DUO_ERR_UNSUPPORTED;
 
@@ -589,13 +601,14 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
     d.q_start = q_start;
     d.total_q = total_q;
     char* dws = static_cast<char*>(workspace) + pneed;
-    const size_t ticket_bytes = decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size);
+    const size_t ticket_bytes =
+        decode_counter_bytes(batch, num_kv_heads, max_blocks_per_head * block_size, gch);
     d.counter = reinterpret_cast<int32_t*>(dws);
-    d.gcounter = d.counter + (size_t)batch * num_kv_heads;
+    d.gcounter = d.counter + (size_t)batch * num_kv_heads * gch;
     d.partial = reinterpret_cast<float*>(dws + ticket_bytes);
     d.n_group = decode_merge_groups(dns);
-    d.gpartial = d.partial + (size_t)batch * num_kv_heads * dns * (num_q_heads / num_kv_heads) *
-                                 (head_dim + 2);
+    d.gpartial = d.partial + (size_t)batch * num_kv_heads * gch * dns *
+                                 decode_record_heads(num_q_heads, num_kv_heads) * (head_dim + 2);
     d.num_blocks = num_blocks;
     d.log2_bs = p.log2_bs;
     d.max_blocks_per_head = max_blocks_per_head;
@@ -603,6 +616,7 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
     d.num_q_heads = num_q_heads;
     d.num_kv_heads = num_kv_heads;
     d.group = num_q_heads / num_kv_heads;
+    d.gchunks = gch;
     d.sink = sink_size;
     d.recent = recent_size;
     d.sink_blocks = p.sink_blocks;
@@ -674,7 +688,7 @@ size_t duo_attn_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, in
   size_t bytes;
   prefill_plan(batch, max_q_len, num_q_heads, n_ret, num_kv_heads, head_dim, dtype, &n_qt,
                &ret_items, &bytes, total_q);
-  if (num_q_heads / num_kv_heads <= 16) {
+  {
     int32_t S, ns;
     size_t dbytes;
     if (decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,

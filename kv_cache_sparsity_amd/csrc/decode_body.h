@@ -72,23 +72,27 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int col = lane & 15;   // MFMA column = q head within the group
   const int quad = lane >> 4;  // k-group of the lane
-  const int G = p.group;
-
   // ---- which item -------------------------------------------------------------------------
+  // A kv head's group of q heads rides in the 16 MFMA columns; a group of more than 16 is taken in
+  // gchunks chunks of 16 q heads (the last may be short), each its own row of items. The chunk is
+  // the fastest index of a row.
   // str_first: streaming items first, then the retrieval splits of every (sequence, retrieval
   // head) row but its last, then the rows' last splits. With one workgroup per CU, the workgroups
   // dispatched last start on the CUs that the short streaming items free, and the last splits are
   // the shortest (the host sizes the splits for that). Otherwise the retrieval items (split
   // fastest), then the streaming items, which start on the CUs of the first retrieval items done.
-  const int n_str_items = p.str_first ? p.batch * p.n_str : 0;
-  const int n_rows = p.batch * p.n_ret;
+  const int gch = p.gchunks;
+  const int n_str_items = p.str_first ? p.batch * p.n_str * gch : 0;
+  const int n_rows = p.batch * p.n_ret * gch;
   const int n_ret_items = n_rows * p.n_split;
-  int b, h, split;
+  int b, h, split, gc;
   bool ret;
   if (blk < n_str_items || blk >= n_str_items + n_ret_items) {
     const int it = blk < n_str_items ? blk : blk - n_ret_items;
-    b = it / p.n_str;
-    h = p.str_heads[it % p.n_str];
+    b = it / (p.n_str * gch);
+    const int r = it % (p.n_str * gch);
+    h = p.str_heads[r / gch];
+    gc = r % gch;
     split = 0;
     ret = false;
   } else {
@@ -104,10 +108,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       split = p.n_split - 1;
       row = r - n_rows * (p.n_split - 1);
     }
-    b = row / p.n_ret;
-    h = p.ret_heads[row % p.n_ret];
+    b = row / (p.n_ret * gch);
+    const int rr = row % (p.n_ret * gch);
+    h = p.ret_heads[rr / gch];
+    gc = rr % gch;
     ret = true;
   }
+  const int G = min(16, p.group - gc * 16);   // q heads (MFMA columns) of this chunk
+  const int Gs = min(16, p.group);            // q heads a merge record has room for
+  const int qh0 = h * p.group + gc * 16;      // the chunk's first q head
   // The row of q and out: b, or in a packed batch the sequence's row when it has exactly one
   // (a sequence with more rows is the prefill tiles' work: every item of it returns here, before
   // any ticket).
@@ -164,7 +173,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     // ---- Q^T operand (B of S^T): column = q head, k = head-dim chunk ------------------------
     v8<T> qT[KC];
     {
-      const T* qrow = static_cast<const T*>(p.q) + (qb * p.num_q_heads + h * G + col) * D;
+      const T* qrow = static_cast<const T*>(p.q) + (qb * p.num_q_heads + qh0 + col) * D;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         // Q8 takes each lane's K codes 16 at a time, so its k-step c pairs lane quad with head
@@ -326,7 +335,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
           if (need != q_kind) {
             q_kind = need;
             const void* base = need == 0 ? q_intra : need == 1 ? q_succ : q_inter;
-            const T* qrow = static_cast<const T*>(base) + (qb * p.num_q_heads + h * G + col) * D;
+            const T* qrow = static_cast<const T*>(base) + (qb * p.num_q_heads + qh0 + col) * D;
 #pragma unroll
             for (int c = 0; c < KC; ++c) qT[c] = (col < G) ? load8(qrow + c * 32 + quad * 8) : zero8<T>();
           }
@@ -462,7 +471,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
 
     // ---- merge the waves; write the output (single item) or a partial -----------------------
     const bool direct = !ret || p.n_split == 1;
-    float* part = p.partial + ((((int64_t)b * p.num_kv_heads + h) * p.n_split + split) * G) * (D + 2);
+    float* part = p.partial + ((((int64_t)b * p.num_kv_heads + h) * gch + gc) * p.n_split + split) *
+                                  Gs * (D + 2);
     for (int idx = tid; idx < G * D; idx += kThreads) {
       const int g = idx / D, d = idx % D;
       float M = sm_m[0][g];
@@ -477,7 +487,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
         den += c * sm_l[w][g];
       }
       if (direct) {
-        T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + h * G + g) * D;
+        T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + qh0 + g) * D;
         o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
       } else {
         store_coherent(part + g * (D + 2) + d, num);
@@ -491,7 +501,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   } else if (!ret || p.n_split == 1) {
     // nothing visible (L == 0): zero output row(s)
     for (int idx = tid; idx < G * D; idx += kThreads) {
-      T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + h * G) * D;
+      T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + qh0) * D;
       o[idx] = from_f32<T>(0.f);
     }
     return;
@@ -510,13 +520,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   // kMergeGroup partials per q head.
   wait_stores_complete();
   __syncthreads();
-  const int64_t row = (int64_t)b * p.num_kv_heads + h;
+  const int64_t row = ((int64_t)b * p.num_kv_heads + h) * gch + gc;
   const int n_act = (L + p.split_tokens - 1) / p.split_tokens;
-  T* const obase = static_cast<T*>(p.out) + (qb * p.num_q_heads + h * G) * D;
-  const int64_t rec_floats = (int64_t)G * (D + 2);
+  T* const obase = static_cast<T*>(p.out) + (qb * p.num_q_heads + qh0) * D;
+  const int64_t rec_floats = (int64_t)Gs * (D + 2);   // record stride
 
-  // Fold n_in records at src ([n_in][G][D + 2], all complete) into the output (rec == nullptr) or
-  // into the record rec: (1) per q head g, one wave reduces the records' (m, l) into the merged max
+  // Fold n_in records at src (rec_floats apart; heads 0 .. G - 1 of each used; all complete) into
+  // the output (rec == nullptr) or into the record rec: (1) per q head g, one wave reduces the records' (m, l) into the merged max
   // and denominator and leaves each record's weight in LDS (the wave buffers are free by now);
   // (2) out[g][d] = sum_s w[s][g] O_s[g][d], two channels per 8-byte load, each thread keeping
   // kMergeLoads loads in flight across its outputs and the records.
@@ -530,7 +540,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
           const int sp = lane + i * kWave;
-          const float* r = src + (int64_t)(max(min(sp, n_in - 1), 0) * G + g) * (D + 2);
+          const float* r = src + max(min(sp, n_in - 1), 0) * rec_floats + g * (D + 2);
           mv[i] = sp < n_in ? load_coherent(r + D) : -INFINITY;
           lv[i] = sp < n_in ? load_coherent(r + D + 1) : 0.f;
           M = fmaxf(M, mv[i]);
@@ -658,7 +668,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
         float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
 #pragma unroll
         for (int i = 0; i < kMergeChunk; ++i) {
-          const float* rec = base + (int64_t)(min(s0 + i, n_act - 1) * G + g) * (D + 2);
+          const float* rec = base + min(s0 + i, n_act - 1) * rec_floats + g * (D + 2);
           mv[i] = load_coherent(rec + D);
           lv[i] = load_coherent(rec + D + 1);
           ov[i] = load_coherent(rec + d);

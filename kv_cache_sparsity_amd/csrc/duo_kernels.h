@@ -38,13 +38,16 @@ struct DecodeParams {
   void* out;
   const float* k_scale;   // int8 cache: [num_blocks][block_size] per-slot scales of K;
   const float* v_scale;   // and of V; 4-bit cache: [num_kv_heads][head_dim] per-channel scales
-  float* partial;     // [batch][num_kv_heads][n_split][group][head_dim + 2]
-  int32_t* counter;   // [batch][num_kv_heads]
-  float* gpartial;    // [batch][num_kv_heads][n_group][group][head_dim + 2] (n_group > 0)
-  int32_t* gcounter;  // [batch][num_kv_heads][n_group]
+  // merge records and tickets per row = (sequence, kv head, chunk of up to 16 q heads); a record
+  // is [min(group, 16)][head_dim + 2] floats
+  float* partial;     // [batch][num_kv_heads][gchunks][n_split] records
+  int32_t* counter;   // [batch][num_kv_heads][gchunks]
+  float* gpartial;    // [batch][num_kv_heads][gchunks][n_group] records (n_group > 0)
+  int32_t* gcounter;  // [batch][num_kv_heads][gchunks][n_group]
   int32_t n_group;    // groups of kMergeGroup splits merged first; 0: one-level merge
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, num_q_heads, num_kv_heads, group;
+  int32_t gchunks;   // ceil(group / 16): chunks of q heads taken one per item
   int32_t sink, recent, sink_blocks, ring_slots;
   int32_t split_tokens, n_split, n_ret, n_str;
   // 1: streaming items first in the grid and the retrieval rows' last splits last (the host then

@@ -226,7 +226,28 @@ void decode_cases() {
   CHECK(g_launches.size() == 1 && g_launches[0].dp.str_first == 0 && g_launches[0].dp.split_tokens == 4096);
   CHECK(decode(m, 8, 32, 8, 128, 2048, ws4096 - 1, 4096) == DUO_ERR_WORKSPACE);
   CHECK(decode(m, 8, 32, 8, 128, 2048, 0, 0) == DUO_ERR_WORKSPACE);
-  CHECK(decode(m, 8, 128, 4, 128, 2048, ws, 0) == DUO_ERR_UNSUPPORTED);    // group 32
+  // a group of 40 q heads per kv head: three chunks of up to 16 q heads, each its own row of items
+  {
+    Mask m2(2, 2);   // kv head 0 retrieval, kv head 1 streaming
+    const size_t w40 = duo_attn_decode_workspace_size(4, 80, 2, 128, 2048, 16, 0);
+    CHECK(w40 > 0);
+    g_launches.clear();
+    CHECK(decode(m2, 4, 80, 2, 128, 2048, w40, 0) == DUO_OK);
+    CHECK(g_launches.size() == 1);
+    if (g_launches.size() == 1) {
+      const duo::DecodeParams& p = g_launches[0].dp;
+      CHECK(p.group == 40 && p.gchunks == 3);
+      // rows: 4 sequences x 1 retrieval head x 3 chunks = 12 -> 256 / 12 = 21 splits of 1600 keys
+      // (with the streaming stretch: (32768 + 576) / 21 to the nearest 64 = 1600)
+      CHECK(p.n_split == 21 && p.split_tokens == 1600);
+      CHECK(g_launches[0].grid == (4 * 1 * 21 + 4 * 1) * 3);
+      // tickets: 4 x 2 x 3 rows, then their group tickets; records of 16 q heads
+      CHECK(p.gcounter == p.counter + 4 * 2 * 3);
+      const size_t rec = (size_t)16 * (128 + 2) * 4;
+      CHECK((const char*)p.gpartial == (const char*)p.partial + (size_t)4 * 2 * 3 * 21 * rec);
+      CHECK((const char*)p.gpartial + (size_t)4 * 2 * 3 * p.n_group * rec <= (const char*)fake() + w40);
+    }
+  }
   CHECK(decode(m, 8, 32, 8, 96, 2048, ws, 0) == DUO_ERR_UNSUPPORTED);
   CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 100) == DUO_ERR_INVALID_ARG);  // not a multiple of 128
   CHECK(decode(m, 8, 32, 8, 128, 2048, ws, 0, 9) == DUO_ERR_UNSUPPORTED);

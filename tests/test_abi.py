@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 10
+    assert duo.abi_version() == 11
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
@@ -97,7 +97,7 @@ def decode(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(table=FAKE + 2), INVALID),
-    (dict(hq=6, hkv=4), INVALID), (dict(hq=40, hkv=2), UNSUPPORTED), (dict(d=80), UNSUPPORTED),
+    (dict(hq=6, hkv=4), INVALID), (dict(d=80), UNSUPPORTED),
     (dict(bs=8), UNSUPPORTED), (dict(bs=24), UNSUPPORTED), (dict(dtype=3), UNSUPPORTED),
     (dict(recent=0), INVALID), (dict(rb=0), INVALID), (dict(recent=33), CAPACITY),
     (dict(mbph=2, rb=2), CAPACITY), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
@@ -167,7 +167,7 @@ MASK_64 = (ctypes.c_uint8 * 64)(*([1] * 64))
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), INVALID), (dict(hq=40, hkv=2), UNSUPPORTED), (dict(recent=33), CAPACITY),
+    (dict(q=None), INVALID), (dict(recent=33), CAPACITY),
     (dict(split=100), INVALID), (dict(mask=ctypes.cast(MASK_BAD, ctypes.c_void_p)), INVALID),
     # 64 sequences x 64 kv heads x 128-key splits over 1M slots: more than the scratch holds
     (dict(batch=64, hq=256, hkv=64, d=256, mbph=65540, split=128,
@@ -203,7 +203,7 @@ def decode_int8(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(ks=None), INVALID), (dict(vs=FAKE + 8), INVALID), (dict(q=None), INVALID),
     (dict(d=80), UNSUPPORTED), (dict(bs=8), UNSUPPORTED), (dict(recent=33), CAPACITY),
-    (dict(ws=None), WORKSPACE), (dict(hq=40, hkv=2), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(hq=6, hkv=4), INVALID),
 ])
 def test_decode_int8_rejects(kw, status):
     assert decode_int8(**kw) == status
@@ -341,7 +341,7 @@ def dca_dec(**kw):
     (dict(batch=0), INVALID), (dict(hkv=0), INVALID), (dict(scale=-1.0), INVALID),
     (dict(split=100), INVALID),
     (dict(chunk=96), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
-    (dict(hq=34), UNSUPPORTED),                 # GQA group of 17 > 16
+    (dict(hq=34, hkv=4), INVALID),              # 34 q heads over 4 kv heads
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
 ])
 def test_dca_decode_rejects(kw, status):

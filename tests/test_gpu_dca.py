@@ -174,6 +174,8 @@ DECODE_CASES = [
          chunk_len=256, lens=[300, 4000, 257], splits=[512, 0]),
     dict(name="bf16-d64-gqa16-c128", dtype=synth.BF16, head_dim=64, group=16, kv=1, block_size=16,
          chunk_len=128, lens=[129, 2500], splits=[256, 0]),
+    dict(name="f16-d128-gqa24-c64", dtype=synth.F16, head_dim=128, group=24, kv=2, block_size=16,
+         chunk_len=64, lens=[65, 1100], splits=[128, 0]),
 ]
 
 

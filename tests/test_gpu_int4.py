@@ -144,6 +144,8 @@ DECODE_CASES = [
          ret=(), block_size=32, sink=30, recent=50, lens=[2000, 31, 80]),
     dict(name="bf16-d128-gqa16", dtype=synth.BF16, head_dim=128, group=16, kv=2, ret=(0,),
          block_size=16, sink=16, recent=256, lens=[5000, 4097]),
+    dict(name="f16-d64-gqa33", dtype=synth.F16, head_dim=64, group=33, kv=1, ret=(0,),
+         block_size=16, sink=0, recent=16, lens=[3000, 1]),
 ]
 
 

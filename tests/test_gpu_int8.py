@@ -159,6 +159,8 @@ DECODE_CASES = [
          block_size=16, sink=0, recent=40, lens=[257, 96]),
     dict(name="bf16-d256-gqa8-all-retrieval", dtype=synth.BF16, head_dim=256, group=8, kv=1,
          ret=(0,), block_size=16, sink=0, recent=16, lens=[1024, 77]),
+    dict(name="f16-d128-gqa20", dtype=synth.F16, head_dim=128, group=20, kv=2, ret=(0,),
+         block_size=16, sink=4, recent=64, lens=[1500, 70]),
 ]
 
 

@@ -132,6 +132,13 @@ DECODE_CASES = [
          block_size=16, sink=16, recent=32, ring_blocks=2, lens=[16, 48, 49, 777]),
     dict(name="bf16-d128-g4-bs256", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(0,),
          block_size=256, sink=3, recent=300, ring_blocks=2, lens=[255, 256, 257, 3000]),
+    # groups of more than 16 q heads: taken in chunks of 16 (the last one short)
+    dict(name="bf16-d128-g20-mixed", dtype=synth.BF16, head_dim=128, group=20, kv=2, ret=(1,),
+         block_size=16, sink=4, recent=40, ring_blocks=3, lens=[0, 17, 900]),
+    dict(name="f16-d64-g48-mqa", dtype=synth.F16, head_dim=64, group=48, kv=1, ret=(0,),
+         block_size=32, sink=0, recent=1, ring_blocks=1, lens=[2049, 3]),
+    dict(name="f16-d256-g40-streaming", dtype=synth.F16, head_dim=256, group=40, kv=2, ret=(),
+         block_size=16, sink=16, recent=100, ring_blocks=8, lens=[700, 15]),
 ]
 
 
@@ -160,6 +167,19 @@ def test_decode_parity(case):
     zero_rows = [b for b, L in enumerate(case["lens"]) if L == 0]
     for b in zero_rows:
         assert (got[b] == 0).all()
+
+
+@pytest.mark.parametrize("split", [128, 1024])
+def test_decode_large_group_explicit_splits(split):
+    """A group of 20 q heads (chunks of 16 and 4) with explicit splits: records of the short chunk
+    and merges across splits."""
+    case = next(c for c in DECODE_CASES if c["name"] == "bf16-d128-g20-mixed")
+    say(f"decode group 20, split {split}")
+    w, cache, K, V, q = _decode_case(case)
+    got = to_host_f64(cache.decode(q, split_tokens=split), w.dtype)
+    want = oracle_decode(w, q, K, V, np.asarray(case["lens"]), cache.mask)
+    check_close(got, want, w.dtype, f"group 20 split={split}")
+    assert (got[0] == 0).all()
 
 
 @pytest.mark.parametrize("split", [128, 256, 1024, 0])
@@ -354,6 +374,9 @@ VARLEN_CASES = [
          block_size=64, sink=0, recent=40, rows=[5, 129, 64], lens=[5, 900, 64]),
     dict(name="f32-d64-all-streaming", dtype=synth.F32, head_dim=64, group=2, kv=1, ret=(),
          block_size=16, sink=7, recent=30, rows=[33, 2], lens=[400, 40]),
+    # a group of 24: the single rows' decode items take the q heads in chunks of 16 and 8
+    dict(name="bf16-d128-gqa24", dtype=synth.BF16, head_dim=128, group=24, kv=2, ret=(1,),
+         block_size=16, sink=4, recent=64, rows=[1, 70, 1, 1], lens=[900, 300, 1, 2000]),
 ]
 
 
