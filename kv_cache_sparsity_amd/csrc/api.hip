@@ -84,17 +84,17 @@ size_t decode_counter_bytes(int32_t batch, int32_t hkv, int32_t cap, int32_t gch
 }
 
 // rows: (sequence, retrieval kv head) pairs the split is sized for (times the chunks of q heads);
-// stream_window: sink + recent when the call has streaming heads, else 0. The workspace-size
-// queries pass rows = batch and no window (one retrieval head per sequence: the smallest split and
+// stretch_keys: see decode_split_tokens (0 unless the streaming items go first). The workspace-size
+// queries pass rows = batch and no stretch (one retrieval head per sequence: the smallest split and
 // the most partials any mask needs).
 int32_t decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t mbph,
                     int32_t bs, int32_t rows, int32_t split_req, int32_t* split_tokens,
-                    int32_t* n_split, size_t* ws_bytes, int32_t stream_window = 0) {
+                    int32_t* n_split, size_t* ws_bytes, int32_t stretch_keys = 0) {
   if (split_req < 0 || (split_req % 128) != 0) return DUO_ERR_INVALID_ARG;
   const int32_t cap = mbph * bs;
   const int32_t gch = decode_group_chunks(hq, hkv);
   const int32_t S = decode_split_tokens((int32_t)std::min<int64_t>((int64_t)rows * gch, INT32_MAX),
-                                        cap, split_req, stream_window);
+                                        cap, split_req, stretch_keys);
   const int32_t ns = (cap + S - 1) / S;
   *split_tokens = S;
   *n_split = ns;
@@ -336,14 +336,22 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   if (st != DUO_OK) return st;
   int32_t S, ns;
   size_t need;
-  // 16-bit caches: streaming items first, and the retrieval rows' last splits shortened by about
-  // one streaming item (for int8 and 4-bit caches a streaming item, bound by latency, is worth many
-  // more keys, and the streaming items keep their place after the retrieval items, where they
-  // overlap the merges)
-  const bool str_first = quant == 0 && n_str > 0 && split_tokens == 0;
+  // With streaming heads and the library's split: streaming items first, and the retrieval rows'
+  // last splits shortened by the keys a streaming item's time would stream. A streaming item is
+  // bound by latency, so its time is about that of (sink + recent + 256) keys of a 16-bit cache
+  // whatever the cache: in keys of this cache, that many times 16-bit bytes per key over this
+  // cache's (2 D + 8 per key for int8 with its two scales, D for 4 bits, 8 D for fp32).
+  const bool str_first = n_str > 0 && split_tokens == 0;
+  int32_t stretch = 0;
+  if (str_first) {
+    const int64_t bpk16 = 4LL * head_dim;
+    const int64_t bpk = quant == 8 ? 2LL * head_dim + 8 : quant == 4 ? head_dim
+                                                        : 2LL * head_dim * elem_bytes(dtype);
+    stretch = (int32_t)std::min<int64_t>(((int64_t)sink_size + recent_size + 256) * bpk16 / bpk,
+                                         INT32_MAX / 2);
+  }
   st = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
-                   batch * (n_ret > 0 ? n_ret : 1), split_tokens, &S, &ns, &need,
-                   str_first ? (int32_t)std::min<int64_t>((int64_t)sink_size + recent_size, INT32_MAX / 2) : 0);
+                   batch * (n_ret > 0 ? n_ret : 1), split_tokens, &S, &ns, &need, stretch);
   if (st != DUO_OK) return st;
   if (noalloc) {
     if (need > kNoAllocScratchBytes) return DUO_ERR_WORKSPACE;

@@ -146,17 +146,18 @@ inline int32_t decode_merge_groups(int32_t n_split) {
 // Up to this many splits per (sequence, kv head) the fused merge takes its two-phase fast path.
 constexpr int32_t kFastMergeSplits = 256;
 // Decode split size (keys per retrieval item) from static sizes. rows = (sequence, retrieval kv
-// head) pairs; stream_window = sink + recent when the call has streaming heads, else 0. Shared by
-// the workspace-size query (stream_window 0: the smallest split) and the call.
+// head) pairs; stretch_keys > 0: the call puts its streaming items first (see below). Shared by the
+// workspace-size query (no stretch: the smallest split) and the call.
 //
 // About one retrieval item per CU (256 on MI355X): n = 256 / rows splits per row (at least 1, at
 // most kFastMergeSplits, so that the fused merge takes its fast path), S = capacity / n rounded up
-// to 64 keys, at least 256. With stream_window > 0 the streaming items come first in the grid and
+// to 64 keys, at least 256. With stretch_keys > 0 the streaming items come first in the grid and
 // the last split of every row comes last, so those last splits start on the CUs the streaming
-// items free: S grows by about one streaming item's keys (stream_window + 256) spread over the
-// row's splits, so that each last split is that much shorter and ends with the others.
+// items free: S grows by stretch_keys (about as many keys as a streaming item's time would stream)
+// spread over the row's splits, so that each last split is that much shorter and ends with the
+// others.
 inline int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_t requested,
-                                   int32_t stream_window = 0) {
+                                   int32_t stretch_keys = 0) {
   if (requested > 0) return requested;
   const int64_t r = rows > 0 ? rows : 1;
   const int64_t cap = capacity_tokens > 0 ? capacity_tokens : 1;
@@ -164,9 +165,9 @@ inline int32_t decode_split_tokens(int32_t rows, int32_t capacity_tokens, int32_
   n = n < 1 ? 1 : n > kFastMergeSplits ? kFastMergeSplits : n;
   int64_t s = ((cap + n - 1) / n + 63) / 64 * 64;
   if (s < 256) s = 256;
-  if (stream_window > 0 && n > 1) {
+  if (stretch_keys > 0 && n > 1) {
     // nearest multiple of 64; kept only while every split still holds keys
-    const int64_t st = ((cap + stream_window + 256 + n - 1) / n + 32) / 64 * 64;
+    const int64_t st = ((cap + stretch_keys + n - 1) / n + 32) / 64 * 64;
     if (st > s && (n - 1) * st < cap) s = st;
   }
   return (int32_t)(s < (int64_t)(INT32_MAX / 64) * 64 ? s : (int64_t)(INT32_MAX / 64) * 64);

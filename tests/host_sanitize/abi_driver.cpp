@@ -286,8 +286,11 @@ void decode_cases() {
                              100000, 16, 2048, (const int32_t*)fake(), 8, 32, 8, 128, DUO_BF16,
                              m.p, 64, 256, 16, 0.088f, fake(), fake(), ws, 0, nullptr) == DUO_OK);
   CHECK(g_launches.size() == 1 && g_launches[0].quant == 8);
-  if (g_launches.size() == 1)   // the int8 cache keeps the streaming items last and plain splits
-    CHECK(g_launches[0].dp.str_first == 0 && g_launches[0].dp.split_tokens == 4096);
+  // streaming items first; a streaming item's time is worth (64 + 256 + 256) x 512 / 264 = 1117
+  // keys of the int8 cache (2 x 128 code bytes + 2 scales per key against 512 bytes of bf16):
+  // (32768 + 1117) / 8 to the nearest 64 = 4224
+  if (g_launches.size() == 1)
+    CHECK(g_launches[0].dp.str_first == 1 && g_launches[0].dp.split_tokens == 4224);
   // 4-bit: per-channel scales required; 16-bit calls only
   g_launches.clear();
   CHECK(duo_attn_decode_int4(fake(), (const uint8_t*)fake(), (const uint8_t*)fake(),
