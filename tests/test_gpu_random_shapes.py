@@ -1,5 +1,5 @@
-"""GPU parity on seeded random shapes: decode, prefill, the int8 decode and Dual Chunk Attention
-against the CPU oracle.
+"""GPU parity on seeded random shapes: decode (GQA groups up to 64), prefill, the int8 and 4-bit
+decodes and Dual Chunk Attention against the CPU oracle.
 
 Each case draws a dtype, head dim, kv-head count, GQA group, page size, sink and recent sizes, a
 retrieval mask, per-sequence lengths and (for prefill) a chunk length, all within the documented
@@ -256,3 +256,87 @@ def test_random_shape_varlen_prefill_parity(i, _need_gpu):
         want = oracle.attend(qs[b], K[b:b + 1], V[b:b + 1], np.asarray(lens[b:b + 1]), cache.mask,
                              sink=w.sink, recent=w.recent, scale=w.scale, dtype=dtype)[0]
         check_close(got[q_start[b]:q_start[b + 1]], want, dtype, f"{name} sequence {b}")
+
+
+# ------------------------------------------------------------------------------------------------
+# the 4-bit cache, and decode with GQA groups of more than 16 q heads, on seeded random shapes
+# ------------------------------------------------------------------------------------------------
+N_INT4 = 12
+N_GROUPS = 10
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_INT4))
+def test_random_shape_int4_decode_parity(i, _need_gpu):
+    from tests.test_gpu_int4 import Int4Cache
+    rng = np.random.default_rng([2028, i])
+    dtype = (synth.F16, synth.BF16)[rng.integers(2)]
+    D = (64, 128, 256)[rng.integers(3)]
+    kv = int(rng.integers(1, 4))
+    G = (1, 2, 4, 8, 16, 24, 33)[rng.integers(7)]
+    bs = (16, 32, 64)[rng.integers(3)]
+    sink, recent = int(rng.integers(0, 40)), int(rng.integers(1, 200))
+    ret = tuple(h for h in range(kv) if rng.random() < 0.5)
+    lens = [int(x) for x in rng.integers(1, 1500, int(rng.integers(1, 4)))]
+    split = (0, 128, 256, 1024)[rng.integers(4)]
+    name = (f"int4 {i}: dtype {dtype} D {D} kv {kv} G {G} bs {bs} sink {sink} recent {recent} "
+            f"ret {ret} lens {lens} split {split}")
+    say(name)
+    w = synth.small(f"rand4-{i}", batch=len(lens), q_heads=kv * G, kv_heads=kv, head_dim=D,
+                    dtype=dtype, block_size=bs, sink=sink, recent=recent, retrieval=ret,
+                    context=max(lens), q_len=1, seed=500 + i)
+    cache = Int4Cache(w)
+    K = logical_kv(w, max(lens), synth.S_K)
+    V = logical_kv(w, max(lens), synth.S_V)
+    cache.fill_per_sequence(K, V, np.asarray(lens))
+    kc, vc = cache.logical_codes(K, V)
+    q = q_decode(w, 0)
+    want = oracle.attend_int4(q[:, None], kc, vc, cache.ks_h, cache.vs_h, np.asarray(lens),
+                              cache.mask, sink=sink, recent=recent, scale=w.scale,
+                              dtype=dtype)[:, 0]
+    got = to_host_f64(cache.decode(q, split_tokens=split), dtype)
+    check_close(got, want, dtype, name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_GROUPS))
+def test_random_shape_large_group_decode_parity(i, _need_gpu):
+    """Groups of 17 to 64 q heads per kv head: the decode takes them in chunks of 16 (the last one
+    short), each chunk its own row of items, tickets and merge records."""
+    rng = np.random.default_rng([2029, i])
+    dtype = (synth.F32, synth.F16, synth.BF16)[rng.integers(3)]
+    D = (64, 128, 256)[rng.integers(3)]
+    kv = int(rng.integers(1, 3))
+    G = (17, 20, 31, 32, 40, 48, 64)[rng.integers(7)]
+    bs = (16, 32)[rng.integers(2)]
+    sink, recent = int(rng.integers(0, 40)), int(rng.integers(1, 200))
+    ret = tuple(h for h in range(kv) if rng.random() < 0.6)
+    lens = [int(x) for x in rng.integers(0, 2500, int(rng.integers(1, 4)))]
+    split = (0, 128, 512)[rng.integers(3)]
+    name = (f"group {i}: dtype {dtype} D {D} kv {kv} G {G} bs {bs} sink {sink} recent {recent} "
+            f"ret {ret} lens {lens} split {split}")
+    say(name)
+    Lm = max(max(lens), 1)
+    w = synth.small(f"randg-{i}", batch=len(lens), q_heads=kv * G, kv_heads=kv, head_dim=D,
+                    dtype=dtype, block_size=bs, sink=sink, recent=recent, retrieval=ret,
+                    context=Lm, q_len=1, seed=700 + i)
+    cache = Cache(w, fill="nan")
+    K = logical_kv(w, Lm, synth.S_K)
+    V = logical_kv(w, Lm, synth.S_V)
+
+    def app(kn, vn, t, before):
+        if kn.shape[1] == 0:    # an empty sequence: nothing to append
+            return before
+        after = torch.zeros(1, dtype=torch.int32, device="cuda")
+        duo.kv_append_circular(cache.k_pool, cache.v_pool, t, to_dev(kn, dtype),
+                               to_dev(vn, dtype), before, after, cache.mask, w.sink, w.recent,
+                               w.ring_blocks)
+        return after
+    cache.lens = _fill(app, K, V, lens, cache.table)
+    q = q_decode(w, 0)
+    got = to_host_f64(cache.decode(q, split_tokens=split), dtype)
+    want = oracle_decode(w, q, K, V, np.asarray(lens), cache.mask)
+    check_close(got, want, dtype, name)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert (got[b] == 0).all()
