@@ -47,6 +47,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert duo.abi_version() == 11
+    with open(os.path.join(ROOT, "include", "duo_attn.h")) as fh:
+        assert f"#define DUO_ATTN_ABI_VERSION {duo.abi_version()}" in fh.read()
     assert duo.status_string(0) == "ok"
     assert "capacity" in duo.status_string(3)
     assert duo.status_string(99) == "unknown status"
