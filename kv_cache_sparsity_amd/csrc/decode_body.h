@@ -18,13 +18,20 @@ namespace {
 template <int D> constexpr int decode_waves() { return D <= 128 ? 8 : 4; }
 
 // Split merge: up to kFastMergeSplits splits per (sequence, kv head) take the two-phase merge
-// (weights in LDS, then the partial outputs with kMergeLoads 8-byte loads in flight per thread).
-constexpr int kMergeLoads = 32;
+// (weights in LDS, then the partial outputs with merge_loads 8-byte loads in flight per thread:
+// 32 with eight waves per workgroup (256 registers a lane), 64 with four (512 registers), so that
+// the 16 records of a D = 256 row come in one round).
+template <int kWaves> constexpr int merge_loads() { return kWaves <= 4 ? 64 : 32; }
 
-// Two consecutive floats (8-byte aligned) read at device coherence, as the single floats are.
+// Two consecutive floats (8-byte aligned) read or written at device coherence, as the single
+// floats are.
 __device__ __forceinline__ uint64_t load_coherent_pair(const float* p) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent_pair(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The decode body. Q4: the cache holds 4-bit codes (two per byte, in words of 8) with one fp32
@@ -470,31 +477,31 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     __syncthreads();
 
     // ---- merge the waves; write the output (single item) or a partial -----------------------
+    // Two channels per thread and pass: a record takes one 8-byte store per pair.
     const bool direct = !ret || p.n_split == 1;
     float* part = p.partial + ((((int64_t)b * p.num_kv_heads + h) * gch + gc) * p.n_split + split) *
                                   Gs * (D + 2);
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int g = idx / D, d = idx % D;
+    for (int idx = tid; idx < G * D / 2; idx += kThreads) {
+      const int g = idx / (D / 2), d = (idx % (D / 2)) * 2;
       float M = sm_m[0][g];
 #pragma unroll
       for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][g]);
       const float Mu = (M == -INFINITY) ? 0.f : M;
-      float num = 0.f, den = 0.f;
+      float num0 = 0.f, num1 = 0.f, den = 0.f;
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
         const float c = fast_exp2(sm_m[w][g] - Mu);
-        num += c * sm_o[w][g][d];
+        num0 += c * sm_o[w][g][d];
+        num1 += c * sm_o[w][g][d + 1];
         den += c * sm_l[w][g];
       }
       if (direct) {
         T* o = static_cast<T*>(p.out) + (qb * p.num_q_heads + qh0 + g) * D;
-        o[d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+        o[d] = from_f32<T>(den > 0.f ? num0 / den : 0.f);
+        o[d + 1] = from_f32<T>(den > 0.f ? num1 / den : 0.f);
       } else {
-        store_coherent(part + g * (D + 2) + d, num);
-        if (d == 0) {
-          store_coherent(part + g * (D + 2) + D, M);
-          store_coherent(part + g * (D + 2) + D + 1, den);
-        }
+        store_coherent_pair(part + g * (D + 2) + d, num0, num1);
+        if (d == 0) store_coherent_pair(part + g * (D + 2) + D, M, den);
       }
     }
     if (direct) return;
@@ -529,20 +536,34 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   // the output (rec == nullptr) or into the record rec: (1) per q head g, one wave reduces the records' (m, l) into the merged max
   // and denominator and leaves each record's weight in LDS (the wave buffers are free by now);
   // (2) out[g][d] = sum_s w[s][g] O_s[g][d], two channels per 8-byte load, each thread keeping
-  // kMergeLoads loads in flight across its outputs and the records.
+  // merge_loads loads in flight across its outputs and the records.
   auto fold_records = [&](const float* src, int n_in, float* rec) {
     float* sm_w = &sm_o[0][0][0];   // [n_in][G]
     constexpr int kR = kFastMergeSplits / kWave;
+    // q heads per wave in the weights phase: the (m, l) loads of all of them go out first
+    constexpr int kGW = (16 + kDecodeWaves - 1) / kDecodeWaves;
     auto weights = [&]() {
-      for (int g = wave; g < G; g += kDecodeWaves) {
+      uint64_t ml[kGW][kR];
+#pragma unroll
+      for (int j = 0; j < kGW; ++j) {
+        const int g = wave + j * kDecodeWaves;
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          const int sp = lane + i * kWave;
+          ml[j][i] = (g < G && sp < n_in) ? load_coherent_pair(src + sp * rec_floats + g * (D + 2) + D) : 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kGW; ++j) {
+        const int g = wave + j * kDecodeWaves;
+        if (g >= G) break;
         float mv[kR], lv[kR];
         float M = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
-          const int sp = lane + i * kWave;
-          const float* r = src + max(min(sp, n_in - 1), 0) * rec_floats + g * (D + 2);
-          mv[i] = sp < n_in ? load_coherent(r + D) : -INFINITY;
-          lv[i] = sp < n_in ? load_coherent(r + D + 1) : 0.f;
+          const bool in = lane + i * kWave < n_in;
+          mv[i] = in ? __uint_as_float((uint32_t)ml[j][i]) : -INFINITY;
+          lv[i] = in ? __uint_as_float((uint32_t)(ml[j][i] >> 32)) : 0.f;
           M = fmaxf(M, mv[i]);
         }
 #pragma unroll
@@ -572,7 +593,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     // to the records (written from other XCDs) overlap.
     auto fold = [&](auto KP) {
       constexpr int kP = decltype(KP)::value;        // channel pairs per thread
-      constexpr int kCS = kMergeLoads / kP;          // records per round
+      constexpr int kCS = merge_loads<kDecodeWaves>() / kP;   // records per round
       float acc0[kP], acc1[kP];
       int gk[kP];
       int64_t off[kP];
