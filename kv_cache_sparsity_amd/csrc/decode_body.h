@@ -220,10 +220,14 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       sl2 *= p.mscale[b];
     }
 
-    // A wave step covers kChunks 32-key chunks (4 runs of 16 keys). In chunk c, K tile t' (two
+    // A wave step covers kChunks 32-key chunks (2 runs of 16 keys each). In chunk c, K tile t' (two
     // per chunk) puts key 8*(r/4) + 4*t' + r%4 of the chunk in MFMA row r, so the S^T accumulator
     // a lane holds for chunk c is keys 8*quad .. 8*quad+7 of the chunk: exactly the keys of its
     // V^T operand (channel dt*16 + col) and of its P^T operand.
+    // Q4 (two chunks, four runs per step) orders the keys so that a lane owns one run: chunk c's
+    // K tile t' puts slot 8c + 4t' + r%4 of run r/4 in MFMA row r, so lane (col, quad) holds slots
+    // 8c .. 8c+7 of run quad in chunk c, and its V codes of a channel for the whole step are the
+    // run's 16 slots: one 8-byte load per channel tile instead of one 4-byte load per chunk.
     const Nib4Consts n4 = Q4 ? nib4_consts<T>() : Nib4Consts{0u, 0u};
     // One 32-key chunk per step for 16-bit and int8 caches (measured best: two waves per SIMD).
     // A 4-bit step moves a quarter of the bytes, so it takes two chunks (measured on the
@@ -253,12 +257,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       const int r = col;
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
-        const int v = kRunsPerStep * step + 2 * c + (r >> 3);
+        const int v = kRunsPerStep * step + (Q4 ? (r >> 2) : 2 * c + (r >> 3));
         const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
         const int64_t base = packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int krow = ((r >> 2) & 1) * 8 + 4 * t + (r & 3);
+          const int krow = (Q4 ? 8 * c : ((r >> 2) & 1) * 8) + 4 * t + (r & 3);
           if constexpr (Q4) {
             // the lane's D / 8 bytes of the row: KC words, one per k-step
             const uint8_t* src = k4 + (packed_page(pr) * page_elems + ((int64_t)packed_row0(pr) + krow) * D) / 2 +
@@ -295,6 +299,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       if constexpr (Q8) load_scales(p.k_scale, step, kS);
     };
     auto load_v = [&](int32_t seg0, int step) {
+      if constexpr (Q4) {
+        // the lane's run (quad) of the step: slots 0 .. 15 of channel dt * 16 + col in one word
+        // pair, slots 8c .. 8c+7 for chunk c
+        const int32_t pr = sm_page[min(kRunsPerStep * step + quad, kRunSeg + kRunsPerStep - 1)];
+        const int64_t base = packed_page(pr) * page_elems + packed_row0(pr);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 w = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x2*>(v4 + (base + (int64_t)(dt * 16 + col) * bs) / 2));
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c) vW[c][dt] = w[c];
+        }
+        return;
+      }
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
@@ -302,10 +320,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
         const int64_t base = packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          if constexpr (Q4)   // the lane's 8 slots of channel dt * 16 + col: one word
-            vW[c][dt] = __builtin_nontemporal_load(
-                reinterpret_cast<const uint32_t*>(v4 + (base + (int64_t)(dt * 16 + col) * bs) / 2));
-          else if constexpr (Q8)
+          if constexpr (Q8)
             vR[c][dt] = load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs);
           else
             vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
@@ -376,14 +391,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
             for (int t = 0; t < 2; ++t) s[c][t] *= kS_cur[c][t];
         }
 
-        // Lane holds keys t0 + 8*(quad&1) + i of run 2c + quad/2, i = 4*t + j.
+        // Lane holds keys t0 + 8*(quad&1) + i of run 2c + quad/2, i = 4*t + j (Q4: keys t0 + 8c + i
+        // of run quad).
         uint32_t keep[kChunks];
         bool full = true;
         float mloc = -INFINITY;
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-          const Run rv = rl.at(geo, seg0 + kRunsPerStep * step + 2 * c + (quad >> 1));
-          const int32_t key0 = rv.t0 + (quad & 1) * 8;
+          const Run rv = rl.at(geo, seg0 + kRunsPerStep * step + (Q4 ? quad : 2 * c + (quad >> 1)));
+          const int32_t key0 = rv.t0 + (Q4 ? 8 * c : (quad & 1) * 8);
           keep[c] = 0;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
