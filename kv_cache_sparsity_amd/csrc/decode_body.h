@@ -242,23 +242,32 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
     // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
     // S^T accumulators and of its P^T operand.
-    auto load_scales = [&](const float* pool, int step, f32x4 (&dst)[kChunks][2]) {
+    // With four waves (D = 256) the look-ahead loads are issued whether or not the wave has a next
+    // step (`live`); a dead one reads page 0 (valid memory, its values unused). Loads that are
+    // always issued keep the loop free of branches around them, so that the compiler waits at each
+    // use for just the loads that use needs: behind a branch it waited for every load in flight,
+    // the step's V included, at the top of each step. There a CU has four waves' loads in flight
+    // and keeping V in flight across the S MFMAs pays (Gemma-2b static decode 31.6 -> 30.7 us);
+    // with eight waves the D <= 128 shapes stream at the chip's paged-read rate and the extra
+    // overlap made them slower (Llama-3-8B 90.9 -> 94.4 us), so they keep the branch.
+    constexpr bool kAlwaysLoad = kDecodeWaves <= 4;
+    auto load_scales = [&](const float* pool, int step, bool live, f32x4 (&dst)[kChunks][2]) {
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
-        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const int32_t pr = live ? sm_page[min(v, kRunSeg + kRunsPerStep - 1)] : 0;
         const f32x4* sp = reinterpret_cast<const f32x4*>(
             pool + ((int64_t)packed_page(pr) << p.log2_bs) + packed_row0(pr) + (quad & 1) * 8);
         dst[c][0] = __builtin_nontemporal_load(sp);
         dst[c][1] = __builtin_nontemporal_load(sp + 1);
       }
     };
-    auto load_k = [&](int32_t seg0, int step) {
+    auto load_k = [&](int32_t seg0, int step, bool live) {
       const int r = col;
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + (Q4 ? (r >> 2) : 2 * c + (r >> 3));
-        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const int32_t pr = live ? sm_page[min(v, kRunSeg + kRunsPerStep - 1)] : 0;
         const int64_t base = packed_page(pr) * page_elems + (int64_t)packed_row0(pr) * D;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -296,13 +305,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
           }
         }
       }
-      if constexpr (Q8) load_scales(p.k_scale, step, kS);
+      if constexpr (Q8) load_scales(p.k_scale, step, live, kS);
     };
-    auto load_v = [&](int32_t seg0, int step) {
+    auto load_v = [&](int32_t seg0, int step, bool live) {
       if constexpr (Q4) {
         // the lane's run (quad) of the step: slots 0 .. 15 of channel dt * 16 + col in one word
         // pair, slots 8c .. 8c+7 for chunk c
-        const int32_t pr = sm_page[min(kRunsPerStep * step + quad, kRunSeg + kRunsPerStep - 1)];
+        const int32_t pr = live ? sm_page[min(kRunsPerStep * step + quad, kRunSeg + kRunsPerStep - 1)] : 0;
         const int64_t base = packed_page(pr) * page_elems + packed_row0(pr);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -316,7 +325,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int v = kRunsPerStep * step + 2 * c + (quad >> 1);
-        const int32_t pr = sm_page[min(v, kRunSeg + kRunsPerStep - 1)];
+        const int32_t pr = live ? sm_page[min(v, kRunSeg + kRunsPerStep - 1)] : 0;
         const int64_t base = packed_page(pr) * page_elems + packed_row0(pr) + (quad & 1) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -326,7 +335,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
             vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
         }
       }
-      if constexpr (Q8) load_scales(p.v_scale, step, vS);
+      if constexpr (Q8) load_scales(p.v_scale, step, live, vS);
     };
 
     for (int32_t seg0 = 0; seg0 < n_runs; seg0 += kRunSeg) {
@@ -339,9 +348,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       __syncthreads();
       const int n_steps = (nseg + kRunsPerStep - 1) / kRunsPerStep;
       int step = wave;
-      if (step < n_steps) {
-        load_k(seg0, step);
-        load_v(seg0, step);
+      if (kAlwaysLoad || step < n_steps) {
+        load_k(seg0, step, step < n_steps);
+        load_v(seg0, step, step < n_steps);
       }
       // Wave w starts with step w; after that each wave claims the next unclaimed step, so waves
       // that run ahead take more steps and all of them finish together.
@@ -383,7 +392,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
             kS_cur[c][1] = kS[c][1];
           }
         }
-        if (has_next) load_k(seg0, nxt);   // next step's K streams in during this step's math
+        // next step's K streams in during this step's math
+        if (kAlwaysLoad || has_next) load_k(seg0, nxt, has_next);
         if constexpr (Q8) {   // scores of the int8 cache: (codes . q) * the key's K scale
 #pragma unroll
           for (int c = 0; c < kChunks; ++c)
@@ -465,7 +475,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
             for (int dt = 0; dt < DT; ++dt) oT[dt] = mfma16(vA[c][dt], pB, oT[dt]);
           }
         }
-        if (has_next) load_v(seg0, nxt);   // V registers are free once the PV MFMAs issued
+        // V registers are free once the PV MFMAs issued
+        if (kAlwaysLoad || has_next) load_v(seg0, nxt, has_next);
         step = nxt;
       }
     }
