@@ -429,8 +429,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
         // exceeds it by more than 8 (log2 units), so the cross-lane max and the O rescale run on
         // few steps; p = 2^(x - m_run) <= 256 in between.
         if (__any(mloc > m_run + 8.f)) {
-          float mx = fmaxf(mloc, shfl_xor(mloc, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float mx = max_xor32(max_xor16(mloc));
           const float m_new = fmaxf(m_run, mx);
           const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
           m_run = m_new;
@@ -481,8 +480,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       }
     }
     // lanes sharing a column hold partial sums over disjoint keys
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
+    l_run = add_xor32(add_xor16(l_run));
     if constexpr (Q4) {
       // every V operand was 24 + code: take 24 times the weights back out, then the channel scale
       const float* vsc = p.v_scale + (int64_t)h * D + quad * 4;
@@ -560,13 +558,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   const int64_t rec_floats = (int64_t)Gs * (D + 2);   // record stride
 
   // Fold n_in records at src (rec_floats apart; heads 0 .. G - 1 of each used; all complete) into
-  // the output (rec == nullptr) or into the record rec: (1) per q head g, one wave reduces the records' (m, l) into the merged max
-  // and denominator and leaves each record's weight in LDS (the wave buffers are free by now);
-  // (2) out[g][d] = sum_s w[s][g] O_s[g][d], two channels per 8-byte load, each thread keeping
-  // merge_loads loads in flight across its outputs and the records.
+  // the output (rec == nullptr) or into the record rec: (1) per q head g, one wave reduces the
+  // records' (m, l) into the merged max and denominator and leaves each record's weight in LDS
+  // (the wave buffers are free by now); (2) out[g][d] = sum_s w[g][s] O_s[g][d], two channels per
+  // 8-byte load, each thread keeping merge_loads loads in flight across its outputs and the
+  // records, and reading its weights four at a time.
   auto fold_records = [&](const float* src, int n_in, float* rec) {
-    float* sm_w = &sm_o[0][0][0];   // [n_in][G]
     constexpr int kR = kFastMergeSplits / kWave;
+    constexpr int kWStride = kR * kWave;   // weights of one q head; zero past n_in
+    float* sm_w = &sm_o[0][0][0];          // [G][kWStride]
     // q heads per wave in the weights phase: the (m, l) loads of all of them go out first
     constexpr int kGW = (16 + kDecodeWaves - 1) / kDecodeWaves;
     auto weights = [&]() {
@@ -593,14 +593,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
           lv[i] = in ? __uint_as_float((uint32_t)(ml[j][i] >> 32)) : 0.f;
           M = fmaxf(M, mv[i]);
         }
-#pragma unroll
-        for (int o = kWave / 2; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+        M = wave_max(M);
         const float Mu = (M == -INFINITY) ? 0.f : M;
         float den = 0.f;
 #pragma unroll
         for (int i = 0; i < kR; ++i) den += (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * lv[i];
-#pragma unroll
-        for (int o = kWave / 2; o >= 1; o >>= 1) den += shfl_xor(den, o);
+        den = wave_sum(den);
         // the output is normalised; a record keeps its max and denominator
         const float inv = rec ? 1.f : (den > 0.f ? 1.f / den : 0.f);
         if (rec && lane == 0) {
@@ -608,10 +606,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
           store_coherent(rec + g * (D + 2) + D + 1, den);
         }
 #pragma unroll
-        for (int i = 0; i < kR; ++i) {
-          const int sp = lane + i * kWave;
-          if (sp < n_in) sm_w[sp * G + g] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
-        }
+        for (int i = 0; i < kR; ++i)
+          sm_w[g * kWStride + lane + i * kWave] = (mv[i] == -INFINITY) ? 0.f : fast_exp2(mv[i] - Mu) * inv;
       }
       __syncthreads();
     };
@@ -641,16 +637,23 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       };
       if (n_in > 0) load_round(0);
       weights();
+      static_assert(kCS % 4 == 0 && kWStride % kCS == 0, "weights are read four at a time");
       for (int s0 = 0; s0 < n_in; s0 += kCS) {
         if (s0 > 0) load_round(s0);
 #pragma unroll
-        for (int k = 0; k < kP; ++k)
+        for (int k = 0; k < kP; ++k) {
+          // records past n_in were loaded from the last one (finite) and weigh 0
+          const f32x4* w4 = reinterpret_cast<const f32x4*>(sm_w + gk[k] * kWStride + s0);
 #pragma unroll
-          for (int i = 0; i < kCS; ++i) {
-            const float wgt = (s0 + i < n_in) ? sm_w[(s0 + i) * G + gk[k]] : 0.f;
-            acc0[k] += wgt * __uint_as_float((uint32_t)v[k][i]);
-            acc1[k] += wgt * __uint_as_float((uint32_t)(v[k][i] >> 32));
+          for (int i4 = 0; i4 < kCS / 4; ++i4) {
+            const f32x4 w = w4[i4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc0[k] += w[e] * __uint_as_float((uint32_t)v[k][4 * i4 + e]);
+              acc1[k] += w[e] * __uint_as_float((uint32_t)(v[k][4 * i4 + e] >> 32));
+            }
           }
+        }
       }
 #pragma unroll
       for (int k = 0; k < kP; ++k) {

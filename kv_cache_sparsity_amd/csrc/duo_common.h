@@ -204,8 +204,6 @@ __device__ __forceinline__ f32x16 mfma32(f32x8 a, f32x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
-
 // A value combined with the same value of lane (lane ^ 32) by one v_permlane32_swap, which trades
 // the upper 32 lanes of its first operand for the lower 32 of its second: given v twice, every lane
 // gets back its own v and its partner's, one in each result. (A shuffle would go through LDS.)
@@ -216,6 +214,43 @@ __device__ __forceinline__ float max_xor32(float v) {
 __device__ __forceinline__ float add_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same with lane (lane ^ 16): v_permlane16_swap trades the odd rows (16 lanes) of its first
+// operand for the even rows of its second.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum / sum over the 64 lanes of a wave, in every lane, without LDS: DPP moves combine lane
+// pairs inside quads (lane ^ 1, lane ^ 2), then the two quads of each 8 (row_half_mirror) and the
+// two 8s of each row (row_mirror); the row swaps above finish it. Each step combines two values
+// that are equal within their group, commutatively, so every lane ends with the same bits.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15 - i within each row
+__device__ __forceinline__ float wave_max(float v) {
+  v = __builtin_elementwise_maximum(v, dpp_move<kDppXor1>(v));
+  v = __builtin_elementwise_maximum(v, dpp_move<kDppXor2>(v));
+  v = __builtin_elementwise_maximum(v, dpp_move<kDppHalfMirror>(v));
+  v = __builtin_elementwise_maximum(v, dpp_move<kDppMirror>(v));
+  return max_xor32(max_xor16(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_move<kDppXor1>(v);
+  v += dpp_move<kDppXor2>(v);
+  v += dpp_move<kDppHalfMirror>(v);
+  v += dpp_move<kDppMirror>(v);
+  return add_xor32(add_xor16(v));
 }
 
 // Device-scope coherent store / load (write-through / read-through the XCD-local L2): used for
