@@ -279,6 +279,47 @@ def test_decode_repeated_calls_and_workspace_reuse():
     say(f"  {same} of 3 repeated calls bitwise equal to the first")
 
 
+_rng_ret = np.random.default_rng(97)
+ALL_RETRIEVAL_CASES = [
+    # 64 sequences: empty, one-token and full rows among random ones
+    dict(name="bf16-d128-g4-b64", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(0, 1),
+         block_size=16, sink=0, recent=1, ring_blocks=1,
+         lens=[0, 1, 4096, 4095] + [int(x) for x in _rng_ret.integers(0, 4097, 60)]),
+    # a Gemma-like static cache: lengths around split boundaries
+    dict(name="f16-d256-g8-mqa", dtype=synth.F16, head_dim=256, group=8, kv=1, ret=(0,),
+         block_size=16, sink=0, recent=1, ring_blocks=1,
+         lens=[0, 1, 5, 383, 384, 385, 2000, 8192]),
+    # q heads in chunks of 16 (two rows per sequence and kv head)
+    dict(name="bf16-d64-g20", dtype=synth.BF16, head_dim=64, group=20, kv=1, ret=(0,),
+         block_size=32, sink=0, recent=1, ring_blocks=1, lens=[1, 700, 3000]),
+    # short rows: one live split each, the rest of the row's items past its length
+    dict(name="f16-d128-short", dtype=synth.F16, head_dim=128, group=2, kv=3, ret=(0, 1, 2),
+         block_size=16, sink=0, recent=1, ring_blocks=1, lens=[1, 2, 15, 16, 17, 40]),
+]
+
+
+@pytest.mark.parametrize("case", ALL_RETRIEVAL_CASES, ids=[c["name"] for c in ALL_RETRIEVAL_CASES])
+def test_decode_all_retrieval_mixed_lengths(case):
+    """No streaming heads, the library's split, lengths from 0 to the capacity (many items past
+    their row's length). Two calls on one workspace, each within the oracle's tolerance, every merge
+    ticket back at zero after each."""
+    say(f"decode, all retrieval heads: {case['name']}")
+    w, cache, K, V, q = _decode_case(case)
+    want = oracle_decode(w, q, K, V, np.asarray(case["lens"]), cache.mask)
+    qd = to_dev(q, w.dtype)
+    ws = duo.decode_workspace(qd, cache.table, w.block_size, 0)
+    gch = -(-case["group"] // 16)
+    for rep in range(2):
+        got = to_host_f64(cache.decode(q, workspace=ws), w.dtype)
+        check_close(got, want, w.dtype, f"{case['name']} call {rep}")
+        for b, L in enumerate(case["lens"]):
+            if L == 0:
+                assert (got[b] == 0).all()
+        torch.cuda.synchronize()
+        nctr = w.batch * w.num_kv_heads * gch
+        assert int(ws[:4 * nctr].view(torch.int32).abs().sum().item()) == 0
+
+
 # ------------------------------------------------------------------------------------------------
 # prefill
 # ------------------------------------------------------------------------------------------------
