@@ -240,8 +240,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     u32x2 kR[kChunks][2][KC], vR[kChunks][DT];
     uint32_t kW[kChunks][2][KC], vW[kChunks][DT];   // Q4: the code words
     f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
-    // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
-    // S^T accumulators and of its P^T operand.
     // With four waves (D = 256) the look-ahead loads are issued whether or not the wave has a next
     // step (`live`); a dead one reads page 0 (valid memory, its values unused). Loads that are
     // always issued keep the loop free of branches around them, so that the compiler waits at each
@@ -251,6 +249,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     // with eight waves the D <= 128 shapes stream at the chip's paged-read rate and the extra
     // overlap made them slower (Llama-3-8B 90.9 -> 94.4 us), so they keep the branch.
     constexpr bool kAlwaysLoad = kDecodeWaves <= 4;
+    // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
+    // S^T accumulators and of its P^T operand.
     auto load_scales = [&](const float* pool, int step, bool live, f32x4 (&dst)[kChunks][2]) {
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
