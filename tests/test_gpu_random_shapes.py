@@ -18,7 +18,7 @@ import synth
 from tests.gpu_harness import (Cache, check_close, logical_kv, oracle_decode, q_decode, q_prefill,
                                say, to_dev, to_host_f64)
 
-N_CASES = 36
+N_CASES = 96
 
 
 @pytest.fixture(scope="module")
@@ -103,8 +103,8 @@ def test_random_shape_parity(i, _need_gpu):
 # ------------------------------------------------------------------------------------------------
 # the int8 cache and Dual Chunk Attention on seeded random shapes
 # ------------------------------------------------------------------------------------------------
-N_INT8 = 12
-N_DCA = 12
+N_INT8 = 30
+N_DCA = 24
 
 
 def _fill(cache_append, K, V, lens, table):
@@ -202,7 +202,7 @@ def test_random_shape_dca_parity(i, _need_gpu):
     check_close(got, want, dtype, name)
 
 
-N_VARLEN = 8
+N_VARLEN = 20
 
 
 @pytest.mark.gpu
@@ -261,8 +261,8 @@ def test_random_shape_varlen_prefill_parity(i, _need_gpu):
 # ------------------------------------------------------------------------------------------------
 # the 4-bit cache, and decode with GQA groups of more than 16 q heads, on seeded random shapes
 # ------------------------------------------------------------------------------------------------
-N_INT4 = 12
-N_GROUPS = 10
+N_INT4 = 36
+N_GROUPS = 30
 
 
 @pytest.mark.gpu
