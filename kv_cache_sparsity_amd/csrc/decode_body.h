@@ -134,9 +134,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     if (s1 - s0 != 1) return;
     qb = s0;
   }
-  int32_t L = max(p.seq_lens[b], 0);
-  if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
-
   HeadGeom geo;
   geo.row = p.table + ((int64_t)b * p.num_kv_heads + h) * p.max_blocks_per_head;
   geo.num_blocks = p.num_blocks;
@@ -144,6 +141,25 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
   geo.sink = p.sink;
   geo.sink_blocks = p.sink_blocks;
   geo.ring_slots = p.ring_slots;
+
+  // A retrieval split's first segment of block-table entries does not depend on the sequence's
+  // length: they are read before it, so that the two reads' round trips overlap (entries of runs
+  // past the length are read and not used; page_of clamps every entry into the pool).
+  constexpr int kPre = (kRunSeg + kThreads - 1) / kThreads;
+  int32_t pre[kPre];
+  if (ret) {
+    const int32_t cap = p.max_blocks_per_head << p.log2_bs;
+    const int32_t t0 = split * p.split_tokens;
+    const int32_t nr = min((min(p.split_tokens, max(cap - t0, 0)) + 15) / 16, kRunSeg);
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const int32_t v = (int32_t)threadIdx.x + j * kThreads;
+      const int32_t slot = t0 + v * 16;
+      pre[j] = v < nr ? pack_run(geo.page_of(slot), geo.row0(slot)) : 0;
+    }
+  }
+  int32_t L = max(p.seq_lens[b], 0);
+  if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
 
   // ---- the item's runs ----------------------------------------------------------------------
   RunList rl;
@@ -341,7 +357,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     for (int32_t seg0 = 0; seg0 < n_runs; seg0 += kRunSeg) {
       const int32_t nseg = min(kRunSeg, n_runs - seg0);
       if (seg0 > 0) __syncthreads();   // everyone is done with the previous segment's pages
-      load_pages<kThreads>(sm_page, geo, rl, seg0, nseg);
+      if (ret && seg0 == 0) {
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+          const int32_t v = (int32_t)threadIdx.x + j * kThreads;
+          if (v < nseg) sm_page[v] = pre[j];
+        }
+      } else {
+        load_pages<kThreads>(sm_page, geo, rl, seg0, nseg);
+      }
       // runs past the end of the list read page 0 (valid memory, fully masked)
       for (int i = nseg + (int)threadIdx.x; i < nseg + kRunsPerStep; i += kThreads) sm_page[i] = 0;
       if (threadIdx.x == 0) sm_next_step = kDecodeWaves;
