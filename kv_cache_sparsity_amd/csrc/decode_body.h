@@ -256,15 +256,17 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     u32x2 kR[kChunks][2][KC], vR[kChunks][DT];
     uint32_t kW[kChunks][2][KC], vW[kChunks][DT];   // Q4: the code words
     f32x4 kS[kChunks][2], vS[kChunks][2];   // Q8: scales of the lane's 8 keys (S^T / P^T slots)
-    // With four waves (D = 256) the look-ahead loads are issued whether or not the wave has a next
-    // step (`live`); a dead one reads page 0 (valid memory, its values unused). Loads that are
-    // always issued keep the loop free of branches around them, so that the compiler waits at each
-    // use for just the loads that use needs: behind a branch it waited for every load in flight,
-    // the step's V included, at the top of each step. There a CU has four waves' loads in flight
-    // and keeping V in flight across the S MFMAs pays (Gemma-2b static decode 31.6 -> 30.7 us);
-    // with eight waves the D <= 128 shapes stream at the chip's paged-read rate and the extra
-    // overlap made them slower (Llama-3-8B 90.9 -> 94.4 us), so they keep the branch.
-    constexpr bool kAlwaysLoad = kDecodeWaves <= 4;
+    // With four waves (D = 256) and for the int8 cache the look-ahead loads are issued whether or
+    // not the wave has a next step (`live`); a dead one reads page 0 (valid memory, its values
+    // unused). Loads that are always issued keep the loop free of branches around them, so that
+    // the compiler waits at each use for just the loads that use needs: behind a branch it waited
+    // for every load in flight, the step's V included, at the top of each step. Keeping V in
+    // flight across the S MFMAs pays where a CU has four waves' loads in flight (Gemma-2b static
+    // decode 31.6 -> 30.7 us) and for int8, whose steps spend longer converting codes (Llama-3-8B
+    // shape 58.4 -> 57.8 us); the 16-bit and 4-bit D <= 128 shapes stream at the chip's paged-read
+    // rate and the extra overlap made them slower (Llama-3-8B 90.9 -> 94.4 us), so they keep the
+    // branch.
+    constexpr bool kAlwaysLoad = kDecodeWaves <= 4 || Q8;
     // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
     // S^T accumulators and of its P^T operand.
     auto load_scales = [&](const float* pool, int step, bool live, f32x4 (&dst)[kChunks][2]) {
