@@ -267,6 +267,14 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     // rate and the extra overlap made them slower (Llama-3-8B 90.9 -> 94.4 us), so they keep the
     // branch.
     constexpr bool kAlwaysLoad = kDecodeWaves <= 4 || Q8;
+    // 16-bit K and V: non-temporal loads (not kept in the caches) with eight waves, plain loads
+    // with four (D = 256). Measured with a 1 GiB read before each launch: plain loads take the
+    // Gemma-2b static decode from 32.2 to 29.5 us, and the eight-wave shapes from 92.5 to 100.7 us
+    // (Llama-3-8B) and 337 to 367 us (1M context).
+    auto load_kv8 = [&](const T* ptr) {
+      if constexpr (kDecodeWaves <= 4 && sizeof(T) == 2) return load8(ptr);
+      else return load8_stream(ptr);
+    };
     // Scales of keys 8*(quad&1) .. +7 of run 2c + quad/2 of the step: the keys of the lane's
     // S^T accumulators and of its P^T operand.
     auto load_scales = [&](const float* pool, int step, bool live, f32x4 (&dst)[kChunks][2]) {
@@ -319,7 +327,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
           } else {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-              kA[c][t][kc] = load8_stream(kpool + base + krow * D + kc * 32 + quad * 8);
+              kA[c][t][kc] = load_kv8(kpool + base + krow * D + kc * 32 + quad * 8);
           }
         }
       }
@@ -350,7 +358,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
           if constexpr (Q8)
             vR[c][dt] = load_codes8_stream(vq + base + (int64_t)(dt * 16 + col) * bs);
           else
-            vA[c][dt] = load8_stream(vpool + base + (int64_t)(dt * 16 + col) * bs);
+            vA[c][dt] = load_kv8(vpool + base + (int64_t)(dt * 16 + col) * bs);
         }
       }
       if constexpr (Q8) load_scales(p.v_scale, step, live, vS);
