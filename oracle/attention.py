@@ -13,6 +13,12 @@ pages do not spell out -- parity unpinned by the pages for this mapping, pinned 
     position once (DuoAttention README, abstract and quick-start's sink_size / recent_size; vLLM issue
     "Could you support Attention Sink?", the sink tokens kept beside the streamed ones). The window
     counts the query's own position.
+    A negative ``recent`` asks for the block-granular window instead (same vLLM issue, ChuanhongLi's
+    comment: keep the sequence's first block as the sink, drop blocks in the middle and keep the
+    recent blocks, with the number of blocks per sequence capped): positions are grouped into blocks
+    of ``block_size`` (block n holds n*block_size .. (n+1)*block_size - 1), and the window is the
+    -recent newest blocks up to the query's own, that block counting as one however few of its
+    positions exist yet. The sink rule j < sink is unchanged.
 Query row i of a call with q_len rows sits at position seq_len - q_len + i: the new tokens are in the
 cache when they are attended (transformers PR, cache update then attention).
 
@@ -27,14 +33,30 @@ import numpy as np
 from .cache import to_f64, gather
 
 
-def visible_positions(p: int, *, retrieval: bool, sink: int, recent: int) -> np.ndarray:
+def in_window(p, j, recent: int, block_size=None):
+    """Is key position j inside the recent window of a query at position p (elementwise)?
+
+    recent >= 0: the recent newest positions, p - j < recent. recent < 0: the -recent newest blocks of
+    block_size positions, counted back from the block holding p: block(j) > block(p) + recent.
+    """
+    p = np.asarray(p, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    if recent >= 0:
+        return p - j < recent
+    if not block_size or block_size < 1:
+        raise ValueError("a block-granular window (recent < 0) needs the block size")
+    return j // block_size > p // block_size + recent
+
+
+def visible_positions(p: int, *, retrieval: bool, sink: int, recent: int,
+                      block_size=None) -> np.ndarray:
     """Sorted logical positions a query at position p may attend to."""
     if p < 0:
         return np.zeros(0, dtype=np.int64)
     j = np.arange(p + 1, dtype=np.int64)
     if retrieval:
         return j
-    return j[(j < sink) | (p - j < recent)]
+    return j[(j < sink) | in_window(p, j, recent, block_size)]
 
 
 def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
@@ -47,23 +69,24 @@ def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.
     return (w @ V) / w.sum()
 
 
-def visible_mask(p_rows, key_pos, *, retrieval: bool, sink: int, recent: int) -> np.ndarray:
+def visible_mask(p_rows, key_pos, *, retrieval: bool, sink: int, recent: int,
+                 block_size=None) -> np.ndarray:
     """Boolean [R][N]: may a query at position p_rows[r] attend the key at position key_pos[n]?
 
     The rule of ``visible_positions``, applied to every (query, key) pair at once: the key is at or
     before the query, and for a streaming head it is a sink (j < sink) or in the recent window
-    (p - j < recent).
+    (``in_window``).
     """
     p = np.asarray(p_rows, dtype=np.int64)[:, None]
     j = np.asarray(key_pos, dtype=np.int64)[None, :]
     ok = (j >= 0) & (j <= p)
     if not retrieval:
-        ok = ok & ((j < sink) | (p - j < recent))
+        ok = ok & ((j < sink) | in_window(p, j, recent, block_size))
     return ok
 
 
 def attend_rows(q_rows, p_rows, K, V, key_pos, *, retrieval: bool, sink: int, recent: int,
-                scale: float) -> np.ndarray:
+                scale: float, block_size=None) -> np.ndarray:
     """Several query rows of one (sequence, kv head) at once, float64: the same softmax attention
     as ``attend_row`` over ``visible_positions``, with the scores of all rows taken in one matrix
     product and the invisible ones set to -inf.
@@ -72,7 +95,8 @@ def attend_rows(q_rows, p_rows, K, V, key_pos, *, retrieval: bool, sink: int, re
     positions key_pos [N], which must include every key any of the rows can see (keys no row sees
     may be left out). Rows with nothing visible give zeros. Returns [R][D].
     """
-    ok = visible_mask(p_rows, key_pos, retrieval=retrieval, sink=sink, recent=recent)
+    ok = visible_mask(p_rows, key_pos, retrieval=retrieval, sink=sink, recent=recent,
+                      block_size=block_size)
     s = np.where(ok, scale * (np.asarray(q_rows, dtype=np.float64) @ K.T), -np.inf)
     seen = ok.any(axis=1)
     m = np.where(seen, s.max(axis=1), 0.0)
@@ -83,12 +107,14 @@ def attend_rows(q_rows, p_rows, K, V, key_pos, *, retrieval: bool, sink: int, re
     return out
 
 
-def attend(q, k, v, seq_lens, retrieval_mask, *, sink, recent, scale, dtype, rows=None):
+def attend(q, k, v, seq_lens, retrieval_mask, *, sink, recent, scale, dtype, rows=None,
+           block_size=None):
     """Reference output for every (or the selected) query rows, float64.
 
     q: [B][q_len][Hq][D] stored elements; k, v: logical caches [B][Hkv][>= max len][D] stored
     elements (position j of head h of sequence b at k[b, h, j]); seq_lens: [B] valid lengths
     including the query rows. rows: optional iterable of (b, i, hq); by default every row.
+    block_size: the block length of a block-granular window (recent < 0).
     Returns out [B][q_len][Hq][D] float64 (unselected rows stay NaN).
     """
     B, q_len, Hq, D = q.shape
@@ -101,7 +127,8 @@ def attend(q, k, v, seq_lens, retrieval_mask, *, sink, recent, scale, dtype, row
     for b, i, hq in rows:
         h = hq // G
         p = int(seq_lens[b]) - q_len + i
-        J = visible_positions(p, retrieval=bool(retrieval_mask[h]), sink=sink, recent=recent)
+        J = visible_positions(p, retrieval=bool(retrieval_mask[h]), sink=sink, recent=recent,
+                              block_size=block_size)
         key = (b, h)
         if key not in cache:
             cache = {key: (to_f64(k[b, h], dtype), to_f64(v[b, h], dtype))}
@@ -123,7 +150,7 @@ def attend_paged(q, k_pool, v_pool, table, seq_lens, retrieval_mask, *, sink, re
         h = hq // G
         ret = bool(retrieval_mask[h])
         p = int(seq_lens[b]) - q_len + i
-        J = visible_positions(p, retrieval=ret, sink=sink, recent=recent)
+        J = visible_positions(p, retrieval=ret, sink=sink, recent=recent, block_size=block_size)
         Ks, Vs = gather(k_pool, v_pool, table, b, h, J, retrieval=ret, sink=sink,
                         block_size=block_size, ring_blocks=ring_blocks)
         out[b, i, hq] = attend_row(to_f64(q[b, i, hq], dtype), to_f64(Ks, dtype),

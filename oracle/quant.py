@@ -91,13 +91,13 @@ def append_int8(k_pool, v_pool, k_scale, v_scale, table, k_new, v_new, seq_lens_
 
 
 def attend_int8(q, k_codes, k_scales, v_codes, v_scales, seq_lens, retrieval_mask, *, sink, recent,
-                scale, dtype, rows=None):
+                scale, dtype, rows=None, block_size=None):
     """Reference output over a logical int8 cache, float64.
 
     q: [B][q_len][Hq][D] stored elements of dtype; k_codes, v_codes: [B][Hkv][>= max len][D] int8;
     k_scales, v_scales: [B][Hkv][>= max len] float32 (position j of head h of sequence b at
-    [b, h, j]). Visible sets, query positions and the softmax are those of oracle.attention.attend,
-    over the dequantized rows code * scale.
+    [b, h, j]). Visible sets, query positions and the softmax are those of oracle.attention.attend
+    (block_size as there), over the dequantized rows code * scale.
     """
     B, q_len, Hq, D = q.shape
     Hkv = k_codes.shape[1]
@@ -109,7 +109,8 @@ def attend_int8(q, k_codes, k_scales, v_codes, v_scales, seq_lens, retrieval_mas
     for b, i, hq in rows:
         h = hq // G
         p = int(seq_lens[b]) - q_len + i
-        J = visible_positions(p, retrieval=bool(retrieval_mask[h]), sink=sink, recent=recent)
+        J = visible_positions(p, retrieval=bool(retrieval_mask[h]), sink=sink, recent=recent,
+                              block_size=block_size)
         key = (b, h)
         if key not in cache:
             cache = {key: (dequantize(k_codes[b, h], k_scales[b, h]),

@@ -439,17 +439,17 @@ def test_row_blocks_rows_before_the_start_are_zero():
 # ------------------------------------------------------------------------------------------------
 # Planted mistakes: each must be caught by one of the pins above
 # ------------------------------------------------------------------------------------------------
-def _window_off_by_one(p, *, retrieval, sink, recent):
+def _window_off_by_one(p, *, retrieval, sink, recent, block_size=None):
     j = np.arange(max(p, -1) + 1)
     return j if retrieval else j[(j < sink) | (p - j <= recent)]
 
 
-def _sink_dropped(p, *, retrieval, sink, recent):
+def _sink_dropped(p, *, retrieval, sink, recent, block_size=None):
     j = np.arange(max(p, -1) + 1)
     return j if retrieval else j[p - j < recent]
 
 
-def _future_leak(p, *, retrieval, sink, recent):
+def _future_leak(p, *, retrieval, sink, recent, block_size=None):
     j = np.arange(max(p, -1) + 2)
     return j if retrieval else j[(j < sink) | (p - j < recent)]
 
@@ -490,19 +490,19 @@ def test_planted_softmax_bugs_are_caught(monkeypatch, bug):
         test_oracle_matches_brute_force(*SWEEP[3])
 
 
-def _mask_window_off_by_one(p_rows, key_pos, *, retrieval, sink, recent):
+def _mask_window_off_by_one(p_rows, key_pos, *, retrieval, sink, recent, block_size=None):
     p, j = np.asarray(p_rows)[:, None], np.asarray(key_pos)[None, :]
     ok = (j >= 0) & (j <= p)
     return ok if retrieval else ok & ((j < sink) | (p - j <= recent))
 
 
-def _mask_sink_dropped(p_rows, key_pos, *, retrieval, sink, recent):
+def _mask_sink_dropped(p_rows, key_pos, *, retrieval, sink, recent, block_size=None):
     p, j = np.asarray(p_rows)[:, None], np.asarray(key_pos)[None, :]
     ok = (j >= 0) & (j <= p)
     return ok if retrieval else ok & (p - j < recent)
 
 
-def _mask_future_leak(p_rows, key_pos, *, retrieval, sink, recent):
+def _mask_future_leak(p_rows, key_pos, *, retrieval, sink, recent, block_size=None):
     p, j = np.asarray(p_rows)[:, None], np.asarray(key_pos)[None, :]
     ok = (j >= 0) & (j <= p + 1)
     return ok if retrieval else ok & ((j < sink) | (p - j < recent))
