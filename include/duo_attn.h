@@ -10,6 +10,9 @@
  *   - vLLM issue "Could you support Attention Sink?", sh1ng's comment: a block-paged cache in which a
  *     streaming head's sink tokens sit in block(s) of their own and the other tokens cycle through a
  *     circular buffer (option 3); its worked tables give the ring index (t - sink) mod ring size.
+ *   - vLLM issue "Could you support Attention Sink?", ChuanhongLi's comment: the same head may instead
+ *     keep whole blocks, the first one as the sink and the newest ones, dropping a middle block when
+ *     a new one starts (the block-granular window below, chosen by a negative recent_size).
  *   - transformers PR "[WIP] Dynamic length in static cache", description: a query only needs the
  *     positions up to its own, not the whole allocated cache; lengths therefore live in a device
  *     array read by the kernels, never on the host, and no launch shape depends on them.
@@ -40,6 +43,17 @@
  *                     with SB = ceil(sink_size / block_size) sink pages in front of the ring.
  *   A streaming head uses table columns [0, SB + ring_blocks); a retrieval head uses every column.
  *   Page ids outside [0, num_blocks) are clamped into range by the kernels (wrong results, no fault).
+ *   Recent window of a streaming head (every attention call), for the query at position p:
+ *     recent_size > 0: positions p - recent_size < j <= p (the recent_size newest, p included);
+ *     recent_size < 0: block-granular, the -recent_size newest blocks of block_size positions up to
+ *                      p's own, that block counting as one however few of its positions exist:
+ *                      (floor(p / block_size) + recent_size) * block_size < j <= p. Blocks are
+ *                      aligned at position 0, so the window holds between
+ *                      (-recent_size - 1) * block_size + 1 and -recent_size * block_size positions.
+ *     recent_size = 0 is rejected (INVALID_ARG) when a streaming head is present. The window's span
+ *     W is recent_size or -recent_size * block_size; the ring must hold the span plus the rows of
+ *     one call: ring_blocks * block_size >= W + q_len - 1 (q_len = 1 for decode), else CAPACITY.
+ *     The append keeps every ring slot either way; only the attention calls apply the window.
  *   Shared sink pages (vLLM attention-sink issue, sh1ng's option 3: the sink block can serve every
  *   request that starts with the same sink tokens): the rows of several sequences may point a
  *   streaming head's sink columns [0, SB) at the same pages when their first sink_size tokens are
@@ -57,7 +71,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 11
+#define DUO_ATTN_ABI_VERSION 12
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -131,7 +145,8 @@ size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  *   workspace           device, >= duo_attn_decode_workspace_size(...) bytes, zero-filled once.
  *   split_tokens        keys per split-K work item: 0 = library's choice, else a multiple of 128.
  * Visible positions of the query at p = seq_lens[b] - 1: retrieval head j in [0, p]; streaming head
- * j < sink_size or p - j < recent_size (within [0, p]). seq_lens[b] = 0 yields a zero output row.
+ * j < sink_size or j in its recent window (see the cache layout; within [0, p]). seq_lens[b] = 0
+ * yields a zero output row.
  * Retrieval lengths above max_blocks_per_head*block_size are clamped to it.
  * The q heads of a kv head are taken up to 16 at a time (a larger GQA group in chunks of 16, each
  * reading the kv head's keys and values once).
@@ -140,7 +155,7 @@ size_t duo_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  * bits of the output, can differ from call to call (every call is within the stated tolerance).
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16),
  *         CAPACITY (streaming heads present and
- *         ring_blocks*block_size < recent_size or SB + ring_blocks > max_blocks_per_head),
+ *         ring_blocks*block_size < the window's span or SB + ring_blocks > max_blocks_per_head),
  *         WORKSPACE.
  */
 int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -203,8 +218,9 @@ size_t duo_attn_prefill_workspace_size(int32_t batch, int32_t q_len, int32_t num
  *   workspace           device, >= duo_attn_prefill_workspace_size(...) bytes, zero-filled once
  *                       (may be NULL when no kv head is a retrieval head).
  * Visible set of row i at position p: as for decode. Streaming heads need
- * ring_blocks*block_size >= recent_size + q_len - 1 so that the oldest key of the first row is still
- * in the ring.
+ * ring_blocks*block_size >= W + q_len - 1 (W the window's span: recent_size, or -recent_size *
+ * block_size for the block-granular window) so that the oldest key of the first row is still in
+ * the ring.
  * Calls sharing one workspace must not run concurrently.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype, block_size not a power of two >= 16),
  *         CAPACITY, WORKSPACE.

@@ -56,13 +56,35 @@ int32_t check_cache(const void* k_pool, const void* v_pool, const int32_t* table
   return DUO_OK;
 }
 
+// A streaming head's recent window, as the kernels take it: for a query at position p it starts at
+// (p & mask) - back and ends at p.
+//   recent > 0: the recent newest positions (mask keeps every bit, back = recent - 1);
+//   recent < 0: the -recent newest blocks of bs positions, the query's own block counting as one
+//               however few of its positions exist (mask clears the offset inside the block,
+//               back = (blocks - 1) * bs). This is the block-granular policy of the vLLM
+//               attention-sink issue (ChuanhongLi's comment): the oldest middle block is dropped
+//               when a new block starts.
+// span is the most positions one window holds.
+struct Window {
+  int32_t mask, back;
+  int64_t span;
+};
+Window window_of(int32_t n_str, int32_t recent, int32_t bs) {
+  if (n_str == 0 || recent == 0) return Window{-1, 0, 0};
+  if (recent > 0) return Window{-1, recent - 1, recent};
+  const int64_t blocks = -(int64_t)recent;
+  return Window{-bs, (int32_t)std::min<int64_t>((blocks - 1) * bs, INT32_MAX), blocks * bs};
+}
+
 int32_t check_stream_geometry(int32_t n_str, int32_t sink, int32_t recent, int32_t ring_blocks,
                               int32_t bs, int32_t mbph, int32_t q_len) {
   if (sink < 0) return DUO_ERR_INVALID_ARG;
   if (n_str == 0) return DUO_OK;
-  if (recent < 1 || ring_blocks < 1) return DUO_ERR_INVALID_ARG;
+  if (recent == 0 || ring_blocks < 1) return DUO_ERR_INVALID_ARG;
   if ((int64_t)sink_blocks(sink, bs) + ring_blocks > mbph) return DUO_ERR_CAPACITY;
-  if ((int64_t)ring_blocks * bs < (int64_t)recent + q_len - 1) return DUO_ERR_CAPACITY;
+  // the oldest key of the first row's window and the newest row's key share the ring
+  if ((int64_t)ring_blocks * bs < window_of(n_str, recent, bs).span + q_len - 1)
+    return DUO_ERR_CAPACITY;
   return DUO_OK;
 }
 
@@ -338,7 +360,7 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   size_t need;
   // With streaming heads and the library's split: streaming items first, and the retrieval rows'
   // last splits shortened by the keys a streaming item's time would stream. A streaming item is
-  // bound by latency, so its time is about that of (sink + recent + 256) keys of a 16-bit cache
+  // bound by latency, so its time is about that of (sink + window + 256) keys of a 16-bit cache
   // whatever the cache: in keys of this cache, that many times 16-bit bytes per key over this
   // cache's (2 D + 8 per key for int8 with its two scales, D for 4 bits, 8 D for fp32).
   const bool str_first = n_str > 0 && split_tokens == 0;
@@ -347,7 +369,8 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
     const int64_t bpk16 = 4LL * head_dim;
     const int64_t bpk = quant == 8 ? 2LL * head_dim + 8 : quant == 4 ? head_dim
                                                         : 2LL * head_dim * elem_bytes(dtype);
-    stretch = (int32_t)std::min<int64_t>(((int64_t)sink_size + recent_size + 256) * bpk16 / bpk,
+    const int64_t span = window_of(n_str, recent_size, block_size).span;
+    stretch = (int32_t)std::min<int64_t>(((int64_t)sink_size + span + 256) * bpk16 / bpk,
                                          INT32_MAX / 2);
   }
   st = decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_head, block_size,
@@ -395,7 +418,8 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.sink = sink_size;
-  p.recent = recent_size;
+  p.win_mask = window_of(n_str, recent_size, block_size).mask;
+  p.win_back = window_of(n_str, recent_size, block_size).back;
   p.sink_blocks = sink_blocks(sink_size, block_size);
   p.ring_slots = n_str > 0 ? ring_blocks * block_size : block_size;
   p.split_tokens = S;
@@ -578,7 +602,8 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.sink = sink_size;
-  p.recent = recent_size;
+  p.win_mask = window_of(n_str, recent_size, block_size).mask;
+  p.win_back = window_of(n_str, recent_size, block_size).back;
   p.sink_blocks = sink_blocks(sink_size, block_size);
   p.ring_slots = n_str > 0 ? ring_blocks * block_size : block_size;
   p.n_qtiles = n_qt;
@@ -626,7 +651,8 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
     d.group = num_q_heads / num_kv_heads;
     d.gchunks = gch;
     d.sink = sink_size;
-    d.recent = recent_size;
+    d.win_mask = window_of(n_str, recent_size, block_size).mask;
+    d.win_back = window_of(n_str, recent_size, block_size).back;
     d.sink_blocks = p.sink_blocks;
     d.ring_slots = p.ring_slots;
     d.split_tokens = dS;

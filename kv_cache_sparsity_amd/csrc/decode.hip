@@ -4,8 +4,11 @@
 // What is computed (DuoAttention README, abstract; transformers PR "[WIP] Dynamic length in static
 // cache", description): the query of sequence b at position p = L - 1 attends, per kv head h, to
 //   retrieval head: positions [0, L)
-//   streaming head: positions [0, min(sink, L)) and [max(sink, L - recent), L)
-// with scores softmax_scale * (q . k) formed in fp32 (vLLM DualChunkAttention PR, review thread on
+//   streaming head: positions [0, min(sink, L)) and [max(sink, W(L - 1)), L)
+// where the recent window of a query at p starts at W(p) = (p & win_mask) - win_back: p - recent + 1
+// for a window of the recent newest positions, or the first position of the -recent newest blocks
+// for the block-granular window (vLLM issue "Could you support Attention Sink?", ChuanhongLi's
+// comment: keep the first block, drop middle blocks, keep the recent blocks), with scores softmax_scale * (q . k) formed in fp32 (vLLM DualChunkAttention PR, review thread on
 // the fp32 scale). Partial results over disjoint key ranges are merged through their log-sum-exp
 // (same review thread).
 //

@@ -173,7 +173,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     rl.n = end > t0 ? (end - t0 + 15) / 16 : 0;
   } else {
     rl.n_sink = (min(p.sink, L) + 15) / 16;
-    rl.ring_lo = max(p.sink, L - p.recent);
+    rl.ring_lo = max(p.sink, ((L - 1) & p.win_mask) - p.win_back);
     int32_t n_ring = 0;
     if (L > p.sink) {
       rl.k_lo = (rl.ring_lo - p.sink) / 16;

@@ -48,7 +48,8 @@ struct DecodeParams {
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t gchunks;   // ceil(group / 16): chunks of q heads taken one per item
-  int32_t sink, recent, sink_blocks, ring_slots;
+  // a streaming head's window for the query at position p: keys from (p & win_mask) - win_back
+  int32_t sink, win_mask, win_back, sink_blocks, ring_slots;
   int32_t split_tokens, n_split, n_ret, n_str;
   // 1: streaming items first in the grid and the retrieval rows' last splits last (the host then
   // shortens the last splits); 0: retrieval items (split fastest), then streaming items
@@ -87,7 +88,8 @@ struct PrefillParams {
   int32_t skip_single_rows;
   int32_t num_blocks, log2_bs, max_blocks_per_head;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group;
-  int32_t sink, recent, sink_blocks, ring_slots;
+  // a streaming head's window for the query at position p: keys from (p & win_mask) - win_back
+  int32_t sink, win_mask, win_back, sink_blocks, ring_slots;
   int32_t n_qtiles, n_ret, n_str, n_split;
   float scale_log2;
   uint8_t ret_heads[kMaxKvHeads];

@@ -3,14 +3,15 @@
 // What is computed (DuoAttention README, abstract and efficiency section; transformers PR
 // "[WIP] Dynamic length in static cache"): query row i of sequence b sits at position
 // p = L - q_len + i and attends causally (keys j <= p); a streaming head further keeps only the sink
-// positions j < sink and its recent window p - j < recent. Scores are softmax_scale * (q . k) in
-// fp32 (vLLM DualChunkAttention PR, review thread).
+// positions j < sink and its recent window j >= W(p) = (p & win_mask) - win_back (p - recent + 1, or
+// the first position of the newest blocks for the block-granular window; see the decode kernel).
+// Scores are softmax_scale * (q . k) in fp32 (vLLM DualChunkAttention PR, review thread).
 //
 // Work decomposition. A work item is (b, q head, tile of R query rows); R = 32 x waves (256 with
 // eight waves, 128 with four). The item walks only the 16-key runs that can be visible to its rows:
 //   retrieval head: runs 0 .. p_hi / 16;
-//   streaming head: the sink runs, then the ring runs covering [p_lo - recent + 1, p_hi].
-// So a streaming item costs about (sink + recent + R) keys whatever the context length. A retrieval
+//   streaming head: the sink runs, then the ring runs covering [W(p_lo), p_hi].
+// So a streaming item costs about (sink + window + R) keys whatever the context length. A retrieval
 // item's key tiles are split in n_split contiguous ranges, one workgroup each; the workgroups write
 // partial softmax states (m, l, O) to the workspace and the last to arrive merges them through
 // their log-sum-exp (vLLM DualChunkAttention PR, review thread) and writes the output. Retrieval
@@ -399,7 +400,7 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(
       rl.n_sink = (min(p.sink, p_hi + 1) + 15) / 16;
       int32_t n_ring = 0;
       if (p_hi >= p.sink) {
-        rl.k_lo = (max(p.sink, p_lo - p.recent + 1) - p.sink) / 16;
+        rl.k_lo = (max(p.sink, (p_lo & p.win_mask) - p.win_back) - p.sink) / 16;
         n_ring = (p_hi - p.sink) / 16 - rl.k_lo + 1;
       }
       rl.n = rl.n_sink + n_ring;
@@ -572,12 +573,13 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(
       // accumulator 4*i + j of block b2 is key 8*half + 4*(i&1) + j of run 2*b2 + (i>>1)
       if (mask) {
         // The keys of run k that this lane's row may see form one interval [lo, hi): present
-        // keys [r.lo, r.hi), causal t <= my_p and, in a ring run, the window t > my_p - recent.
+        // keys [r.lo, r.hi), causal t <= my_p and, in a ring run, the window that starts at
+        // (my_p & win_mask) - win_back.
         // Key t is kept iff t - lo, taken unsigned, is below hi - lo: one compare per score.
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const Run& r = runs[k];
-          const int32_t lo = r.windowed ? max(r.lo, my_p - p.recent + 1) : r.lo;
+          const int32_t lo = r.windowed ? max(r.lo, (my_p & p.win_mask) - p.win_back) : r.lo;
           const int32_t hi = min(r.hi, my_p + 1);
           const uint32_t width = (uint32_t)max(hi - lo, 0);
           const int32_t d0 = r.t0 + 8 * half - lo;   // the lane's first key of the run, from lo
@@ -661,10 +663,12 @@ __global__ void __launch_bounds__((TileGeo<T, D>::kThreads), 1) prefill_kernel(
           const Run& r = runs[i];
           const int32_t a = max(r.t0, r.lo), e = min(r.t0 + 16, r.hi);   // present keys [a, e)
           // some key visible to some row: the closest pair is key min(e-1, hi) seen from row
-          // max(lo, that key)
-          const bool vis = a < e && a <= hi && (!r.windowed || lo - min(e - 1, hi) < p.recent);
+          // max(lo, that key) (a window starts at or before its query and never moves back as the
+          // query moves on, so row lo has the lowest start)
+          const bool vis = a < e && a <= hi &&
+                           (!r.windowed || min(e - 1, hi) >= (lo & p.win_mask) - p.win_back);
           const bool full = r.lo <= r.t0 && r.t0 + 16 <= r.hi && r.t0 + 15 <= lo &&
-                            (!r.windowed || hi - r.t0 < p.recent);
+                            (!r.windowed || r.t0 >= (hi & p.win_mask) - p.win_back);
           all_full = all_full && full;
           any_vis = any_vis || vis;
         }

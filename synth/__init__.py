@@ -121,8 +121,10 @@ class Workload:
 
 
 def _ring_blocks_for(recent: int, q_len: int, block_size: int) -> int:
-    # the ring must still hold the oldest key the first query of a chunk sees
-    return -(-(recent + q_len - 1) // block_size)
+    # the ring must still hold the oldest key the first query of a chunk sees; a negative recent
+    # is a window of -recent whole blocks
+    span = recent if recent > 0 else -recent * block_size
+    return -(-(span + q_len - 1) // block_size)
 
 
 def _max_blocks(capacity_tokens: int, sink: int, ring_blocks: int, block_size: int) -> int:

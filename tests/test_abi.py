@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 11
+    assert duo.abi_version() == 12
     with open(os.path.join(ROOT, "include", "duo_attn.h")) as fh:
         assert f"#define DUO_ATTN_ABI_VERSION {duo.abi_version()}" in fh.read()
     assert duo.status_string(0) == "ok"
@@ -102,6 +102,8 @@ def decode(**kw):
     (dict(hq=6, hkv=4), INVALID), (dict(d=80), UNSUPPORTED),
     (dict(bs=8), UNSUPPORTED), (dict(bs=24), UNSUPPORTED), (dict(dtype=3), UNSUPPORTED),
     (dict(recent=0), INVALID), (dict(rb=0), INVALID), (dict(recent=33), CAPACITY),
+    (dict(recent=-3), CAPACITY),            # three 16-position blocks > a ring of 32 slots
+    (dict(recent=-2**31), CAPACITY),
     (dict(mbph=2, rb=2), CAPACITY), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
     (dict(split=100), INVALID), (dict(split=-128), INVALID),
     (dict(mask=ctypes.cast(MASK_BAD, ctypes.c_void_p)), INVALID), (dict(batch=70000), UNSUPPORTED),
@@ -258,6 +260,8 @@ def prefill(**kw):
     (dict(q=None), INVALID), (dict(q_len=0), INVALID), (dict(lens=None), INVALID),
     (dict(d=256, dtype=0), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(bs=4), UNSUPPORTED),
     (dict(q_len=50), CAPACITY),            # ring of 64 slots < recent 16 + q_len 50 - 1
+    (dict(recent=-3), CAPACITY),           # ring of 64 slots < 3 blocks of 16 + q_len 32 - 1
+    (dict(recent=0), INVALID),
     (dict(rb=20), CAPACITY),               # 1 sink page + 20 ring pages > 20 table columns
 ])
 def test_prefill_rejects(kw, status):
