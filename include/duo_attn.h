@@ -47,7 +47,7 @@
  *     recent_size > 0: positions p - recent_size < j <= p (the recent_size newest, p included);
  *     recent_size < 0: block-granular, the -recent_size newest blocks of block_size positions up to
  *                      p's own, that block counting as one however few of its positions exist:
- *                      (floor(p / block_size) + recent_size) * block_size < j <= p. Blocks are
+ *                      (floor(p / block_size) + recent_size + 1) * block_size <= j <= p. Blocks are
  *                      aligned at position 0, so the window holds between
  *                      (-recent_size - 1) * block_size + 1 and -recent_size * block_size positions.
  *     recent_size = 0 is rejected (INVALID_ARG) when a streaming head is present. The window's span
