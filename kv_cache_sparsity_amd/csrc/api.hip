@@ -418,8 +418,9 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.sink = sink_size;
-  p.win_mask = window_of(n_str, recent_size, block_size).mask;
-  p.win_back = window_of(n_str, recent_size, block_size).back;
+  const Window win = window_of(n_str, recent_size, block_size);
+  p.win_mask = win.mask;
+  p.win_back = win.back;
   p.sink_blocks = sink_blocks(sink_size, block_size);
   p.ring_slots = n_str > 0 ? ring_blocks * block_size : block_size;
   p.split_tokens = S;
@@ -602,8 +603,9 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.sink = sink_size;
-  p.win_mask = window_of(n_str, recent_size, block_size).mask;
-  p.win_back = window_of(n_str, recent_size, block_size).back;
+  const Window win = window_of(n_str, recent_size, block_size);
+  p.win_mask = win.mask;
+  p.win_back = win.back;
   p.sink_blocks = sink_blocks(sink_size, block_size);
   p.ring_slots = n_str > 0 ? ring_blocks * block_size : block_size;
   p.n_qtiles = n_qt;
@@ -651,8 +653,8 @@ static int32_t prefill_impl(const void* q, const void* k_pool, const void* v_poo
     d.group = num_q_heads / num_kv_heads;
     d.gchunks = gch;
     d.sink = sink_size;
-    d.win_mask = window_of(n_str, recent_size, block_size).mask;
-    d.win_back = window_of(n_str, recent_size, block_size).back;
+    d.win_mask = win.mask;
+    d.win_back = win.back;
     d.sink_blocks = p.sink_blocks;
     d.ring_slots = p.ring_slots;
     d.split_tokens = dS;
