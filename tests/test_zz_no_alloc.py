@@ -1,7 +1,9 @@
 """duo_attn_decode_noalloc: the decode without a workspace argument (the library's static per-GPU
 scratch serves instead), through the C ABI, against duo_attn_decode with a caller-owned workspace
 on the same inputs, and against the oracle. Two calls in a row, the second with a smaller input,
-so the second finds the scratch as the first left it."""
+so the second finds the scratch as the first left it. Last, the call inside a captured HIP graph
+(the callers it is for cannot allocate while capturing), replayed with eager work and a changed
+query between replays, each replay checked against an eager call and the oracle."""
 import os
 
 import numpy as np
@@ -84,3 +86,49 @@ def test_noalloc_decode_repeats_with_explicit_splits():
                                     cache.mask, w.sink, w.recent, w.ring_blocks, w.scale, out,
                                     split_tokens=split)
         check_close(to_host_f64(out, w.dtype), want, w.dtype, f"noalloc split {split}")
+
+
+def test_noalloc_decode_replays_from_a_captured_graph():
+    case = CASES[0]
+    say(f"graph capture of the no-alloc decode {case['name']}")
+    w, cache, K, V, lens = _setup(case, 81)
+    queries = [q_decode(w, s) for s in range(3)]
+    q = to_dev(queries[0], w.dtype)
+    out = torch.empty_like(q)
+
+    def call(stream=None):
+        duo.duo_attn_decode_noalloc(q, cache.k_pool, cache.v_pool, cache.table, cache.lens,
+                                    cache.mask, w.sink, w.recent, w.ring_blocks, w.scale, out,
+                                    stream=stream)
+
+    call()                      # first call on this device: the scratch address is looked up here
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(stream=side)       # a warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call(stream=side)
+    torch.cuda.synchronize()
+
+    for rep, qi in enumerate([0, 0, 1, 2, 1]):
+        q.copy_(to_dev(queries[qi], w.dtype))
+        # eager reference on the same inputs, then unrelated eager work, then the replay
+        call()
+        torch.cuda.synchronize()
+        eager = to_host_f64(out, w.dtype)
+        out.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host_f64(out, w.dtype)
+        assert np.isfinite(got).all(), f"replay {rep}: non-finite output"
+        err = float(np.abs(got - eager).max())
+        say(f"  replay {rep} (query {qi}): max |replay - eager| = {err:.3e}; scratch {float(scratch):.1f}")
+        assert err <= 1e-2
+        check_close(got, oracle_decode(w, queries[qi], K, V, lens, cache.mask), w.dtype,
+                    f"replay {rep}")
