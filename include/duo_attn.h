@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 12
+#define DUO_ATTN_ABI_VERSION 13
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -165,6 +165,44 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                         const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                         int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
                         size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/*
+ * duo_attn_append_decode -- kv_append_circular of one token per sequence and duo_attn_decode of
+ * that token's queries, in one launch.
+ *
+ * Source: transformers PR "[WIP] Dynamic length in static cache", description (the cache is
+ * updated at the new position, then the query attends up to it) and DuoAttention README (decode
+ * over retrieval and streaming heads); the result is that of the two calls in sequence.
+ *
+ *   q                   device [batch][num_q_heads][head_dim] of dtype (the new tokens' queries).
+ *   k_new, v_new        device [batch][1][num_kv_heads][head_dim] of dtype: token b goes to position
+ *                       seq_lens_before[b] of every kv head of sequence b, by the slot rule of
+ *                       kv_append_circular (retrieval positions past max_blocks_per_head*block_size
+ *                       are not written); bit-exact copies.
+ *   k_pool, v_pool      device, layout above; the token's slots are written, the rest read.
+ *   seq_lens_before     device int32 [batch]: tokens in the cache before the call. The query of
+ *                       sequence b sits at position seq_lens_before[b] and sees the keys of
+ *                       duo_attn_decode with seq_lens[b] = seq_lens_before[b] + 1.
+ *   seq_lens_after      device int32 [batch] or NULL: receives seq_lens_before[b] + 1. Must not
+ *                       alias seq_lens_before.
+ *   workspace           as for duo_attn_decode (duo_attn_decode_workspace_size gives its size).
+ * Other arguments, outputs, the window and the ring requirements: as for duo_attn_decode.
+ * Each work item whose keys hold the new position writes the token before reading any key; no
+ * other item reads that slot (a retrieval split reads only its own keys, and the ring slot the
+ * token takes held a position older than any window), so the launch needs no ordering between
+ * items beyond that.
+ * Errors: as for duo_attn_decode; also INVALID_ARG (k_new or v_new null or misaligned,
+ *         seq_lens_after misaligned or equal to seq_lens_before).
+ */
+int32_t duo_attn_append_decode(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                               void* v_pool, const int32_t* block_table, int32_t num_blocks,
+                               int32_t block_size, int32_t max_blocks_per_head,
+                               const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                               int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                               float softmax_scale, void* out, void* workspace,
+                               size_t workspace_bytes, int32_t split_tokens, void* stream);
 
 /*
  * duo_attn_decode_noalloc -- duo_attn_decode for callers that cannot allocate device memory (code

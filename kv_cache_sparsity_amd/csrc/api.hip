@@ -327,9 +327,18 @@ struct DcaArgs {
   int32_t chunk_len;
 };
 
+// The fused append of duo_attn_append_decode: one token per (sequence, kv head) and the lengths
+// after it.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  int32_t* seq_lens_after;
+};
+
 // The decode behind the three caches (quant 0: 16-bit or fp32, 8: int8 codes + per-slot scales,
 // 4: 4-bit codes + per-(kv head, channel) scales); dca != nullptr: Dual Chunk Attention (16-bit
-// cache, full heads).
+// cache, full heads); app != nullptr: the token at position seq_lens[b] is appended first (quant 0,
+// no dca).
 static int32_t decode_impl(int quant, const void* q, const void* k_pool, const void* v_pool,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
                            int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
@@ -338,7 +347,8 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
                            const uint8_t* head_is_retrieval, int32_t sink_size, int32_t recent_size,
                            int32_t ring_blocks, float softmax_scale, void* out, void* workspace,
                            size_t workspace_bytes, int32_t split_tokens, void* stream,
-                           const DcaArgs* dca = nullptr, bool noalloc = false) {
+                           const DcaArgs* dca = nullptr, bool noalloc = false,
+                           const AppendArgs* app = nullptr) {
   const CallEvents events;
   int32_t st = check_cache(k_pool, v_pool, block_table, num_blocks, block_size, max_blocks_per_head,
                            seq_lens, batch, num_q_heads, num_kv_heads, head_dim, dtype,
@@ -349,6 +359,15 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   if (quant == 4 && dtype == DUO_F32) return DUO_ERR_UNSUPPORTED;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
+  if (app != nullptr) {
+    if (quant != 0 || dca != nullptr) return DUO_ERR_UNSUPPORTED;
+    if (!app->k_new || !app->v_new || !aligned(app->k_new, 16) || !aligned(app->v_new, 16))
+      return DUO_ERR_INVALID_ARG;
+    // the lengths are read by every work item while one item per sequence writes the new ones
+    if (app->seq_lens_after &&
+        (!aligned(app->seq_lens_after, 4) || app->seq_lens_after == seq_lens))
+      return DUO_ERR_INVALID_ARG;
+  }
   uint8_t ret[kMaxKvHeads], str[kMaxKvHeads];
   int32_t n_ret, n_str;
   if (!split_heads(head_is_retrieval, num_kv_heads, ret, &n_ret, str, &n_str))
@@ -402,6 +421,9 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   p.v_pool = v_pool;
   p.table = block_table;
   p.seq_lens = seq_lens;
+  p.k_new = app ? app->k_new : nullptr;
+  p.v_new = app ? app->v_new : nullptr;
+  p.seq_lens_after = app ? app->seq_lens_after : nullptr;
   p.out = out;
   p.counter = static_cast<int32_t*>(workspace);
   p.gcounter = p.counter + (size_t)batch * num_kv_heads * gch;
@@ -460,6 +482,23 @@ int32_t duo_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                      softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+int32_t duo_attn_append_decode(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                               void* v_pool, const int32_t* block_table, int32_t num_blocks,
+                               int32_t block_size, int32_t max_blocks_per_head,
+                               const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype, const uint8_t* head_is_retrieval,
+                               int32_t sink_size, int32_t recent_size, int32_t ring_blocks,
+                               float softmax_scale, void* out, void* workspace,
+                               size_t workspace_bytes, int32_t split_tokens, void* stream) {
+  const AppendArgs app{k_new, v_new, seq_lens_after};
+  return decode_impl(0, q, k_pool, v_pool, nullptr, nullptr, block_table, num_blocks, block_size,
+                     max_blocks_per_head, seq_lens_before, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                     softmax_scale, out, workspace, workspace_bytes, split_tokens, stream, nullptr,
+                     false, &app);
 }
 
 int32_t duo_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,

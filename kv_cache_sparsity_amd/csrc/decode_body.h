@@ -55,7 +55,9 @@ struct DecodeLds {
 
 // One decode work item `blk` of the grid the host planned (see decode.hip), with `lds` pointing at
 // DecodeLds<kWavesT, D>::kBytes of LDS. kWavesT waves per workgroup.
-template <typename T, int D, bool Q8, bool DCA = false, bool Q4 = false, int kWavesT = decode_waves<D>()>
+// APPEND: the fused append of decode_append_kernel (see DecodeParams::k_new).
+template <typename T, int D, bool Q8, bool DCA = false, bool Q4 = false, int kWavesT = decode_waves<D>(),
+          bool APPEND = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char* lds) {
   constexpr int kDecodeWaves = kWavesT;
   constexpr int kThreads = kDecodeWaves * kWave;
@@ -159,6 +161,38 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     }
   }
   int32_t L = max(p.seq_lens[b], 0);
+  if constexpr (APPEND) {
+    // The call's token of (b, h) goes to position t = L (the length before it), and every item of
+    // the sequence attends over L + 1 keys. The item whose keys hold position t writes the token
+    // into its slot before reading any key, as kv_append_circular would (a retrieval head: slot t,
+    // unless t is past the row's capacity; a streaming head: its sink or ring slot); the q-head
+    // chunks of a kv head each write the same bits. No other item reads that slot: a retrieval
+    // split reads only its own keys, and the ring slot the token takes held a position older than
+    // any window (the ring holds at least the window's span). One item per sequence stores the
+    // new length.
+    const int32_t t = L;
+    L = t + 1;
+    const bool writer_of_len = gc == 0 && split == 0 &&
+                               (p.n_ret > 0 ? ret && h == p.ret_heads[0] : h == p.str_heads[0]);
+    if (p.seq_lens_after != nullptr && writer_of_len && threadIdx.x == 0) p.seq_lens_after[b] = L;
+    const int32_t cap = p.max_blocks_per_head << p.log2_bs;
+    if (ret ? (t < cap && t / p.split_tokens == split) : true) {
+      const int32_t slot = (ret || t < p.sink) ? t : (p.sink_blocks << p.log2_bs) + (t - p.sink) % p.ring_slots;
+      const int64_t page = geo.page_of(slot);
+      const int32_t row = geo.row0(slot);
+      const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D;
+      const T* kn = static_cast<const T*>(p.k_new) + src;
+      const T* vn = static_cast<const T*>(p.v_new) + src;
+      T* kdst = static_cast<T*>(const_cast<void*>(p.k_pool)) + ((page << p.log2_bs) + row) * D;
+      T* vdst = static_cast<T*>(const_cast<void*>(p.v_pool)) + ((page * D) << p.log2_bs) + row;
+      for (int d = (int)threadIdx.x; d < D; d += kThreads) {
+        kdst[d] = kn[d];
+        vdst[(int64_t)d << p.log2_bs] = vn[d];
+      }
+      wait_stores_complete();   // the token is in place before any key of the item is read
+      __syncthreads();
+    }
+  }
   if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
 
   // ---- the item's runs ----------------------------------------------------------------------

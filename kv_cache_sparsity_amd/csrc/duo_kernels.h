@@ -68,6 +68,13 @@ struct DecodeParams {
   // has exactly one row, which then takes the place of row b. null: row b.
   const int32_t* q_start;
   int32_t total_q;
+  // fused append (decode_append_kernel only): the token of each (sequence, kv head) that sits at
+  // position seq_lens[b], laid out [batch][num_kv_heads][head_dim] (one step of kv_append_circular's
+  // input); the items then attend over seq_lens[b] + 1 keys, and seq_lens_after[b] (may be null)
+  // receives that length
+  const void* k_new;
+  const void* v_new;
+  int32_t* seq_lens_after;
 };
 
 struct PrefillParams {

@@ -138,5 +138,6 @@ def oracle_decode(w, q_bits, K, V, lens, mask, rows=None):
     """Oracle for decode queries [B][Hq][D] over logical storage K, V."""
     q4 = q_bits[:, None]
     o = oracle.attend(q4, K, V, lens, mask, sink=w.sink, recent=w.recent, scale=w.scale,
-                      dtype=w.dtype, rows=None if rows is None else [(b, 0, hq) for b, hq in rows])
+                      dtype=w.dtype, rows=None if rows is None else [(b, 0, hq) for b, hq in rows],
+                      block_size=w.block_size)
     return o[:, 0]

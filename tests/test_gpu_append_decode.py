@@ -1,0 +1,150 @@
+"""duo_attn_append_decode, through the C ABI: the fused append of one token per sequence and the
+decode of its queries, against the two calls it stands for (kv_append_circular, then
+duo_attn_decode over seq_lens + 1) on twin caches, and against the oracle.
+
+Bars: pools bit-exact against the two calls (the token lands in the same slot with the same bits,
+and nothing else changes); lengths after the call exact; outputs within the usual bound of the
+fp64 oracle (1e-4 fp32, 2e-2 bf16/fp16) and of the two-call output. Pools start filled with NaN.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_sparsity_amd as duo
+import synth
+from tests.gpu_harness import (Cache, check_close, logical_kv, oracle_decode, q_decode, say, to_dev,
+                               to_host_bits, to_host_f64, TOL)
+from tests.test_gpu_parity import _append_per_sequence
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(duo.LIB_PATH):
+        pytest.fail("libduoattn.so is not built; the GPU tests need the HIP library")
+
+
+CASES = [
+    # ring of 48 slots behind 4 sinks; the first token of a sequence (length 0) and ring wraps
+    dict(name="bf16-d128-g4-mixed", dtype=synth.BF16, head_dim=128, group=4, kv=4, ret=(0, 2),
+         block_size=16, sink=4, recent=40, ring_blocks=3, lens=[0, 15, 16, 47, 48, 300, 1000]),
+    dict(name="f16-d256-g8-all-streaming", dtype=synth.F16, head_dim=256, group=8, kv=1, ret=(),
+         block_size=16, sink=16, recent=100, ring_blocks=8, lens=[99, 700]),
+    dict(name="f32-d64-g2-bs32", dtype=synth.F32, head_dim=64, group=2, kv=2, ret=(1,),
+         block_size=32, sink=0, recent=33, ring_blocks=2, lens=[31, 32, 64, 65]),
+    # a group of 20 q heads: two chunks of one kv head each write the token
+    dict(name="bf16-d128-g20-chunks", dtype=synth.BF16, head_dim=128, group=20, kv=2, ret=(1,),
+         block_size=16, sink=5, recent=64, ring_blocks=5, lens=[500, 63]),
+    # block-granular window of two 16-position blocks
+    dict(name="bf16-d128-block-window", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(0,),
+         block_size=16, sink=16, recent=-2, ring_blocks=2, lens=[16, 31, 32, 47, 100]),
+]
+STEPS = 3
+
+
+def _setup(case, seed):
+    lens = np.asarray(case["lens"])
+    Lmax = int(lens.max()) + STEPS
+    w = synth.small(case["name"], batch=len(lens), q_heads=case["kv"] * case["group"],
+                    kv_heads=case["kv"], head_dim=case["head_dim"], dtype=case["dtype"],
+                    block_size=case["block_size"], sink=case["sink"], recent=case["recent"],
+                    retrieval=case["ret"], context=Lmax, ring_blocks=case["ring_blocks"],
+                    seed=seed)
+    K = logical_kv(w, Lmax, synth.S_K)
+    V = logical_kv(w, Lmax, synth.S_V)
+    fused, split = Cache(w, fill="nan"), Cache(w, fill="nan")
+    _append_per_sequence(fused, K, V, lens)
+    _append_per_sequence(split, K, V, lens)
+    return w, K, V, lens, fused, split
+
+
+def _same_bits(a, b, dtype):
+    """Pools equal bit for bit (fp32 pools come back as floats: compare their bit patterns, so
+    that the NaN of unwritten slots matches itself)."""
+    x, y = to_host_bits(a, dtype), to_host_bits(b, dtype)
+    if dtype == synth.F32:
+        x, y = x.view(np.uint32), y.view(np.uint32)
+    return np.array_equal(x, y)
+
+
+def _token(w, X, lens):
+    """[batch][1][kv heads][D] storage bits of position lens[b] of each sequence."""
+    t = np.stack([X[b, :, int(lens[b])] for b in range(w.batch)])   # [B][Hkv][D]
+    return to_dev(np.ascontiguousarray(t[:, None]), w.dtype)
+
+
+@pytest.mark.parametrize("split_tokens", [0, 128])
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_append_decode_equals_append_then_decode(case, split_tokens):
+    say(f"append+decode {case['name']} split {split_tokens}")
+    w, K, V, lens, fused, split = _setup(case, 71)
+    for step in range(STEPS):
+        q = to_dev(q_decode(w, step), w.dtype)
+        k_new, v_new = _token(w, K, lens), _token(w, V, lens)
+        before = torch.from_numpy(lens.astype(np.int32)).cuda()
+        # the fused call
+        after_f = torch.full_like(before, -1)
+        out_f = torch.empty_like(q)
+        ws_f = duo.decode_workspace(q, fused.table, w.block_size, split_tokens)
+        duo.duo_attn_append_decode(q, k_new, v_new, fused.k_pool, fused.v_pool, fused.table, before,
+                                   after_f, fused.mask, w.sink, w.recent, w.ring_blocks, w.scale,
+                                   out_f, ws_f, split_tokens)
+        # the two calls
+        after_s = torch.full_like(before, -1)
+        out_s = torch.empty_like(q)
+        duo.kv_append_circular(split.k_pool, split.v_pool, split.table, k_new, v_new, before,
+                               after_s, split.mask, w.sink, w.recent, w.ring_blocks)
+        ws_s = duo.decode_workspace(q, split.table, w.block_size, split_tokens)
+        duo.duo_attn_decode(q, split.k_pool, split.v_pool, split.table, after_s, split.mask,
+                            w.sink, w.recent, w.ring_blocks, w.scale, out_s, ws_s, split_tokens)
+        torch.cuda.synchronize()
+        lens = lens + 1
+        assert (after_f.cpu().numpy() == lens).all(), after_f
+        assert _same_bits(fused.k_pool, split.k_pool, w.dtype)
+        assert _same_bits(fused.v_pool, split.v_pool, w.dtype)
+        got = to_host_f64(out_f, w.dtype)
+        want = oracle_decode(w, to_host_bits(q, w.dtype), K, V, lens, fused.mask)
+        check_close(got, want, w.dtype, f"{case['name']} step {step}")
+        assert float(np.abs(got - to_host_f64(out_s, w.dtype)).max()) <= TOL[w.dtype]
+
+
+def test_append_decode_at_the_retrieval_capacity():
+    """A retrieval row already full: the token is not written (as kv_append_circular), the decode
+    attends over the row's capacity, and the new length still counts the token."""
+    case = dict(name="bf16-capacity", dtype=synth.BF16, head_dim=128, group=4, kv=2, ret=(0,),
+                block_size=16, sink=4, recent=40, ring_blocks=3, lens=[64, 63])
+    say("append+decode at capacity")
+    lens = np.asarray(case["lens"])
+    w = synth.small(case["name"], batch=2, q_heads=8, kv_heads=2, head_dim=128, dtype=synth.BF16,
+                    block_size=16, sink=4, recent=40, retrieval=(0,), context=64, ring_blocks=3,
+                    capacity=64, seed=72)
+    K = logical_kv(w, 65, synth.S_K)
+    V = logical_kv(w, 65, synth.S_V)
+    fused, split = Cache(w, fill="nan"), Cache(w, fill="nan")
+    _append_per_sequence(fused, K, V, lens)
+    _append_per_sequence(split, K, V, lens)
+    q = to_dev(q_decode(w, 0), w.dtype)
+    k_new, v_new = _token(w, K, lens), _token(w, V, lens)
+    before = torch.from_numpy(lens.astype(np.int32)).cuda()
+    after_f, after_s = torch.full_like(before, -1), torch.full_like(before, -1)
+    out_f, out_s = torch.empty_like(q), torch.empty_like(q)
+    duo.duo_attn_append_decode(q, k_new, v_new, fused.k_pool, fused.v_pool, fused.table, before,
+                               after_f, fused.mask, w.sink, w.recent, w.ring_blocks, w.scale,
+                               out_f, duo.decode_workspace(q, fused.table, w.block_size))
+    duo.kv_append_circular(split.k_pool, split.v_pool, split.table, k_new, v_new, before, after_s,
+                           split.mask, w.sink, w.recent, w.ring_blocks)
+    duo.duo_attn_decode(q, split.k_pool, split.v_pool, split.table, after_s, split.mask, w.sink,
+                        w.recent, w.ring_blocks, w.scale, out_s,
+                        duo.decode_workspace(q, split.table, w.block_size))
+    torch.cuda.synchronize()
+    assert (after_f.cpu().numpy() == lens + 1).all()
+    assert _same_bits(fused.k_pool, split.k_pool, w.dtype)
+    assert _same_bits(fused.v_pool, split.v_pool, w.dtype)
+    got, ref = to_host_f64(out_f, w.dtype), to_host_f64(out_s, w.dtype)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - ref).max()) <= TOL[w.dtype]
