@@ -266,6 +266,24 @@ def decode_leg(args, torch, duo):
     kern_s = float(np.mean(kern_all))
     nbytes = decode_bytes(w, np.full(w.batch, L))
     traffic = measured_traffic("decode")
+
+    # The same step as one launch (duo_attn_append_decode: the append fused into the decode),
+    # timed the same way, back to back.
+    lens_fused = torch.empty_like(lens_before)
+
+    def fused_step(i):
+        kp, vp = layers[i % len(layers)]
+        duo.duo_attn_append_decode(q, k_tok, v_tok, kp, vp, table, lens_before, lens_fused, mask,
+                                   w.sink, w.recent, w.ring_blocks, w.scale, out, ws)
+
+    for i in range(args.warmup):
+        fused_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused_step(args.warmup + i)
+    torch.cuda.synchronize()
+    fused_s = (time.perf_counter() - t0) / args.steps
     res = {
         "w": w, "K": K, "V": V, "q_bits": q_bits, "out": out,
         "value": nbytes / step_s / 1e9, "ms_per_step": step_s * 1e3, "bytes": nbytes,
@@ -277,9 +295,13 @@ def decode_leg(args, torch, duo):
                      **spread_us(kern_all),
                      "cold": f"{FLUSH_BYTES >> 20} MiB read before each sampled launch",
                      "algorithmic_bytes_per_launch": nbytes},
+        "fused_step": {"call": "duo_attn_append_decode (1 token/seq, one launch)",
+                       "us_per_step": round(fused_s * 1e6, 2),
+                       "GB/s": round(nbytes / fused_s / 1e9, 1)},
     }
     log(f"[decode] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
-        f"{res['value']:.0f} GB/s per step, {nbytes / kern_s / 1e9:.0f} GB/s kernel")
+        f"{res['value']:.0f} GB/s per step, {nbytes / kern_s / 1e9:.0f} GB/s kernel; "
+        f"fused step {fused_s * 1e6:.1f} us")
     return res
 
 
@@ -910,6 +932,7 @@ def main():
                    "block_size": w.block_size, "layers_rotated": args.layers,
                    "step": "kv_append_circular(1 token/seq) + duo_attn_decode",
                    "algorithmic_bytes_per_step": dec["bytes"] if dec else None},
+        "fused_step": dec["fused_step"] if dec else None,
         "roofline": dec["roofline"] if dec else None,
         "cpu_baseline": cpu,
         "prefill": pre,
