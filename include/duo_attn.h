@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 13
+#define DUO_ATTN_ABI_VERSION 14
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -372,6 +372,26 @@ int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* 
                              int32_t recent_size, int32_t ring_blocks, float softmax_scale,
                              void* out, void* workspace, size_t workspace_bytes,
                              int32_t split_tokens, void* stream);
+
+/*
+ * duo_attn_append_decode_int8 -- kv_append_circular_int8 of one token per sequence and
+ * duo_attn_decode_int8 of that token's queries, in one launch (see duo_attn_append_decode). The
+ * work item that writes the token quantizes it exactly as kv_append_circular_int8 does (the same
+ * codes and scale bits). Arguments: those of duo_attn_append_decode, with the int8 pools and
+ * their scale pools (written at the token's slot). Errors: as duo_attn_append_decode and
+ * duo_attn_decode_int8.
+ */
+int32_t duo_attn_append_decode_int8(const void* q, const void* k_new, const void* v_new,
+                                    int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                                    const int32_t* block_table, int32_t num_blocks,
+                                    int32_t block_size, int32_t max_blocks_per_head,
+                                    const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t dtype,
+                                    const uint8_t* head_is_retrieval, int32_t sink_size,
+                                    int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    int32_t split_tokens, void* stream);
 
 /*
  * The 4-bit cache -- the same paged, per-head circular layout with 4-bit codes and one fp32 scale

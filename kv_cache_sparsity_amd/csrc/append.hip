@@ -148,13 +148,6 @@ __device__ __forceinline__ float elem_to_f32(uint32_t bits, int dtype) {
   }
 }
 
-// Symmetric int8 code of x for a row whose largest magnitude is amax > 0: x * (127 / amax), both
-// operations correctly rounded fp32, rounded half to even and clamped to [-127, 127].
-__device__ __forceinline__ int32_t quant_code(float x, float inv) {
-  const float c = rintf(__fmul_rn(x, inv));
-  return (int32_t)fminf(fmaxf(c, -127.f), 127.f);
-}
-
 // int8 cache: every new K and V row is quantized with one fp32 scale, amax / 127 (0 for an all-zero
 // row, whose codes are 0), and its codes and scale go to the row's slot: codes into the pages (K
 // token-major, V channel-major, one byte per element) and the scale into k_scale / v_scale at

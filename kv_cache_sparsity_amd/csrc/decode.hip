@@ -74,6 +74,13 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_append_
   decode_body<T, D, false, false, false, decode_waves<D>(), true>(p, blockIdx.x, lds);
 }
 
+// Decode over the int8 cache with the fused append: the token is quantized as the int8 append does.
+template <typename T, int D>
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_append_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[DecodeLds<decode_waves<D>(), D>::kBytes];
+  decode_body<T, D, true, false, false, decode_waves<D>(), true>(p, blockIdx.x, lds);
+}
+
 // Decode over the int8 cache (one fp32 scale per slot for K and for V).
 template <typename T, int D>
 __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_kernel(const DecodeParams p) {
@@ -105,7 +112,10 @@ void launch_d(const DecodeParams& p, int quant, int grid, hipStream_t stream) {
       return;
     }
   }
-  if (quant == 8)
+  if (quant == 8 && p.k_new != nullptr)
+    hipExtLaunchKernelGGL((decode_int8_append_kernel<T, D>), dim3(grid),
+                          dim3(decode_waves<D>() * kWave), 0, stream, ev.start, ev.stop, 0, p);
+  else if (quant == 8)
     hipExtLaunchKernelGGL((decode_int8_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave), 0,
                           stream, ev.start, ev.stop, 0, p);
   else if (p.k_new != nullptr)

@@ -183,11 +183,40 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D;
       const T* kn = static_cast<const T*>(p.k_new) + src;
       const T* vn = static_cast<const T*>(p.v_new) + src;
-      T* kdst = static_cast<T*>(const_cast<void*>(p.k_pool)) + ((page << p.log2_bs) + row) * D;
-      T* vdst = static_cast<T*>(const_cast<void*>(p.v_pool)) + ((page * D) << p.log2_bs) + row;
-      for (int d = (int)threadIdx.x; d < D; d += kThreads) {
-        kdst[d] = kn[d];
-        vdst[(int64_t)d << p.log2_bs] = vn[d];
+      if constexpr (Q8) {
+        // the int8 append's arithmetic (quant_code): wave 0 quantizes the K row, wave 1 the V row;
+        // codes into the pages (K token-major, V channel-major), the row's scale amax / 127 into
+        // k_scale / v_scale at [page][row]
+        if (wave < 2) {
+          const T* x_row = wave == 0 ? kn : vn;
+          float x[D / kWave];
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < D / kWave; ++i) {
+            x[i] = (float)x_row[lane + kWave * i];
+            amax = fmaxf(amax, fabsf(x[i]));
+          }
+          amax = wave_max(amax);
+          const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
+          int8_t* codes = static_cast<int8_t*>(const_cast<void*>(wave == 0 ? p.k_pool : p.v_pool));
+#pragma unroll
+          for (int i = 0; i < D / kWave; ++i) {
+            const int d = lane + kWave * i;
+            const int64_t at = wave == 0 ? ((page << p.log2_bs) + row) * D + d
+                                         : ((page * D + d) << p.log2_bs) + row;
+            codes[at] = (int8_t)quant_code(x[i], inv);
+          }
+          if (lane == 0)
+            const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale)[(page << p.log2_bs) + row] =
+                amax > 0.f ? __fdiv_rn(amax, 127.f) : 0.f;
+        }
+      } else {
+        T* kdst = static_cast<T*>(const_cast<void*>(p.k_pool)) + ((page << p.log2_bs) + row) * D;
+        T* vdst = static_cast<T*>(const_cast<void*>(p.v_pool)) + ((page * D) << p.log2_bs) + row;
+        for (int d = (int)threadIdx.x; d < D; d += kThreads) {
+          kdst[d] = kn[d];
+          vdst[(int64_t)d << p.log2_bs] = vn[d];
+        }
       }
       wait_stores_complete();   // the token is in place before any key of the item is read
       __syncthreads();

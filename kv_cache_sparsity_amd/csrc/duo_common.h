@@ -56,6 +56,15 @@ __device__ __forceinline__ v8<T> zero8() {
 // fp32 -> element, round to nearest even (hardware conversions on gfx950).
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return T(x); }
 
+// Symmetric int8 code of x for a row whose largest magnitude is amax > 0, with inv = 127 / amax
+// (correctly rounded): x * inv correctly rounded fp32, rounded half to even and clamped to
+// [-127, 127]. The row's scale is amax / 127, correctly rounded (0 and codes 0 for an all-zero
+// row). Shared by the int8 append and the decode's fused append, which must store the same bits.
+__device__ __forceinline__ int32_t quant_code(float x, float inv) {
+  const float c = rintf(__fmul_rn(x, inv));
+  return (int32_t)fminf(fmaxf(c, -127.f), 127.f);
+}
+
 // Eight int8 codes (8 consecutive bytes, 8-byte aligned) streamed past the caches, as two words.
 __device__ __forceinline__ u32x2 load_codes8_stream(const int8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
