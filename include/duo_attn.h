@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_ABI_VERSION 14
+#define DUO_ATTN_ABI_VERSION 15
 
 typedef enum { DUO_F32 = 0, DUO_F16 = 1, DUO_BF16 = 2 } duo_dtype_t;
 
@@ -449,6 +449,27 @@ int32_t duo_attn_decode_int4(const void* q, const uint8_t* k_pool, const uint8_t
                              int32_t recent_size, int32_t ring_blocks, float softmax_scale,
                              void* out, void* workspace, size_t workspace_bytes,
                              int32_t split_tokens, void* stream);
+
+/*
+ * duo_attn_append_decode_int4 -- kv_append_circular_int4 of one token per sequence and
+ * duo_attn_decode_int4 of that token's queries, in one launch (see duo_attn_append_decode). The
+ * work item that writes the token quantizes it exactly as kv_append_circular_int4 does (the same
+ * code bits): the K row's words whole, and for V each channel's 4-bit field of the token's slot
+ * merged into its word (no other item of the launch changes that word's other fields). Arguments:
+ * those of duo_attn_append_decode, with the 4-bit pools and the per-(kv head, channel) scales.
+ * Errors: as duo_attn_append_decode and duo_attn_decode_int4.
+ */
+int32_t duo_attn_append_decode_int4(const void* q, const void* k_new, const void* v_new,
+                                    uint8_t* k_pool, uint8_t* v_pool, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_table,
+                                    int32_t num_blocks, int32_t block_size,
+                                    int32_t max_blocks_per_head, const int32_t* seq_lens_before,
+                                    int32_t* seq_lens_after, int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                    const uint8_t* head_is_retrieval, int32_t sink_size,
+                                    int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    int32_t split_tokens, void* stream);
 
 /*
  * Dual Chunk Attention -- the prefill and decode of the vLLM PR "[Model] Implement DualChunkAttention

@@ -26,7 +26,8 @@ DUO_F32, DUO_F16, DUO_BF16 = 0, 1, 2
 STATUS = {0: "DUO_OK", 1: "DUO_ERR_INVALID_ARG", 2: "DUO_ERR_UNSUPPORTED", 3: "DUO_ERR_CAPACITY",
           4: "DUO_ERR_WORKSPACE", 5: "DUO_ERR_HIP"}
 SYMBOLS = ("kv_append_circular", "duo_attn_decode_workspace_size", "duo_attn_decode",
-           "duo_attn_append_decode", "duo_attn_append_decode_int8", "duo_attn_decode_noalloc",
+           "duo_attn_append_decode", "duo_attn_append_decode_int8", "duo_attn_append_decode_int4",
+           "duo_attn_decode_noalloc",
            "duo_attn_prefill_workspace_size", "duo_attn_prefill", "duo_attn_prefill_varlen", "duo_attn_prefill_varlen_workspace_size",
            "kv_append_circular_int8", "kv_append_circular_int4", "duo_attn_decode_int4",
            "duo_attn_decode_int8", "dca_attn_prefill_workspace_size", "dca_attn_prefill",
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.duo_attn_append_decode_int8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                   _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                                                   _I32, _I32, _F, _P, _P, _SZ, _I32, _P]
+        L.duo_attn_append_decode_int4.restype = _I32
+        L.duo_attn_append_decode_int4.argtypes = L.duo_attn_append_decode_int8.argtypes
         L.kv_append_circular_int4.restype = _I32
         L.kv_append_circular_int4.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
                                               _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
@@ -586,6 +589,40 @@ def kv_append_circular_int4(k_pool, v_pool, k_scale, v_scale, block_table, k_new
     _check("kv_append_circular_int4", st)
 
 
+def duo_attn_append_decode_int4(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table,
+                                seq_lens_before, seq_lens_after, head_is_retrieval, sink_size: int,
+                                recent_size: int, ring_blocks: int, softmax_scale: float, out,
+                                workspace, split_tokens: int = 0, stream=None) -> None:
+    """kv_append_circular_int4 of one token per sequence (k_new, v_new [batch][1][kv heads][D] in
+    q's dtype) and duo_attn_decode_int4 of its queries over seq_lens_before + 1 keys, in one
+    launch."""
+    num_blocks, block_size, head_dim = _int4_pools(k_pool, v_pool, k_scale, v_scale)
+    _check_tensor(q, "q", shape=(None, None, head_dim))
+    if q.device != k_pool.device:
+        _fail(f"q is on {q.device}, the pools on {k_pool.device}")
+    batch, num_q_heads, _ = q.shape
+    hkv = _kv_heads(block_table)
+    if int(k_scale.shape[0]) != hkv:
+        _fail(f"k_scale has {k_scale.shape[0]} kv heads, the block table {hkv}")
+    _check_tables(block_table, seq_lens_before, batch, hkv, q, "seq_lens_before")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _check_tensor(t, n, shape=(batch, 1, hkv, head_dim), like=q)
+    if seq_lens_after is not None:
+        _check_tensor(seq_lens_after, "seq_lens_after", dtype=_int32(), shape=(batch,), like=q)
+    _check_tensor(out, "out", shape=tuple(q.shape), like=q)
+    _check_workspace(workspace, q)
+    _check_gpu(q, "q")
+    mask = _HostMask(head_is_retrieval, hkv)
+    st = lib().duo_attn_append_decode_int4(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_table), num_blocks, block_size, block_table.shape[2],
+        _ptr(seq_lens_before), _ptr(seq_lens_after), batch, num_q_heads, hkv, head_dim,
+        _dtype_tag(q), mask.ptr, sink_size, recent_size, ring_blocks, softmax_scale, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), split_tokens,
+        _stream(stream))
+    _check("duo_attn_append_decode_int4", st)
+
+
 def duo_attn_decode_int4(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
                          head_is_retrieval, sink_size: int, recent_size: int, ring_blocks: int,
                          softmax_scale: float, out, workspace, split_tokens: int = 0,
@@ -697,7 +734,7 @@ def profile_next_launch(start_event=None, stop_event=None) -> None:
 
 
 __all__ = ["kv_append_circular", "duo_attn_decode", "duo_attn_append_decode",
-           "duo_attn_append_decode_int8", "duo_attn_prefill",
+           "duo_attn_append_decode_int8", "duo_attn_append_decode_int4", "duo_attn_prefill",
            "duo_attn_decode_noalloc",
            "NOALLOC_SCRATCH_BYTES",
            "kv_append_circular_int8", "duo_attn_decode_int8", "duo_attn_prefill_varlen",

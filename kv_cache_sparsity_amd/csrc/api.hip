@@ -337,8 +337,7 @@ struct AppendArgs {
 
 // The decode behind the three caches (quant 0: 16-bit or fp32, 8: int8 codes + per-slot scales,
 // 4: 4-bit codes + per-(kv head, channel) scales); dca != nullptr: Dual Chunk Attention (16-bit
-// cache, full heads); app != nullptr: the token at position seq_lens[b] is appended first (quant 0
-// or 8, no dca).
+// cache, full heads); app != nullptr: the token at position seq_lens[b] is appended first (no dca).
 static int32_t decode_impl(int quant, const void* q, const void* k_pool, const void* v_pool,
                            const float* k_scale, const float* v_scale, const int32_t* block_table,
                            int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_head,
@@ -360,7 +359,7 @@ static int32_t decode_impl(int quant, const void* q, const void* k_pool, const v
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return DUO_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return DUO_ERR_INVALID_ARG;
   if (app != nullptr) {
-    if ((quant != 0 && quant != 8) || dca != nullptr) return DUO_ERR_UNSUPPORTED;
+    if (dca != nullptr) return DUO_ERR_UNSUPPORTED;
     if (!app->k_new || !app->v_new || !aligned(app->k_new, 16) || !aligned(app->v_new, 16))
       return DUO_ERR_INVALID_ARG;
     // the lengths are read by every work item while one item per sequence writes the new ones
@@ -547,6 +546,25 @@ int32_t duo_attn_decode_int8(const void* q, const int8_t* k_pool, const int8_t* 
                      block_size, max_blocks_per_head, seq_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
                      softmax_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+int32_t duo_attn_append_decode_int4(const void* q, const void* k_new, const void* v_new,
+                                    uint8_t* k_pool, uint8_t* v_pool, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_table,
+                                    int32_t num_blocks, int32_t block_size,
+                                    int32_t max_blocks_per_head, const int32_t* seq_lens_before,
+                                    int32_t* seq_lens_after, int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                    const uint8_t* head_is_retrieval, int32_t sink_size,
+                                    int32_t recent_size, int32_t ring_blocks, float softmax_scale,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    int32_t split_tokens, void* stream) {
+  const AppendArgs app{k_new, v_new, seq_lens_after};
+  return decode_impl(4, q, k_pool, v_pool, k_scale, v_scale, block_table, num_blocks, block_size,
+                     max_blocks_per_head, seq_lens_before, batch, num_q_heads, num_kv_heads,
+                     head_dim, dtype, head_is_retrieval, sink_size, recent_size, ring_blocks,
+                     softmax_scale, out, workspace, workspace_bytes, split_tokens, stream, nullptr,
+                     false, &app);
 }
 
 int32_t duo_attn_decode_int4(const void* q, const uint8_t* k_pool, const uint8_t* v_pool,

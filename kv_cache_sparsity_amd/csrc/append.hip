@@ -250,18 +250,6 @@ __global__ void __launch_bounds__(kAppendThreads) append_int8_kernel(const Appen
   }
 }
 
-// 4-bit code of x with a per-channel scale s (0 -> code 0): x / s correctly rounded, rounded half
-// to even and clamped to [-7, 7]; stored as u = code + 8.
-__device__ __forceinline__ uint32_t quant4_u(float x, float s) {
-  if (!(s > 0.f)) return 8u;
-  const float c = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -7.f), 7.f);
-  return (uint32_t)((int32_t)c + 8);
-}
-
-// Position of element e (0..7) of a run of 8 codes in its 32-bit word: even elements in the low
-// half, odd ones in the high half, 4 bits each, the first lowest.
-__device__ __forceinline__ int nibble_shift(int e) { return (e & 1) * 16 + (e >> 1) * 4; }
-
 // 4-bit cache: every new K and V row is quantized with the static scales of its kv head
 // (k_scale, v_scale [num_kv_heads][head_dim]). K rows (head_dim / 8 words, token-major) are written
 // whole. A V page row holds the block_size codes of one channel, 8 tokens to a word, so a token

@@ -81,6 +81,13 @@ __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_ap
   decode_body<T, D, true, false, false, decode_waves<D>(), true>(p, blockIdx.x, lds);
 }
 
+// Decode over the 4-bit cache with the fused append (the 4-bit append's codes).
+template <typename T, int D>
+__global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int4_append_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[DecodeLds<decode_waves<D>(), D>::kBytes];
+  decode_body<T, D, false, false, true, decode_waves<D>(), true>(p, blockIdx.x, lds);
+}
+
 // Decode over the int8 cache (one fp32 scale per slot for K and for V).
 template <typename T, int D>
 __global__ void __launch_bounds__((decode_waves<D>() * kWave), 1) decode_int8_kernel(const DecodeParams p) {
@@ -107,8 +114,12 @@ void launch_d(const DecodeParams& p, int quant, int grid, hipStream_t stream) {
   const LaunchEvents ev = current_launch_events();
   if constexpr (!std::is_same<T, float>::value) {
     if (quant == 4) {
-      hipExtLaunchKernelGGL((decode_int4_kernel<T, D>), dim3(grid), dim3(decode_waves<D>() * kWave),
-                            0, stream, ev.start, ev.stop, 0, p);
+      if (p.k_new != nullptr)
+        hipExtLaunchKernelGGL((decode_int4_append_kernel<T, D>), dim3(grid),
+                              dim3(decode_waves<D>() * kWave), 0, stream, ev.start, ev.stop, 0, p);
+      else
+        hipExtLaunchKernelGGL((decode_int4_kernel<T, D>), dim3(grid),
+                              dim3(decode_waves<D>() * kWave), 0, stream, ev.start, ev.stop, 0, p);
       return;
     }
   }

@@ -210,6 +210,28 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
             const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale)[(page << p.log2_bs) + row] =
                 amax > 0.f ? __fdiv_rn(amax, 127.f) : 0.f;
         }
+      } else if constexpr (Q4) {
+        // the 4-bit append's arithmetic (quant4_u, the kv head's channel scales): the K row's
+        // D / 8 words whole; for V, each channel's nibble of the token's slot merged into its word
+        // by a plain read-modify-write (in this launch no other item changes the word's other
+        // nibbles, and every item that writes the token writes the same bits)
+        const float* ksc = p.k_scale + (int64_t)h * D;
+        const float* vsc = p.v_scale + (int64_t)h * D;
+        uint32_t* kw = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(const_cast<void*>(p.k_pool)) +
+                                                   ((page << p.log2_bs) + row) * (D / 2));
+        uint32_t* vw = static_cast<uint32_t*>(const_cast<void*>(p.v_pool));
+        for (int j = (int)threadIdx.x; j < D / 8; j += kThreads) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            word |= quant4_u((float)kn[8 * j + e], ksc[8 * j + e]) << nibble_shift(e);
+          kw[j] = word;
+        }
+        const int sh = nibble_shift(row & 7);
+        for (int d = (int)threadIdx.x; d < D; d += kThreads) {
+          uint32_t* w = vw + ((((page * D + d) << p.log2_bs) + row) >> 3);
+          *w = (*w & ~(0xFu << sh)) | (quant4_u((float)vn[d], vsc[d]) << sh);
+        }
       } else {
         T* kdst = static_cast<T*>(const_cast<void*>(p.k_pool)) + ((page << p.log2_bs) + row) * D;
         T* vdst = static_cast<T*>(const_cast<void*>(p.v_pool)) + ((page * D) << p.log2_bs) + row;

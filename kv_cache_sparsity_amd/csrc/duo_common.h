@@ -65,6 +65,19 @@ __device__ __forceinline__ int32_t quant_code(float x, float inv) {
   return (int32_t)fminf(fmaxf(c, -127.f), 127.f);
 }
 
+// 4-bit code of x with a per-channel scale s (0 -> code 0): x / s correctly rounded, rounded half
+// to even and clamped to [-7, 7]; stored as u = code + 8. Shared by the 4-bit append and the
+// decode's fused append.
+__device__ __forceinline__ uint32_t quant4_u(float x, float s) {
+  if (!(s > 0.f)) return 8u;
+  const float c = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -7.f), 7.f);
+  return (uint32_t)((int32_t)c + 8);
+}
+
+// Position of element e (0..7) of a run of 8 codes in its 32-bit word: even elements in the low
+// half, odd ones in the high half, 4 bits each, the first lowest.
+__device__ __forceinline__ int nibble_shift(int e) { return (e & 1) * 16 + (e >> 1) * 4; }
+
 // Eight int8 codes (8 consecutive bytes, 8-byte aligned) streamed past the caches, as two words.
 __device__ __forceinline__ u32x2 load_codes8_stream(const int8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));

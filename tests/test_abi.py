@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert duo.abi_version() == 14
+    assert duo.abi_version() == 15
     with open(os.path.join(ROOT, "include", "duo_attn.h")) as fh:
         assert f"#define DUO_ATTN_ABI_VERSION {duo.abi_version()}" in fh.read()
     assert duo.status_string(0) == "ok"
@@ -162,6 +162,29 @@ def append_decode_int8(**kw):
 ])
 def test_append_decode_int8_rejects(kw, status):
     assert append_decode_int8(**kw) == status
+
+
+def append_decode_int4(**kw):
+    a = dict(q=FAKE, k_new=FAKE + 4096, v_new=FAKE + 8192, k_pool=FAKE, v_pool=FAKE,
+             ks=FAKE + 12288, vs=FAKE + 16384, table=FAKE, num_blocks=64, bs=16, mbph=20,
+             before=FAKE, after=LENS_AFTER, batch=2, hq=8, hkv=2, d=128, dtype=2,
+             mask=ctypes.cast(MASK_RS, ctypes.c_void_p), sink=4, recent=16, rb=2, scale=0.1,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30, split=0)
+    a.update(kw)
+    return duo.lib().duo_attn_append_decode_int4(
+        a["q"], a["k_new"], a["v_new"], a["k_pool"], a["v_pool"], a["ks"], a["vs"], a["table"],
+        a["num_blocks"], a["bs"], a["mbph"], a["before"], a["after"], a["batch"], a["hq"],
+        a["hkv"], a["d"], a["dtype"], a["mask"], a["sink"], a["recent"], a["rb"], a["scale"],
+        a["out"], a["ws"], a["ws_bytes"], a["split"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v_new=None), INVALID), (dict(ks=None), INVALID), (dict(after=FAKE), INVALID),
+    (dict(dtype=0), UNSUPPORTED), (dict(d=80), UNSUPPORTED), (dict(recent=33), CAPACITY),
+    (dict(ws=None), WORKSPACE),
+])
+def test_append_decode_int4_rejects(kw, status):
+    assert append_decode_int4(**kw) == status
 
 
 # ---- varlen prefill ---------------------------------------------------------------------------

@@ -1,7 +1,7 @@
-"""duo_attn_append_decode and duo_attn_append_decode_int8, through the C ABI: the fused append of
-one token per sequence and the decode of its queries, against the two calls each stands for
-(kv_append_circular[_int8], then duo_attn_decode[_int8] over seq_lens + 1) on twin caches, and
-against the oracle.
+"""duo_attn_append_decode and its int8 and 4-bit forms, through the C ABI: the fused append of one
+token per sequence and the decode of its queries, against the two calls each stands for
+(kv_append_circular[_int8|_int4], then duo_attn_decode[_int8|_int4] over seq_lens + 1) on twin
+caches, and against the oracle.
 
 Bars: pools bit-exact against the two calls (the token lands in the same slot with the same bits,
 and nothing else changes); lengths after the call exact; outputs within the usual bound of the
@@ -18,6 +18,7 @@ import oracle
 import synth
 from tests.gpu_harness import (Cache, check_close, logical_kv, oracle_decode, q_decode, say, to_dev,
                                to_host_bits, to_host_f64, TOL)
+from tests.test_gpu_int4 import Int4Cache
 from tests.test_gpu_int8 import Int8Cache, _logical_codes
 from tests.test_gpu_parity import _append_per_sequence
 
@@ -207,6 +208,63 @@ def test_append_decode_int8_equals_append_then_decode(case, split_tokens):
         got = to_host_f64(out_f, w.dtype)
         want = oracle.attend_int8(q_bits[:, None], kc, ks, vc, vs, lens, fused.mask, sink=w.sink,
                                   recent=w.recent, scale=w.scale, dtype=w.dtype,
+                                  block_size=w.block_size)[:, 0]
+        check_close(got, want, w.dtype, f"{case['name']} step {step}")
+        assert float(np.abs(got - to_host_f64(out_s, w.dtype)).max()) <= TOL[w.dtype]
+
+
+INT4_CASES = [
+    dict(name="int4-bf16-d128-g4-mixed", dtype=synth.BF16, head_dim=128, group=4, kv=4, ret=(0, 2),
+         block_size=16, sink=4, recent=40, ring_blocks=3, lens=[0, 15, 47, 300, 1000]),
+    dict(name="int4-f16-d256-g8", dtype=synth.F16, head_dim=256, group=8, kv=1, ret=(0,),
+         block_size=16, sink=16, recent=100, ring_blocks=8, lens=[99, 700]),
+    dict(name="int4-bf16-d64-bs64", dtype=synth.BF16, head_dim=64, group=2, kv=2, ret=(1,),
+         block_size=64, sink=9, recent=70, ring_blocks=2, lens=[8, 63, 64, 65, 500]),
+]
+
+
+@pytest.mark.parametrize("split_tokens", [0, 128])
+@pytest.mark.parametrize("case", INT4_CASES, ids=[c["name"] for c in INT4_CASES])
+def test_append_decode_int4_equals_append_then_decode(case, split_tokens):
+    say(f"append+decode 4-bit {case['name']} split {split_tokens}")
+    lens = np.asarray(case["lens"])
+    Lmax = int(lens.max()) + STEPS
+    w = synth.small(case["name"], batch=len(lens), q_heads=case["kv"] * case["group"],
+                    kv_heads=case["kv"], head_dim=case["head_dim"], dtype=case["dtype"],
+                    block_size=case["block_size"], sink=case["sink"], recent=case["recent"],
+                    retrieval=case["ret"], context=Lmax, ring_blocks=case["ring_blocks"], seed=74)
+    K = logical_kv(w, Lmax, synth.S_K)
+    V = logical_kv(w, Lmax, synth.S_V)
+    fused, split = Int4Cache(w), Int4Cache(w)
+    kc, vc = fused.logical_codes(K, V)
+    fused.fill_per_sequence(K, V, lens)
+    split.fill_per_sequence(K, V, lens)
+    for step in range(STEPS):
+        q_bits = q_decode(w, step)
+        q = to_dev(q_bits, w.dtype)
+        k_new, v_new = _token(w, K, lens), _token(w, V, lens)
+        before = torch.from_numpy(lens.astype(np.int32)).cuda()
+        after_f, after_s = torch.full_like(before, -1), torch.full_like(before, -1)
+        out_f, out_s = torch.empty_like(q), torch.empty_like(q)
+        duo.duo_attn_append_decode_int4(
+            q, k_new, v_new, fused.k_pool, fused.v_pool, fused.k_scale, fused.v_scale, fused.table,
+            before, after_f, fused.mask, w.sink, w.recent, w.ring_blocks, w.scale, out_f,
+            duo.decode_workspace(q, fused.table, w.block_size, split_tokens), split_tokens)
+        duo.kv_append_circular_int4(split.k_pool, split.v_pool, split.k_scale, split.v_scale,
+                                    split.table, k_new, v_new, before, after_s, split.mask, w.sink,
+                                    w.recent, w.ring_blocks)
+        duo.duo_attn_decode_int4(q, split.k_pool, split.v_pool, split.k_scale, split.v_scale,
+                                 split.table, after_s, split.mask, w.sink, w.recent, w.ring_blocks,
+                                 w.scale, out_s,
+                                 duo.decode_workspace(q, split.table, w.block_size, split_tokens),
+                                 split_tokens)
+        torch.cuda.synchronize()
+        lens = lens + 1
+        assert (after_f.cpu().numpy() == lens).all(), after_f
+        assert torch.equal(fused.k_pool, split.k_pool) and torch.equal(fused.v_pool, split.v_pool)
+        got = to_host_f64(out_f, w.dtype)
+        want = oracle.attend_int4(q_bits[:, None], kc, vc, fused.ks_h, fused.vs_h, lens, fused.mask,
+                                  sink=w.sink, recent=w.recent, scale=w.scale, dtype=w.dtype,
                                   block_size=w.block_size)[:, 0]
         check_close(got, want, w.dtype, f"{case['name']} step {step}")
         assert float(np.abs(got - to_host_f64(out_s, w.dtype)).max()) <= TOL[w.dtype]
