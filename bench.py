@@ -471,27 +471,25 @@ def decode_quant_leg(args, torch, duo, dec, bits: int):
     kern_all = sample_kernels(torch, step, args.warmup + args.steps, KERNEL_SAMPLES, args.flush)
     kern_s = float(np.mean(kern_all))
     nbytes = decode_bytes(w, np.full(w.batch, L), int8_cache=bits == 8, int4_cache=bits == 4)
-    fused = None
-    if bits == 8:
-        # the same step as one launch (duo_attn_append_decode_int8), back to back
-        lens_fused = torch.empty_like(lens_before)
+    # the same step as one launch (duo_attn_append_decode_int8 / _int4), back to back
+    fused_call = duo.duo_attn_append_decode_int8 if bits == 8 else duo.duo_attn_append_decode_int4
+    lens_fused = torch.empty_like(lens_before)
 
-        def fused_step(i):
-            pools = layers[i % len(layers)]
-            duo.duo_attn_append_decode_int8(q, k_tok, v_tok, *pools, table, lens_before,
-                                            lens_fused, mask, w.sink, w.recent, w.ring_blocks,
-                                            w.scale, out, ws)
+    def fused_step(i):
+        pools = layers[i % len(layers)]
+        fused_call(q, k_tok, v_tok, *pools, table, lens_before, lens_fused, mask, w.sink, w.recent,
+                   w.ring_blocks, w.scale, out, ws)
 
-        for i in range(args.warmup):
-            fused_step(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            fused_step(args.warmup + i)
-        torch.cuda.synchronize()
-        fused_s = (time.perf_counter() - t0) / args.steps
-        fused = {"call": "duo_attn_append_decode_int8 (1 token/seq, one launch)",
-                 "us_per_step": round(fused_s * 1e6, 2), "GB/s": round(nbytes / fused_s / 1e9, 1)}
+    for i in range(args.warmup):
+        fused_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused_step(args.warmup + i)
+    torch.cuda.synchronize()
+    fused_s = (time.perf_counter() - t0) / args.steps
+    fused = {"call": f"duo_attn_append_decode_int{bits} (1 token/seq, one launch)",
+             "us_per_step": round(fused_s * 1e6, 2), "GB/s": round(nbytes / fused_s / 1e9, 1)}
     res = {
         "workload": w.name + f"-int{bits}-kv", "value": round(nbytes / step_s / 1e9, 1),
         "unit": "GB/s", "ms_per_step": round(step_s * 1e3, 4),
@@ -508,8 +506,7 @@ def decode_quant_leg(args, torch, duo, dec, bits: int):
                      "cold": f"{FLUSH_BYTES >> 20} MiB read before each sampled launch",
                      "algorithmic_bytes_per_launch": nbytes},
     }
-    if fused is not None:
-        res["fused_step"] = fused
+    res["fused_step"] = fused
     log(f"[{tag}] step {step_s * 1e6:.1f} us, kernel {kern_s * 1e6:.1f} us, "
         f"{res['value']:.0f} GB/s per step, {nbytes / kern_s / 1e9:.0f} GB/s kernel, "
         f"{res['step_speedup_vs_bf16']}x the bf16 step")
