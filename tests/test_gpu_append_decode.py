@@ -268,3 +268,73 @@ def test_append_decode_int4_equals_append_then_decode(case, split_tokens):
                                   block_size=w.block_size)[:, 0]
         check_close(got, want, w.dtype, f"{case['name']} step {step}")
         assert float(np.abs(got - to_host_f64(out_s, w.dtype)).max()) <= TOL[w.dtype]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("bits", [16, 8, 4])
+def test_llama3_8b_append_decode_batch8_ctx32768(bits):
+    """The fused call at the full Llama-3-8B decode shape (batch 8, 32768 tokens, 32 q heads over 8
+    kv heads, half of them retrieval), in the launch configuration the benchmark times: the cache
+    holds 32767 tokens, the call appends the 32768th and attends over all of them. Pools against
+    the standalone append on a copy of the same pools, bit for bit; outputs against the oracle."""
+    w = synth.llama3_8b_decode()
+    say(f"workload {w.name}, append+decode, {bits}-bit cache" if bits < 16
+        else f"workload {w.name}, append+decode")
+    L = w.context
+    K = logical_kv(w, L, synth.S_K)
+    V = logical_kv(w, L, synth.S_V)
+    lens = np.full(w.batch, L - 1)
+    if bits == 16:
+        cache = Cache(w, fill="nan")
+        cache.append_logical(K, V, 0, L - 1, chunk=8192)
+    else:
+        cache = Int8Cache(w) if bits == 8 else Int4Cache(w)
+        cache.fill_per_sequence(K, V, lens)
+    scales = [] if bits == 16 else [cache.k_scale, cache.v_scale]
+    twin = [t.clone() for t in [cache.k_pool, cache.v_pool] + scales]
+    q_bits = q_decode(w, 0)
+    q = to_dev(q_bits, w.dtype)
+    k_new, v_new = _token(w, K, lens), _token(w, V, lens)
+    before = torch.from_numpy(lens.astype(np.int32)).cuda()
+    after_f, after_s = torch.full_like(before, -1), torch.full_like(before, -1)
+    out_f, out_s = torch.empty_like(q), torch.empty_like(q)
+    ws = duo.decode_workspace(q, cache.table, w.block_size)
+    common = (w.sink, w.recent, w.ring_blocks)
+    if bits == 16:
+        duo.duo_attn_append_decode(q, k_new, v_new, cache.k_pool, cache.v_pool, cache.table, before,
+                                   after_f, cache.mask, *common, w.scale, out_f, ws)
+        duo.kv_append_circular(*twin, cache.table, k_new, v_new, before, after_s, cache.mask,
+                               *common)
+        torch.cuda.synchronize()
+        duo.duo_attn_decode(q, *twin, cache.table, after_s, cache.mask, *common, w.scale, out_s, ws)
+    else:
+        fused = duo.duo_attn_append_decode_int8 if bits == 8 else duo.duo_attn_append_decode_int4
+        append = duo.kv_append_circular_int8 if bits == 8 else duo.kv_append_circular_int4
+        decode = duo.duo_attn_decode_int8 if bits == 8 else duo.duo_attn_decode_int4
+        fused(q, k_new, v_new, cache.k_pool, cache.v_pool, cache.k_scale, cache.v_scale,
+              cache.table, before, after_f, cache.mask, *common, w.scale, out_f, ws)
+        append(*twin, cache.table, k_new, v_new, before, after_s, cache.mask, *common)
+        torch.cuda.synchronize()
+        decode(q, *twin, cache.table, after_s, cache.mask, *common, w.scale, out_s, ws)
+    torch.cuda.synchronize()
+    assert (after_f.cpu().numpy() == L).all() and (after_s.cpu().numpy() == L).all()
+    for a, b in zip([cache.k_pool, cache.v_pool] + scales, twin):
+        if a.dtype == torch.float32:
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        else:
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    got = to_host_f64(out_f, w.dtype)
+    full = np.full(w.batch, L)
+    if bits == 16:
+        want = oracle_decode(w, q_bits, K, V, full, cache.mask)
+    elif bits == 8:
+        kc, ks, vc, vs = _logical_codes(K, V, w.dtype)
+        want = oracle.attend_int8(q_bits[:, None], kc, ks, vc, vs, full, cache.mask, sink=w.sink,
+                                  recent=w.recent, scale=w.scale, dtype=w.dtype)[:, 0]
+    else:
+        kc, vc = cache.logical_codes(K, V)
+        want = oracle.attend_int4(q_bits[:, None], kc, vc, cache.ks_h, cache.vs_h, full,
+                                  cache.mask, sink=w.sink, recent=w.recent, scale=w.scale,
+                                  dtype=w.dtype)[:, 0]
+    check_close(got, want, w.dtype, f"{w.name} append+decode {bits}-bit")
+    assert float(np.abs(got - to_host_f64(out_s, w.dtype)).max()) <= TOL[w.dtype]
