@@ -160,6 +160,46 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       pre[j] = v < nr ? pack_run(geo.page_of(slot), geo.row0(slot)) : 0;
     }
   }
+  // APPEND: the call's token of (b, h) does not depend on the length either: its elements (and the
+  // 4-bit channel scales) are loaded before it, into the registers the writing item stores from.
+  // One element per thread (D <= kThreads); the int8 quantizer takes the K row in wave 0 and the V
+  // row in wave 1, D / kWave elements a lane; the 4-bit K words take 8 elements a thread.
+  [[maybe_unused]] T tok_k = T(), tok_v = T();
+  [[maybe_unused]] T tok_k8[8];
+  [[maybe_unused]] float tok_x[D / kWave];
+  [[maybe_unused]] float tok_ks[8], tok_vs = 0.f;
+  if constexpr (APPEND) {
+    static_assert(D <= kThreads, "one token element per thread");
+    const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D;
+    const T* kn = static_cast<const T*>(p.k_new) + src;
+    const T* vn = static_cast<const T*>(p.v_new) + src;
+    const int d = (int)threadIdx.x;
+    if constexpr (Q8) {
+      if (wave < 2) {
+        const T* x_row = wave == 0 ? kn : vn;
+#pragma unroll
+        for (int i = 0; i < D / kWave; ++i) tok_x[i] = (float)x_row[lane + kWave * i];
+      }
+    } else if constexpr (Q4) {
+      if (d < D / 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          tok_k8[e] = kn[8 * d + e];
+          tok_ks[e] = p.k_scale[(int64_t)h * D + 8 * d + e];
+        }
+      }
+      if (d < D) {
+        tok_v = vn[d];
+        tok_vs = p.v_scale[(int64_t)h * D + d];
+      }
+    } else {
+      if (d < D) {
+        tok_k = kn[d];
+        tok_v = vn[d];
+      }
+    }
+  }
+  [[maybe_unused]] bool wrote = false;   // APPEND: this item stored the token
   int32_t L = max(p.seq_lens[b], 0);
   if constexpr (APPEND) {
     // The call's token of (b, h) goes to position t = L (the length before it), and every item of
@@ -178,33 +218,45 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
     const int32_t cap = p.max_blocks_per_head << p.log2_bs;
     if (ret ? (t < cap && t / p.split_tokens == split) : true) {
       const int32_t slot = (ret || t < p.sink) ? t : (p.sink_blocks << p.log2_bs) + (t - p.sink) % p.ring_slots;
-      const int64_t page = geo.page_of(slot);
-      const int32_t row = geo.row0(slot);
-      const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D;
-      const T* kn = static_cast<const T*>(p.k_new) + src;
-      const T* vn = static_cast<const T*>(p.v_new) + src;
+      int64_t page;
+      int32_t row;
+      // a retrieval split read its token run's table entry before the length (pre): the thread
+      // holding it passes it on through that run's cell of the page staging, which stores the
+      // same value there again (runs start at multiples of 16 slots, so the row is the run's
+      // first row plus t mod 16)
+      const int32_t vt = ret ? (t - split * p.split_tokens) >> 4 : kRunSeg;
+      if (vt < kRunSeg) {
+        if ((int)threadIdx.x == vt % kThreads) {
+#pragma unroll
+          for (int j = 0; j < kPre; ++j)
+            if (j == vt / kThreads) sm_page[vt] = pre[j];
+        }
+        __syncthreads();
+        const int32_t pr = sm_page[vt];
+        page = packed_page(pr);
+        row = packed_row0(pr) + (t & 15);
+      } else {
+        page = geo.page_of(slot);
+        row = geo.row0(slot);
+      }
+      const int d = (int)threadIdx.x;
       if constexpr (Q8) {
         // the int8 append's arithmetic (quant_code): wave 0 quantizes the K row, wave 1 the V row;
         // codes into the pages (K token-major, V channel-major), the row's scale amax / 127 into
         // k_scale / v_scale at [page][row]
         if (wave < 2) {
-          const T* x_row = wave == 0 ? kn : vn;
-          float x[D / kWave];
           float amax = 0.f;
 #pragma unroll
-          for (int i = 0; i < D / kWave; ++i) {
-            x[i] = (float)x_row[lane + kWave * i];
-            amax = fmaxf(amax, fabsf(x[i]));
-          }
+          for (int i = 0; i < D / kWave; ++i) amax = fmaxf(amax, fabsf(tok_x[i]));
           amax = wave_max(amax);
           const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
           int8_t* codes = static_cast<int8_t*>(const_cast<void*>(wave == 0 ? p.k_pool : p.v_pool));
 #pragma unroll
           for (int i = 0; i < D / kWave; ++i) {
-            const int d = lane + kWave * i;
-            const int64_t at = wave == 0 ? ((page << p.log2_bs) + row) * D + d
-                                         : ((page * D + d) << p.log2_bs) + row;
-            codes[at] = (int8_t)quant_code(x[i], inv);
+            const int dd = lane + kWave * i;
+            const int64_t at = wave == 0 ? ((page << p.log2_bs) + row) * D + dd
+                                         : ((page * D + dd) << p.log2_bs) + row;
+            codes[at] = (int8_t)quant_code(tok_x[i], inv);
           }
           if (lane == 0)
             const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale)[(page << p.log2_bs) + row] =
@@ -215,33 +267,30 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
         // D / 8 words whole; for V, each channel's nibble of the token's slot merged into its word
         // by a plain read-modify-write (in this launch no other item changes the word's other
         // nibbles, and every item that writes the token writes the same bits)
-        const float* ksc = p.k_scale + (int64_t)h * D;
-        const float* vsc = p.v_scale + (int64_t)h * D;
-        uint32_t* kw = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(const_cast<void*>(p.k_pool)) +
-                                                   ((page << p.log2_bs) + row) * (D / 2));
-        uint32_t* vw = static_cast<uint32_t*>(const_cast<void*>(p.v_pool));
-        for (int j = (int)threadIdx.x; j < D / 8; j += kThreads) {
+        if (d < D / 8) {
           uint32_t word = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            word |= quant4_u((float)kn[8 * j + e], ksc[8 * j + e]) << nibble_shift(e);
-          kw[j] = word;
+            word |= quant4_u((float)tok_k8[e], tok_ks[e]) << nibble_shift(e);
+          reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(const_cast<void*>(p.k_pool)) +
+                                      ((page << p.log2_bs) + row) * (D / 2))[d] = word;
         }
-        const int sh = nibble_shift(row & 7);
-        for (int d = (int)threadIdx.x; d < D; d += kThreads) {
-          uint32_t* w = vw + ((((page * D + d) << p.log2_bs) + row) >> 3);
-          *w = (*w & ~(0xFu << sh)) | (quant4_u((float)vn[d], vsc[d]) << sh);
+        if (d < D) {
+          const int sh = nibble_shift(row & 7);
+          uint32_t* w = static_cast<uint32_t*>(const_cast<void*>(p.v_pool)) +
+                        ((((page * D + d) << p.log2_bs) + row) >> 3);
+          *w = (*w & ~(0xFu << sh)) | (quant4_u((float)tok_v, tok_vs) << sh);
         }
       } else {
-        T* kdst = static_cast<T*>(const_cast<void*>(p.k_pool)) + ((page << p.log2_bs) + row) * D;
-        T* vdst = static_cast<T*>(const_cast<void*>(p.v_pool)) + ((page * D) << p.log2_bs) + row;
-        for (int d = (int)threadIdx.x; d < D; d += kThreads) {
-          kdst[d] = kn[d];
-          vdst[(int64_t)d << p.log2_bs] = vn[d];
+        if (d < D) {
+          T* kdst = static_cast<T*>(const_cast<void*>(p.k_pool)) + ((page << p.log2_bs) + row) * D;
+          T* vdst = static_cast<T*>(const_cast<void*>(p.v_pool)) + ((page * D) << p.log2_bs) + row;
+          kdst[d] = tok_k;
+          vdst[(int64_t)d << p.log2_bs] = tok_v;
         }
       }
-      wait_stores_complete();   // the token is in place before any key of the item is read
-      __syncthreads();
+      // the stores complete at the first page staging below, before any wave reads a key
+      wrote = true;
     }
   }
   if (ret) L = min(L, p.max_blocks_per_head << p.log2_bs);
@@ -464,6 +513,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int blk, char
       // runs past the end of the list read page 0 (valid memory, fully masked)
       for (int i = nseg + (int)threadIdx.x; i < nseg + kRunsPerStep; i += kThreads) sm_page[i] = 0;
       if (threadIdx.x == 0) sm_next_step = kDecodeWaves;
+      if constexpr (APPEND) {
+        // the token stored above is in place before any key of the item is read
+        if (seg0 == 0 && wrote) wait_stores_complete();
+      }
       __syncthreads();
       const int n_steps = (nseg + kRunsPerStep - 1) / kRunsPerStep;
       int step = wave;

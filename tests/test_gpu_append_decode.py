@@ -338,3 +338,20 @@ def test_llama3_8b_append_decode_batch8_ctx32768(bits):
                                   dtype=w.dtype)[:, 0]
     check_close(got, want, w.dtype, f"{w.name} append+decode {bits}-bit")
     assert float(np.abs(got - to_host_f64(out_s, w.dtype)).max()) <= TOL[w.dtype]
+
+
+LONG_CASE = dict(name="bf16-d128-g4-long-splits", dtype=synth.BF16, head_dim=128, group=4, kv=2,
+                 ret=(0,), block_size=16, sink=4, recent=40, ring_blocks=3,
+                 lens=[9000, 20000, 8191, 8192, 16383])
+
+
+@pytest.mark.parametrize("bits", [16, 4])
+def test_append_decode_with_splits_past_one_run_segment(bits):
+    """Splits of 16384 keys: a token more than 512 runs (8192 keys) into its split takes its page
+    from the block table after the length, the others from the entries the split read before it
+    (both kinds here, and tokens at the first and last run of a segment)."""
+    if bits == 16:
+        test_append_decode_equals_append_then_decode(LONG_CASE, 16384)
+    else:
+        test_append_decode_int4_equals_append_then_decode(dict(LONG_CASE, name="int4-long-splits"),
+                                                          16384)
